@@ -1,0 +1,204 @@
+"""CPU oracle for the low-precision MoE expert forward: ctypes wrapper.
+
+TEST INFRASTRUCTURE ONLY: only tests/, the smoke check and the benchmark's
+CPU-baseline leg import this package.  The product library never loads it.
+
+The arithmetic lives in moe_oracle.c (plain C, fp64 accumulation, OpenMP);
+this module only builds that file with gcc and marshals numpy arrays.
+Parity pins are in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile moe_oracle.c -> liboracle.so with gcc (IEEE semantics, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("oft_block", ctypes.c_int32), ("adapter_expert_stride", ctypes.c_int64)]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = ctypes.CDLL(build())
+            _lib.oracle_route.restype = ctypes.c_int
+            _lib.oracle_permute.restype = ctypes.c_int
+            _lib.oracle_forward.restype = ctypes.c_int
+            _lib.oracle_combine.restype = ctypes.c_int
+            _lib.oracle_lm_head_logprob.restype = ctypes.c_int
+            _lib.oracle_num_threads.restype = ctypes.c_int
+        return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def route(logits: np.ndarray, k: int):
+    """-> (topk_ids[T][k] int32, topk_w[T][k] float32)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    if lib().oracle_route(T, E, k, _p(logits), _p(ids), _p(w)) != 0:
+        raise ValueError("oracle_route: invalid arguments")
+    return ids, w
+
+
+def permute(ids: np.ndarray, E: int):
+    """-> dict(counts, offsets, sorted_rows, row_of, active) (int32 arrays)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    R = T * k
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sorted_rows = np.empty(R, np.int32)
+    row_of = np.empty(R, np.int32)
+    active = np.empty(E, np.int32)
+    na = ctypes.c_int32(0)
+    if lib().oracle_permute(T, E, k, _p(ids), _p(counts), _p(offsets), _p(sorted_rows), _p(row_of),
+                            _p(active), ctypes.byref(na)) != 0:
+        raise ValueError("oracle_permute: invalid ids")
+    return dict(counts=counts, offsets=offsets, sorted_rows=sorted_rows, row_of=row_of,
+                active=active[:na.value].copy())
+
+
+def decode(kind: str, codes: np.ndarray) -> np.ndarray:
+    """kind in bf16 | int4 | e4m3 | e2m1 | e8m0 -> float64 values."""
+    fmt = {"bf16": 0, "int4": 1, "e4m3": 2, "e2m1": 3, "e8m0": 4}[kind]
+    codes = _c(codes, np.uint16 if fmt == 0 else np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    lib().oracle_decode(fmt, ctypes.c_int64(codes.size), _p(codes), _p(out))
+    return out
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_encode_e4m3(ctypes.c_int64(v.size), _p(v), _p(out))
+    return out
+
+
+def quant_fp8(v: np.ndarray):
+    """[R][K] fp32 -> (codes [R][K] uint8, scales [R][K/128] fp32)."""
+    v = _c(v, np.float32)
+    R, K = v.shape
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R, K // 128), np.float32)
+    lib().oracle_quant_fp8(R, K, _p(v), _p(q), _p(s))
+    return q, s
+
+
+def quant_mxfp8(v: np.ndarray):
+    """[R][K] fp32 -> (codes [R][K] uint8, E8M0 scale bytes [R][K/32])."""
+    v = _c(v, np.float32)
+    R, K = v.shape
+    q = np.empty((R, K), np.uint8)
+    e = np.empty((R, K // 32), np.uint8)
+    lib().oracle_quant_mxfp8(R, K, _p(v), _p(q), _p(e))
+    return q, e
+
+
+def dequant(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One expert's packed [N][K] weights -> fp32 [N][K]."""
+    out = np.empty((N, K), np.float32)
+    lib().oracle_dequant(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), _p(out))
+    return out
+
+
+def forward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, chunk_experts=1,
+            tokens=None, adapter_expert_stride=None, return_y=False, return_routing=False):
+    """Oracle MoE expert forward.  x: [T][H] bf16 bits (uint16); logits [T][E] fp32;
+    weights/scales in the packed storage layouts; oft [E][H/32][32][32] bf16 bits
+    (or [H/32][32][32] with adapter_expert_stride=0) or None.
+    tokens: optional int array of token indices to compute (default: all).
+    Returns out [n][H] fp32 (+ y [n][k][H], + (ids, w) when requested)."""
+    layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0,
+                   (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride)
+    x = _c(x, np.uint16)
+    logits = _c(logits, np.float32)
+    w13 = _c(w13, np.uint8)
+    w2 = _c(w2, np.uint8)
+    s13 = np.ascontiguousarray(s13)
+    s2 = np.ascontiguousarray(s2)
+    oft_a = None if oft is None else _c(oft, np.uint16)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tok is None else len(tok)
+    out = np.empty((n, H), np.float32)
+    y = np.empty((n, k, H), np.float32) if return_y else None
+    ids = np.empty((T, k), np.int32) if return_routing else None
+    w = np.empty((T, k), np.float32) if return_routing else None
+    rc = lib().oracle_forward(ctypes.byref(layer), _p(x), _p(logits), _p(w13), _p(w2), _p(s13), _p(s2),
+                              _p(oft_a), int(chunk_experts), _p(tok), int(n), _p(out), _p(y), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("oracle_forward: invalid arguments")
+    res = [out]
+    if return_y:
+        res.append(y)
+    if return_routing:
+        res.append((ids, w))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def forward_inputs(li, chunk_experts=None, tokens=None, **kw):
+    """oracle forward on a synth.LayerInputs bundle."""
+    c = li.cfg
+    return forward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2,
+                   oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts,
+                   tokens=tokens, **kw)
+
+
+def combine(y_perm_bf16: np.ndarray, w: np.ndarray, row_of: np.ndarray) -> np.ndarray:
+    y = _c(y_perm_bf16, np.uint16)
+    w = _c(w, np.float32)
+    row_of = _c(row_of, np.int32)
+    T, k = w.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.float32)
+    lib().oracle_combine(T, k, H, _p(y), _p(w), _p(row_of), _p(out))
+    return out
+
+
+def lm_head_logprob(h: np.ndarray, w_lm_bf16: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    h = _c(h, np.float32)
+    w = _c(w_lm_bf16, np.uint16)
+    tg = _c(targets, np.int32)
+    T, H = h.shape
+    V = w.shape[0]
+    lp = np.empty(T, np.float32)
+    if lib().oracle_lm_head_logprob(T, H, V, _p(h), _p(w), _p(tg), _p(lp)) != 0:
+        raise ValueError("oracle_lm_head_logprob: target out of range")
+    return lp

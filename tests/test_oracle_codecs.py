@@ -1,0 +1,158 @@
+"""Pins of the oracle's codecs and activation quantizers (CPU only).
+
+Each check compares the oracle's C code against something it does not share:
+torch's float8/bfloat16 casts, numpy integer shifts, frexp/ldexp, or the OCP
+value tables.  Formats: INT4 (Orbit announcement, 技术细节 / Kimi INT4 base),
+FP8 E4M3 with [128,128] / [1,128] fp32 scales (NeMo RL FP8 post, Table 1),
+MXFP4 / MXFP8 (the mixed-precision sampler post names MXFP4 as a serving
+format; element and scale codes follow OCP MX v1.0)."""
+import numpy as np
+import pytest
+
+import oracle
+from tests import refimpl
+
+
+def test_bf16_decode_all_patterns():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode("bf16", codes)
+    ref = refimpl.bf16_to_f32(codes).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_int4_decode_matches_int8_shift():
+    nib = np.arange(16, dtype=np.uint8)
+    got = oracle.decode("int4", nib)
+    assert np.array_equal(got, refimpl.int4_values(nib))
+    assert got.min() == -8 and got.max() == 7
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e4m3", codes)
+    ref = refimpl.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    # OCP E4M3FN: only S.1111.111 is NaN, largest finite is 448, smallest subnormal 2^-9
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isnan(got).sum() == 2
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e2m1_decode_matches_ocp_table():
+    nib = np.arange(16, dtype=np.uint8)
+    got = oracle.decode("e2m1", nib)
+    assert np.array_equal(got, refimpl.E2M1_TABLE)
+    assert np.array_equal(np.signbit(got), np.signbit(refimpl.E2M1_TABLE))
+
+
+def test_e8m0_decode():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e8m0", codes)
+    assert np.isnan(got[255])
+    assert np.array_equal(got[:255], np.ldexp(1.0, np.arange(255) - 127))
+    assert got[127] == 1.0
+
+
+def test_e4m3_encode_round_trip_every_code():
+    """Representable values round-trip exactly (every non-NaN code, incl. -0)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = refimpl.e4m3_to_f64(codes).astype(np.float32)
+    vals[codes == 0x80] = -0.0
+    assert np.array_equal(oracle.encode_e4m3(vals), codes)
+
+
+def test_e4m3_encode_rne_vs_torch_all_bf16_values():
+    v = refimpl.bf16_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    fin = np.isfinite(v) & (np.abs(v) <= 464.0)
+    got = oracle.encode_e4m3(v[fin])
+    ref = refimpl.f32_to_e4m3_sat(v[fin])
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_midpoints_and_saturation():
+    # exact midpoints between neighbouring codes go to the even code
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    lo = refimpl.e4m3_to_f64(codes)
+    hi = refimpl.e4m3_to_f64(codes + 1)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)  # exact in fp32
+    got = oracle.encode_e4m3(mid)
+    expect = np.where(codes % 2 == 0, codes, codes + 1).astype(np.uint8)
+    assert np.array_equal(got, expect)
+    big = np.array([448.0, 449.0, 500.0, 1e30, np.inf, -1e30, -np.inf], np.float32)
+    assert list(oracle.encode_e4m3(big)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert oracle.encode_e4m3(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_act_quant_bitexact_vs_numpy(seed):
+    r = np.random.default_rng(seed)
+    v = (r.standard_normal((37, 512)) * np.exp(r.uniform(-8, 8, (37, 1)))).astype(np.float32)
+    v[3, 128:256] = 0.0  # an all-zero block -> scale 1, codes 0
+    q, s = oracle.quant_fp8(v)
+    q2, s2 = refimpl.quant_fp8_rows(v)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(q, q2)
+    assert s[3, 1] == 1.0 and not q[3, 128:256].any()
+    # every non-zero block holds a +-448 code (s = amax/448)
+    blk = q.reshape(37, 4, 128)
+    nz = np.abs(v.reshape(37, 4, 128)).max(axis=2) > 0
+    has448 = ((blk & 0x7F) == 0x7E).any(axis=2)
+    assert np.array_equal(has448, nz)
+    # dequantization error within half an E4M3 step of the block scale
+    deq = refimpl.e4m3_to_f64(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+    sc = np.repeat(s.astype(np.float64), 128, axis=1)
+    a = np.abs(v) / sc  # magnitude in code space
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(a, 1e-300))) - 3), 2.0 ** -9) * sc
+    ulp = step
+    assert np.all(np.abs(deq - v) <= ulp * 0.5 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mxfp8_act_quant_bitexact_vs_numpy(seed):
+    r = np.random.default_rng(seed)
+    v = (r.standard_normal((29, 256)) * np.exp(r.uniform(-20, 20, (29, 1)))).astype(np.float32)
+    v[5, 32:64] = 0.0
+    q, e = oracle.quant_mxfp8(v)
+    q2, e2 = refimpl.quant_mxfp8_rows(v)
+    assert np.array_equal(e, e2) and np.array_equal(q, q2)
+    assert e[5, 1] == 127 and not q[5, 32:64].any()
+    # the largest code of a non-zero block has exponent field 15 (values 256..448)
+    mags = (q & 0x7F).reshape(29, 8, 32).max(axis=2)
+    nz = np.abs(v.reshape(29, 8, 32)).max(axis=2) > 0
+    assert np.all((mags[nz] >> 3) == 15)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_dequant_matches_reference(fmt):
+    r = np.random.default_rng(fmt)
+    N, K = 256, 384
+    if fmt == 1:
+        q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = refimpl.torch.from_numpy(r.uniform(0.005, 0.02, (N, K // 32)).astype(np.float32)).to(refimpl.torch.bfloat16).view(refimpl.torch.int16).numpy().view(np.uint16)
+    elif fmt == 2:
+        q = refimpl.f32_to_e4m3_sat(r.standard_normal((N, K)).astype(np.float32) * 100)
+        s = r.uniform(1e-4, 1e-3, (N // 128, K // 128)).astype(np.float32)
+    else:
+        q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = r.integers(110, 130, (N, K // 32), dtype=np.uint8)
+    got = oracle.dequant(fmt, N, K, q, s)
+    ref = refimpl.dequant(fmt, q, s, N, K)
+    assert np.array_equal(got.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+
+
+def test_int4_layout_one_hot():
+    """Element 2i sits in the low nibble of byte i; scale g covers k in [32g, 32g+32)."""
+    N, K = 2, 64
+    q = np.zeros((N, K // 2), np.uint8)
+    q[0, 0] = 0x0F | (0x3 << 4)   # k=0 -> -1, k=1 -> 3
+    q[1, 20] = 0x08               # k=40 -> -8
+    s = np.full((N, K // 32), 0x3F80, np.uint16)  # 1.0
+    s[1, 1] = 0x4000              # 2.0 for k in [32, 64) of row 1
+    w = oracle.dequant(1, N, K, q, s)
+    expect = np.zeros((N, K), np.float32)
+    expect[0, 0], expect[0, 1], expect[1, 40] = -1.0, 3.0, -16.0
+    assert np.array_equal(w, expect)
