@@ -1,0 +1,174 @@
+/*
+ * moe_lp.h -- C ABI of the MI355X (gfx950) low-precision MoE expert forward.
+ *
+ * The operation (Orbit announcement, section 技术细节, "Active-expert-chunked
+ * dequantization"): each token activates only the experts its router
+ * selects; the selected experts are processed in fixed-size chunks whose
+ * frozen low-precision weights are dequantized temporarily for a grouped
+ * GEMM and released afterwards.  Weight formats: INT4 (Kimi INT4 base, same
+ * page), FP8 E4M3 with [128,128] fp32 block scales and [1,128] activation
+ * scales (NeMo RL FP8 post, Table 1), MXFP4 (named as a serving format in
+ * the mixed-precision sampler post).  The optional BF16 adapter is an OFT
+ * orthogonal rotation of the expert input (Orbit analysis page, section on
+ * why OFT matters); passing no adapter gives the frozen base, i.e. the
+ * reference policy of that page.
+ *
+ * Conventions for every entry point
+ *  - All array arguments are DEVICE pointers owned by the caller (e.g. torch
+ *    tensors).  Only the descriptor structs live in host memory.  The library
+ *    allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it; no call synchronises the host and no call copies
+ *    device data to the host.  Buffers must stay alive until the work is done.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error the call returns a non-zero moe_status and enqueues nothing.  Kernel
+ *    launch failures return MOE_ERR_DEVICE.  Non-finite logits or activations
+ *    are a precondition violation (not checked).
+ *  - Device pointers must be 16-byte aligned.
+ *  - Row-major everywhere; weights are stored K-contiguous (Y = X W^T).
+ */
+#ifndef MOE_LP_H
+#define MOE_LP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_LP_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad shape, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid but outside the supported limits */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < the matching *_workspace_bytes() */
+  MOE_ERR_DEVICE = 4               /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum {
+  /* Two's-complement 4-bit codes, element 2i in the low nibble of byte i;
+   * bf16 scale per (output row n, 32 consecutive k).  w = q * s.
+   * Activations into the GEMMs: 16-bit floats (no activation quantization). */
+  MOE_W_INT4_G32_BF16 = 1,
+  /* OCP E4M3FN codes, one byte each; fp32 scale per [128,128] block
+   * [n/128][k/128].  Activations (x and the SwiGLU output) are quantized to
+   * E4M3 with an fp32 scale per [1,128] block: s = amax/448, q = RNE(v/s). */
+  MOE_W_FP8_E4M3_B128 = 2,
+  /* OCP MXFP4: E2M1 codes (low nibble first) with an E8M0 scale byte per
+   * (n, 32 consecutive k).  Activations are quantized to MXFP8: E4M3 codes
+   * with an E8M0 scale per 32, shared exponent floor(log2 amax) - 8. */
+  MOE_W_MXFP4 = 3
+} moe_wformat;
+
+/* Layer description (host memory). */
+typedef struct {
+  int32_t num_tokens;  /* T >= 0 (T = 0 is a no-op) */
+  int32_t hidden;      /* H: multiple of 256                                */
+  int32_t inter;       /* I: multiple of 128 (expert intermediate size)     */
+  int32_t num_experts; /* E: 1..1024                                        */
+  int32_t top_k;       /* k: 1..min(16, E)                                  */
+  int32_t wformat;     /* a moe_wformat value                               */
+  int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation  */
+  int32_t reserved;
+  int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
+} moe_layer;
+
+/* Packed expert weights.
+ *   w13: [E][2I][H]  gate rows 0..I-1 then up rows I..2I-1 (packed bytes per format)
+ *   w2 : [E][H][I]   down projection */
+typedef struct {
+  const void* w13;
+  const void* w2;
+} moe_qweights;
+
+/* Scales, layouts per format:
+ *   INT4 : s13 bf16 [E][2I][H/32],   s2 bf16 [E][H][I/32]
+ *   FP8  : s13 fp32 [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]
+ *   MXFP4: s13 u8   [E][2I][H/32],   s2 u8   [E][H][I/32]  (E8M0) */
+typedef struct {
+  const void* s13;
+  const void* s2;
+} moe_scales;
+
+/* Routing result (all device arrays, caller-owned).  R = T*k.
+ *   topk_ids[T][k]      int32, slots in descending logit order (ties: smaller id)
+ *   topk_w[T][k]        fp32, softmax over the k selected logits
+ *   expert_offsets[E+1] int32, exclusive scan of per-expert counts; [E] = R
+ *   sorted_rows[R]      int32, permuted row -> flat pair t*k+j, stable in (t, j)
+ *   row_of[R]           int32, flat pair -> permuted row (inverse of sorted_rows)
+ *   active_experts[E]   int32, experts with >= 1 row in ascending id (first num_active valid)
+ *   num_active[1]       int32 */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* expert_offsets;
+  int32_t* sorted_rows;
+  int32_t* row_of;
+  int32_t* active_experts;
+  int32_t* num_active;
+} moe_route_out;
+
+/* Workspace bytes moe_expert_forward needs for this layer (independent of
+ * chunk_experts, which is accepted for symmetry; any value >= 1 gives the
+ * same size).  Returns 0 for an invalid descriptor. */
+size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
+
+/* Workspace bytes moe_route_permute needs (scan scratch only). */
+size_t moe_route_workspace_bytes(const moe_layer* layer);
+
+/* Router top-k + softmax over the selected logits, then the expert histogram,
+ * exclusive scan and stable permutation by expert (Orbit announcement,
+ * 技术细节: router-selected experts grouped dynamically).
+ * logits: [T][E] fp32.  Outputs are bit-exact functions of the logits except
+ * topk_w (fp32 softmax). */
+moe_status moe_route_permute(const moe_layer* layer, const float* logits, const moe_route_out* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* The MoE expert forward (Orbit announcement, 技术细节, active-expert-chunked
+ * dequantization): route, permute, then for each chunk of `chunk_experts`
+ * consecutive active experts (ascending id) run the grouped
+ * dequantize + GEMM1 (gate/up) + SwiGLU and the grouped dequantize + GEMM2
+ * (down), and finally the weighted combine
+ *   out[t] = sum_j topk_w[t][j] * y[t][j]   (fp32 sum in ascending j, bf16 out).
+ * x: [T][H] bf16; logits: [T][E] fp32; adapter: NULL or bf16
+ * R[E or 1][H/32][32][32] (x' = x R_e, rows of R index the input dim);
+ * out: [T][H] bf16.  The launch count is fixed by (E, chunk_experts); the
+ * result does not depend on chunk_experts.  ws: >= moe_workspace_bytes(). */
+moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const float* logits,
+                              const moe_qweights* qweights, const moe_scales* scales,
+                              const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
+ * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:
+ * [T*k][H] bf16.  Atomic-free and deterministic. */
+moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w,
+                       const int32_t* row_of, void* out_bf16, void* stream);
+
+/* Workspace bytes moe_lm_head_logprob needs: T*V fp32 logits + 256 B. */
+size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V);
+
+/* Log-prob of target tokens under an LM head (the rollout log-probs whose
+ * train/rollout agreement the NeMo RL FP8 post measures with its
+ * token-mult-prob-error):  z = h / sqrt(mean(h^2) + 1e-6) (a final
+ * parameter-free RMSNorm), logits = z W_lm^T (fp32 accumulation),
+ * logprob[t] = logits[t][y_t] - logsumexp_v logits[t][v].
+ * h: [T][H] bf16; w_lm: [V][H] bf16; targets: [T] int32 in [0, V);
+ * logprob: [T] fp32.  H multiple of 128, T <= 4096. */
+moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf16, const void* w_lm_bf16,
+                               const int32_t* targets, float* logprob, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* moe_status_str(moe_status status);
+
+/* MOE_LP_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LP_H */

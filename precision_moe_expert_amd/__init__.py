@@ -1,0 +1,9 @@
+"""MI355X (gfx950) low-precision MoE expert forward.
+
+The compute lives in libmoe_lp.so (HIP kernels behind the C ABI of
+include/moe_lp.h); `binding` marshals torch tensors into it.  `synth` holds the
+seeded synthetic input generators.
+"""
+from . import binding  # noqa: F401
+from .binding import (FMT_FP8, FMT_INT4, FMT_MXFP4, MoeError, combine, expert_forward,  # noqa: F401
+                      lm_head_logprob, make_layer, route_permute, workspace_bytes)

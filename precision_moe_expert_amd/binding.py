@@ -1,0 +1,174 @@
+"""ctypes binding of libmoe_lp.so (include/moe_lp.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the MoE expert forward runs in the library's kernels.
+If the library is missing the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_lp.so")
+_lib = None
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
+FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
+
+EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
+            "moe_route_permute", "moe_expert_forward", "moe_combine", "moe_lm_head_workspace_bytes",
+            "moe_lm_head_logprob")
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wformat", ctypes.c_int32),
+                ("oft_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("adapter_expert_stride", ctypes.c_int64)]
+
+
+class MoeQWeights(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
+class MoeScales(ctypes.Structure):
+    _fields_ = [("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
+class MoeRouteOut(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("sorted_rows", ctypes.c_void_p), ("row_of", ctypes.c_void_p), ("active_experts", ctypes.c_void_p),
+                ("num_active", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.moe_abi_version.restype = ctypes.c_int32
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_int32]
+        L.moe_route_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
+        L.moe_lm_head_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_lm_head_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.moe_route_permute.restype = ctypes.c_int
+        L.moe_route_permute.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.POINTER(MoeRouteOut),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.moe_expert_forward.restype = ctypes.c_int
+        L.moe_expert_forward.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales), ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+        L.moe_lm_head_logprob.restype = ctypes.c_int
+        L.moe_lm_head_logprob.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None) -> MoeLayer:
+    stride = (H // 32) * 1024 if adapter_expert_stride is None else adapter_expert_stride
+    return MoeLayer(T, H, I, E, k, fmt, 32 if oft else 0, 0, stride if oft else 0)
+
+
+def workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(layer), int(chunk_experts))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def route_permute(logits: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = None) -> dict:
+    """Router top-k + permutation; returns a dict of device tensors."""
+    T, E, k = layer.num_tokens, layer.num_experts, layer.top_k
+    dev = logits.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(topk_ids=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               expert_offsets=torch.empty(E + 1, **i32), sorted_rows=torch.empty(T * k, **i32),
+               row_of=torch.empty(T * k, **i32), active_experts=torch.empty(E, **i32),
+               num_active=torch.zeros(4, **i32))
+    ro = MoeRouteOut(*[_ptr(out[n]) for n in ("topk_ids", "topk_w", "expert_offsets", "sorted_rows", "row_of",
+                                              "active_experts", "num_active")])
+    if ws is None:
+        ws = alloc_workspace(lib().moe_route_workspace_bytes(ctypes.byref(layer)), dev)
+    _check(lib().moe_route_permute(ctypes.byref(layer), _ptr(logits), ctypes.byref(ro), _ptr(ws), ws.numel(),
+                                   _stream()), "moe_route_permute")
+    return out
+
+
+def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, w2, s13, s2, adapter=None,
+                   chunk_experts: int = 1, out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """moe_expert_forward: x [T][H] bf16, logits [T][E] fp32 -> out [T][H] bf16."""
+    if out is None:
+        out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2))
+    _check(lib().moe_expert_forward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
+                                    _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "moe_expert_forward")
+    return out
+
+
+def combine(layer: MoeLayer, y_perm: torch.Tensor, topk_w: torch.Tensor, row_of: torch.Tensor,
+            out: torch.Tensor | None = None):
+    if out is None:
+        out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=y_perm.device)
+    _check(lib().moe_combine(ctypes.byref(layer), _ptr(y_perm), _ptr(topk_w), _ptr(row_of), _ptr(out), _stream()),
+           "moe_combine")
+    return out
+
+
+def lm_head_logprob(h: torch.Tensor, w_lm: torch.Tensor, targets: torch.Tensor, ws: torch.Tensor | None = None):
+    T, H = h.shape
+    V = w_lm.shape[0]
+    lp = torch.empty(T, dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws = alloc_workspace(lib().moe_lm_head_workspace_bytes(T, V), h.device)
+    _check(lib().moe_lm_head_logprob(T, H, V, _ptr(h), _ptr(w_lm), _ptr(targets), _ptr(lp), _ptr(ws), ws.numel(),
+                                     _stream()), "moe_lm_head_logprob")
+    return lp

@@ -1,0 +1,211 @@
+// Activation preparation: the expert GEMMs' A operand, once per token (no
+// adapter) or once per permuted row (OFT adapter, which depends on the expert).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// x bf16 [T][H] -> fp16 in the INT4-path layout (groups of 8 stored in the
+// order 0,4,1,5,2,6,3,7).  bf16 -> fp16 is exact for |x| in [2^-14, 65504].
+__global__ __launch_bounds__(256) void k_act_f16(const uint16_t* __restrict__ x, int64_t n8,
+                                                 uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+    f[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+  }
+  uint4 o;
+  o.x = pack_f16x2(f[0], f[4]);
+  o.y = pack_f16x2(f[1], f[5]);
+  o.z = pack_f16x2(f[2], f[6]);
+  o.w = pack_f16x2(f[3], f[7]);
+  reinterpret_cast<uint4*>(out)[i] = o;
+}
+
+// FP8 [1,128] activation quantization (NeMo RL FP8 post, Table 1, input
+// activations): per 128-block s = amax/448 (IEEE fp32 division; 1 if amax =
+// 0), codes = E4M3(v / s).  One wave per token; a lane owns 32 elements, four
+// lanes a block.
+__global__ __launch_bounds__(256) void k_act_fp8(const uint16_t* __restrict__ x, int T, int H,
+                                                 uint8_t* __restrict__ q, float* __restrict__ sc) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (t >= T) return;
+  for (int base = 0; base < H; base += 2048) {
+    const int c0 = base + lane * 32;
+    const bool valid = c0 < H;
+    float v[32];
+    float amax = 0.0f;
+    if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 u = src[j];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[8 * j + 2 * h] = bf16_bits_to_f32(w[h] & 0xFFFFu);
+          v[8 * j + 2 * h + 1] = bf16_bits_to_f32(w[h] >> 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = fmaxf(amax, shfl_xor(amax, 1));
+    amax = fmaxf(amax, shfl_xor(amax, 2));
+    if (!valid) continue;
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    uint32_t packed[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) packed[j] = cvt_e4m3x4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+    uint4* dst = reinterpret_cast<uint4*>(q + (int64_t)t * H + c0);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    if ((lane & 3) == 0) sc[(int64_t)t * (H / 128) + c0 / 128] = s;
+  }
+}
+
+// floor(log2(a)) of a positive finite float, from its bit pattern.
+MOE_DEV int floor_log2_pos(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int ef = (int)(b >> 23);
+  if (ef > 0) return ef - 127;
+  return (31 - __builtin_clz(b & 0x7FFFFFu)) - 149;
+}
+
+// 2^n as a float for n in [-127, 127].
+MOE_DEV float exp2_int(int n) {
+  return n >= -126 ? __uint_as_float((uint32_t)(n + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// MXFP8 quantization of 32 values: shared exponent X = floor(log2 amax) - 8
+// (clamped to [-127, 127]; 0 when amax = 0), codes = E4M3(v * 2^-X) with
+// saturation.  Writes 32 code bytes as 8 dwords and returns the E8M0 byte.
+MOE_DEV uint32_t mx_quant32(const float* v, float amax, uint32_t* packed) {
+  int X = 0;
+  if (amax > 0.0f) {
+    X = floor_log2_pos(amax) - 8;
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  }
+  const float m = exp2_int(-X);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) packed[j] = cvt_e4m3x4(v[4 * j] * m, v[4 * j + 1] * m, v[4 * j + 2] * m, v[4 * j + 3] * m);
+  return (uint32_t)(X + 127);
+}
+
+// MXFP8 activation quantization per token: a lane owns one 32-block.
+__global__ __launch_bounds__(256) void k_act_mxfp8(const uint16_t* __restrict__ x, int T, int H,
+                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (t >= T) return;
+  for (int c0 = lane * 32; c0 < H; c0 += 2048) {
+    float v[32];
+    float amax = 0.0f;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 u = src[j];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[8 * j + 2 * h] = bf16_bits_to_f32(w[h] & 0xFFFFu);
+        v[8 * j + 2 * h + 1] = bf16_bits_to_f32(w[h] >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    uint32_t packed[8];
+    const uint32_t eb = mx_quant32(v, amax, packed);
+    uint4* dst = reinterpret_cast<uint4*>(q + (int64_t)t * H + c0);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    e8[(int64_t)t * (H / 32) + c0 / 32] = (uint8_t)eb;
+  }
+}
+
+// OFT rotation x' = x R_e (R_e block-diagonal, 32x32 bf16 blocks; row i of a
+// block indexes the input dim) for every permuted row, on bf16 MFMA with fp32
+// accumulation, written as fp16 in the INT4-path layout.  Work item = 16 rows
+// of one expert (the 16-row tile list); the 4 waves split the H/32 blocks.
+__global__ __launch_bounds__(256) void k_oft_f16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
+                                                 int64_t r_stride, int H, int k, const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ sorted_rows,
+                                                 const int32_t* __restrict__ active,
+                                                 const int32_t* __restrict__ num_active,
+                                                 const int32_t* __restrict__ tile16, uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t rs[4][32 * 32];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int ln = lane & 15, lg = lane >> 4;
+  const int na = *num_active;
+  const int ngroups = tile16[na];
+  const int nb = H / 32;
+  for (int gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
+    int lo = 0, hi = na - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile16[mid] <= gi) lo = mid; else hi = mid - 1;
+    }
+    const int e = active[lo];
+    const int r0 = offsets[e] + (gi - tile16[lo]) * 16;
+    const int nrows = min(16, offsets[e + 1] - r0);
+    const int tok = sorted_rows[r0 + min(ln, nrows - 1)] / k;
+    const uint16_t* xrow = x + (int64_t)tok * H;
+    const uint16_t* Re = R + (int64_t)e * r_stride;
+    for (int b = wave; b < nb; b += 4) {
+      // stage R_e[b] (2 KB) in this wave's LDS slice
+      const uint4* src = reinterpret_cast<const uint4*>(Re + (int64_t)b * 1024);
+      uint4* dst = reinterpret_cast<uint4*>(rs[wave]);
+      dst[lane * 2] = src[lane * 2];
+      dst[lane * 2 + 1] = src[lane * 2 + 1];
+      __syncthreads();
+      const uint4 av = *reinterpret_cast<const uint4*>(xrow + b * 32 + lg * 8);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint16_t bv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bv[i] = rs[wave][(lg * 8 + i) * 32 + half * 16 + ln];
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, bv);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma_bf16_16x16x32(a, bb, acc);
+        const int col = i4act_pos(b * 32 + half * 16 + ln);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = lg * 4 + i;
+          if (m < nrows) {
+            const _Float16 hv = (_Float16)acc[i];
+            out[(int64_t)(r0 + m) * H + col] = __builtin_bit_cast(uint16_t, hv);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s) {
+  const int64_t n8 = (int64_t)T * H / 8;
+  if (n8 == 0) return;
+  hipLaunchKernelGGL(k_act_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
+}
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_fp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc);
+}
+void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_mxfp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, e8);
+}
+void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                    const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                    const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s) {
+  (void)E;
+  hipLaunchKernelGGL(k_oft_f16, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows, active,
+                     num_active, tile16, out);
+}
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE expert library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+#define MOE_DEV __device__ __forceinline__
+
+// Format ids (same values as moe_wformat).
+enum { FMT_INT4 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+
+MOE_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+MOE_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+MOE_DEV uint32_t pack_f16x2(float a, float b) {
+  _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// E4M3FN codes of two fp32 values (RNE, saturating to +-448) packed in the
+// low 16 bits (a in byte 0, b in byte 1).  The hardware conversion rounds to
+// nearest even but maps magnitudes above 464 to NaN, hence the clamp.
+MOE_DEV uint32_t cvt_e4m3x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four E4M3FN codes in one dword (byte i = code of v[i]).
+MOE_DEV uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  c = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
+  d = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+MOE_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// 16x16x32 fp16 MFMA: lane l supplies A[l%16][8*(l/16)+i], B[8*(l/16)+i][l%16];
+// accumulator element i of lane l is C[4*(l/16)+i][l%16].
+MOE_DEV f32x4 mfma_f16_16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+MOE_DEV f32x4 mfma_bf16_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x128 E4M3 x E4M3 MFMA, no scaling.  Lane l supplies 32 bytes of row
+// (A) / column (B) l%16; any K assignment shared by A and B gives the dot
+// product.
+MOE_DEV f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// 16x16x128 E4M3 (A) x E2M1 (B) MFMA with E8M0 block scales.  Layout on gfx950:
+//   A lane l: bytes 0..15 = A[l%16][16*(l/16) + i], bytes 16..31 = A[l%16][64 + 16*(l/16) + i]
+//   B lane l: 32 nibbles (low first) = B[32*(l/16) + i][l%16]
+//   scale byte 0 of lane l: A row l%16 (resp. B column l%16), K block l/16 (k in [32j, 32j+32))
+MOE_DEV f32x4 mfma_fp8_fp4_scaled_16x16x128(const i32x8& a, const i32x4& b, int sa, int sb, const f32x4& c) {
+  i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, sa, 0, sb);
+}
+
+MOE_DEV int lane_id() { return (int)(threadIdx.x & 63); }
+
+template <typename T>
+MOE_DEV T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Position of element n inside the INT4-path activation layout: every aligned
+// group of 8 fp16 values is stored in the order [0,4,1,5,2,6,3,7], matching
+// the order in which the in-register INT4 unpack produces weight pairs.
+MOE_DEV int i4act_pos(int n) { return (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1); }

@@ -1,0 +1,63 @@
+// Internal launcher interface between the C-ABI host code and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_TOPK = 16;
+constexpr int PAIRS_PER_BLOCK = 2048;  // flat (token, slot) pairs per histogram / scatter block
+
+// Everything a grouped-GEMM launch over one chunk of active experts needs.
+struct GemmArgs {
+  // A operand: activation rows.  a_per_token: row r reads token sorted_rows[r]/k.
+  const void* a;            // codes / fp16 values, [rows][K]
+  const void* a_scale;      // FP8: fp32 [rows][K/128]; MXFP4 path: E8M0 [rows][K/32]
+  int a_per_token;
+  // B operand: packed expert weights [E][N][K] and their scales.
+  const uint8_t* w;
+  const void* w_scale;
+  int64_t w_expert_bytes;      // bytes between experts' packed weights
+  int64_t ws_expert_elems;     // elements between experts' scales
+  int N, K;                    // GEMM1: N = 2I, K = H.  GEMM2: N = H, K = I.
+  int inter;                   // I (GEMM1 pairs column n with n + I)
+  // output
+  void* out;                   // GEMM1: activation-format h [R][I]; GEMM2: bf16 y [R][N]
+  void* out_scale;             // GEMM1 FP8: fp32 [R][I/128]; MXFP4: E8M0 [R][I/32]
+  // routing / schedule (device)
+  const int32_t* offsets;
+  const int32_t* sorted_rows;
+  const int32_t* active;
+  const int32_t* num_active;
+  const int32_t* tile_start;   // per active expert prefix of ceil(count/BM) (+ total)
+  int top_k;
+  int chunk;                   // chunk index c
+  int chunk_experts;           // C
+};
+
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
+                    int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
+                    int32_t* tile_16, hipStream_t s);
+
+// Activation preparation (per token rows, no adapter).
+void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, hipStream_t s);
+void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, hipStream_t s);
+// OFT rotation of every permuted row into the INT4-path activation layout.
+void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                    const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                    const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s);
+
+// Grouped GEMMs over one chunk; bm = rows per tile (16, 32, 64 or 128).
+void launch_gemm_int4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+void launch_gemm_fp8(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+void launch_gemm_mxfp4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+
+void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
+                    hipStream_t s);
+void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,
+                    float* logits_ws, float* inv_rms_ws, float* logprob, hipStream_t s);
+
+}  // namespace moe

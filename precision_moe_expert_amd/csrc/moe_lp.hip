@@ -1,0 +1,327 @@
+// Host side of the C ABI declared in include/moe_lp.h: argument validation,
+// workspace carving and the fixed launch sequence of the MoE expert forward.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "moe_lp.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Byte layout of the forward workspace; offsets relative to its base.
+struct WsLayout {
+  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, hist;
+  size_t act, act_scale, h, h_scale, y;
+  size_t total;
+};
+
+struct Dims {
+  int T, H, I, E, k, fmt;
+  bool oft;
+  int64_t R;
+  int nblk;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the descriptor (pointer checks are done by each entry point).
+moe_status check_layer(const moe_layer* L, Dims* d) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (L->num_tokens < 0 || L->hidden <= 0 || L->inter <= 0 || L->num_experts <= 0 || L->top_k <= 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (L->top_k > L->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+  if (L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_FP8_E4M3_B128 && L->wformat != MOE_W_MXFP4)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (L->oft_block != 0 && L->oft_block != 32) return MOE_ERR_UNSUPPORTED;
+  if (L->adapter_expert_stride < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (L->hidden % 256 != 0 || L->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (L->num_experts > MAX_EXPERTS || L->top_k > MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
+  d->T = L->num_tokens;
+  d->H = L->hidden;
+  d->I = L->inter;
+  d->E = L->num_experts;
+  d->k = L->top_k;
+  d->fmt = L->wformat;
+  d->oft = L->oft_block != 0;
+  d->R = (int64_t)d->T * d->k;
+  d->nblk = (int)((d->R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK);
+  return MOE_OK;
+}
+
+WsLayout layout(const Dims& d) {
+  WsLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t R = (size_t)d.R, T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+  w.ids = take(R * 4);
+  w.wts = take(R * 4);
+  w.offsets = take((E + 1) * 4);
+  w.sorted_rows = take(R * 4);
+  w.row_of = take(R * 4);
+  w.active = take(E * 4);
+  w.num_active = take(16);
+  w.tile_a = take((E + 1) * 4);
+  w.tile_16 = take((E + 1) * 4);
+  w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
+  const size_t arows = d.oft ? R : T;
+  if (d.fmt == MOE_W_INT4_G32_BF16) {
+    w.act = take(arows * H * 2);
+    w.act_scale = take(0);
+    w.h = take(R * I * 2);
+    w.h_scale = take(0);
+  } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
+    w.act = take(arows * H);
+    w.act_scale = take(arows * (H / 128) * 4);
+    w.h = take(R * I);
+    w.h_scale = take(R * (I / 128) * 4);
+  } else {
+    w.act = take(arows * H);
+    w.act_scale = take(arows * (H / 32));
+    w.h = take(R * I);
+    w.h_scale = take(R * (I / 32));
+  }
+  w.y = take(R * H * 2);
+  w.total = o;
+  return w;
+}
+
+// Rows per GEMM tile from the mean rows per expert.
+int choose_bm(const Dims& d) {
+  const int64_t mean = d.R / d.E;
+  if (mean <= 16) return 16;
+  if (mean <= 48) return 32;
+  if (mean <= 96) return 64;
+  return 128;
+}
+
+int gemm_grid(const Dims& d, int bm, int chunk, int nblk_n) {
+  int64_t tiles = d.R / bm + chunk;
+  if (tiles > (int64_t)d.E + d.R / bm) tiles = (int64_t)d.E + d.R / bm;
+  int64_t g = tiles * nblk_n;
+  if (g > 1024) g = 1024;
+  if (g < 8) g = 8;
+  return (int)((g + 7) / 8 * 8);
+}
+
+moe_status launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_LP_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, format or limit";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_DEVICE: return "device launch error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
+  Dims d;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
+  return layout(d).total;
+}
+
+size_t moe_route_workspace_bytes(const moe_layer* layer) {
+  Dims d;
+  if (check_layer(layer, &d) != MOE_OK) return 0;
+  return align_up((size_t)(d.E + 1) * 4) * 2 + align_up((size_t)(d.nblk > 0 ? d.nblk : 1) * d.E * 4);
+}
+
+moe_status moe_route_permute(const moe_layer* layer, const float* logits, const moe_route_out* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.T == 0) return MOE_OK;
+  const void* ptrs[] = {logits, out->topk_ids, out->topk_w, out->expert_offsets, out->sorted_rows,
+                        out->row_of, out->active_experts, out->num_active, ws};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < moe_route_workspace_bytes(layer)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  int32_t* tile_a = reinterpret_cast<int32_t*>(base);
+  int32_t* tile_16 = reinterpret_cast<int32_t*>(base + align_up((size_t)(d.E + 1) * 4));
+  int32_t* hist = reinterpret_cast<int32_t*>(base + 2 * align_up((size_t)(d.E + 1) * 4));
+  launch_route(logits, d.T, d.E, d.k, out->topk_ids, out->topk_w, s);
+  launch_permute(out->topk_ids, (int)d.R, d.E, choose_bm(d), hist, out->expert_offsets, out->sorted_rows,
+                 out->row_of, out->active_experts, out->num_active, tile_a, tile_16, s);
+  return launch_status();
+}
+
+moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const float* logits,
+                              const moe_qweights* qw, const moe_scales* sc, const void* adapter_bf16,
+                              int32_t chunk_experts, void* out_bf16, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.T == 0) return MOE_OK;
+  const void* ptrs[] = {x_bf16, logits, qw->w13, qw->w2, sc->s13, sc->s2, out_bf16, ws};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.oft && !aligned16(adapter_bf16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.oft && (layer->adapter_expert_stride % 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  const WsLayout wl = layout(d);
+  if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  int32_t* ids = I32(wl.ids);
+  float* wts = reinterpret_cast<float*>(base + wl.wts);
+  int32_t* offsets = I32(wl.offsets);
+  int32_t* sorted_rows = I32(wl.sorted_rows);
+  int32_t* row_of = I32(wl.row_of);
+  int32_t* active = I32(wl.active);
+  int32_t* num_active = I32(wl.num_active);
+  int32_t* tile_a = I32(wl.tile_a);
+  int32_t* tile_16 = I32(wl.tile_16);
+  int32_t* hist = I32(wl.hist);
+  void* act = base + wl.act;
+  void* act_scale = base + wl.act_scale;
+  void* h = base + wl.h;
+  void* h_scale = base + wl.h_scale;
+  uint16_t* y = reinterpret_cast<uint16_t*>(base + wl.y);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const int bm = choose_bm(d);
+
+  // 1-2. route and permute
+  launch_route(logits, d.T, d.E, d.k, ids, wts, s);
+  launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, s);
+
+  // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
+  if (d.fmt == MOE_W_INT4_G32_BF16) {
+    if (d.oft)
+      launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
+                     sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
+    else
+      launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
+  } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
+    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), s);
+  } else {
+    launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), s);
+  }
+
+  // 4. chunk loop over the active experts: GEMM1 (+SwiGLU) then GEMM2 per chunk
+  const int nchunks = (d.E + chunk_experts - 1) / chunk_experts;
+  GemmArgs g1{}, g2{};
+  g1.a = act;
+  g1.a_scale = act_scale;
+  g1.a_per_token = d.oft ? 0 : 1;
+  g1.w = static_cast<const uint8_t*>(qw->w13);
+  g1.w_scale = sc->s13;
+  g1.N = 2 * d.I;
+  g1.K = d.H;
+  g1.inter = d.I;
+  g1.out = h;
+  g1.out_scale = h_scale;
+  g2.a = h;
+  g2.a_scale = h_scale;
+  g2.a_per_token = 0;
+  g2.w = static_cast<const uint8_t*>(qw->w2);
+  g2.w_scale = sc->s2;
+  g2.N = d.H;
+  g2.K = d.I;
+  g2.inter = d.I;
+  g2.out = y;
+  g2.out_scale = nullptr;
+  const int64_t n13 = (int64_t)2 * d.I * d.H, n2 = (int64_t)d.H * d.I;
+  if (d.fmt == MOE_W_INT4_G32_BF16) {
+    g1.w_expert_bytes = n13 / 2; g1.ws_expert_elems = n13 / 32;
+    g2.w_expert_bytes = n2 / 2;  g2.ws_expert_elems = n2 / 32;
+  } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
+    g1.w_expert_bytes = n13; g1.ws_expert_elems = n13 / (128 * 128);
+    g2.w_expert_bytes = n2;  g2.ws_expert_elems = n2 / (128 * 128);
+  } else {
+    g1.w_expert_bytes = n13 / 2; g1.ws_expert_elems = n13 / 32;
+    g2.w_expert_bytes = n2 / 2;  g2.ws_expert_elems = n2 / 32;
+  }
+  for (GemmArgs* g : {&g1, &g2}) {
+    g->offsets = offsets;
+    g->sorted_rows = sorted_rows;
+    g->active = active;
+    g->num_active = num_active;
+    g->tile_start = tile_a;
+    g->top_k = d.k;
+    g->chunk_experts = chunk_experts;
+  }
+  const int grid1 = gemm_grid(d, bm, chunk_experts, d.I / 128);
+  const int grid2 = gemm_grid(d, bm, chunk_experts, d.H / 256);
+  for (int c = 0; c < nchunks; ++c) {
+    g1.chunk = c;
+    g2.chunk = c;
+    if (d.fmt == MOE_W_INT4_G32_BF16) {
+      launch_gemm_int4(g1, true, bm, grid1, s);
+      launch_gemm_int4(g2, false, bm, grid2, s);
+    } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
+      launch_gemm_fp8(g1, true, bm, grid1, s);
+      launch_gemm_fp8(g2, false, bm, grid2, s);
+    } else {
+      launch_gemm_mxfp4(g1, true, bm, grid1, s);
+      launch_gemm_mxfp4(g2, false, bm, grid2, s);
+    }
+  }
+
+  // 5. weighted combine back to token order
+  launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s);
+  return launch_status();
+}
+
+moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w, const int32_t* row_of,
+                       void* out_bf16, void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  const void* ptrs[] = {y_perm_bf16, topk_w, row_of, out_bf16};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  launch_combine(static_cast<const uint16_t*>(y_perm_bf16), topk_w, row_of, d.T, d.k, d.H,
+                 static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V) {
+  if (T < 0 || V <= 0) return 0;
+  return align_up((size_t)T * (size_t)V * 4) + align_up((size_t)T * 4);
+}
+
+moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf16, const void* w_lm_bf16,
+                               const int32_t* targets, float* logprob, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || H <= 0 || V <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128 != 0 || T > 4096) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const void* ptrs[] = {h_bf16, w_lm_bf16, targets, logprob, ws};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < moe_lm_head_workspace_bytes(T, V)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  char* base = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(base);
+  float* inv_rms = reinterpret_cast<float*>(base + align_up((size_t)T * (size_t)V * 4));
+  launch_lm_head(static_cast<const uint16_t*>(h_bf16), static_cast<const uint16_t*>(w_lm_bf16), targets, T, H, V,
+                 logits, inv_rms, logprob, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Work scheduling shared by the grouped GEMMs: a chunk of active experts
+// (Orbit announcement, 技术细节: router-selected experts grouped into
+// fixed-size batches) becomes a device-built list of (expert, BM-row tile)
+// entries; each work item is one tile times one N block.  The grid is
+// persistent: every workgroup walks items with stride gridDim.x and exits
+// when the chunk has none left, so the launch count never depends on data.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+struct ChunkWork {
+  int a0, a1;    // active-expert index range of the chunk
+  int t0;        // first tile of the chunk
+  int ntiles;
+  int nwork;
+};
+
+MOE_DEV bool chunk_work(const GemmArgs& p, int nblk, ChunkWork& cw) {
+  const int na = *p.num_active;
+  cw.a0 = p.chunk * p.chunk_experts;
+  if (cw.a0 >= na) return false;
+  cw.a1 = min(cw.a0 + p.chunk_experts, na);
+  cw.t0 = p.tile_start[cw.a0];
+  cw.ntiles = p.tile_start[cw.a1] - cw.t0;
+  cw.nwork = cw.ntiles * nblk;
+  return cw.nwork > 0;
+}
+
+struct Tile {
+  int e;       // expert id
+  int rbase;   // first permuted row
+  int nrows;   // valid rows (1..BM)
+  int nb;      // N block
+};
+
+// Item wk -> (tile, N block), tiles fastest so that concurrently running
+// workgroups share an expert's weights.
+MOE_DEV Tile tile_of(const GemmArgs& p, const ChunkWork& cw, int wk, int bm) {
+  Tile t;
+  t.nb = wk / cw.ntiles;
+  const int tile = cw.t0 + wk % cw.ntiles;
+  int lo = cw.a0, hi = cw.a1 - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  t.e = p.active[lo];
+  const int m0 = (tile - p.tile_start[lo]) * bm;
+  t.rbase = p.offsets[t.e] + m0;
+  t.nrows = min(bm, p.offsets[t.e + 1] - t.rbase);
+  return t;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
+// XCD (and its L2) takes a contiguous range of work items.  grid % 8 == 0.
+MOE_DEV int xcd_virtual_id() {
+  const int g = gridDim.x, b = blockIdx.x;
+  return (b & 7) * (g >> 3) + (b >> 3);
+}
+
+}  // namespace moe

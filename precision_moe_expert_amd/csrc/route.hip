@@ -1,0 +1,194 @@
+// Router top-k + softmax and the expert permutation (histogram, scan,
+// stable scatter) for gfx950.  Orbit announcement, 技术细节: each token
+// activates only its router-selected experts, which are then grouped.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Monotone unsigned key of a float (larger float -> larger key); -0 and +0
+// map to the same key.
+MOE_DEV uint32_t float_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+MOE_DEV float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+
+// One wave per token.  Each lane keeps up to 16 logits (E <= 1024) as
+// 64-bit keys (value key << 32 | (0xFFFF - id)): the wave maximum is the
+// largest logit and, among equal logits, the smallest expert id.
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
+                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  uint64_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int e = lane + 64 * i;
+    key[i] = (e < E) ? (((uint64_t)float_key(row[e]) << 32) | (uint64_t)(0xFFFFu - e)) : 0ull;
+  }
+  float sel_val[16];
+  int sel_id[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)best, m, 64), hi = __shfl_xor((uint32_t)(best >> 32), m, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+      }
+      sel_id[j] = 0xFFFF - (int)(best & 0xFFFFu);
+      sel_val[j] = key_float((uint32_t)(best >> 32));
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key[i] == best) key[i] = 0;  // keys are unique (distinct ids), so only the winner clears
+    }
+  }
+  // softmax over the selected logits, relative to the largest (slot 0)
+  float z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < k) z += expf(sel_val[j] - sel_val[0]);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < k && lane == j) {
+      ids[(int64_t)t * k + j] = sel_id[j];
+      w[(int64_t)t * k + j] = expf(sel_val[j] - sel_val[0]) / z;
+    }
+}
+
+// Per-block expert histogram of PAIRS_PER_BLOCK consecutive flat pairs.
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, int R, int E,
+                                              int32_t* __restrict__ hist) {
+  __shared__ int32_t cnt[MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * PAIRS_PER_BLOCK;
+  for (int i = threadIdx.x; i < PAIRS_PER_BLOCK; i += 256) {
+    int p = p0 + i;
+    if (p < R) atomicAdd(&cnt[ids[p]], 1);  // counting only: order-independent
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Exclusive scan of 1024 values held one per thread (blockDim = 1024).
+MOE_DEV int block_excl_scan_1024(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int a = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += a;
+    __syncthreads();
+  }
+  int incl = sh[tid];
+  *total = sh[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// One workgroup of 1024 threads (thread = expert).  Turns the per-block
+// histograms into per-(block, expert) scatter bases, writes the expert
+// offsets, the ascending active-expert list, and the per-active-expert tile
+// prefixes for tiles of bm_a rows and of 16 rows.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int bm_a,
+                                               int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+                                               int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
+                                               int32_t* __restrict__ tile_16) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) {  // running per-expert prefix over blocks
+      int h = hist[(int64_t)b * E + e];
+      hist[(int64_t)b * E + e] = cnt;
+      cnt += h;
+    }
+  int total;
+  const int off = block_excl_scan_1024(e < E ? cnt : 0, sh, &total);
+  if (e < E) {
+    offsets[e] = off;
+    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;
+  }
+  if (e == 0) offsets[E] = total;
+  const int act = (e < E && cnt > 0) ? 1 : 0;
+  int na;
+  const int pos = block_excl_scan_1024(act, sh, &na);
+  int nta, nt16;
+  const int ta = block_excl_scan_1024(act ? (cnt + bm_a - 1) / bm_a : 0, sh, &nta);
+  const int t16 = block_excl_scan_1024(act ? (cnt + 15) / 16 : 0, sh, &nt16);
+  if (act) {
+    active[pos] = e;
+    tile_a[pos] = ta;
+    tile_16[pos] = t16;
+  }
+  if (e == 0) {
+    *num_active = na;
+    tile_a[na] = nta;
+    tile_16[na] = nt16;
+  }
+}
+
+// Stable scatter: one wave walks its block's pairs in (t, j) order, 64 at a
+// time.  Lanes holding the same expert are found with ballots over the bits
+// of the id; a pair's rank is the number of lower lanes with its expert.
+// Positions come from per-expert LDS counters seeded with the block's scatter
+// bases, so no global atomics decide any position.
+__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids, int R, int E,
+                                                const int32_t* __restrict__ base, int32_t* __restrict__ sorted_rows,
+                                                int32_t* __restrict__ row_of) {
+  __shared__ int32_t cnt[MAX_EXPERTS];
+  const int lane = lane_id();
+  for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int p0 = blockIdx.x * PAIRS_PER_BLOCK;
+  for (int c = 0; c < PAIRS_PER_BLOCK; c += 64) {
+    const int p = p0 + c + lane;
+    const bool valid = p < R;
+    const int e = valid ? ids[p] : 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      uint64_t bb = __ballot(valid && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    const int rank = __popcll(m & lt_mask);
+    int pos = 0;
+    if (valid) pos = cnt[e] + rank;
+    __syncthreads();
+    if (valid) {
+      sorted_rows[pos] = p;
+      row_of[p] = pos;
+      if ((m >> lane) == 1ull) cnt[e] = pos + 1;  // highest lane of the group advances the counter
+    }
+    __syncthreads();
+  }
+}
+
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  if (T == 0) return;
+  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+}
+
+void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
+                    int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
+                    int32_t* tile_16, hipStream_t s) {
+  const int nblk = (R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK;
+  if (nblk > 0) hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(256), 0, s, ids, R, E, hist);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active, tile_a,
+                     tile_16);
+  if (nblk > 0) hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(64), 0, s, ids, R, E, hist, sorted_rows, row_of);
+}
+
+}  // namespace moe

@@ -1,0 +1,115 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, reports workspace sizes, and rejects invalid arguments on the
+host before anything is enqueued (every call here fails validation, so no
+kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from precision_moe_expert_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_lp.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    fns = declared_functions()
+    for name in ("moe_route_permute", "moe_expert_forward", "moe_combine", "moe_workspace_bytes",
+                 "moe_lm_head_logprob", "moe_status_str", "moe_abi_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert binding.status_str(s)
+    assert binding.status_str(99) == "unknown status"
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "moe_lp.h"\nint main(void){ moe_layer l; (void)l; return MOE_OK; }\n')
+    import subprocess
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c", str(src),
+                           "-o", str(tmp_path / "t.o")])
+
+
+def test_workspace_sizes():
+    L = binding.make_layer(4096, 2048, 768, 128, 8, binding.FMT_FP8)
+    n = binding.workspace_bytes(L, 16)
+    R = 4096 * 8
+    assert n >= R * 2048 * 2 + R * 768 + 4096 * 2048  # y + h + x codes
+    assert binding.workspace_bytes(L, 1) == n          # independent of the chunk size
+    assert binding.workspace_bytes(binding.make_layer(4096, 2048, 768, 128, 8, 9), 16) == 0
+    assert binding.lib().moe_lm_head_workspace_bytes(64, 32000) >= 64 * 32000 * 4
+
+
+FAKE = 1 << 20  # aligned non-null address; never dereferenced because validation fails first
+
+
+def _fwd(layer, x=FAKE, lg=FAKE, w=FAKE, adapter=None, chunk=1, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    qw = binding.MoeQWeights(w, w)
+    sc = binding.MoeScales(w, w)
+    return binding.lib().moe_expert_forward(ctypes.byref(layer), x, lg, ctypes.byref(qw), ctypes.byref(sc), adapter,
+                                            chunk, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(H=200), binding.MOE_ERR_UNSUPPORTED),
+    (dict(I=100), binding.MOE_ERR_UNSUPPORTED),
+    (dict(E=2000), binding.MOE_ERR_UNSUPPORTED),
+    (dict(k=17, E=32), binding.MOE_ERR_UNSUPPORTED),
+    (dict(k=9, E=8), binding.MOE_ERR_INVALID_ARGUMENT),
+    (dict(k=0), binding.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), binding.MOE_ERR_INVALID_ARGUMENT),
+    (dict(fmt=7), binding.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_forward_rejects_bad_layer(case, expect):
+    p = dict(T=64, H=256, I=512, E=8, k=2, fmt=1)
+    p.update(case)
+    L = binding.make_layer(p["T"], p["H"], p["I"], p["E"], p["k"], p["fmt"])
+    assert _fwd(L) == expect
+
+
+def test_forward_rejects_bad_pointers_and_workspace():
+    L = binding.make_layer(64, 256, 512, 8, 2, 1)
+    assert _fwd(L, x=None) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(L, out=FAKE + 4) == binding.MOE_ERR_INVALID_ARGUMENT       # misaligned
+    assert _fwd(L, chunk=0) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(L, adapter=FAKE) == binding.MOE_ERR_INVALID_ARGUMENT       # adapter without oft_block
+    assert _fwd(L, ws_bytes=1000) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    Lo = binding.make_layer(64, 256, 512, 8, 2, 1, oft=True)
+    assert _fwd(Lo) == binding.MOE_ERR_INVALID_ARGUMENT                    # oft_block without adapter
+    Lf = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_FP8, oft=True)
+    assert _fwd(Lf, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED           # OFT only on the INT4 path
+    L0 = binding.make_layer(0, 256, 512, 8, 2, 1)
+    assert _fwd(L0, x=None, lg=None, w=None, out=None, ws=None) == binding.MOE_OK  # T = 0: no-op
+
+
+def test_other_entry_points_reject_bad_args():
+    L = binding.make_layer(64, 256, 512, 8, 2, 1)
+    lib = binding.lib()
+    assert lib.moe_combine(ctypes.byref(L), None, FAKE, FAKE, FAKE, None) == binding.MOE_ERR_INVALID_ARGUMENT
+    ro = binding.MoeRouteOut(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    assert lib.moe_route_permute(ctypes.byref(L), FAKE, ctypes.byref(ro), FAKE, 1 << 30, None) == \
+        binding.MOE_ERR_INVALID_ARGUMENT
+    ro = binding.MoeRouteOut(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.moe_route_permute(ctypes.byref(L), FAKE, ctypes.byref(ro), FAKE, 8, None) == \
+        binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_lm_head_logprob(4, 100, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_lm_head_logprob(4, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == \
+        binding.MOE_ERR_WORKSPACE_TOO_SMALL

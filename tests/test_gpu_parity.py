@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing, permutation and index outputs are compared bit for bit; expert
+outputs per row against the relative L2 bound ROW_TOL (bf16 output).  Shapes
+span several tiles with ragged tails; the method's degenerate cases (ties,
+k = E, one hot expert, chunk sizes 1..E) are included."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_moe_expert_amd import binding, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def small(fmt, T=77, H=256, I=384, E=12, k=3, oft=False, zipf=0.0, chunk=4, cfg_id=None):
+    return synth.LayerConfig(f"small_f{fmt}", cfg_id or (40 + fmt + (5 if oft else 0)), T=T, H=H, E=E, k=k, I=I,
+                             fmt=fmt, chunk=chunk, oft=oft, zipf_alpha=zipf)
+
+
+def check_route(logits: np.ndarray, k: int, E: int):
+    T = logits.shape[0]
+    layer = binding.make_layer(T, 256, 128, E, k, 1)
+    got = binding.route_permute(gu.dev(np.ascontiguousarray(logits, np.float32)), layer)
+    torch.cuda.synchronize()
+    ids, w = oracle.route(logits, k)
+    P = oracle.permute(ids, E)
+    assert np.array_equal(got["topk_ids"].cpu().numpy(), ids)
+    assert np.max(np.abs(got["topk_w"].cpu().numpy() - w)) <= 1e-5
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), P["offsets"])
+    assert np.array_equal(got["sorted_rows"].cpu().numpy(), P["sorted_rows"])
+    assert np.array_equal(got["row_of"].cpu().numpy(), P["row_of"])
+    na = int(got["num_active"][0].item())
+    assert na == len(P["active"])
+    assert np.array_equal(got["active_experts"].cpu().numpy()[:na], P["active"])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_route_bitexact_configs(name):
+    cfg = synth.CONFIGS[name]
+    check_route(synth.gen_logits(cfg), cfg.k, cfg.E)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (5, 4, 4), (300, 130, 16), (2049, 1024, 8), (4099, 64, 1)])
+def test_route_bitexact_edge(T, E, k):
+    r = np.random.default_rng(T * 7 + E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg[0, :] = 0.25                          # all tied -> ids 0..k-1
+    if T > 2:
+        lg[1, ::2] = 1.0                     # many ties
+        lg[2, :] = -0.0
+        lg[2, 1::3] = 0.0                    # -0 == +0
+    if T > 10:
+        lg[3:10, 0] += 50.0                  # a hot expert
+    check_route(lg, k, E)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_forward_small_vs_oracle(fmt):
+    cfg = small(fmt)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    ref = oracle.forward_inputs(li)
+    err = gu.row_rel_err(out, ref)
+    print(f"fmt {fmt}: max row rel err {err.max():.3e}, mean {err.mean():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
+@pytest.mark.parametrize("oft", [False, True])
+def test_forward_int4_oft_small(oft):
+    cfg = small(1, T=53, H=512, I=256, E=9, k=4, oft=oft, chunk=2)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    ref = oracle.forward_inputs(li)
+    err = gu.row_rel_err(out, ref)
+    print(f"oft {oft}: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
+def test_forward_c1_vs_oracle():
+    li = synth.make_inputs(synth.CONFIGS["c1"])
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    err = gu.row_rel_err(out, oracle.forward_inputs(li))
+    print(f"c1: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_chunk_size_bitwise_invariance(fmt):
+    cfg = small(fmt, E=9, k=3, zipf=1.2)
+    d = gu.DevInputs(synth.make_inputs(cfg))
+    outs = [d.forward(chunk=c).clone() for c in (1, 2, 4, 9, 64)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_run_twice_bitwise(fmt):
+    d = gu.DevInputs(synth.make_inputs(small(fmt)))
+    a = d.forward().clone()
+    b = d.forward().clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_oft_identity_equals_no_adapter():
+    cfg = small(1, oft=True)
+    li = synth.make_inputs(cfg)
+    li.oft[:] = 0
+    li.oft[:, :, np.arange(32), np.arange(32)] = 0x3F80
+    d = gu.DevInputs(li)
+    a = d.forward().clone()
+    li.oft = None
+    d2 = gu.DevInputs(li)
+    b = d2.forward().clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_combine_vs_oracle():
+    r = np.random.default_rng(5)
+    T, k, H, E = 97, 4, 512, 16
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.route(lg, k)
+    P = oracle.permute(ids, E)
+    y = synth._to_bf16_bits((r.standard_normal((T * k, H)) * 3).astype(np.float32))
+    layer = binding.make_layer(T, H, 128, E, k, 1)
+    out = binding.combine(layer, gu.dev(y, "bf16"), gu.dev(w), gu.dev(P["row_of"]))
+    got = gu.bf16_to_np(out)
+    ref = oracle.combine(y, w, P["row_of"])
+    # fp32 fused sum in ascending j vs fp64: at most one bf16 rounding step apart
+    ulp = np.abs(ref) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(got - ref) <= ulp)
+
+
+def test_lm_head_logprob_vs_oracle():
+    r = np.random.default_rng(6)
+    T, H, V = 37, 512, 5000
+    h = synth._to_bf16_bits((r.standard_normal((T, H)) * 20).astype(np.float32))
+    w = synth._to_bf16_bits((r.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32))
+    tg = r.integers(0, V, T).astype(np.int32)
+    lp = binding.lm_head_logprob(gu.dev(h, "bf16"), gu.dev(w, "bf16"), gu.dev(tg)).cpu().numpy()
+    from tests import refimpl
+    ref = oracle.lm_head_logprob(refimpl.bf16_to_f32(h), w, tg)
+    assert np.max(np.abs(lp - ref)) <= 1e-3
+
+
+def test_t0_is_noop():
+    layer = binding.make_layer(0, 256, 128, 8, 2, 1)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    z = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = binding.expert_forward(layer, x, lg, z, z, z, z, chunk_experts=1,
+                                 out=torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
+    assert out.shape == (0, 256)
