@@ -1,0 +1,198 @@
+"""Benchmark of the low-precision MoE expert forward on one MI355X.
+
+One step = one moe_expert_forward (route, permute, activation preparation,
+chunked dequant + GEMM1 + SwiGLU, dequant + GEMM2, combine) over one batch of
+synthetic input already resident in HBM.  Default workload: the
+Qwen3-30B-A3B-shaped FP8 layer (4096 tokens, hidden 2048, 128 experts, top-8,
+inter 768, [128,128] block-scaled E4M3 weights, chunks of 16 experts).
+
+Prints one JSON line: tokens/s (value), TFLOP/s and % of the format's MFMA
+peak, algorithmic HBM GB/s, the roofline of the dominant kernel (per-launch
+durations from HIP events recorded on the launch stream by the library's
+timed entry point), and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE expert-layer tokens/s + TFLOP/s (% MFMA peak) / HBM GB/s per weight format"
+HBM_PEAK = 8.0e12
+MFMA_PEAK = {1: 2.5e15, 2: 5.0e15, 3: 5.0e15}  # fp16 MFMA (INT4 path), fp8, fp8 x fp4 (issued at the fp8 rate)
+DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a"}
+
+
+def weight_bytes_per_expert(fmt: int, N: int, K: int) -> float:
+    if fmt == 1:
+        return N * K / 2 + N * (K // 32) * 2
+    if fmt == 2:
+        return N * K + (N // 128) * (K // 128) * 4
+    return N * K / 2 + N * (K // 32)
+
+
+def act_bytes(fmt: int, rows: int, K: int) -> float:
+    """Bytes of one activation matrix in the GEMM input format."""
+    if fmt == 1:
+        return rows * K * 2
+    if fmt == 2:
+        return rows * K + rows * (K // 128) * 4
+    return rows * K + rows * (K // 32)
+
+
+def accounting(cfg, counts: np.ndarray) -> dict:
+    """Algorithmic FLOPs and compulsory HBM bytes of the step and of each GEMM stage."""
+    T, H, I, E, k, fmt = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt
+    R = T * k
+    na = int((counts > 0).sum())
+    w13 = weight_bytes_per_expert(fmt, 2 * I, H)
+    w2 = weight_bytes_per_expert(fmt, H, I)
+    oft = 64 * H if cfg.oft else 0  # R_e: (H/32) blocks of 32x32 bf16
+    flops1 = 4.0 * R * H * I + (2.0 * R * H * 32 if cfg.oft else 0.0)
+    flops2 = 2.0 * R * H * I
+    a_rows = R if cfg.oft else T
+    g1_bytes = na * w13 + act_bytes(fmt, a_rows, H) + act_bytes(fmt, R, I)
+    g2_bytes = na * w2 + act_bytes(fmt, R, I) + R * H * 2
+    step_bytes = na * (w13 + w2 + oft) + 2 * T * H * 2 + 4 * T * E + 8 * T * k
+    return dict(active=na, flops=flops1 + flops2, bytes=step_bytes, gemm1=(flops1, g1_bytes), gemm2=(flops2, g2_bytes))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", help="c1..c5 (default c2: the Qwen3-30B-A3B-shaped FP8 layer)")
+    ap.add_argument("--chunk", type=int, default=None, help="chunk_experts (default: the workload's)")
+    ap.add_argument("--tile-rows", type=int, default=0, help="grouped-GEMM tile rows (0: automatic)")
+    ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle token sample (default: sized per workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the expert-parallel split "
+              "across GPUs is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from precision_moe_expert_amd import binding, synth
+
+    cfg = synth.CONFIGS[args.config]
+    if args.chunk:
+        cfg = cfg.replace(chunk=args.chunk)
+    li = synth.make_inputs(cfg, with_lm=False)
+
+    def dev(a, bf16=False):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        return t.view(torch.bfloat16) if bf16 else t
+
+    x, logits = dev(li.x, True), dev(li.logits)
+    w13, w2, s13, s2 = dev(li.w13), dev(li.w2), dev(li.s13), dev(li.s2)
+    oft = dev(li.oft, True) if li.oft is not None else None
+    layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
+                               tile_rows=args.tile_rows)
+    ws = binding.alloc_workspace(binding.workspace_bytes(layer, cfg.chunk))
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        binding.expert_forward(layer, x, logits, w13, w2, s13, s2, adapter=oft, chunk_experts=cfg.chunk, out=out,
+                               ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = max(wall * 1e3, ev0.elapsed_time(ev1)) / args.steps
+
+    # per-stage HIP-event durations over the same number of steps
+    stage_ms = {s: 0.0 for s in binding.STAGES}
+    stage_n = {s: 0 for s in binding.STAGES}
+    for _ in range(args.steps):
+        _, st = binding.expert_forward_timed(layer, x, logits, w13, w2, s13, s2, adapter=oft,
+                                             chunk_experts=cfg.chunk, out=out, ws=ws)
+        for s, (ms, n) in st.items():
+            stage_ms[s] += ms
+            stage_n[s] += n
+
+    # expert row counts from the library's own routing (accounting only)
+    r = binding.route_permute(logits, layer)
+    torch.cuda.synchronize()
+    counts = np.diff(r["expert_offsets"].cpu().numpy())
+    acc = accounting(cfg, counts)
+
+    sec = ms_per_step / 1e3
+    peak = MFMA_PEAK[cfg.fmt]
+    dom = max(("gemm1", "gemm2"), key=lambda s: stage_ms[s])
+    launch_ms = stage_ms[dom] / max(stage_n[dom], 1)
+    launches_per_step = stage_n[dom] / args.steps
+    f_dom, b_dom = acc[dom]
+    f_launch, b_launch = f_dom / launches_per_step, b_dom / launches_per_step
+    if b_launch / HBM_PEAK >= f_launch / peak:
+        roof = dict(bound="hbm", achieved=b_launch / (launch_ms / 1e3) / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=f_launch / (launch_ms / 1e3) / 1e12, peak=peak / 1e12, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"{dom} ({'k_gemm_' + {1: 'int4', 2: 'fp8', 3: 'mxfp4'}[cfg.fmt]})"
+    roof["launch_ms"] = launch_ms
+    roof["algorithmic_bytes_per_launch"] = b_launch
+    roof["algorithmic_flops_per_launch"] = f_launch
+
+    result = {
+        "metric": METRIC,
+        "value": cfg.T / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE[cfg.fmt],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE expert layer", "tokens": cfg.T, "hidden": cfg.H,
+                   "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I, "weight_format": synth.FMT_NAMES[cfg.fmt],
+                   "chunk_experts": cfg.chunk, "tile_rows": args.tile_rows or "auto", "oft_adapter": cfg.oft, "active_experts": acc["active"]},
+        "tflops": acc["flops"] / sec / 1e12,
+        "pct_mfma_peak": 100.0 * acc["flops"] / sec / peak,
+        "hbm_gbps_algorithmic": acc["bytes"] / sec / 1e9,
+        "pct_hbm_peak": 100.0 * acc["bytes"] / sec / HBM_PEAK,
+        "stages_ms_per_step": {s: stage_ms[s] / args.steps for s in binding.STAGES},
+        "temp_dequant_bytes": {"materialized_chunk_scheme": cfg.chunk * 3 * cfg.H * cfg.I * 2,
+                               "this_build_global": 0},
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        n = args.cpu_tokens or {1: 64, 2: 256, 3: 16, 4: 16, 5: 16}[cfg.cfg_id]
+        n = min(n, cfg.T)
+        toks = np.arange(n, dtype=np.int32)
+        c0 = time.perf_counter()
+        oracle.forward_inputs(li, tokens=toks)
+        csec = time.perf_counter() - c0
+        result["cpu_baseline"] = {"value": n / csec, "unit": "tokens/s", "cores": oracle.num_threads(),
+                                  "kind": "oracle", "sample": f"first {n} of {cfg.T} tokens (full routing, "
+                                  f"chunked dequant of the experts they touch), {csec:.1f} s"}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

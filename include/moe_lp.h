@@ -71,7 +71,7 @@ typedef struct {
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */
   int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation  */
-  int32_t reserved;
+  int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128 or 192 */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
 } moe_layer;
 
@@ -140,6 +140,29 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const 
                               const moe_qweights* qweights, const moe_scales* scales,
                               const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Stages reported by moe_expert_forward_timed. */
+enum {
+  MOE_STAGE_ROUTE = 0,   /* router top-k + softmax                          */
+  MOE_STAGE_PERMUTE = 1, /* histogram, scan, stable scatter, tile lists      */
+  MOE_STAGE_ACT = 2,     /* GEMM1 input: activation format and OFT rotation  */
+  MOE_STAGE_GEMM1 = 3,   /* dequant + gate/up GEMM + SwiGLU, one per chunk   */
+  MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM, one per chunk               */
+  MOE_STAGE_COMBINE = 5, /* weighted combine                                 */
+  MOE_NUM_STAGES = 6
+};
+
+/* moe_expert_forward with per-stage timing, for measurement: a HIP event is
+ * recorded on `stream` around every launch group, and the call synchronises
+ * the stream before it returns (unlike moe_expert_forward).  stage_ms and
+ * stage_launches are HOST arrays of MOE_NUM_STAGES entries, filled with the
+ * summed event durations (milliseconds) and the number of launch groups of
+ * each stage.  Same arguments, result and errors as moe_expert_forward. */
+moe_status moe_expert_forward_timed(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                    const moe_qweights* qweights, const moe_scales* scales,
+                                    const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                                    void* ws, size_t ws_bytes, void* stream, float* stage_ms,
+                                    int32_t* stage_launches);
 
 /* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
  * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:

@@ -18,14 +18,15 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
-            "moe_route_permute", "moe_expert_forward", "moe_combine", "moe_lm_head_workspace_bytes",
-            "moe_lm_head_logprob")
+            "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
+            "moe_lm_head_workspace_bytes", "moe_lm_head_logprob")
+STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine")
 
 
 class MoeLayer(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wformat", ctypes.c_int32),
-                ("oft_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("oft_block", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
                 ("adapter_expert_stride", ctypes.c_int64)]
 
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales), ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]
+        L.moe_expert_forward_timed.restype = ctypes.c_int
+        L.moe_expert_forward_timed.argtypes = L.moe_expert_forward.argtypes + [ctypes.POINTER(ctypes.c_float),
+                                                                                ctypes.POINTER(ctypes.c_int32)]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -108,9 +112,9 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None) -> MoeLayer:
+def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None, tile_rows=0) -> MoeLayer:
     stride = (H // 32) * 1024 if adapter_expert_stride is None else adapter_expert_stride
-    return MoeLayer(T, H, I, E, k, fmt, 32 if oft else 0, 0, stride if oft else 0)
+    return MoeLayer(T, H, I, E, k, fmt, 32 if oft else 0, tile_rows, stride if oft else 0)
 
 
 def workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
@@ -152,6 +156,24 @@ def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, 
                                     _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws), ws.numel(), _stream()),
            "moe_expert_forward")
     return out
+
+
+def expert_forward_timed(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=None, chunk_experts: int = 1,
+                         out=None, ws=None):
+    """moe_expert_forward_timed: same result, plus per-stage event times.
+    Returns (out, {stage: (ms, launches)})."""
+    if out is None:
+        out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2))
+    ms = (ctypes.c_float * len(STAGES))()
+    n = (ctypes.c_int32 * len(STAGES))()
+    _check(lib().moe_expert_forward_timed(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
+                                          ctypes.byref(sc), _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws),
+                                          ws.numel(), _stream(), ms, n), "moe_expert_forward_timed")
+    return out, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
 
 
 def combine(layer: MoeLayer, y_perm: torch.Tensor, topk_w: torch.Tensor, row_of: torch.Tensor,

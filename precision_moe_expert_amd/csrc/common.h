@@ -8,6 +8,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (HIP's uint4 is a union struct whose copies become
+// memcpys through the stack; this one stays in registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define MOE_DEV __device__ __forceinline__
@@ -75,6 +78,16 @@ MOE_DEV f32x4 mfma_fp8_fp4_scaled_16x16x128(const i32x8& a, const i32x4& b, int 
 }
 
 MOE_DEV int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes every wave wait for all of its outstanding global loads
+// (s_waitcnt vmcnt(0)) and so cancels any prefetch that runs across the
+// barrier; the GEMM main loops keep weight loads in flight across K steps.
+MOE_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <typename T>
 MOE_DEV T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }

@@ -10,7 +10,10 @@
 // Tile: BM rows x 256 output columns per workgroup (4 waves x 4 subtiles of
 // 16 columns); K step 128.  A (fp16 activations) is staged through a
 // double-buffered LDS tile shared by the 4 waves; B is read by each wave
-// straight from HBM (every weight is used by exactly one wave).
+// straight from HBM (every weight is used by exactly one wave) through a
+// three-slot register ring, two K steps ahead of its use.  The unpack costs
+// about 2.5 vector ops per weight, so the tile is as tall as the rows per
+// expert allow (up to 192) to keep it under the MFMA time.
 // GEMM1 pairs gate column n with up column I + n inside the same wave and
 // writes h = silu(gate) * up (fp16); GEMM2 writes y (bf16).
 #include "common.h"
@@ -35,11 +38,17 @@ MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2) {
   return r;
 }
 
+MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; }
+
 template <int BM, bool G1>
-__global__ __launch_bounds__(256) void k_gemm_int4(GemmArgs p) {
+__global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_int4(GemmArgs p) {
   constexpr int MT = BM / 16;
+  // register prefetch ring: weights and activation rows of step kt + RING - 1
+  // are issued while step kt computes (deep for short tiles, whose per-step
+  // compute is too short to cover a memory round trip, shallow where
+  // registers are scarce)
+  constexpr int RING = (BM <= 16 ? 6 : BM <= 32 ? 4 : BM <= 48 ? 3 : BM <= 96 ? 2 : 3);  // deepest ring that fits without spills
   constexpr int LDA = 128 + 8;  // fp16 elements per LDS row (16-byte pad)
-  constexpr int ALOADS = (BM * 16 + 255) / 256;
   __shared__ __align__(16) uint16_t As[2][BM * LDA];
   const int nblk = G1 ? p.inter / 128 : p.N / 256;
   ChunkWork cw;
@@ -47,9 +56,12 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmArgs p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int K = p.K, KT = K / 128;
-  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const char* Abase = static_cast<const char*>(p.a);
+  const int lpart = threadIdx.x & 15;
 
-  for (int wk = xcd_virtual_id(); wk < cw.nwork; wk += gridDim.x) {
+  for (int base = 0; base < cw.nwork; base += gridDim.x) {
+    const int wk = xcd_item(base, cw.nwork);
+    if (wk < 0) continue;
     const Tile tl = tile_of(p, cw, wk, BM);
     int col[4];
     if (G1) {
@@ -60,23 +72,22 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
     }
-    const uint8_t* wrow[4];
-    const uint16_t* srow[4];
+    // B: per-expert base (uniform) + 32-bit per-lane offsets
+    const uint8_t* wexp = p.w + tl.e * p.w_expert_bytes;
+    const uint16_t* sexp = static_cast<const uint16_t*>(p.w_scale) + tl.e * p.ws_expert_elems;
+    uint32_t woff[4], soff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wrow[i] = p.w + tl.e * p.w_expert_bytes + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
-      srow[i] = static_cast<const uint16_t*>(p.w_scale) + tl.e * p.ws_expert_elems + (int64_t)(col[i] + ln) * (K / 32) + lg;
+      woff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 2) + lg * 16;
+      soff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 32) + lg;
     }
-    // loader: thread -> (row, 16-byte part) for each of its ALOADS rows
-    const int lpart = threadIdx.x & 15;
-    const uint16_t* arow[ALOADS];
-    int lrow[ALOADS];
+    // A: thread copies 16-byte part `lpart` of rows (tid/16) + 16j
+    uint32_t aoff[MT];
 #pragma unroll
-    for (int j = 0; j < ALOADS; ++j) {
-      lrow[j] = (threadIdx.x >> 4) + 16 * j;
-      const int rr = tl.rbase + min(lrow[j], tl.nrows - 1);
+    for (int j = 0; j < MT; ++j) {
+      const int rr = tl.rbase + min((int)(threadIdx.x >> 4) + 16 * j, tl.nrows - 1);
       const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      arow[j] = A + (int64_t)src * K + lpart * 8;
+      aoff[j] = (uint32_t)src * (uint32_t)(K * 2) + lpart * 16;
     }
     f32x4 acc[MT][4];
 #pragma unroll
@@ -84,66 +95,82 @@ __global__ __launch_bounds__(256) void k_gemm_int4(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 areg[ALOADS];
-    uint4 bcur[4], bnext[4];
-    uint16_t scur[4], snext[4];
+    auto loadB = [&](int kt, u32x4 (&b)[4], uint16_t (&s)[4]) {
 #pragma unroll
-    for (int j = 0; j < ALOADS; ++j)
-      if (lrow[j] < BM) areg[j] = *reinterpret_cast<const uint4*>(arow[j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bcur[i] = *reinterpret_cast<const uint4*>(wrow[i]);
-      scur[i] = srow[i][0];
-    }
-#pragma unroll
-    for (int j = 0; j < ALOADS; ++j)
-      if (lrow[j] < BM) *reinterpret_cast<uint4*>(&As[0][lrow[j] * LDA + lpart * 8]) = areg[j];
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < KT) {
-#pragma unroll
-        for (int j = 0; j < ALOADS; ++j)
-          if (lrow[j] < BM) areg[j] = *reinterpret_cast<const uint4*>(arow[j] + (kt + 1) * 128);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bnext[i] = *reinterpret_cast<const uint4*>(wrow[i] + (kt + 1) * 64);
-          snext[i] = srow[i][(kt + 1) * 4];
-        }
+      for (int i = 0; i < 4; ++i) {
+        b[i] = *reinterpret_cast<const u32x4*>(wexp + woff[i] + kt * 64);
+        s[i] = sexp[soff[i] + kt * 4];
       }
+    };
+    auto loadA = [&](int kt, u32x4 (&areg)[MT]) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) areg[j] = *reinterpret_cast<const u32x4*>(Abase + aoff[j] + kt * 256);
+    };
+    auto storeA = [&](int buf, const u32x4 (&areg)[MT]) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        *reinterpret_cast<u32x4*>(&As[buf][((threadIdx.x >> 4) + 16 * j) * LDA + lpart * 8]) = areg[j];
+    };
+    // one K step: prefetch B(kt+2) into bl and A(kt+1) into registers,
+    // compute with B(kt) in bc and A(kt) in LDS, then publish A(kt+1)
+    auto step = [&](int kt, const u32x4 (&bc)[4], const uint16_t (&sc)[4], u32x4 (&bl)[4], uint16_t (&sl)[4], const u32x4 (&acur)[MT], u32x4 (&al)[MT]) {
+      // prefetch target, clamped so that every step issues the same loads: the
+      // compiler can then wait for exactly the loads a step needs instead of
+      // draining all of them
+      const int kpre = min(kt + RING - 1, KT - 1);
+      loadA(kpre, al);
+      // A must be issued before B: the vector-memory counter
+      // completes in order, so waiting for A would otherwise also wait for B
+      __builtin_amdgcn_sched_barrier(0);
+      loadB(kpre, bl, sl);
+      // keep the prefetches here: the scheduler would otherwise sink them
+      // next to their first use and expose the full memory latency
+      __builtin_amdgcn_sched_barrier(0);
+      const int buf = kt & 1;
       f16x2 s2[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const _Float16 sh = (_Float16)bf16_bits_to_f32(scur[i]);
+        const _Float16 sh = (_Float16)bf16_bits_to_f32(sc[i]);
         s2[i] = (f16x2){sh, sh};
       }
+      const uint16_t* arow = &As[buf][ln * LDA + lg * 32];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         f16x8 bf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wv = s == 0 ? bcur[i].x : s == 1 ? bcur[i].y : s == 2 ? bcur[i].z : bcur[i].w;
-          bf[i] = int4x8_to_f16(wv, s2[i]);
-        }
+        for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bc[i], s), s2[i]);
+        // A fragments are read two m-subtiles ahead of their MFMAs
+        f16x8 af[3];
+        af[0] = *reinterpret_cast<const f16x8*>(arow + s * 8);
+        if (MT > 1) af[1] = *reinterpret_cast<const f16x8*>(arow + 16 * LDA + s * 8);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const f16x8 af = *reinterpret_cast<const f16x8*>(&As[buf][(m * 16 + ln) * LDA + lg * 32 + s * 8]);
+          if (m + 2 < MT) af[(m + 2) % 3] = *reinterpret_cast<const f16x8*>(arow + (m + 2) * 16 * LDA + s * 8);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af, bf[i], acc[m][i]);
+          for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[m % 3], bf[i], acc[m][i]);
         }
       }
-      if (kt + 1 < KT) {
+      if (kt + 1 < KT) storeA(buf ^ 1, acur);
+      lds_barrier();
+    };
+
+    u32x4 bq[RING][4];
+    uint16_t wq[RING][4];
+    u32x4 aq[RING][MT];
+    // prologue: steps 0 .. RING-2 in flight, step 0's activation tile in LDS
 #pragma unroll
-        for (int j = 0; j < ALOADS; ++j)
-          if (lrow[j] < BM) *reinterpret_cast<uint4*>(&As[buf ^ 1][lrow[j] * LDA + lpart * 8]) = areg[j];
+    for (int r = 0; r + 1 < RING; ++r) {
+      loadA(min(r, KT - 1), aq[r]);
+      loadB(min(r, KT - 1), bq[r], wq[r]);
+    }
+    storeA(0, aq[0]);
+    lds_barrier();
+    for (int kt = 0; kt < KT; kt += RING) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bcur[i] = bnext[i];
-          scur[i] = snext[i];
-        }
-      }
-      __syncthreads();
+      for (int r = 0; r < RING; ++r)
+        if (kt + r < KT)
+          step(kt + r, bq[r], wq[r], bq[(r + RING - 1) % RING], wq[(r + RING - 1) % RING], aq[(r + 1) % RING],
+               aq[(r + RING - 1) % RING]);
     }
 
     if (G1) {
@@ -185,7 +212,10 @@ static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
     case 16: hipLaunchKernelGGL((k_gemm_int4<16, G1>), dim3(grid), dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL((k_gemm_int4<32, G1>), dim3(grid), dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL((k_gemm_int4<64, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_int4<128, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 48: hipLaunchKernelGGL((k_gemm_int4<48, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 96: hipLaunchKernelGGL((k_gemm_int4<96, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_gemm_int4<128, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_int4<192, G1>), dim3(grid), dim3(256), 0, s, a); break;
   }
 }
 

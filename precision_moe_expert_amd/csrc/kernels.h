@@ -34,6 +34,7 @@ struct GemmArgs {
   int top_k;
   int chunk;                   // chunk index c
   int chunk_experts;           // C
+  int nb_fastest;              // 1: item order (tile, N block) with N blocks fastest
 };
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "kernels.h"
 #include "moe_lp.h"
 
@@ -25,6 +27,7 @@ struct Dims {
   bool oft;
   int64_t R;
   int nblk;
+  int tile_rows;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -43,6 +46,12 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if (L->num_experts > MAX_EXPERTS || L->top_k > MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
+  if (L->tile_rows != 0 && L->tile_rows != 16 && L->tile_rows != 32 && L->tile_rows != 48 && L->tile_rows != 64 &&
+      L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 192)
+    return MOE_ERR_UNSUPPORTED;
+  // the GEMMs address activation rows with 32-bit byte offsets
+  if ((int64_t)L->num_tokens * L->top_k * (int64_t)(L->hidden > L->inter ? L->hidden : L->inter) * 2 >= (1ll << 32))
+    return MOE_ERR_UNSUPPORTED;
   d->T = L->num_tokens;
   d->H = L->hidden;
   d->I = L->inter;
@@ -52,6 +61,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   d->oft = L->oft_block != 0;
   d->R = (int64_t)d->T * d->k;
   d->nblk = (int)((d->R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK);
+  d->tile_rows = L->tile_rows;
   return MOE_OK;
 }
 
@@ -96,11 +106,15 @@ WsLayout layout(const Dims& d) {
   return w;
 }
 
-// Rows per GEMM tile from the mean rows per expert.
+// Rows per GEMM tile from the mean rows per expert and the weight format
+// (measured on MI355X: the INT4 unpack favours two workgroups per CU at 64
+// rows; FP8 and MXFP4 favour 128-row tiles once experts have that many rows).
 int choose_bm(const Dims& d) {
+  if (d.tile_rows) return d.tile_rows;
   const int64_t mean = d.R / d.E;
   if (mean <= 16) return 16;
-  if (mean <= 48) return 32;
+  if (mean <= 32) return 32;
+  if (d.fmt == MOE_W_INT4_G32_BF16) return 64;
   if (mean <= 96) return 64;
   return 128;
 }
@@ -115,6 +129,49 @@ int gemm_grid(const Dims& d, int bm, int chunk, int nblk_n) {
 }
 
 moe_status launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// Optional per-stage timing: a HIP event is recorded on the stream before and
+// after every launch group; durations are read after one stream sync.
+struct StageTimer {
+  hipStream_t s;
+  std::vector<hipEvent_t> ev;  // start/stop pairs
+  std::vector<int> stage_of;
+  bool ok = true;
+  void begin(int stage) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) ok = false;
+    ev.push_back(a);
+    ev.push_back(b);
+    stage_of.push_back(stage);
+    if (ok && hipEventRecord(a, s) != hipSuccess) ok = false;
+  }
+  void end() {
+    if (ok && hipEventRecord(ev.back(), s) != hipSuccess) ok = false;
+  }
+  void finish(float* ms, int32_t* counts) {
+    for (int i = 0; i < MOE_NUM_STAGES; ++i) { ms[i] = 0.0f; counts[i] = 0; }
+    if (ok && hipStreamSynchronize(s) != hipSuccess) ok = false;
+    for (size_t i = 0; i < stage_of.size(); ++i) {
+      float t = 0.0f;
+      if (ok && hipEventElapsedTime(&t, ev[2 * i], ev[2 * i + 1]) == hipSuccess) {
+        ms[stage_of[i]] += t;
+        counts[stage_of[i]] += 1;
+      }
+      if (ev[2 * i]) (void)hipEventDestroy(ev[2 * i]);
+      if (ev[2 * i + 1]) (void)hipEventDestroy(ev[2 * i + 1]);
+    }
+  }
+};
+
+struct Scope {
+  StageTimer* t;
+  Scope(StageTimer* tm, int stage) : t(tm) { if (t) t->begin(stage); }
+  ~Scope() { if (t) t->end(); }
+};
+
+moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float* logits, const moe_qweights* qw,
+                        const moe_scales* sc, const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                        void* ws, size_t ws_bytes, void* stream, StageTimer* tm);
 
 }  // namespace
 
@@ -171,6 +228,32 @@ moe_status moe_route_permute(const moe_layer* layer, const float* logits, const 
 moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const float* logits,
                               const moe_qweights* qw, const moe_scales* sc, const void* adapter_bf16,
                               int32_t chunk_experts, void* out_bf16, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(layer, x_bf16, logits, qw, sc, adapter_bf16, chunk_experts, out_bf16, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+moe_status moe_expert_forward_timed(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                    const moe_qweights* qw, const moe_scales* sc, const void* adapter_bf16,
+                                    int32_t chunk_experts, void* out_bf16, void* ws, size_t ws_bytes, void* stream,
+                                    float* stage_ms, int32_t* stage_launches) {
+  if (stage_ms == nullptr || stage_launches == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  StageTimer* tm = new StageTimer();
+  tm->s = static_cast<hipStream_t>(stream);
+  moe_status st = forward_impl(layer, x_bf16, logits, qw, sc, adapter_bf16, chunk_experts, out_bf16, ws, ws_bytes,
+                               stream, tm);
+  tm->finish(stage_ms, stage_launches);
+  const bool ok = tm->ok;
+  delete tm;
+  if (st == MOE_OK && !ok) st = MOE_ERR_DEVICE;
+  return st;
+}
+
+}  // extern "C"
+
+namespace {
+moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float* logits, const moe_qweights* qw,
+                        const moe_scales* sc, const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                        void* ws, size_t ws_bytes, void* stream, StageTimer* tm) {
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
@@ -207,10 +290,13 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const 
   const int bm = choose_bm(d);
 
   // 1-2. route and permute
-  launch_route(logits, d.T, d.E, d.k, ids, wts, s);
-  launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, s);
+  { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
+  { Scope sc_(tm, MOE_STAGE_PERMUTE);
+    launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, s); }
 
   // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
+  {
+  Scope sc_(tm, MOE_STAGE_ACT);
   if (d.fmt == MOE_W_INT4_G32_BF16) {
     if (d.oft)
       launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
@@ -221,6 +307,7 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const 
     launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), s);
   } else {
     launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), s);
+  }
   }
 
   // 4. chunk loop over the active experts: GEMM1 (+SwiGLU) then GEMM2 per chunk
@@ -266,27 +353,31 @@ moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const 
     g->top_k = d.k;
     g->chunk_experts = chunk_experts;
   }
+  // share whichever operand of a work item is larger: its activation tile
+  // (bm rows x K) or its 256-column weight slice
+  auto a_bytes = [&](int K) { return (double)bm * K * (d.fmt == MOE_W_INT4_G32_BF16 ? 2.0 : 1.0); };
+  const double b_per_k = d.fmt == MOE_W_FP8_E4M3_B128 ? 256.0 : 128.0;
+  g1.nb_fastest = a_bytes(d.H) > b_per_k * d.H ? 1 : 0;
+  g2.nb_fastest = a_bytes(d.I) > b_per_k * d.I ? 1 : 0;
   const int grid1 = gemm_grid(d, bm, chunk_experts, d.I / 128);
   const int grid2 = gemm_grid(d, bm, chunk_experts, d.H / 256);
   for (int c = 0; c < nchunks; ++c) {
     g1.chunk = c;
     g2.chunk = c;
-    if (d.fmt == MOE_W_INT4_G32_BF16) {
-      launch_gemm_int4(g1, true, bm, grid1, s);
-      launch_gemm_int4(g2, false, bm, grid2, s);
-    } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
-      launch_gemm_fp8(g1, true, bm, grid1, s);
-      launch_gemm_fp8(g2, false, bm, grid2, s);
-    } else {
-      launch_gemm_mxfp4(g1, true, bm, grid1, s);
-      launch_gemm_mxfp4(g2, false, bm, grid2, s);
-    }
+    auto gemm = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4
+              : d.fmt == MOE_W_FP8_E4M3_B128 ? launch_gemm_fp8 : launch_gemm_mxfp4;
+    { Scope sc_(tm, MOE_STAGE_GEMM1); gemm(g1, true, bm, grid1, s); }
+    { Scope sc_(tm, MOE_STAGE_GEMM2); gemm(g2, false, bm, grid2, s); }
   }
 
   // 5. weighted combine back to token order
-  launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s);
+  { Scope sc_(tm, MOE_STAGE_COMBINE);
+    launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s); }
   return launch_status();
 }
+}  // namespace
+
+extern "C" {
 
 moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w, const int32_t* row_of,
                        void* out_bf16, void* stream) {

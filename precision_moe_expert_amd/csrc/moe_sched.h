@@ -35,12 +35,21 @@ struct Tile {
   int nb;      // N block
 };
 
-// Item wk -> (tile, N block), tiles fastest so that concurrently running
-// workgroups share an expert's weights.
+// Item wk -> (tile, N block).  With tiles fastest, workgroups that run at
+// the same time share an expert's weight slice; with N blocks fastest they
+// share one tile of activation rows.  The host picks the order whose shared
+// operand is the larger one.
 MOE_DEV Tile tile_of(const GemmArgs& p, const ChunkWork& cw, int wk, int bm) {
   Tile t;
-  t.nb = wk / cw.ntiles;
-  const int tile = cw.t0 + wk % cw.ntiles;
+  const int nblk = cw.nwork / cw.ntiles;
+  int tile;
+  if (p.nb_fastest) {
+    t.nb = wk % nblk;
+    tile = cw.t0 + wk / nblk;
+  } else {
+    t.nb = wk / cw.ntiles;
+    tile = cw.t0 + wk % cw.ntiles;
+  }
   int lo = cw.a0, hi = cw.a1 - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -53,11 +62,18 @@ MOE_DEV Tile tile_of(const GemmArgs& p, const ChunkWork& cw, int wk, int bm) {
   return t;
 }
 
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
-// XCD (and its L2) takes a contiguous range of work items.  grid % 8 == 0.
-MOE_DEV int xcd_virtual_id() {
-  const int g = gridDim.x, b = blockIdx.x;
-  return (b & 7) * (g >> 3) + (b >> 3);
+// Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Items are walked in rounds of gridDim.x; within a round of n items, XCD x
+// takes the contiguous item range [x*per, (x+1)*per), per = ceil(n/8), so that
+// neighbouring items (the row tiles of one expert, which read the same
+// weights) share an L2.  Returns -1 for a block with nothing in this round.
+// gridDim.x must be a multiple of 8.
+MOE_DEV int xcd_item(int round_base, int nwork) {
+  const int n = min((int)gridDim.x, nwork - round_base);
+  const int per = (n + 7) >> 3;
+  const int b = blockIdx.x;
+  const int slot = (b & 7) * per + (b >> 3);
+  return ((b >> 3) < per && slot < n) ? round_base + slot : -1;
 }
 
 }  // namespace moe

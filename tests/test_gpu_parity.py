@@ -157,3 +157,18 @@ def test_t0_is_noop():
     out = binding.expert_forward(layer, x, lg, z, z, z, z, chunk_experts=1,
                                  out=torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
     assert out.shape == (0, 256)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
+def test_forward_every_tile_height(fmt, tile_rows):
+    """Each grouped-GEMM tile height against the oracle: ~250 rows per expert,
+    so tall tiles run full and ragged; I = 768 gives three 256-wide N blocks."""
+    cfg = small(fmt, T=300, H=512, I=768, E=5, k=4, chunk=2, cfg_id=60 + fmt)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    d.layer.tile_rows = tile_rows
+    out = gu.bf16_to_np(d.forward())
+    err = gu.row_rel_err(out, oracle.forward_inputs(li))
+    print(f"fmt {fmt} tile {tile_rows}: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
