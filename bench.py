@@ -148,8 +148,15 @@ def main():
     else:
         roof = dict(bound="mfma", achieved=f_launch / (launch_ms / 1e3) / 1e12, peak=peak / 1e12, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = f"{dom} ({'k_gemm_' + {1: 'int4', 2: 'fp8', 3: 'mxfp4'}[cfg.fmt]})"
+    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4"}[cfg.fmt]
+    bm = binding.tile_rows(layer)
+    kname = f"k_gemm_{fmt_name}<{bm}, {'true' if dom == 'gemm1' else 'false'}>"
+    roof["kernel"] = kname
+    # HBM bytes per launch measured by rocprofv3 counters (copy-calibrated),
+    # valid only while the kernel source is unchanged
+    from precision_moe_expert_amd import profiling
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{fmt_name}_{cfg.name}_traffic.txt"))
+    roof["traffic"] = tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname else None
     roof["launch_ms"] = launch_ms
     roof["algorithmic_bytes_per_launch"] = b_launch
     roof["algorithmic_flops_per_launch"] = f_launch

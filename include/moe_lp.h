@@ -118,6 +118,10 @@ size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
 /* Workspace bytes moe_route_permute needs (scan scratch only). */
 size_t moe_route_workspace_bytes(const moe_layer* layer);
 
+/* Rows per grouped-GEMM tile that moe_expert_forward uses for this layer
+ * (layer->tile_rows if set, else the automatic choice); 0 if invalid. */
+int32_t moe_tile_rows(const moe_layer* layer);
+
 /* Router top-k + softmax over the selected logits, then the expert histogram,
  * exclusive scan and stable permutation by expert (Orbit announcement,
  * 技术细节: router-selected experts grouped dynamically).

@@ -17,7 +17,7 @@ _lib = None
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
 FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
 
-EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
+EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_rows",
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
             "moe_lm_head_workspace_bytes", "moe_lm_head_logprob")
 STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine")
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_int32]
+        L.moe_tile_rows.restype = ctypes.c_int32
+        L.moe_tile_rows.argtypes = [ctypes.POINTER(MoeLayer)]
         L.moe_route_workspace_bytes.restype = ctypes.c_size_t
         L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
         L.moe_lm_head_workspace_bytes.restype = ctypes.c_size_t
@@ -119,6 +121,10 @@ def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None, tile_r
 
 def workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(layer), int(chunk_experts))
+
+
+def tile_rows(layer: MoeLayer) -> int:
+    return lib().moe_tile_rows(ctypes.byref(layer))
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:

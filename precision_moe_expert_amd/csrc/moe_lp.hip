@@ -196,6 +196,12 @@ size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   return layout(d).total;
 }
 
+int32_t moe_tile_rows(const moe_layer* layer) {
+  Dims d;
+  if (check_layer(layer, &d) != MOE_OK) return 0;
+  return choose_bm(d);
+}
+
 size_t moe_route_workspace_bytes(const moe_layer* layer) {
   Dims d;
   if (check_layer(layer, &d) != MOE_OK) return 0;
@@ -353,12 +359,11 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     g->top_k = d.k;
     g->chunk_experts = chunk_experts;
   }
-  // share whichever operand of a work item is larger: its activation tile
-  // (bm rows x K) or its 256-column weight slice
-  auto a_bytes = [&](int K) { return (double)bm * K * (d.fmt == MOE_W_INT4_G32_BF16 ? 2.0 : 1.0); };
-  const double b_per_k = d.fmt == MOE_W_FP8_E4M3_B128 ? 256.0 : 128.0;
-  g1.nb_fastest = a_bytes(d.H) > b_per_k * d.H ? 1 : 0;
-  g2.nb_fastest = a_bytes(d.I) > b_per_k * d.I ? 1 : 0;
+  // expert-major item order (N blocks fastest, an expert's tiles adjacent):
+  // an XCD then works on all items of one or two experts at once, so both
+  // the expert's weight slices and its activation tiles stay in that L2
+  g1.nb_fastest = 1;
+  g2.nb_fastest = 1;
   const int grid1 = gemm_grid(d, bm, chunk_experts, d.I / 128);
   const int grid2 = gemm_grid(d, bm, chunk_experts, d.H / 256);
   for (int c = 0; c < nchunks; ++c) {
