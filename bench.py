@@ -189,7 +189,7 @@ def main():
 
     if not args.no_cpu_baseline:
         import oracle
-        n = args.cpu_tokens or {1: 64, 2: 256, 3: 16, 4: 16, 5: 16}[cfg.cfg_id]
+        n = args.cpu_tokens or {1: 64, 2: 2048, 3: 16, 4: 16, 5: 16}[cfg.cfg_id]
         n = min(n, cfg.T)
         toks = np.arange(n, dtype=np.int32)
         c0 = time.perf_counter()
