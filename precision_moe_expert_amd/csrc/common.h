@@ -52,7 +52,8 @@ MOE_DEV uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)r;
 }
 
-MOE_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g); the reciprocal is the hardware one (1 ulp).
+MOE_DEV float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // 16x16x32 fp16 MFMA: lane l supplies A[l%16][8*(l/16)+i], B[8*(l/16)+i][l%16];
 // accumulator element i of lane l is C[4*(l/16)+i][l%16].
@@ -92,7 +93,64 @@ MOE_DEV void lds_barrier() {
 template <typename T>
 MOE_DEV T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Maximum of non-negative floats (e.g. |x|) over the 16 lanes of a DPP row
+// (lanes 16r .. 16r+15), returned in every lane of the row: quad swaps
+// (xor 1, xor 2), then row rotations by 4 and 8, register to register.  For
+// non-negative IEEE values the integer order of the bit patterns is the
+// numeric order (a NaN, all exponent bits set, wins).
+template <int CTRL>
+MOE_DEV int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+MOE_DEV float row16_max_nonneg(float v) {
+  int x = __float_as_int(v);
+  x = max(x, dpp_i32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp_i32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp_i32<0x124>(x));  // row_ror:4
+  x = max(x, dpp_i32<0x128>(x));  // row_ror:8
+  return __int_as_float(x);
+}
+
 // Position of element n inside the INT4-path activation layout: every aligned
 // group of 8 fp16 values is stored in the order [0,4,1,5,2,6,3,7], matching
 // the order in which the in-register INT4 unpack produces weight pairs.
 MOE_DEV int i4act_pos(int n) { return (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1); }
+
+// ---- direct global -> LDS loads (gfx950 global_load_lds_*) ----------------
+// Each lane moves its bytes to LDS at  base + lane * size  (base in M0; the
+// base must be wave-uniform).  These loads count on the vector-memory counter
+// like any other load; the GEMM main loops issue only these in their K loops
+// and wait for exactly the stage they need with wait_vmcnt<N>().  Loads the
+// compiler issues elsewhere are younger or older than the awaited ones, so
+// they can only make such a wait longer, never too short.
+MOE_DEV uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+MOE_DEV void dma_b128(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
+MOE_DEV void dma_b32(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
+MOE_DEV void dma_b16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
+MOE_DEV void dma_b8(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
+// Wave-uniform read through the scalar unit (constant address space), so that
+// it is counted by lgkmcnt and never by the vmcnt that the LDS-DMA rings wait on.
+MOE_DEV float ld_uniform_f32(const float* p) { return *(const __attribute__((address_space(4))) float*)p; }
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most n (0..3, wave-uniform) stages of NPER loads each are in flight.
+template <int NPER>
+MOE_DEV void wait_stages(int n) {
+  if (n >= 3) wait_vmcnt<3 * NPER>();
+  else if (n == 2) wait_vmcnt<2 * NPER>();
+  else if (n == 1) wait_vmcnt<NPER>();
+  else wait_vmcnt<0>();
+}

@@ -13,34 +13,46 @@
 
 namespace moe {
 
+// LDS bytes of one pipeline stage: activation rows (128 B each, whole DMA
+// groups of 8 rows per wave), one fp32 activation scale per row slot (1 KB),
+// and each wave's weight fragments (4 subtiles x 2 halves x 1 KB).
+template <int BM>
+struct Fp8Stage {
+  static constexpr int NA = (BM * 8 + 255) / 256;  // activation DMA groups per wave
+  static constexpr int ROWS = NA * 32;              // activation row slots
+  static constexpr int A_BYTES = ROWS * 128;
+  static constexpr int AS_OFF = A_BYTES;
+  static constexpr int B_OFF = AS_OFF + 1024;
+  static constexpr int BYTES = B_OFF + 4 * 8 * 1024;
+  static constexpr int S = (152 * 1024) / BYTES > 4 ? 4 : (152 * 1024) / BYTES;  // stages
+  static constexpr int NPER = NA + 1 + 8;           // DMA instructions per wave per stage
+};
+
 template <int BM, bool G1>
-__global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_fp8(GemmArgs p) {
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p) {
   constexpr int MT = BM / 16;
-  // register prefetch ring: weights and activation rows of step kt + RING - 1
-  // are issued while step kt computes (deep for short tiles, whose per-step
-  // compute is too short to cover a memory round trip, shallow where
-  // registers are scarce)
-  constexpr int RING = (BM <= 16 ? 4 : BM <= 32 ? 3 : 2);  // deepest ring that fits without spills
-  constexpr int LDA = 128 + 16;  // bytes per LDS row
-  constexpr int NCHUNK = BM * 8;  // 16-byte pieces per A tile
-  constexpr int ALOADS = (NCHUNK + 255) / 256;
-  constexpr bool AFULL = NCHUNK % 256 == 0;  // every thread loads ALOADS pieces
-  __shared__ __align__(16) uint8_t As[2][BM * LDA];
-  __shared__ __align__(16) float Ss[2][BM];
+  using ST = Fp8Stage<BM>;
+  constexpr int S = ST::S;
+  static_assert(S >= 2 && S <= 5, "LDS stages");
+  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
+  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
   __shared__ float red[4][BM];
   const int nblk = G1 ? p.inter / 128 : p.N / 256;
   ChunkWork cw;
   if (!chunk_work(p, nblk, cw)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
-  const float* AS = static_cast<const float*>(p.a_scale);
+  const char* ASbase = static_cast<const char*>(p.a_scale);
+  const float* WS = static_cast<const float*>(p.w_scale);
+  const uint32_t smem0 = lds_u32(smem);
 
   for (int base = 0; base < cw.nwork; base += gridDim.x) {
     const int wk = xcd_item(base, cw.nwork);
     if (wk < 0) continue;
     const Tile tl = tile_of(p, cw, wk, BM);
+    lds_barrier();  // every wave is done with the previous item's stages
     int col[4];
     if (G1) {
       const int g0 = tl.nb * 128 + wave * 32;
@@ -50,124 +62,135 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_fp8(GemmArgs p
 #pragma unroll
       for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
     }
-    const uint8_t* wexp = p.w + tl.e * p.w_expert_bytes;
-    const float* wsexp = static_cast<const float*>(p.w_scale) + tl.e * p.ws_expert_elems;
-    uint32_t woff[4], wsoff[4];
+    // per-lane global sources of this item's DMA pieces (K offset added per step)
+    const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
+    const float* wsexp = WS + tl.e * p.ws_expert_elems;
+    const char* bsrc[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      woff[i] = (uint32_t)(col[i] + ln) * (uint32_t)K + lg * 32;
-      wsoff[i] = (uint32_t)(col[i] / 128) * (uint32_t)KT;
-    }
-    uint32_t aoff[ALOADS];
-    int lrow[ALOADS], lpart[ALOADS];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < ALOADS; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      lrow[j] = c / 8;
-      lpart[j] = c % 8;
-      const int rr = tl.rbase + min(min(lrow[j], BM - 1), tl.nrows - 1);
-      const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      aoff[j] = (uint32_t)src * (uint32_t)K + lpart[j] * 16;
+      for (int h = 0; h < 2; ++h) bsrc[i][h] = wexp + (int64_t)(col[i] + ln) * K + (lg + 4 * h) * 16;
+    const char* asrc[ST::NA];
+#pragma unroll
+    for (int j = 0; j < ST::NA; ++j) {
+      const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/8, slot c%8
+      const int row = c >> 3, slot = c & 7;
+      const int part = slot ^ (row & 7);               // XOR swizzle of 16-byte parts
+      const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+      const int sr = p.sorted_rows[rr];
+      const int src = p.a_per_token ? sr / p.top_k : rr;
+      asrc[j] = Abase + (int64_t)src * K + part * 16;
     }
-    const float* srow = nullptr;
-    if (threadIdx.x < BM) {
-      const int rr = tl.rbase + min((int)threadIdx.x, tl.nrows - 1);
-      const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      srow = AS + (int64_t)src * KT;
+    const char* ssrc;
+    {
+      const int row = wave * 64 + lane;
+      const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+      const int sr = p.sorted_rows[rr];
+      const int src = p.a_per_token ? sr / p.top_k : rr;
+      ssrc = ASbase + (int64_t)src * KT * 4;
     }
+    auto issue = [&](int kt, int slot) {
+      const uint32_t sb = smem0 + slot * ST::BYTES;
+#pragma unroll
+      for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
+      dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dma_b128(bsrc[i][h] + kt * 128, sb + ST::B_OFF + (wave * 8 + i * 2 + h) * 1024);
+    };
     f32x4 acc[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto loadB = [&](int kt, u32x4 (&b)[4][2], float (&ws)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        b[i][0] = *reinterpret_cast<const u32x4*>(wexp + woff[i] + kt * 128);
-        b[i][1] = *reinterpret_cast<const u32x4*>(wexp + woff[i] + kt * 128 + 16);
-        ws[i] = wsexp[wsoff[i] + kt];
+    for (int s = 0; s + 1 < S; ++s)
+      if (s < KT) issue(s, s);
+    const float* ws0 = wsexp + (col[0] / 128) * KT;
+    const float* ws2 = wsexp + (col[2] / 128) * KT;
+    float wnext[2] = {ld_uniform_f32(ws0), ld_uniform_f32(ws2)};
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+      lds_barrier();                                    // ... and every other wave's
+      if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+      const float wc0 = wnext[0], wc2 = wnext[1];
+      if (kt + 1 < KT) {
+        wnext[0] = ld_uniform_f32(ws0 + kt + 1);
+        wnext[1] = ld_uniform_f32(ws2 + kt + 1);
       }
-    };
-    auto loadA = [&](int kt, u32x4 (&areg)[ALOADS], float& sreg) {
-#pragma unroll
-      for (int j = 0; j < ALOADS; ++j)
-        if (AFULL || lrow[j] < BM) areg[j] = *reinterpret_cast<const u32x4*>(Abase + aoff[j] + kt * 128);
-      if (srow) sreg = srow[kt];
-    };
-    auto storeA = [&](int buf, const u32x4 (&areg)[ALOADS], float sreg) {
-#pragma unroll
-      for (int j = 0; j < ALOADS; ++j)
-        if (AFULL || lrow[j] < BM) *reinterpret_cast<u32x4*>(&As[buf][lrow[j] * LDA + lpart[j] * 16]) = areg[j];
-      if (srow) Ss[buf][threadIdx.x] = sreg;
-    };
-    auto step = [&](int kt, const u32x4 (&bc)[4][2], const float (&wc)[4], u32x4 (&bl)[4][2], float (&wl)[4], const u32x4 (&acur)[ALOADS], const float& scur, u32x4 (&al)[ALOADS], float& sl_a) {
-      // prefetch target, clamped so that every step issues the same loads: the
-      // compiler can then wait for exactly the loads a step needs instead of
-      // draining all of them
-      const int kpre = min(kt + RING - 1, KT - 1);
-      loadA(kpre, al, sl_a);
-      // A must be issued before B: the vector-memory counter
-      // completes in order, so waiting for A would otherwise also wait for B
-      __builtin_amdgcn_sched_barrier(0);
-      loadB(kpre, bl, wl);
-      // keep the prefetches here: the scheduler would otherwise sink them
-      // next to their first use and expose the full memory latency
-      __builtin_amdgcn_sched_barrier(0);
-      const int buf = kt & 1;
+      const uint8_t* st = smem + (kt % S) * ST::BYTES;
+      const float* As = reinterpret_cast<const float*>(st + ST::AS_OFF);
       i32x8 bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bf[i] = (i32x8){(int)bc[i][0].x, (int)bc[i][0].y, (int)bc[i][0].z, (int)bc[i][0].w,
-                        (int)bc[i][1].x, (int)bc[i][1].y, (int)bc[i][1].z, (int)bc[i][1].w};
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 8 + i * 2) * 1024 + lane * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 8 + i * 2 + 1) * 1024 + lane * 16);
+        bf[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      auto read_a = [&](int m, i32x8& af, f32x4& sa) {
+        const int r = m * 16 + ln;
+        const uint8_t* arow = st + r * 128;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+        af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sa = *reinterpret_cast<const f32x4*>(As + m * 16 + lg * 4);
+      };
+      // Software pipeline over row blocks: the MFMAs of block m run while the
+      // VALU folds block m-1's partial products into the accumulators with
+      // their (activation x weight) block scales.
+      i32x8 afc;
+      f32x4 sac;
+      read_a(0, afc, sac);
+      f32x4 prev[4], psc01, psc23;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const i32x8 af = *reinterpret_cast<const i32x8*>(&As[buf][(m * 16 + ln) * LDA + lg * 32]);
-        const f32x4 sa = *reinterpret_cast<const f32x4*>(&Ss[buf][m * 16 + lg * 4]);
-        // subtiles 0,1 share one weight-scale block and 2,3 another (GEMM1: gate, up)
-        f32x4 sc01, sc23;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sc01[q] = sa[q] * wc[0];
-          sc23[q] = sa[q] * wc[2];
-        }
+        i32x8 afn;
+        f32x4 san;
+        if (m + 1 < MT) read_a(m + 1, afn, san);
+        // one MFMA of block m per group, with the VALU work of block m-1
+        // (sched_barrier keeps the compiler from bunching the MFMAs, which
+        // would leave the VALU work waiting behind them)
+        f32x4 part[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 part = mfma_fp8_16x16x128(af, bf[i], zero);
-          const f32x4& sc = i < 2 ? sc01 : sc23;
+          part[i] = mfma_fp8_16x16x128(afc, bf[i], zero);
+          if (m > 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[m][i][q] = fmaf(part[q], sc[q], acc[m][i][q]);
+            for (int q = 0; q < 4; ++q)
+              acc[m - 1][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m - 1][i][q]);
+          }
+          // subtiles 0,1 share one weight-scale block and 2,3 another (GEMM1: gate, up)
+          if (i == 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) psc01[q] = sac[q] * wc0;
+          }
+          if (i == 3) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) psc23[q] = sac[q] * wc2;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) prev[i] = part[i];
+        if (m + 1 < MT) {
+          afc = afn;
+          sac = san;
         }
       }
-      if (kt + 1 < KT) storeA(buf ^ 1, acur, scur);
-      lds_barrier();
-    };
-
-    u32x4 bq[RING][4][2];
-    float wq[RING][4];
-    u32x4 aq[RING][ALOADS];
-    float sq[RING];
 #pragma unroll
-    for (int r = 0; r < RING; ++r) sq[r] = 0;
-    // prologue: steps 0 .. RING-2 in flight, step 0's activation tile in LDS
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r + 1 < RING; ++r) {
-      loadA(min(r, KT - 1), aq[r], sq[r]);
-      loadB(min(r, KT - 1), bq[r], wq[r]);
-    }
-    storeA(0, aq[0], sq[0]);
-    lds_barrier();
-    for (int kt = 0; kt < KT; kt += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        if (kt + r < KT)
-          step(kt + r, bq[r], wq[r], bq[(r + RING - 1) % RING], wq[(r + RING - 1) % RING], aq[(r + 1) % RING],
-               sq[(r + 1) % RING], aq[(r + RING - 1) % RING], sq[(r + RING - 1) % RING]);
-      }
+        for (int q = 0; q < 4; ++q)
+          acc[MT - 1][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[MT - 1][i][q]);
     }
 
+    // Epilogue: results go through LDS (the stage buffers are free once every
+    // wave has passed the barrier below) so that global stores are 16 B per lane.
     if (G1) {
+      constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
       float hv[MT][4][2];
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -179,14 +202,10 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_fp8(GemmArgs p
             hv[m][i][n] = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
             am = fmaxf(am, fabsf(hv[m][i][n]));
           }
-          am = fmaxf(am, shfl_xor(am, 1));
-          am = fmaxf(am, shfl_xor(am, 2));
-          am = fmaxf(am, shfl_xor(am, 4));
-          am = fmaxf(am, shfl_xor(am, 8));
+          am = row16_max_nonneg(am);
           if (ln == 0) red[wave][m * 16 + lg * 4 + i] = am;
         }
-      __syncthreads();
-      uint8_t* Hq = static_cast<uint8_t*>(p.out);
+      lds_barrier();
       float* Hs = static_cast<float*>(p.out_scale);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -194,29 +213,44 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_fp8(GemmArgs p
         for (int i = 0; i < 4; ++i) {
           const int row = m * 16 + lg * 4 + i;
           const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
-          const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
-          if (row < tl.nrows) {
-            const uint32_t c2 = cvt_e4m3x2(hv[m][i][0] / s, hv[m][i][1] / s);
-            uint8_t* dst = Hq + (int64_t)(tl.rbase + row) * p.inter;
-            dst[col[0] + ln] = (uint8_t)(c2 & 0xFF);
-            dst[col[1] + ln] = (uint8_t)(c2 >> 8);
-            if (wave == 0 && ln == 0) Hs[(int64_t)(tl.rbase + row) * (p.inter / 128) + tl.nb] = s;
-          }
+          // the row's [1,128] block scale amax/448; codes h/s with the hardware reciprocal
+          const float sc = amax == 0.0f ? 1.0f : amax * (1.0f / 448.0f);
+          const float inv = __builtin_amdgcn_rcpf(sc);
+          const uint32_t c2 = cvt_e4m3x2(hv[m][i][0] * inv, hv[m][i][1] * inv);
+          smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
+          smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+          if (wave == 0 && ln == 0 && row < tl.nrows)
+            Hs[(int64_t)(tl.rbase + row) * (p.inter / 128) + tl.nb] = sc;
         }
-      __syncthreads();
+      lds_barrier();
+      uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
+      for (int c = threadIdx.x; c < BM * 8; c += 256) {
+        const int row = c >> 3, part = c & 7;
+        if (row < tl.nrows)
+          *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
+              *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
+      }
     } else {
-      uint16_t* Y = static_cast<uint16_t*>(p.out);
+      constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
+      lds_barrier();
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = m * 16 + lg * 4 + i;
-          if (row < tl.nrows) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-              Y[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
-          }
+          for (int n = 0; n < 4; ++n)
+            *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+                (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
         }
+      lds_barrier();
+      char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
+      for (int c = threadIdx.x; c < BM * 32; c += 256) {
+        const int row = c >> 5, part = c & 31;
+        if (row < tl.nrows)
+          *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
+              *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
+      }
     }
   }
 }
@@ -224,13 +258,13 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_fp8(GemmArgs p
 template <bool G1>
 static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
   switch (bm) {
-    case 16: hipLaunchKernelGGL((k_gemm_fp8<16, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_fp8<32, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm_fp8<64, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 48: hipLaunchKernelGGL((k_gemm_fp8<48, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((k_gemm_fp8<96, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_gemm_fp8<128, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_fp8<192, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 16: launch_persistent<k_gemm_fp8<16, G1>>(a, grid, s); break;
+    case 32: launch_persistent<k_gemm_fp8<32, G1>>(a, grid, s); break;
+    case 64: launch_persistent<k_gemm_fp8<64, G1>>(a, grid, s); break;
+    case 48: launch_persistent<k_gemm_fp8<48, G1>>(a, grid, s); break;
+    case 96: launch_persistent<k_gemm_fp8<96, G1>>(a, grid, s); break;
+    case 128: launch_persistent<k_gemm_fp8<128, G1>>(a, grid, s); break;
+    default: launch_persistent<k_gemm_fp8<192, G1>>(a, grid, s); break;
   }
 }
 

@@ -209,13 +209,13 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_int4(GemmArgs 
 template <bool G1>
 static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
   switch (bm) {
-    case 16: hipLaunchKernelGGL((k_gemm_int4<16, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_int4<32, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm_int4<64, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 48: hipLaunchKernelGGL((k_gemm_int4<48, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((k_gemm_int4<96, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_gemm_int4<128, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_int4<192, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 16: launch_persistent<k_gemm_int4<16, G1>>(a, grid, s); break;
+    case 32: launch_persistent<k_gemm_int4<32, G1>>(a, grid, s); break;
+    case 64: launch_persistent<k_gemm_int4<64, G1>>(a, grid, s); break;
+    case 48: launch_persistent<k_gemm_int4<48, G1>>(a, grid, s); break;
+    case 96: launch_persistent<k_gemm_int4<96, G1>>(a, grid, s); break;
+    case 128: launch_persistent<k_gemm_int4<128, G1>>(a, grid, s); break;
+    default: launch_persistent<k_gemm_int4<192, G1>>(a, grid, s); break;
   }
 }
 

@@ -172,10 +172,7 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_mxfp4(GemmArgs
           const float h0 = silu_f32(acc[m][0][i]) * acc[m][2][i];
           const float h1 = silu_f32(acc[m][1][i]) * acc[m][3][i];
           float am = fmaxf(fabsf(h0), fabsf(h1));
-          am = fmaxf(am, shfl_xor(am, 1));
-          am = fmaxf(am, shfl_xor(am, 2));
-          am = fmaxf(am, shfl_xor(am, 4));
-          am = fmaxf(am, shfl_xor(am, 8));
+          am = row16_max_nonneg(am);
           int X = 0;
           if (am > 0.0f) {
             X = (int)floor_log2_pos_mx(am) - 8;
@@ -211,13 +208,13 @@ __global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_mxfp4(GemmArgs
 template <bool G1>
 static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
   switch (bm) {
-    case 16: hipLaunchKernelGGL((k_gemm_mxfp4<16, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_gemm_mxfp4<32, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm_mxfp4<64, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 48: hipLaunchKernelGGL((k_gemm_mxfp4<48, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 96: hipLaunchKernelGGL((k_gemm_mxfp4<96, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_gemm_mxfp4<128, G1>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mxfp4<192, G1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 16: launch_persistent<k_gemm_mxfp4<16, G1>>(a, grid, s); break;
+    case 32: launch_persistent<k_gemm_mxfp4<32, G1>>(a, grid, s); break;
+    case 64: launch_persistent<k_gemm_mxfp4<64, G1>>(a, grid, s); break;
+    case 48: launch_persistent<k_gemm_mxfp4<48, G1>>(a, grid, s); break;
+    case 96: launch_persistent<k_gemm_mxfp4<96, G1>>(a, grid, s); break;
+    case 128: launch_persistent<k_gemm_mxfp4<128, G1>>(a, grid, s); break;
+    default: launch_persistent<k_gemm_mxfp4<192, G1>>(a, grid, s); break;
   }
 }
 

@@ -7,7 +7,7 @@ namespace moe {
 
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 16;
-constexpr int PAIRS_PER_BLOCK = 2048;  // flat (token, slot) pairs per histogram / scatter block
+constexpr int PAIRS_PER_BLOCK = 512;  // flat (token, slot) pairs per histogram / scatter block
 
 // Everything a grouped-GEMM launch over one chunk of active experts needs.
 struct GemmArgs {
@@ -31,6 +31,7 @@ struct GemmArgs {
   const int32_t* active;
   const int32_t* num_active;
   const int32_t* tile_start;   // per active expert prefix of ceil(count/BM) (+ total)
+  const int32_t* tiles;        // per tile {expert, first row, valid rows, active index}
   int top_k;
   int chunk;                   // chunk index c
   int chunk_experts;           // C
@@ -40,7 +41,9 @@ struct GemmArgs {
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
                     int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
-                    int32_t* tile_16, hipStream_t s);
+                    int32_t* tile_16, int32_t* tile_desc, hipStream_t s);
+// Upper bound on the number of row tiles of any height >= 16 (descriptor table entries).
+inline int64_t max_row_tiles(int64_t R, int E) { return R / 16 + E; }
 
 // Activation preparation (per token rows, no adapter).
 void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
@@ -55,6 +58,37 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
 void launch_gemm_int4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
 void launch_gemm_fp8(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
 void launch_gemm_mxfp4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+
+// Launch a persistent grouped-GEMM kernel on at most as many workgroups as
+// can be resident at once (CUs x occupancy, rounded down to a multiple of 8),
+// so that every workgroup that is dealt items starts immediately instead of
+// waiting behind empty ones.  Occupancy is looked up once per kernel and the
+// CU count once per device.
+inline int device_cus(int dev) {
+  static int cache[64] = {0};
+  if (dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+template <void (*K)(GemmArgs)>
+inline void launch_persistent(const GemmArgs& a, int grid, hipStream_t s) {
+  static int occ = 0;
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, K, 256, 0) != hipSuccess || o <= 0) o = 1;
+    occ = o;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int cap = occ * device_cus(dev) / 8 * 8;
+  if (cap < 8) cap = 8;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(K, dim3(grid), dim3(256), 0, s, a);
+}
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
                     hipStream_t s);

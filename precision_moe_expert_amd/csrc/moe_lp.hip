@@ -17,7 +17,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Byte layout of the forward workspace; offsets relative to its base.
 struct WsLayout {
-  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, hist;
+  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, hist;
   size_t act, act_scale, h, h_scale, y;
   size_t total;
 };
@@ -83,6 +83,7 @@ WsLayout layout(const Dims& d) {
   w.num_active = take(16);
   w.tile_a = take((E + 1) * 4);
   w.tile_16 = take((E + 1) * 4);
+  w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
   const size_t arows = d.oft ? R : T;
   if (d.fmt == MOE_W_INT4_G32_BF16) {
@@ -205,7 +206,8 @@ int32_t moe_tile_rows(const moe_layer* layer) {
 size_t moe_route_workspace_bytes(const moe_layer* layer) {
   Dims d;
   if (check_layer(layer, &d) != MOE_OK) return 0;
-  return align_up((size_t)(d.E + 1) * 4) * 2 + align_up((size_t)(d.nblk > 0 ? d.nblk : 1) * d.E * 4);
+  return align_up((size_t)(d.E + 1) * 4) * 2 + align_up((size_t)max_row_tiles(d.R, d.E) * 16) +
+         align_up((size_t)(d.nblk > 0 ? d.nblk : 1) * d.E * 4);
 }
 
 moe_status moe_route_permute(const moe_layer* layer, const float* logits, const moe_route_out* out, void* ws,
@@ -224,10 +226,12 @@ moe_status moe_route_permute(const moe_layer* layer, const float* logits, const 
   char* base = static_cast<char*>(ws);
   int32_t* tile_a = reinterpret_cast<int32_t*>(base);
   int32_t* tile_16 = reinterpret_cast<int32_t*>(base + align_up((size_t)(d.E + 1) * 4));
-  int32_t* hist = reinterpret_cast<int32_t*>(base + 2 * align_up((size_t)(d.E + 1) * 4));
+  int32_t* tiles = reinterpret_cast<int32_t*>(base + 2 * align_up((size_t)(d.E + 1) * 4));
+  int32_t* hist = reinterpret_cast<int32_t*>(base + 2 * align_up((size_t)(d.E + 1) * 4) +
+                                             align_up((size_t)max_row_tiles(d.R, d.E) * 16));
   launch_route(logits, d.T, d.E, d.k, out->topk_ids, out->topk_w, s);
   launch_permute(out->topk_ids, (int)d.R, d.E, choose_bm(d), hist, out->expert_offsets, out->sorted_rows,
-                 out->row_of, out->active_experts, out->num_active, tile_a, tile_16, s);
+                 out->row_of, out->active_experts, out->num_active, tile_a, tile_16, tiles, s);
   return launch_status();
 }
 
@@ -286,6 +290,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   int32_t* num_active = I32(wl.num_active);
   int32_t* tile_a = I32(wl.tile_a);
   int32_t* tile_16 = I32(wl.tile_16);
+  int32_t* tiles = I32(wl.tiles);
   int32_t* hist = I32(wl.hist);
   void* act = base + wl.act;
   void* act_scale = base + wl.act_scale;
@@ -298,7 +303,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   // 1-2. route and permute
   { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
   { Scope sc_(tm, MOE_STAGE_PERMUTE);
-    launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, s); }
+    launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
+                   tiles, s); }
 
   // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
   {
@@ -356,6 +362,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     g->active = active;
     g->num_active = num_active;
     g->tile_start = tile_a;
+    g->tiles = tiles;
     g->top_k = d.k;
     g->chunk_experts = chunk_experts;
   }

@@ -50,15 +50,11 @@ MOE_DEV Tile tile_of(const GemmArgs& p, const ChunkWork& cw, int wk, int bm) {
     t.nb = wk / cw.ntiles;
     tile = cw.t0 + wk % cw.ntiles;
   }
-  int lo = cw.a0, hi = cw.a1 - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  t.e = p.active[lo];
-  const int m0 = (tile - p.tile_start[lo]) * bm;
-  t.rbase = p.offsets[t.e] + m0;
-  t.nrows = min(bm, p.offsets[t.e + 1] - t.rbase);
+  const i32x4 d = *reinterpret_cast<const i32x4*>(p.tiles + 4 * (int64_t)tile);
+  t.e = d[0];
+  t.rbase = d[1];
+  t.nrows = d[2];
+  (void)bm;
   return t;
 }
 

@@ -15,49 +15,50 @@ MOE_DEV uint32_t float_key(float f) {
 }
 MOE_DEV float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// One wave per token.  Each lane keeps up to 16 logits (E <= 1024) as
-// 64-bit keys (value key << 32 | (0xFFFF - id)): the wave maximum is the
+// One wave per token.  Each lane keeps SLOTS = ceil(E/64) logits (E <= 1024)
+// as 64-bit keys (value key << 32 | (0xFFFF - id)): the wave maximum is the
 // largest logit and, among equal logits, the smallest expert id.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (int64_t)t * E;
-  uint64_t key[16];
+  uint64_t key[SLOTS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int e = lane + 64 * i;
+  for (int i = 0; i < SLOTS; ++i) {
+    const int e = lane + 64 * i;
     key[i] = (e < E) ? (((uint64_t)float_key(row[e]) << 32) | (uint64_t)(0xFFFFu - e)) : 0ull;
   }
-  float sel_val[16];
-  int sel_id[16];
+  float sel_val[MAX_TOPK];
+  int sel_id[MAX_TOPK];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < MAX_TOPK; ++j) {
     if (j < k) {
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+      for (int i = 0; i < SLOTS; ++i) best = key[i] > best ? key[i] : best;
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)best, m, 64), hi = __shfl_xor((uint32_t)(best >> 32), m, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
+        const uint32_t lo = __shfl_xor((uint32_t)best, m, 64), hi = __shfl_xor((uint32_t)(best >> 32), m, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
         best = o > best ? o : best;
       }
       sel_id[j] = 0xFFFF - (int)(best & 0xFFFFu);
       sel_val[j] = key_float((uint32_t)(best >> 32));
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < SLOTS; ++i)
         if (key[i] == best) key[i] = 0;  // keys are unique (distinct ids), so only the winner clears
     }
   }
   // softmax over the selected logits, relative to the largest (slot 0)
   float z = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < MAX_TOPK; ++j)
     if (j < k) z += expf(sel_val[j] - sel_val[0]);
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < MAX_TOPK; ++j)
     if (j < k && lane == j) {
       ids[(int64_t)t * k + j] = sel_id[j];
       w[(int64_t)t * k + j] = expf(sel_val[j] - sel_val[0]) / z;
@@ -103,21 +104,27 @@ MOE_DEV int block_excl_scan_1024(int v, int* sh, int* total) {
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int bm_a,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
-                                               int32_t* __restrict__ tile_16) {
+                                               int32_t* __restrict__ tile_16, int32_t* __restrict__ tile_desc) {
   __shared__ int sh[1024];
+  __shared__ int s_tstart[MAX_EXPERTS + 1], s_exp[MAX_EXPERTS], s_off[MAX_EXPERTS], s_cnt[MAX_EXPERTS];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E)
-    for (int b = 0; b < nblk; ++b) {  // running per-expert prefix over blocks
-      int h = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = cnt;
-      cnt += h;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {  // running per-expert prefix over blocks
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = (b0 + i < nblk) ? hist[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < nblk) hist[(int64_t)(b0 + i) * E + e] = cnt;
+        cnt += h[i];
+      }
     }
   int total;
   const int off = block_excl_scan_1024(e < E ? cnt : 0, sh, &total);
   if (e < E) {
     offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;
+    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;  // independent updates, pipelined
   }
   if (e == 0) offsets[E] = total;
   const int act = (e < E && cnt > 0) ? 1 : 0;
@@ -130,11 +137,29 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
     active[pos] = e;
     tile_a[pos] = ta;
     tile_16[pos] = t16;
+    s_tstart[pos] = ta;
+    s_exp[pos] = e;
+    s_off[pos] = off;
+    s_cnt[pos] = cnt;
   }
   if (e == 0) {
     *num_active = na;
     tile_a[na] = nta;
     tile_16[na] = nt16;
+    s_tstart[na] = nta;
+  }
+  __syncthreads();
+  // One descriptor per bm_a-row tile, in (active expert, tile) order:
+  // {expert, first permuted row, valid rows, active index}.
+  for (int t = threadIdx.x; t < nta; t += blockDim.x) {
+    int lo = 0, hi = na - 1;  // last active expert whose first tile is <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r0 = (t - s_tstart[lo]) * bm_a;
+    const i32x4 d = {s_exp[lo], s_off[lo] + r0, min(bm_a, s_cnt[lo] - r0), lo};
+    *reinterpret_cast<i32x4*>(tile_desc + 4 * (int64_t)t) = d;
   }
 }
 
@@ -178,16 +203,21 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  const dim3 g((T + 3) / 4), b(256);
+  if (E <= 64) hipLaunchKernelGGL(k_route_topk<1>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 128) hipLaunchKernelGGL(k_route_topk<2>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, T, E, k, ids, w);
+  else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, s, logits, T, E, k, ids, w);
 }
 
 void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
                     int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
-                    int32_t* tile_16, hipStream_t s) {
+                    int32_t* tile_16, int32_t* tile_desc, hipStream_t s) {
   const int nblk = (R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK;
   if (nblk > 0) hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(256), 0, s, ids, R, E, hist);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active, tile_a,
-                     tile_16);
+                     tile_16, tile_desc);
   if (nblk > 0) hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(64), 0, s, ids, R, E, hist, sorted_rows, row_of);
 }
 
