@@ -138,19 +138,28 @@ def main():
 
     sec = ms_per_step / 1e3
     peak = MFMA_PEAK[cfg.fmt]
-    dom = max(("gemm1", "gemm2"), key=lambda s: stage_ms[s])
-    launch_ms = stage_ms[dom] / max(stage_n[dom], 1)
-    launches_per_step = stage_n[dom] / args.steps
-    f_dom, b_dom = acc[dom]
+    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4"}[cfg.fmt]
+    bm = binding.tile_rows(layer)
+    if cfg.fmt == 2:
+        # FP8: every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
+        dom = "gemm"
+        launches = stage_n["gemm1"] + stage_n["gemm2"]
+        launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
+        f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
+        kname = f"k_gemm_fp8<{bm}>"
+    else:
+        dom = max(("gemm1", "gemm2"), key=lambda s: stage_ms[s])
+        launches = stage_n[dom]
+        launch_ms = stage_ms[dom] / max(launches, 1)
+        f_dom, b_dom = acc[dom]
+        kname = f"k_gemm_{fmt_name}<{bm}, {'true' if dom == 'gemm1' else 'false'}>"
+    launches_per_step = launches / args.steps
     f_launch, b_launch = f_dom / launches_per_step, b_dom / launches_per_step
     if b_launch / HBM_PEAK >= f_launch / peak:
         roof = dict(bound="hbm", achieved=b_launch / (launch_ms / 1e3) / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s")
     else:
         roof = dict(bound="mfma", achieved=f_launch / (launch_ms / 1e3) / 1e12, peak=peak / 1e12, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4"}[cfg.fmt]
-    bm = binding.tile_rows(layer)
-    kname = f"k_gemm_{fmt_name}<{bm}, {'true' if dom == 'gemm1' else 'false'}>"
     roof["kernel"] = kname
     # HBM bytes per launch measured by rocprofv3 counters (copy-calibrated),
     # valid only while the kernel source is unchanged

@@ -151,7 +151,7 @@ enum {
   MOE_STAGE_PERMUTE = 1, /* histogram, scan, stable scatter, tile lists      */
   MOE_STAGE_ACT = 2,     /* GEMM1 input: activation format and OFT rotation  */
   MOE_STAGE_GEMM1 = 3,   /* dequant + gate/up GEMM + SwiGLU, one per chunk   */
-  MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM, one per chunk               */
+  MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM, one per chunk (FP8: see below) */
   MOE_STAGE_COMBINE = 5, /* weighted combine                                 */
   MOE_NUM_STAGES = 6
 };
@@ -161,7 +161,11 @@ enum {
  * the stream before it returns (unlike moe_expert_forward).  stage_ms and
  * stage_launches are HOST arrays of MOE_NUM_STAGES entries, filled with the
  * summed event durations (milliseconds) and the number of launch groups of
- * each stage.  Same arguments, result and errors as moe_expert_forward. */
+ * each stage.  Same arguments, result and errors as moe_expert_forward.
+ * FP8 weights run one launch per chunk c = 0..n that does chunk c's GEMM1
+ * together with chunk c-1's GEMM2 (n = number of chunks): launches 0..n-1
+ * are reported under MOE_STAGE_GEMM1 and the last, GEMM2-only launch under
+ * MOE_STAGE_GEMM2. */
 moe_status moe_expert_forward_timed(const moe_layer* layer, const void* x_bf16, const float* logits,
                                     const moe_qweights* qweights, const moe_scales* scales,
                                     const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,

@@ -28,18 +28,13 @@ struct Fp8Stage {
   static constexpr int NPER = NA + 1 + 8;           // DMA instructions per wave per stage
 };
 
+// One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
+// 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
-__global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p) {
+__device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, float (*red)[BM]) {
   constexpr int MT = BM / 16;
   using ST = Fp8Stage<BM>;
   constexpr int S = ST::S;
-  static_assert(S >= 2 && S <= 5, "LDS stages");
-  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
-  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
-  __shared__ float red[4][BM];
-  const int nblk = G1 ? p.inter / 128 : p.N / 256;
-  ChunkWork cw;
-  if (!chunk_work(p, nblk, cw)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int K = p.K, KT = K / 128;
@@ -47,11 +42,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p) {
   const char* ASbase = static_cast<const char*>(p.a_scale);
   const float* WS = static_cast<const float*>(p.w_scale);
   const uint32_t smem0 = lds_u32(smem);
-
-  for (int base = 0; base < cw.nwork; base += gridDim.x) {
-    const int wk = xcd_item(base, cw.nwork);
-    if (wk < 0) continue;
-    const Tile tl = tile_of(p, cw, wk, BM);
+  {
     lds_barrier();  // every wave is done with the previous item's stages
     int col[4];
     if (G1) {
@@ -255,22 +246,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p) {
   }
 }
 
-template <bool G1>
-static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
-  switch (bm) {
-    case 16: launch_persistent<k_gemm_fp8<16, G1>>(a, grid, s); break;
-    case 32: launch_persistent<k_gemm_fp8<32, G1>>(a, grid, s); break;
-    case 64: launch_persistent<k_gemm_fp8<64, G1>>(a, grid, s); break;
-    case 48: launch_persistent<k_gemm_fp8<48, G1>>(a, grid, s); break;
-    case 96: launch_persistent<k_gemm_fp8<96, G1>>(a, grid, s); break;
-    case 128: launch_persistent<k_gemm_fp8<128, G1>>(a, grid, s); break;
-    default: launch_persistent<k_gemm_fp8<192, G1>>(a, grid, s); break;
+// Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
+// items of chunk p2.chunk (either may be empty: chunk < 0 or past the last
+// active expert).  The two have no dependence on each other (GEMM2 of a chunk
+// reads the h that the previous launch wrote), so one launch keeps every CU
+// busy where two launches would each leave a partial last round.  Items are
+// split into contiguous per-XCD ranges (neighbouring items share weights in
+// that XCD's L2), GEMM1 items first; the workgroups of an XCD take items from
+// its range through an atomic counter, so every workgroup exits once the
+// range is used up.
+template <int BM>
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  using ST = Fp8Stage<BM>;
+  constexpr int S = ST::S;
+  static_assert(S >= 2 && S <= 5, "LDS stages");
+  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
+  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ float red[4][BM];
+  __shared__ int s_item;
+  ChunkWork c1, c2;
+  const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
+  const int n2 = chunk_work(p2, p2.N / 256, c2) ? c2.nwork : 0;
+  const int x = blockIdx.x & 7;
+  const int per1 = (n1 + 7) >> 3, per2 = (n2 + 7) >> 3;
+  const int b1 = x * per1, b2 = x * per2;
+  const int len1 = max(0, min(n1, b1 + per1) - b1), len2 = max(0, min(n2, b2 + per2) - b2);
+  int32_t* q = queue + x;
+  if (threadIdx.x == 0) s_item = atomicAdd(q, 1);
+  __syncthreads();
+  int cur = s_item;
+  while (cur < len1 + len2) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(q, 1);  // claimed now, read after the item
+    if (cur < len1) fp8_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, red);
+    else fp8_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, red);
+    if (threadIdx.x == 0) s_item = nxt;
+    lds_barrier();
+    cur = s_item;
   }
 }
 
-void launch_gemm_fp8(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s) {
-  if (gemm1) launch_bm<true>(a, bm, grid, s);
-  else launch_bm<false>(a, bm, grid, s);
+void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                          hipStream_t s) {
+  switch (bm) {
+    case 16: launch_persistent2<k_gemm_fp8<16>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_fp8<32>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_fp8<64>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_fp8<48>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_fp8<96>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_fp8<128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_fp8<192>>(g1, g2, queue, grid, s); break;
+  }
 }
 
 }  // namespace moe

@@ -41,7 +41,7 @@ struct GemmArgs {
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
                     int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
-                    int32_t* tile_16, int32_t* tile_desc, hipStream_t s);
+                    int32_t* tile_16, int32_t* tile_desc, int32_t* queue, int nqueue, hipStream_t s);
 // Upper bound on the number of row tiles of any height >= 16 (descriptor table entries).
 inline int64_t max_row_tiles(int64_t R, int E) { return R / 16 + E; }
 
@@ -56,7 +56,10 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
 
 // Grouped GEMMs over one chunk; bm = rows per tile (16, 32, 64 or 128).
 void launch_gemm_int4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
-void launch_gemm_fp8(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+// FP8: one launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2
+// (either may be empty); queue: 8 zeroed per-XCD item counters for this launch.
+void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                          hipStream_t s);
 void launch_gemm_mxfp4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
 
 // Launch a persistent grouped-GEMM kernel on at most as many workgroups as
@@ -74,20 +77,27 @@ inline int device_cus(int dev) {
   }
   return cache[dev];
 }
-template <void (*K)(GemmArgs)>
-inline void launch_persistent(const GemmArgs& a, int grid, hipStream_t s) {
-  static int occ = 0;
-  if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, K, 256, 0) != hipSuccess || o <= 0) o = 1;
-    occ = o;
-  }
+template <typename F>
+inline int resident_grid(F kernel, int grid) {
+  int o = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, 256, 0) != hipSuccess || o <= 0) o = 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  int cap = occ * device_cus(dev) / 8 * 8;
+  int cap = o * device_cus(dev) / 8 * 8;
   if (cap < 8) cap = 8;
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(K, dim3(grid), dim3(256), 0, s, a);
+  return grid > cap ? cap : grid;
+}
+template <void (*K)(GemmArgs)>
+inline void launch_persistent(const GemmArgs& a, int grid, hipStream_t s) {
+  static int cap = 0;  // resident workgroups (per kernel; the library runs on one GPU model)
+  if (cap == 0) cap = resident_grid(K, 1 << 30);
+  hipLaunchKernelGGL(K, dim3(grid < cap ? grid : cap), dim3(256), 0, s, a);
+}
+template <void (*K)(GemmArgs, GemmArgs, int32_t*)>
+inline void launch_persistent2(const GemmArgs& a, const GemmArgs& b, int32_t* q, int grid, hipStream_t s) {
+  static int cap = 0;
+  if (cap == 0) cap = resident_grid(K, 1 << 30);
+  hipLaunchKernelGGL(K, dim3(grid < cap ? grid : cap), dim3(256), 0, s, a, b, q);
 }
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,

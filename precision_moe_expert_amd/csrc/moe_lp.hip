@@ -17,7 +17,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Byte layout of the forward workspace; offsets relative to its base.
 struct WsLayout {
-  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, hist;
+  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
   size_t act, act_scale, h, h_scale, y;
   size_t total;
 };
@@ -65,6 +65,10 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   return MOE_OK;
 }
 
+// Per-XCD work-queue counters of the FP8 pair launches: 8 per launch, at most
+// num_experts + 1 launches (chunk_experts >= 1).
+int queue_ints(const Dims& d) { return 8 * (d.E + 1); }
+
 WsLayout layout(const Dims& d) {
   WsLayout w{};
   size_t o = 0;
@@ -84,6 +88,7 @@ WsLayout layout(const Dims& d) {
   w.tile_a = take((E + 1) * 4);
   w.tile_16 = take((E + 1) * 4);
   w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
+  w.queue = take((size_t)queue_ints(d) * 4);
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
   const size_t arows = d.oft ? R : T;
   if (d.fmt == MOE_W_INT4_G32_BF16) {
@@ -231,7 +236,7 @@ moe_status moe_route_permute(const moe_layer* layer, const float* logits, const 
                                              align_up((size_t)max_row_tiles(d.R, d.E) * 16));
   launch_route(logits, d.T, d.E, d.k, out->topk_ids, out->topk_w, s);
   launch_permute(out->topk_ids, (int)d.R, d.E, choose_bm(d), hist, out->expert_offsets, out->sorted_rows,
-                 out->row_of, out->active_experts, out->num_active, tile_a, tile_16, tiles, s);
+                 out->row_of, out->active_experts, out->num_active, tile_a, tile_16, tiles, nullptr, 0, s);
   return launch_status();
 }
 
@@ -291,6 +296,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   int32_t* tile_a = I32(wl.tile_a);
   int32_t* tile_16 = I32(wl.tile_16);
   int32_t* tiles = I32(wl.tiles);
+  int32_t* queue = I32(wl.queue);
   int32_t* hist = I32(wl.hist);
   void* act = base + wl.act;
   void* act_scale = base + wl.act_scale;
@@ -304,7 +310,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
   { Scope sc_(tm, MOE_STAGE_PERMUTE);
     launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
-                   tiles, s); }
+                   tiles, queue, d.fmt == MOE_W_FP8_E4M3_B128 ? queue_ints(d) : 0, s); }
 
   // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
   {
@@ -373,13 +379,23 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   g2.nb_fastest = 1;
   const int grid1 = gemm_grid(d, bm, chunk_experts, d.I / 128);
   const int grid2 = gemm_grid(d, bm, chunk_experts, d.H / 256);
-  for (int c = 0; c < nchunks; ++c) {
-    g1.chunk = c;
-    g2.chunk = c;
-    auto gemm = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4
-              : d.fmt == MOE_W_FP8_E4M3_B128 ? launch_gemm_fp8 : launch_gemm_mxfp4;
-    { Scope sc_(tm, MOE_STAGE_GEMM1); gemm(g1, true, bm, grid1, s); }
-    { Scope sc_(tm, MOE_STAGE_GEMM2); gemm(g2, false, bm, grid2, s); }
+  if (d.fmt == MOE_W_FP8_E4M3_B128) {
+    // launch c runs chunk c's GEMM1 together with chunk c-1's GEMM2
+    const int grid = grid1 > grid2 ? grid1 : grid2;
+    for (int c = 0; c <= nchunks; ++c) {
+      g1.chunk = c < nchunks ? c : -1;
+      g2.chunk = c - 1;
+      Scope sc_(tm, c < nchunks ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2);
+      launch_gemm_fp8_pair(g1, g2, queue + 8 * c, bm, grid, s);
+    }
+  } else {
+    auto gemm = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4 : launch_gemm_mxfp4;
+    for (int c = 0; c < nchunks; ++c) {
+      g1.chunk = c;
+      g2.chunk = c;
+      { Scope sc_(tm, MOE_STAGE_GEMM1); gemm(g1, true, bm, grid1, s); }
+      { Scope sc_(tm, MOE_STAGE_GEMM2); gemm(g2, false, bm, grid2, s); }
+    }
   }
 
   // 5. weighted combine back to token order

@@ -18,6 +18,7 @@ struct ChunkWork {
 };
 
 MOE_DEV bool chunk_work(const GemmArgs& p, int nblk, ChunkWork& cw) {
+  if (p.chunk < 0) return false;
   const int na = *p.num_active;
   cw.a0 = p.chunk * p.chunk_experts;
   if (cw.a0 >= na) return false;

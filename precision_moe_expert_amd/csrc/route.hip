@@ -104,7 +104,8 @@ MOE_DEV int block_excl_scan_1024(int v, int* sh, int* total) {
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int bm_a,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
-                                               int32_t* __restrict__ tile_16, int32_t* __restrict__ tile_desc) {
+                                               int32_t* __restrict__ tile_16, int32_t* __restrict__ tile_desc,
+                                               int32_t* __restrict__ queue, int nqueue) {
   __shared__ int sh[1024];
   __shared__ int s_tstart[MAX_EXPERTS + 1], s_exp[MAX_EXPERTS], s_off[MAX_EXPERTS], s_cnt[MAX_EXPERTS];
   const int e = threadIdx.x;
@@ -148,6 +149,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
     tile_16[na] = nt16;
     s_tstart[na] = nta;
   }
+  for (int i = threadIdx.x; i < nqueue; i += blockDim.x) queue[i] = 0;  // GEMM work-queue counters
   __syncthreads();
   // One descriptor per bm_a-row tile, in (active expert, tile) order:
   // {expert, first permuted row, valid rows, active index}.
@@ -213,11 +215,11 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 
 void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,
                     int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
-                    int32_t* tile_16, int32_t* tile_desc, hipStream_t s) {
+                    int32_t* tile_16, int32_t* tile_desc, int32_t* queue, int nqueue, hipStream_t s) {
   const int nblk = (R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK;
   if (nblk > 0) hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(256), 0, s, ids, R, E, hist);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active, tile_a,
-                     tile_16, tile_desc);
+                     tile_16, tile_desc, queue, nqueue);
   if (nblk > 0) hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(64), 0, s, ids, R, E, hist, sorted_rows, row_of);
 }
 
