@@ -140,13 +140,13 @@ def main():
     peak = MFMA_PEAK[cfg.fmt]
     fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4"}[cfg.fmt]
     bm = binding.tile_rows(layer)
-    if cfg.fmt == 2:
-        # FP8: every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
+    if True:
+        # every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
         dom = "gemm"
         launches = stage_n["gemm1"] + stage_n["gemm2"]
         launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
         f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
-        kname = f"k_gemm_fp8<{bm}>"
+        kname = f"k_gemm_{fmt_name}<{bm}>"
     else:
         dom = max(("gemm1", "gemm2"), key=lambda s: stage_ms[s])
         launches = stage_n[dom]

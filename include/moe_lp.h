@@ -150,8 +150,8 @@ enum {
   MOE_STAGE_ROUTE = 0,   /* router top-k + softmax                          */
   MOE_STAGE_PERMUTE = 1, /* histogram, scan, stable scatter, tile lists      */
   MOE_STAGE_ACT = 2,     /* GEMM1 input: activation format and OFT rotation  */
-  MOE_STAGE_GEMM1 = 3,   /* dequant + gate/up GEMM + SwiGLU, one per chunk   */
-  MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM, one per chunk (FP8: see below) */
+  MOE_STAGE_GEMM1 = 3,   /* dequant + gate/up GEMM + SwiGLU                  */
+  MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM (launch pairing: see below)  */
   MOE_STAGE_COMBINE = 5, /* weighted combine                                 */
   MOE_NUM_STAGES = 6
 };
@@ -162,7 +162,7 @@ enum {
  * stage_launches are HOST arrays of MOE_NUM_STAGES entries, filled with the
  * summed event durations (milliseconds) and the number of launch groups of
  * each stage.  Same arguments, result and errors as moe_expert_forward.
- * FP8 weights run one launch per chunk c = 0..n that does chunk c's GEMM1
+ * The grouped GEMMs run one launch per chunk c = 0..n that does chunk c's GEMM1
  * together with chunk c-1's GEMM2 (n = number of chunks): launches 0..n-1
  * are reported under MOE_STAGE_GEMM1 and the last, GEMM2-only launch under
  * MOE_STAGE_GEMM2. */

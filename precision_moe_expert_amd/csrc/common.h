@@ -146,11 +146,17 @@ MOE_DEV void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// Wait until at most n (0..3, wave-uniform) stages of NPER loads each are in flight.
+// Wait until at most n (wave-uniform) stages of NPER loads each are in
+// flight.  Counts above the counter's range (63) are clamped, which only
+// waits longer.
+template <int N>
+MOE_DEV void wait_vmcnt_clamped() { wait_vmcnt<(N > 63 ? 63 : N)>(); }
 template <int NPER>
 MOE_DEV void wait_stages(int n) {
-  if (n >= 3) wait_vmcnt<3 * NPER>();
-  else if (n == 2) wait_vmcnt<2 * NPER>();
-  else if (n == 1) wait_vmcnt<NPER>();
+  if (n >= 5) wait_vmcnt_clamped<5 * NPER>();
+  else if (n == 4) wait_vmcnt_clamped<4 * NPER>();
+  else if (n == 3) wait_vmcnt_clamped<3 * NPER>();
+  else if (n == 2) wait_vmcnt_clamped<2 * NPER>();
+  else if (n == 1) wait_vmcnt_clamped<NPER>();
   else wait_vmcnt<0>();
 }

@@ -8,12 +8,9 @@
 // nothing is written back to memory and no dequantized copy exists.
 //
 // Tile: BM rows x 256 output columns per workgroup (4 waves x 4 subtiles of
-// 16 columns); K step 128.  A (fp16 activations) is staged through a
-// double-buffered LDS tile shared by the 4 waves; B is read by each wave
-// straight from HBM (every weight is used by exactly one wave) through a
-// three-slot register ring, two K steps ahead of its use.  The unpack costs
-// about 2.5 vector ops per weight, so the tile is as tall as the rows per
-// expert allow (up to 192) to keep it under the MFMA time.
+// 16 columns); K step 128.  Activation rows, weight nibbles and group scales
+// stream into an LDS stage ring by global_load_lds DMA (see the FP8 kernel
+// for the scheme); each wave unpacks its own weight fragments from LDS.
 // GEMM1 pairs gate column n with up column I + n inside the same wave and
 // writes h = silu(gate) * up (fp16); GEMM2 writes y (bf16).
 #include "common.h"
@@ -40,188 +37,222 @@ MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2) {
 
 MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; }
 
+// LDS bytes of one pipeline stage: activation rows (256 B = 128 fp16 each,
+// 16-byte parts XOR-swizzled by row), each wave's weight fragments (4
+// subtiles x 1 KB of nibbles) and two dwords of bf16 group scales per
+// weight row.
+template <int BM>
+struct I4Stage {
+  static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
+  static constexpr int A_BYTES = BM * 256;
+  static constexpr int B_OFF = A_BYTES;
+  static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
+  static constexpr int BYTES = BS_OFF + 4 * 2 * 256;
+  // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
+  // a second resident workgroup covers one's item start-up and waits; one at
+  // 32 rows (a deeper ring wins there) and above 64 rows, where the
+  // activation tile fills the LDS.
+  static constexpr int WPC = (BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
+  static constexpr int SMAX = BM <= 32 ? 7 : 5;
+  static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
+  static constexpr int NPER = NA + 4 + 2;             // DMA instructions per wave per stage
+};
+
+// One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
+// 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
-__global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_int4(GemmArgs p) {
+__device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
   constexpr int MT = BM / 16;
-  // register prefetch ring: weights and activation rows of step kt + RING - 1
-  // are issued while step kt computes (deep for short tiles, whose per-step
-  // compute is too short to cover a memory round trip, shallow where
-  // registers are scarce)
-  constexpr int RING = (BM <= 16 ? 6 : BM <= 32 ? 4 : BM <= 48 ? 3 : BM <= 96 ? 2 : 3);  // deepest ring that fits without spills
-  constexpr int LDA = 128 + 8;  // fp16 elements per LDS row (16-byte pad)
-  __shared__ __align__(16) uint16_t As[2][BM * LDA];
-  const int nblk = G1 ? p.inter / 128 : p.N / 256;
-  ChunkWork cw;
-  if (!chunk_work(p, nblk, cw)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  using ST = I4Stage<BM>;
+  constexpr int S = ST::S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
-  const int lpart = threadIdx.x & 15;
-
-  for (int base = 0; base < cw.nwork; base += gridDim.x) {
-    const int wk = xcd_item(base, cw.nwork);
-    if (wk < 0) continue;
-    const Tile tl = tile_of(p, cw, wk, BM);
-    int col[4];
-    if (G1) {
-      const int g0 = tl.nb * 128 + wave * 32;
-      col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
-    } else {
-      const int c0 = tl.nb * 256 + wave * 64;
+  const uint32_t smem0 = lds_u32(smem);
+  lds_barrier();  // every wave is done with the previous item's stages
+  int col[4];
+  if (G1) {
+    const int g0 = tl.nb * 128 + wave * 32;
+    col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
+  } else {
+    const int c0 = tl.nb * 256 + wave * 64;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
-    }
-    // B: per-expert base (uniform) + 32-bit per-lane offsets
-    const uint8_t* wexp = p.w + tl.e * p.w_expert_bytes;
-    const uint16_t* sexp = static_cast<const uint16_t*>(p.w_scale) + tl.e * p.ws_expert_elems;
-    uint32_t woff[4], soff[4];
+    for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
+  }
+  // per-lane global sources of this item's DMA pieces (K offset added per step)
+  const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
+  const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * 2;
+  const char* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  const char* bssrc;
+  {
+    int cc = col[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if ((lane >> 4) == i) cc = col[i];
+    bssrc = sexp + (int64_t)(cc + (lane & 15)) * (K / 32) * 2;
+  }
+  const char* asrc[ST::NA];
+#pragma unroll
+  for (int j = 0; j < ST::NA; ++j) {
+    const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/16, slot c%16
+    const int row = c >> 4, slot = c & 15;
+    const int part = slot ^ (row & 15);              // XOR swizzle of 16-byte parts
+    const int rr = tl.rbase + min(row, tl.nrows - 1);
+    const int sr = p.sorted_rows[rr];
+    const int src = p.a_per_token ? sr / p.top_k : rr;
+    asrc[j] = Abase + (int64_t)src * K * 2 + part * 16;
+  }
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sb = smem0 + slot * ST::BYTES;
+#pragma unroll
+    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dma_b32(bssrc + kt * 8 + h * 4, sb + ST::BS_OFF + (wave * 2 + h) * 256);
+  };
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int s = 0; s + 1 < S; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    lds_barrier();                                    // ... and every other wave's
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const uint8_t* st = smem + (kt % S) * ST::BYTES;
+    u32x4 bq[4];
+    f16x2 s2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      woff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 2) + lg * 16;
-      soff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 32) + lg;
+      bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + (wave * 2 + (lg >> 1)) * 256 + (i * 16 + ln) * 4);
+      const _Float16 sh = (_Float16)bf16_bits_to_f32((uint16_t)((lg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+      s2[i] = (f16x2){sh, sh};
     }
-    // A: thread copies 16-byte part `lpart` of rows (tid/16) + 16j
-    uint32_t aoff[MT];
+    // activation fragment of row block m, 32-K sub-step s: logical part 4*lg + s
+    auto read_a = [&](int m, int s) {
+      const int r = m * 16 + ln;
+      return *reinterpret_cast<const f16x8*>(st + r * 256 + (((4 * lg + s) ^ (r & 15)) << 4));
+    };
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int rr = tl.rbase + min((int)(threadIdx.x >> 4) + 16 * j, tl.nrows - 1);
-      const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      aoff[j] = (uint32_t)src * (uint32_t)(K * 2) + lpart * 16;
+    for (int s = 0; s < 4; ++s) {
+      f16x8 bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bq[i], s), s2[i]);
+      f16x8 afc = read_a(0, s);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        f16x8 afn = afc;
+        if (m + 1 < MT) afn = read_a(m + 1, s);  // next row block's operand in flight
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(afc, bf[i], acc[m][i]);
+        afc = afn;
+      }
     }
-    f32x4 acc[MT][4];
+  }
+
+  // Epilogue: results go through LDS (the stage buffers are free once every
+  // wave has passed the barrier below) so that global stores are 16 B per lane.
+  lds_barrier();
+  if (G1) {
+    constexpr int HS = 272;  // staged row stride (bytes) of the 128 fp16 h values
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-
-    auto loadB = [&](int kt, u32x4 (&b)[4], uint16_t (&s)[4]) {
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        b[i] = *reinterpret_cast<const u32x4*>(wexp + woff[i] + kt * 64);
-        s[i] = sexp[soff[i] + kt * 4];
-      }
-    };
-    auto loadA = [&](int kt, u32x4 (&areg)[MT]) {
+        const int row = m * 16 + lg * 4 + i;
 #pragma unroll
-      for (int j = 0; j < MT; ++j) areg[j] = *reinterpret_cast<const u32x4*>(Abase + aoff[j] + kt * 256);
-    };
-    auto storeA = [&](int buf, const u32x4 (&areg)[MT]) {
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-        *reinterpret_cast<u32x4*>(&As[buf][((threadIdx.x >> 4) + 16 * j) * LDA + lpart * 8]) = areg[j];
-    };
-    // one K step: prefetch B(kt+2) into bl and A(kt+1) into registers,
-    // compute with B(kt) in bc and A(kt) in LDS, then publish A(kt+1)
-    auto step = [&](int kt, const u32x4 (&bc)[4], const uint16_t (&sc)[4], u32x4 (&bl)[4], uint16_t (&sl)[4], const u32x4 (&acur)[MT], u32x4 (&al)[MT]) {
-      // prefetch target, clamped so that every step issues the same loads: the
-      // compiler can then wait for exactly the loads a step needs instead of
-      // draining all of them
-      const int kpre = min(kt + RING - 1, KT - 1);
-      loadA(kpre, al);
-      // A must be issued before B: the vector-memory counter
-      // completes in order, so waiting for A would otherwise also wait for B
-      __builtin_amdgcn_sched_barrier(0);
-      loadB(kpre, bl, sl);
-      // keep the prefetches here: the scheduler would otherwise sink them
-      // next to their first use and expose the full memory latency
-      __builtin_amdgcn_sched_barrier(0);
-      const int buf = kt & 1;
-      f16x2 s2[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 sh = (_Float16)bf16_bits_to_f32(sc[i]);
-        s2[i] = (f16x2){sh, sh};
-      }
-      const uint16_t* arow = &As[buf][ln * LDA + lg * 32];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        f16x8 bf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bc[i], s), s2[i]);
-        // A fragments are read two m-subtiles ahead of their MFMAs
-        f16x8 af[3];
-        af[0] = *reinterpret_cast<const f16x8*>(arow + s * 8);
-        if (MT > 1) af[1] = *reinterpret_cast<const f16x8*>(arow + 16 * LDA + s * 8);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m + 2 < MT) af[(m + 2) % 3] = *reinterpret_cast<const f16x8*>(arow + (m + 2) * 16 * LDA + s * 8);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[m % 3], bf[i], acc[m][i]);
+        for (int n = 0; n < 2; ++n) {
+          const float hv = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
+          const _Float16 hh = (_Float16)hv;
+          // h is stored in the activation order that GEMM2's unpack expects
+          *reinterpret_cast<uint16_t*>(smem + row * HS + i4act_pos(wave * 32 + n * 16 + ln) * 2) =
+              __builtin_bit_cast(uint16_t, hh);
         }
       }
-      if (kt + 1 < KT) storeA(buf ^ 1, acur);
-      lds_barrier();
-    };
-
-    u32x4 bq[RING][4];
-    uint16_t wq[RING][4];
-    u32x4 aq[RING][MT];
-    // prologue: steps 0 .. RING-2 in flight, step 0's activation tile in LDS
-#pragma unroll
-    for (int r = 0; r + 1 < RING; ++r) {
-      loadA(min(r, KT - 1), aq[r]);
-      loadB(min(r, KT - 1), bq[r], wq[r]);
-    }
-    storeA(0, aq[0]);
     lds_barrier();
-    for (int kt = 0; kt < KT; kt += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r)
-        if (kt + r < KT)
-          step(kt + r, bq[r], wq[r], bq[(r + RING - 1) % RING], wq[(r + RING - 1) % RING], aq[(r + 1) % RING],
-               aq[(r + RING - 1) % RING]);
+    char* H = static_cast<char*>(p.out) + (int64_t)tl.nb * 256;
+    for (int c = threadIdx.x; c < BM * 16; c += 256) {
+      const int row = c >> 4, part = c & 15;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(H + (int64_t)(tl.rbase + row) * p.inter * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
     }
-
-    if (G1) {
-      uint16_t* H = static_cast<uint16_t*>(p.out);
+  } else {
+    constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + lg * 4 + i;
-          if (row < tl.nrows) {
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-              const float hv = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
-              const _Float16 hh = (_Float16)hv;
-              H[(int64_t)(tl.rbase + row) * p.inter + i4act_pos(col[n] + ln)] = __builtin_bit_cast(uint16_t, hh);
-            }
-          }
-        }
-    } else {
-      uint16_t* Y = static_cast<uint16_t*>(p.out);
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + lg * 4 + i;
-          if (row < tl.nrows) {
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              Y[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
-          }
-        }
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+              (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
+      }
+    lds_barrier();
+    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
+    for (int c = threadIdx.x; c < BM * 32; c += 256) {
+      const int row = c >> 5, part = c & 31;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
     }
   }
 }
 
-template <bool G1>
-static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
+// Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
+// items of chunk p2.chunk (either may be empty), dealt through per-XCD
+// atomic work counters exactly as for the FP8 weights.
+template <int BM>
+__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  using ST = I4Stage<BM>;
+  constexpr int S = ST::S;
+  static_assert(S >= 2 && S <= 7, "LDS stages");
+  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
+  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ int s_item;
+  ChunkWork c1, c2;
+  const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
+  const int n2 = chunk_work(p2, p2.N / 256, c2) ? c2.nwork : 0;
+  const int x = blockIdx.x & 7;
+  const int per1 = (n1 + 7) >> 3, per2 = (n2 + 7) >> 3;
+  const int b1 = x * per1, b2 = x * per2;
+  const int len1 = max(0, min(n1, b1 + per1) - b1), len2 = max(0, min(n2, b2 + per2) - b2);
+  int32_t* q = queue + x;
+  if (threadIdx.x == 0) s_item = atomicAdd(q, 1);
+  __syncthreads();
+  int cur = s_item;
+  while (cur < len1 + len2) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(q, 1);  // claimed now, read after the item
+    if (cur < len1) i4_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else i4_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (threadIdx.x == 0) s_item = nxt;
+    lds_barrier();
+    cur = s_item;
+  }
+}
+
+void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                           hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent<k_gemm_int4<16, G1>>(a, grid, s); break;
-    case 32: launch_persistent<k_gemm_int4<32, G1>>(a, grid, s); break;
-    case 64: launch_persistent<k_gemm_int4<64, G1>>(a, grid, s); break;
-    case 48: launch_persistent<k_gemm_int4<48, G1>>(a, grid, s); break;
-    case 96: launch_persistent<k_gemm_int4<96, G1>>(a, grid, s); break;
-    case 128: launch_persistent<k_gemm_int4<128, G1>>(a, grid, s); break;
-    default: launch_persistent<k_gemm_int4<192, G1>>(a, grid, s); break;
+    case 16: launch_persistent2<k_gemm_int4<16>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_int4<32>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_int4<64>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_int4<48>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_int4<96>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_int4<128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_int4<192>>(g1, g2, queue, grid, s); break;
   }
-}
-
-void launch_gemm_int4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s) {
-  if (gemm1) launch_bm<true>(a, bm, grid, s);
-  else launch_bm<false>(a, bm, grid, s);
 }
 
 }  // namespace moe

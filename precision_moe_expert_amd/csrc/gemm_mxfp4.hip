@@ -8,8 +8,9 @@
 //   B (E2M1): 32 nibbles  = k in [32g, 32g+32)
 //   scales  : lane l carries row (column) l%16's scale of K block g.
 // GEMM1's epilogue quantizes h = silu(gate) * up to MXFP8; a wave's 32 h
-// columns are exactly one scale block, so the block maximum is a wave-local
-// shuffle reduction.
+// columns are exactly one scale block, so the block maximum is a row-local
+// DPP reduction.  Operands stream through an LDS ring filled by
+// global_load_lds DMA (see the FP8 kernel for the scheme).
 #include "common.h"
 #include "kernels.h"
 #include "moe_sched.h"
@@ -22,205 +23,241 @@ MOE_DEV float floor_log2_pos_mx(float a) {
   return ef > 0 ? (float)(ef - 127) : (float)((31 - __builtin_clz(b & 0x7FFFFFu)) - 149);
 }
 
+// LDS bytes of one pipeline stage: activation rows (128 B of E4M3 codes each,
+// whole DMA groups of 8 rows per wave), one dword of four E8M0 activation
+// scales per row slot, each wave's weight fragments (4 subtiles x 1 KB of
+// E2M1) and one dword of four E8M0 weight scales per weight row.
+template <int BM>
+struct MxStage {
+  static constexpr int NA = (BM * 8 + 255) / 256;  // activation DMA groups per wave
+  static constexpr int A_BYTES = NA * 32 * 128;
+  static constexpr int AS_OFF = A_BYTES;
+  static constexpr int B_OFF = AS_OFF + 1024;
+  static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
+  static constexpr int BYTES = BS_OFF + 4 * 256;
+  // Two workgroups per CU (up to 128-row tiles): with no per-block rescale
+  // the MFMA loop fits in 256 registers, and a second resident workgroup
+  // covers one's barrier and LDS waits with the other's MFMAs (measured on
+  // MI355X: 19% faster than one workgroup with a deeper ring).
+  static constexpr int WPC = BM <= 128 ? 2 : 1;
+  static constexpr int S = (152 * 1024 / WPC) / BYTES > 5 ? 5 : (152 * 1024 / WPC) / BYTES;  // stages
+  static constexpr int NPER = NA + 1 + 4 + 1;        // DMA instructions per wave per stage
+};
+
+// One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
+// 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
-__global__ __launch_bounds__(256, (BM <= 96 ? 2 : 1)) void k_gemm_mxfp4(GemmArgs p) {
+__device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
   constexpr int MT = BM / 16;
-  // register prefetch ring: weights and activation rows of step kt + RING - 1
-  // are issued while step kt computes (deep for short tiles, whose per-step
-  // compute is too short to cover a memory round trip, shallow where
-  // registers are scarce)
-  constexpr int RING = (BM <= 32 ? 6 : BM <= 64 ? 3 : BM <= 96 ? 2 : 3);  // deepest ring that fits without spills
-  constexpr int LDA = 128 + 16;
-  constexpr int NCHUNK = BM * 8;
-  constexpr int ALOADS = (NCHUNK + 255) / 256;
-  constexpr bool AFULL = NCHUNK % 256 == 0;  // every thread loads ALOADS pieces
-  __shared__ __align__(16) uint8_t As[2][BM * LDA];
-  __shared__ __align__(16) uint32_t Ss[2][BM];
-  const int nblk = G1 ? p.inter / 128 : p.N / 256;
-  ChunkWork cw;
-  if (!chunk_work(p, nblk, cw)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  using ST = MxStage<BM>;
+  constexpr int S = ST::S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
-  const uint8_t* AS = static_cast<const uint8_t*>(p.a_scale);
-
-  for (int base = 0; base < cw.nwork; base += gridDim.x) {
-    const int wk = xcd_item(base, cw.nwork);
-    if (wk < 0) continue;
-    const Tile tl = tile_of(p, cw, wk, BM);
-    int col[4];
-    if (G1) {
-      const int g0 = tl.nb * 128 + wave * 32;
-      col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
-    } else {
-      const int c0 = tl.nb * 256 + wave * 64;
+  const char* ASbase = static_cast<const char*>(p.a_scale);
+  const uint32_t smem0 = lds_u32(smem);
+  lds_barrier();  // every wave is done with the previous item's stages
+  int col[4];
+  if (G1) {
+    const int g0 = tl.nb * 128 + wave * 32;
+    col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
+  } else {
+    const int c0 = tl.nb * 256 + wave * 64;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
-    }
-    const uint8_t* wexp = p.w + tl.e * p.w_expert_bytes;
-    const uint8_t* wsexp = static_cast<const uint8_t*>(p.w_scale) + tl.e * p.ws_expert_elems;
-    uint32_t woff[4], wsoff[4];
+    for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
+  }
+  // per-lane global sources of this item's DMA pieces (K offset added per step)
+  const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
+  const char* wsexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems;
+  const char* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  const char* bssrc;
+  {
+    int cc = col[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if ((lane >> 4) == i) cc = col[i];
+    bssrc = wsexp + (int64_t)(cc + (lane & 15)) * (K / 32);
+  }
+  const char* asrc[ST::NA];
+#pragma unroll
+  for (int j = 0; j < ST::NA; ++j) {
+    const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/8, slot c%8
+    const int row = c >> 3, slot = c & 7;
+    const int part = slot ^ (row & 7);               // XOR swizzle of 16-byte parts
+    const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+    const int sr = p.sorted_rows[rr];
+    const int src = p.a_per_token ? sr / p.top_k : rr;
+    asrc[j] = Abase + (int64_t)src * K + part * 16;
+  }
+  const char* ssrc;
+  {
+    const int row = wave * 64 + lane;
+    const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+    const int sr = p.sorted_rows[rr];
+    const int src = p.a_per_token ? sr / p.top_k : rr;
+    ssrc = ASbase + (int64_t)src * (K / 32);
+  }
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sb = smem0 + slot * ST::BYTES;
+#pragma unroll
+    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
+    dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
+    dma_b32(bssrc + kt * 4, sb + ST::BS_OFF + wave * 256);
+  };
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int s = 0; s + 1 < S; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    lds_barrier();                                    // ... and every other wave's
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const uint8_t* st = smem + (kt % S) * ST::BYTES;
+    i32x4 bf[4];
+    int sb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      woff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 2) + lg * 16;
-      wsoff[i] = (uint32_t)(col[i] + ln) * (uint32_t)(K / 32) + lg;
+      bf[i] = *reinterpret_cast<const i32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
+      sb[i] = (int)((*reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + wave * 256 + (i * 16 + ln) * 4) >> (8 * lg)) & 0xFFu);
     }
-    uint32_t aoff[ALOADS];
-    int lrow[ALOADS], lpart[ALOADS];
+    auto read_a = [&](int m, i32x8& af, int& sa) {
+      const int r = m * 16 + ln;
+      const uint8_t* arow = st + r * 128;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+      af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa = (int)((*reinterpret_cast<const uint32_t*>(st + ST::AS_OFF + r * 4) >> (8 * lg)) & 0xFFu);
+    };
+    i32x8 afc;
+    int sac;
+    read_a(0, afc, sac);
 #pragma unroll
-    for (int j = 0; j < ALOADS; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      lrow[j] = c / 8;
-      lpart[j] = c % 8;
-      const int rr = tl.rbase + min(min(lrow[j], BM - 1), tl.nrows - 1);
-      const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      aoff[j] = (uint32_t)src * (uint32_t)K + lpart[j] * 16;
+    for (int m = 0; m < MT; ++m) {
+      i32x8 afn;
+      int san = 0;
+      if (m + 1 < MT) read_a(m + 1, afn, san);  // next row block's operands in flight
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(afc, bf[i], sac, sb[i], acc[m][i]);
+      if (m + 1 < MT) {
+        afc = afn;
+        sac = san;
+      }
     }
-    const uint32_t* srow = nullptr;
-    if (threadIdx.x < BM) {
-      const int rr = tl.rbase + min((int)threadIdx.x, tl.nrows - 1);
-      const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
-      srow = reinterpret_cast<const uint32_t*>(AS + (int64_t)src * (K / 32));
-    }
-    f32x4 acc[MT][4];
+  }
+
+  // Epilogue: results go through LDS (the stage buffers are free once every
+  // wave has passed the barrier below) so that global stores are 16 B per lane.
+  if (G1) {
+    constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
+    uint8_t* He = static_cast<uint8_t*>(p.out_scale);
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-
-    auto loadB = [&](int kt, u32x4 (&b)[4], int (&ws)[4]) {
+      for (int i = 0; i < 4; ++i) {
+        const float h0 = silu_f32(acc[m][0][i]) * acc[m][2][i];
+        const float h1 = silu_f32(acc[m][1][i]) * acc[m][3][i];
+        // this wave's 32 h columns of the row are one MXFP8 block
+        const float am = row16_max_nonneg(fmaxf(fabsf(h0), fabsf(h1)));
+        int X = 0;
+        if (am > 0.0f) {
+          X = (int)floor_log2_pos_mx(am) - 8;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        }
+        const float mul = (-X >= -126) ? __uint_as_float((uint32_t)(-X + 127) << 23) : __uint_as_float(0x00400000u);
+        const int row = m * 16 + lg * 4 + i;
+        const uint32_t c2 = cvt_e4m3x2(h0 * mul, h1 * mul);
+        smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
+        smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+        if (ln == 0 && row < tl.nrows)
+          He[(int64_t)(tl.rbase + row) * (p.inter / 32) + col[0] / 32] = (uint8_t)(X + 127);
+      }
+    lds_barrier();
+    uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
+    for (int c = threadIdx.x; c < BM * 8; c += 256) {
+      const int row = c >> 3, part = c & 7;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
+    }
+  } else {
+    constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        b[i] = *reinterpret_cast<const u32x4*>(wexp + woff[i] + kt * 64);
-        ws[i] = wsexp[wsoff[i] + kt * 4];
+        const int row = m * 16 + lg * 4 + i;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+              (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
       }
-    };
-    auto loadA = [&](int kt, u32x4 (&areg)[ALOADS], uint32_t& sreg) {
-#pragma unroll
-      for (int j = 0; j < ALOADS; ++j)
-        if (AFULL || lrow[j] < BM) areg[j] = *reinterpret_cast<const u32x4*>(Abase + aoff[j] + kt * 128);
-      if (srow) sreg = srow[kt];
-    };
-    auto storeA = [&](int buf, const u32x4 (&areg)[ALOADS], uint32_t sreg) {
-#pragma unroll
-      for (int j = 0; j < ALOADS; ++j)
-        if (AFULL || lrow[j] < BM) *reinterpret_cast<u32x4*>(&As[buf][lrow[j] * LDA + lpart[j] * 16]) = areg[j];
-      if (srow) Ss[buf][threadIdx.x] = sreg;
-    };
-    auto step = [&](int kt, const u32x4 (&bc)[4], const int (&wc)[4], u32x4 (&bl)[4], int (&wl)[4], const u32x4 (&acur)[ALOADS], const uint32_t& scur, u32x4 (&al)[ALOADS], uint32_t& sl_a) {
-      // prefetch target, clamped so that every step issues the same loads: the
-      // compiler can then wait for exactly the loads a step needs instead of
-      // draining all of them
-      const int kpre = min(kt + RING - 1, KT - 1);
-      loadA(kpre, al, sl_a);
-      // A must be issued before B: the vector-memory counter
-      // completes in order, so waiting for A would otherwise also wait for B
-      __builtin_amdgcn_sched_barrier(0);
-      loadB(kpre, bl, wl);
-      // keep the prefetches here: the scheduler would otherwise sink them
-      // next to their first use and expose the full memory latency
-      __builtin_amdgcn_sched_barrier(0);
-      const int buf = kt & 1;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint8_t* ar = &As[buf][(m * 16 + ln) * LDA];
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(ar + lg * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(ar + 64 + lg * 16);
-        const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const int sa = (int)((Ss[buf][m * 16 + ln] >> (8 * lg)) & 0xFFu);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const i32x4 bv = {(int)bc[i].x, (int)bc[i].y, (int)bc[i].z, (int)bc[i].w};
-          acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(af, bv, sa, wc[i], acc[m][i]);
-        }
-      }
-      if (kt + 1 < KT) storeA(buf ^ 1, acur, scur);
-      lds_barrier();
-    };
-
-    u32x4 bq[RING][4];
-    int wq[RING][4];
-    u32x4 aq[RING][ALOADS];
-    uint32_t sq[RING];
-#pragma unroll
-    for (int r = 0; r < RING; ++r) sq[r] = 0;
-    // prologue: steps 0 .. RING-2 in flight, step 0's activation tile in LDS
-#pragma unroll
-    for (int r = 0; r + 1 < RING; ++r) {
-      loadA(min(r, KT - 1), aq[r], sq[r]);
-      loadB(min(r, KT - 1), bq[r], wq[r]);
-    }
-    storeA(0, aq[0], sq[0]);
     lds_barrier();
-    for (int kt = 0; kt < KT; kt += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        if (kt + r < KT)
-          step(kt + r, bq[r], wq[r], bq[(r + RING - 1) % RING], wq[(r + RING - 1) % RING], aq[(r + 1) % RING],
-               sq[(r + 1) % RING], aq[(r + RING - 1) % RING], sq[(r + RING - 1) % RING]);
-      }
-    }
-
-    if (G1) {
-      uint8_t* Hq = static_cast<uint8_t*>(p.out);
-      uint8_t* He = static_cast<uint8_t*>(p.out_scale);
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float h0 = silu_f32(acc[m][0][i]) * acc[m][2][i];
-          const float h1 = silu_f32(acc[m][1][i]) * acc[m][3][i];
-          float am = fmaxf(fabsf(h0), fabsf(h1));
-          am = row16_max_nonneg(am);
-          int X = 0;
-          if (am > 0.0f) {
-            X = (int)floor_log2_pos_mx(am) - 8;
-            X = X < -127 ? -127 : (X > 127 ? 127 : X);
-          }
-          const float mul = (-X >= -126) ? __uint_as_float((uint32_t)(-X + 127) << 23) : __uint_as_float(0x00400000u);
-          const int row = m * 16 + lg * 4 + i;
-          if (row < tl.nrows) {
-            const uint32_t c2 = cvt_e4m3x2(h0 * mul, h1 * mul);
-            uint8_t* dst = Hq + (int64_t)(tl.rbase + row) * p.inter;
-            dst[col[0] + ln] = (uint8_t)(c2 & 0xFF);
-            dst[col[1] + ln] = (uint8_t)(c2 >> 8);
-            if (ln == 0) He[(int64_t)(tl.rbase + row) * (p.inter / 32) + col[0] / 32] = (uint8_t)(X + 127);
-          }
-        }
-    } else {
-      uint16_t* Y = static_cast<uint16_t*>(p.out);
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + lg * 4 + i;
-          if (row < tl.nrows) {
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              Y[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
-          }
-        }
+    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
+    for (int c = threadIdx.x; c < BM * 32; c += 256) {
+      const int row = c >> 5, part = c & 31;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
     }
   }
 }
 
-template <bool G1>
-static void launch_bm(const GemmArgs& a, int bm, int grid, hipStream_t s) {
+// Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
+// items of chunk p2.chunk (either may be empty), dealt through per-XCD
+// atomic work counters exactly as for the FP8 weights.
+template <int BM>
+__global__ __launch_bounds__(256, MxStage<BM>::WPC) void k_gemm_mxfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  using ST = MxStage<BM>;
+  constexpr int S = ST::S;
+  static_assert(S >= 2 && S <= 5, "LDS stages");
+  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
+  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ int s_item;
+  ChunkWork c1, c2;
+  const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
+  const int n2 = chunk_work(p2, p2.N / 256, c2) ? c2.nwork : 0;
+  const int x = blockIdx.x & 7;
+  const int per1 = (n1 + 7) >> 3, per2 = (n2 + 7) >> 3;
+  const int b1 = x * per1, b2 = x * per2;
+  const int len1 = max(0, min(n1, b1 + per1) - b1), len2 = max(0, min(n2, b2 + per2) - b2);
+  int32_t* q = queue + x;
+  if (threadIdx.x == 0) s_item = atomicAdd(q, 1);
+  __syncthreads();
+  int cur = s_item;
+  while (cur < len1 + len2) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(q, 1);  // claimed now, read after the item
+    if (cur < len1) mx_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else mx_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (threadIdx.x == 0) s_item = nxt;
+    lds_barrier();
+    cur = s_item;
+  }
+}
+
+void launch_gemm_mxfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                            hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent<k_gemm_mxfp4<16, G1>>(a, grid, s); break;
-    case 32: launch_persistent<k_gemm_mxfp4<32, G1>>(a, grid, s); break;
-    case 64: launch_persistent<k_gemm_mxfp4<64, G1>>(a, grid, s); break;
-    case 48: launch_persistent<k_gemm_mxfp4<48, G1>>(a, grid, s); break;
-    case 96: launch_persistent<k_gemm_mxfp4<96, G1>>(a, grid, s); break;
-    case 128: launch_persistent<k_gemm_mxfp4<128, G1>>(a, grid, s); break;
-    default: launch_persistent<k_gemm_mxfp4<192, G1>>(a, grid, s); break;
+    case 16: launch_persistent2<k_gemm_mxfp4<16>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_mxfp4<32>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_mxfp4<64>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_mxfp4<48>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_mxfp4<96>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_mxfp4<128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_mxfp4<192>>(g1, g2, queue, grid, s); break;
   }
-}
-
-void launch_gemm_mxfp4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s) {
-  if (gemm1) launch_bm<true>(a, bm, grid, s);
-  else launch_bm<false>(a, bm, grid, s);
 }
 
 }  // namespace moe

@@ -54,13 +54,15 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                     const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s);
 
-// Grouped GEMMs over one chunk; bm = rows per tile (16, 32, 64 or 128).
-void launch_gemm_int4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
-// FP8: one launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2
-// (either may be empty); queue: 8 zeroed per-XCD item counters for this launch.
+// Grouped GEMMs; bm = rows per tile (16, 32, 48, 64, 96, 128 or 192).  One
+// launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2 (either may
+// be empty); queue: 8 zeroed per-XCD item counters for this launch.
+void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                           hipStream_t s);
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                           hipStream_t s);
-void launch_gemm_mxfp4(const GemmArgs& a, bool gemm1, int bm, int grid, hipStream_t s);
+void launch_gemm_mxfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                            hipStream_t s);
 
 // Launch a persistent grouped-GEMM kernel on at most as many workgroups as
 // can be resident at once (CUs x occupancy, rounded down to a multiple of 8),
@@ -86,12 +88,6 @@ inline int resident_grid(F kernel, int grid) {
   int cap = o * device_cus(dev) / 8 * 8;
   if (cap < 8) cap = 8;
   return grid > cap ? cap : grid;
-}
-template <void (*K)(GemmArgs)>
-inline void launch_persistent(const GemmArgs& a, int grid, hipStream_t s) {
-  static int cap = 0;  // resident workgroups (per kernel; the library runs on one GPU model)
-  if (cap == 0) cap = resident_grid(K, 1 << 30);
-  hipLaunchKernelGGL(K, dim3(grid < cap ? grid : cap), dim3(256), 0, s, a);
 }
 template <void (*K)(GemmArgs, GemmArgs, int32_t*)>
 inline void launch_persistent2(const GemmArgs& a, const GemmArgs& b, int32_t* q, int grid, hipStream_t s) {

@@ -65,7 +65,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   return MOE_OK;
 }
 
-// Per-XCD work-queue counters of the FP8 pair launches: 8 per launch, at most
+// Per-XCD work-queue counters of the grouped-GEMM pair launches: 8 per launch, at most
 // num_experts + 1 launches (chunk_experts >= 1).
 int queue_ints(const Dims& d) { return 8 * (d.E + 1); }
 
@@ -310,7 +310,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
   { Scope sc_(tm, MOE_STAGE_PERMUTE);
     launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
-                   tiles, queue, d.fmt == MOE_W_FP8_E4M3_B128 ? queue_ints(d) : 0, s); }
+                   tiles, queue, queue_ints(d), s); }
 
   // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
   {
@@ -379,23 +379,15 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   g2.nb_fastest = 1;
   const int grid1 = gemm_grid(d, bm, chunk_experts, d.I / 128);
   const int grid2 = gemm_grid(d, bm, chunk_experts, d.H / 256);
-  if (d.fmt == MOE_W_FP8_E4M3_B128) {
-    // launch c runs chunk c's GEMM1 together with chunk c-1's GEMM2
-    const int grid = grid1 > grid2 ? grid1 : grid2;
-    for (int c = 0; c <= nchunks; ++c) {
-      g1.chunk = c < nchunks ? c : -1;
-      g2.chunk = c - 1;
-      Scope sc_(tm, c < nchunks ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2);
-      launch_gemm_fp8_pair(g1, g2, queue + 8 * c, bm, grid, s);
-    }
-  } else {
-    auto gemm = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4 : launch_gemm_mxfp4;
-    for (int c = 0; c < nchunks; ++c) {
-      g1.chunk = c;
-      g2.chunk = c;
-      { Scope sc_(tm, MOE_STAGE_GEMM1); gemm(g1, true, bm, grid1, s); }
-      { Scope sc_(tm, MOE_STAGE_GEMM2); gemm(g2, false, bm, grid2, s); }
-    }
+  // launch c runs chunk c's GEMM1 together with chunk c-1's GEMM2
+  const int grid = grid1 > grid2 ? grid1 : grid2;
+  auto pair = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4_pair
+            : d.fmt == MOE_W_FP8_E4M3_B128 ? launch_gemm_fp8_pair : launch_gemm_mxfp4_pair;
+  for (int c = 0; c <= nchunks; ++c) {
+    g1.chunk = c < nchunks ? c : -1;
+    g2.chunk = c - 1;
+    Scope sc_(tm, c < nchunks ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2);
+    pair(g1, g2, queue + 8 * c, bm, grid, s);
   }
 
   // 5. weighted combine back to token order
