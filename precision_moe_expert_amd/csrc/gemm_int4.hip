@@ -19,19 +19,27 @@
 
 namespace moe {
 
-// 8 INT4 codes (one dword, element i in bits 4i..4i+3) times scale s ->
-// 8 fp16 values ordered (0,4),(1,5),(2,6),(3,7): (1024 + (q ^ 8)) as fp16
-// bits 0x6400 | u, minus 1032, times s.
-MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2) {
-  const uint32_t u = w ^ 0x88888888u;
-  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  f16x2 h[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t d = ((u >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-    h[j] = (__builtin_bit_cast(f16x2, d) + bias) * s2;
-  }
-  f16x8 r = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+// 8 INT4 codes (one dword, element i in bits 4i..4i+3, two's complement) times
+// scale s -> 8 fp16 values ordered (0,4),(1,5),(2,6),(3,7).  Each pair comes
+// from one bitop3 that keeps the two code fields, flips their sign bit (q + 8)
+// and sets the exponent of 1024, i.e. fp16 1024 + (q + 8) for codes in bits
+// 0-3 / 16-19, or 1024 + 16 (q + 8) for codes in bits 4-7 / 20-23 (still
+// inside the 10-bit mantissa, so no shift is needed).  Subtracting the bias
+// gives q or 16 q exactly; multiplying by s or s/16 gives q s, exact in fp16.
+// bitop3 truth table 0x6A: b ? (c ? ~a : a) : c.
+MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2, f16x2 s2_16) {
+  const f16x2 bias0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 bias1 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t v = w >> 8;
+  const uint32_t d0 = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, 0x6A);
+  const uint32_t d1 = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, 0x6A);
+  const uint32_t d2 = __builtin_amdgcn_bitop3_b32(v, 0x000F000Fu, 0x64086408u, 0x6A);
+  const uint32_t d3 = __builtin_amdgcn_bitop3_b32(v, 0x00F000F0u, 0x64806480u, 0x6A);
+  const f16x2 h0 = (__builtin_bit_cast(f16x2, d0) + bias0) * s2;
+  const f16x2 h1 = (__builtin_bit_cast(f16x2, d1) + bias1) * s2_16;
+  const f16x2 h2 = (__builtin_bit_cast(f16x2, d2) + bias0) * s2;
+  const f16x2 h3 = (__builtin_bit_cast(f16x2, d3) + bias1) * s2_16;
+  f16x8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
   return r;
 }
 
@@ -129,13 +137,15 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
     u32x4 bq[4];
-    f16x2 s2[4];
+    f16x2 s2[4], s2_16[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + (wave * 2 + (lg >> 1)) * 256 + (i * 16 + ln) * 4);
-      const _Float16 sh = (_Float16)bf16_bits_to_f32((uint16_t)((lg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+      const float sf = bf16_bits_to_f32((uint16_t)((lg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+      const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
       s2[i] = (f16x2){sh, sh};
+      s2_16[i] = (f16x2){sh16, sh16};
     }
     // activation fragment of row block m, 32-K sub-step s: logical part 4*lg + s
     auto read_a = [&](int m, int s) {
@@ -146,7 +156,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     for (int s = 0; s < 4; ++s) {
       f16x8 bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bq[i], s), s2[i]);
+      for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bq[i], s), s2[i], s2_16[i]);
       f16x8 afc = read_a(0, s);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
