@@ -6,141 +6,150 @@
 // a_scale[row][kb] * w_scale[n/128][kb] and added to the fp32 accumulator.
 // GEMM1's epilogue forms h = silu(gate) * up and quantizes it to FP8 with a
 // [1,128] scale: the workgroup's 128 h columns are one scale block, so the
-// row maximum is reduced across the 4 waves through LDS.
+// row maximum is reduced across the column waves through LDS.
+//
+// Workgroup: 8 waves, two per SIMD.  Wave (wr, wc) computes the 64 output
+// columns of column group wc for half wr of the tile's row blocks; the two
+// waves of a SIMD share their weight fragments in LDS, and while one waits
+// on LDS or a barrier the other keeps the matrix core and the VALU busy
+// (the per-block rescale costs 6 VALU instructions per MFMA).
 #include "common.h"
 #include "kernels.h"
 #include "moe_sched.h"
 
 namespace moe {
 
+constexpr int FP8_THREADS = 512;
+
 // LDS bytes of one pipeline stage: activation rows (128 B each, whole DMA
-// groups of 8 rows per wave), one fp32 activation scale per row slot (1 KB),
-// and each wave's weight fragments (4 subtiles x 2 halves x 1 KB).
+// groups of 8 rows per wave), one fp32 activation scale per slot (512 slots,
+// one DMA per wave), and the weight fragments (4 column groups x 4 subtiles
+// x 2 halves x 1 KB, each half loaded by one of the group's two waves).
 template <int BM>
 struct Fp8Stage {
-  static constexpr int NA = (BM * 8 + 255) / 256;  // activation DMA groups per wave
-  static constexpr int ROWS = NA * 32;              // activation row slots
-  static constexpr int A_BYTES = ROWS * 128;
+  static constexpr int NA = (BM * 8 + 511) / 512;  // activation DMA groups per wave
+  static constexpr int A_BYTES = NA * 8 * 1024;
   static constexpr int AS_OFF = A_BYTES;
-  static constexpr int B_OFF = AS_OFF + 1024;
+  static constexpr int B_OFF = AS_OFF + 2048;
   static constexpr int BYTES = B_OFF + 4 * 8 * 1024;
   static constexpr int S = (152 * 1024) / BYTES > 4 ? 4 : (152 * 1024) / BYTES;  // stages
-  static constexpr int NPER = NA + 1 + 8;           // DMA instructions per wave per stage
+  static constexpr int NPER = NA + 1 + 4;           // DMA instructions per wave per stage
+  static constexpr int MT = BM / 16;                // row blocks of the tile
+  static constexpr int MTW = (MT + 1) / 2;          // row blocks per wave (row group 0 takes the extra one)
 };
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
 // 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
 __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, float (*red)[BM]) {
-  constexpr int MT = BM / 16;
   using ST = Fp8Stage<BM>;
-  constexpr int S = ST::S;
+  constexpr int S = ST::S, MT = ST::MT, MTW = ST::MTW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wc = wave & 3, wr = wave >> 2;
   const int ln = lane & 15, lg = lane >> 4;
+  const int mb0 = wr * MTW;                       // first row block of this wave
+  const int nmb = min(MTW, MT - mb0);             // row blocks of this wave (wave-uniform)
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
   const char* ASbase = static_cast<const char*>(p.a_scale);
   const float* WS = static_cast<const float*>(p.w_scale);
   const uint32_t smem0 = lds_u32(smem);
+  lds_barrier();  // every wave is done with the previous item's stages
+  int col[4];
+  if (G1) {
+    const int g0 = tl.nb * 128 + wc * 32;
+    col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
+  } else {
+    const int c0 = tl.nb * 256 + wc * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
+  }
+  // per-lane global sources of this item's DMA pieces (K offset added per step)
+  const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
+  const float* wsexp = WS + tl.e * p.ws_expert_elems;
+  const char* bsrc[4];  // half wr of each subtile's fragment
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * K + (lg + 4 * wr) * 16;
+  const char* asrc[ST::NA];
+#pragma unroll
+  for (int j = 0; j < ST::NA; ++j) {
+    const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/8, slot c%8
+    const int row = c >> 3, slot = c & 7;
+    const int part = slot ^ (row & 7);               // XOR swizzle of 16-byte parts
+    const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+    const int sr = p.sorted_rows[rr];
+    const int src = p.a_per_token ? sr / p.top_k : rr;
+    asrc[j] = Abase + (int64_t)src * K + part * 16;
+  }
+  const char* ssrc;
   {
-    lds_barrier();  // every wave is done with the previous item's stages
-    int col[4];
-    if (G1) {
-      const int g0 = tl.nb * 128 + wave * 32;
-      col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
-    } else {
-      const int c0 = tl.nb * 256 + wave * 64;
+    const int row = wave * 64 + lane;
+    const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
+    const int sr = p.sorted_rows[rr];
+    const int src = p.a_per_token ? sr / p.top_k : rr;
+    ssrc = ASbase + (int64_t)src * KT * 4;
+  }
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sb = smem0 + slot * ST::BYTES;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
-    }
-    // per-lane global sources of this item's DMA pieces (K offset added per step)
-    const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
-    const float* wsexp = WS + tl.e * p.ws_expert_elems;
-    const char* bsrc[4][2];
+    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
+    dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 128, sb + ST::B_OFF + (wc * 8 + i * 2 + wr) * 1024);
+  };
+  f32x4 acc[MTW][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bsrc[i][h] = wexp + (int64_t)(col[i] + ln) * K + (lg + 4 * h) * 16;
-    const char* asrc[ST::NA];
+  for (int m = 0; m < MTW; ++m)
 #pragma unroll
-    for (int j = 0; j < ST::NA; ++j) {
-      const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/8, slot c%8
-      const int row = c >> 3, slot = c & 7;
-      const int part = slot ^ (row & 7);               // XOR swizzle of 16-byte parts
-      const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
-      const int sr = p.sorted_rows[rr];
-      const int src = p.a_per_token ? sr / p.top_k : rr;
-      asrc[j] = Abase + (int64_t)src * K + part * 16;
-    }
-    const char* ssrc;
-    {
-      const int row = wave * 64 + lane;
-      const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
-      const int sr = p.sorted_rows[rr];
-      const int src = p.a_per_token ? sr / p.top_k : rr;
-      ssrc = ASbase + (int64_t)src * KT * 4;
-    }
-    auto issue = [&](int kt, int slot) {
-      const uint32_t sb = smem0 + slot * ST::BYTES;
-#pragma unroll
-      for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
-      dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) dma_b128(bsrc[i][h] + kt * 128, sb + ST::B_OFF + (wave * 8 + i * 2 + h) * 1024);
-    };
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
-    for (int s = 0; s + 1 < S; ++s)
-      if (s < KT) issue(s, s);
-    const float* ws0 = wsexp + (col[0] / 128) * KT;
-    const float* ws2 = wsexp + (col[2] / 128) * KT;
-    float wnext[2] = {ld_uniform_f32(ws0), ld_uniform_f32(ws2)};
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
-      lds_barrier();                                    // ... and every other wave's
-      if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
-      const float wc0 = wnext[0], wc2 = wnext[1];
-      if (kt + 1 < KT) {
-        wnext[0] = ld_uniform_f32(ws0 + kt + 1);
-        wnext[1] = ld_uniform_f32(ws2 + kt + 1);
-      }
-      const uint8_t* st = smem + (kt % S) * ST::BYTES;
-      const float* As = reinterpret_cast<const float*>(st + ST::AS_OFF);
-      i32x8 bf[4];
+  for (int s = 0; s + 1 < S; ++s)
+    if (s < KT) issue(s, s);
+  const float* ws0 = wsexp + (col[0] / 128) * KT;
+  const float* ws2 = wsexp + (col[2] / 128) * KT;
+  float wnext[2] = {ld_uniform_f32(ws0), ld_uniform_f32(ws2)};
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    lds_barrier();                                    // ... and every other wave's
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const float wc0 = wnext[0], wc2 = wnext[1];
+    if (kt + 1 < KT) {
+      wnext[0] = ld_uniform_f32(ws0 + kt + 1);
+      wnext[1] = ld_uniform_f32(ws2 + kt + 1);
+    }
+    if (nmb == 0) continue;  // a 16-row tile leaves row group 1 without work
+    const uint8_t* st = smem + (kt % S) * ST::BYTES;
+    const float* As = reinterpret_cast<const float*>(st + ST::AS_OFF);
+    i32x8 bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 8 + i * 2) * 1024 + lane * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 8 + i * 2 + 1) * 1024 + lane * 16);
-        bf[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      auto read_a = [&](int m, i32x8& af, f32x4& sa) {
-        const int r = m * 16 + ln;
-        const uint8_t* arow = st + r * 128;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
-        af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sa = *reinterpret_cast<const f32x4*>(As + m * 16 + lg * 4);
-      };
-      // Software pipeline over row blocks: the MFMAs of block m run while the
-      // VALU folds block m-1's partial products into the accumulators with
-      // their (activation x weight) block scales.
-      i32x8 afc;
-      f32x4 sac;
-      read_a(0, afc, sac);
-      f32x4 prev[4], psc01, psc23;
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wc * 8 + i * 2) * 1024 + lane * 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wc * 8 + i * 2 + 1) * 1024 + lane * 16);
+      bf[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto read_a = [&](int m, i32x8& af, f32x4& sa) {
+      const int r = (mb0 + m) * 16 + ln;
+      const uint8_t* arow = st + r * 128;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+      af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa = *reinterpret_cast<const f32x4*>(As + (mb0 + m) * 16 + lg * 4);
+    };
+    // Software pipeline over row blocks: the MFMAs of block m run while the
+    // VALU folds block m-1's partial products into the accumulators with
+    // their (activation x weight) block scales.
+    i32x8 afc;
+    f32x4 sac;
+    read_a(0, afc, sac);
+    f32x4 prev[4], psc01, psc23;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MTW; ++m) {
+      if (m < nmb) {
         i32x8 afn;
         f32x4 san;
-        if (m + 1 < MT) read_a(m + 1, afn, san);
+        if (m + 1 < nmb) read_a(m + 1, afn, san);
         // one MFMA of block m per group, with the VALU work of block m-1
         // (sched_barrier keeps the compiler from bunching the MFMAs, which
         // would leave the VALU work waiting behind them)
@@ -166,82 +175,90 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) prev[i] = part[i];
-        if (m + 1 < MT) {
+        if (m + 1 < nmb) {
           afc = afn;
           sac = san;
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[MT - 1][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[MT - 1][i][q]);
     }
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+      if (m + 1 == nmb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[m][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m][i][q]);
+      }
+  }
 
-    // Epilogue: results go through LDS (the stage buffers are free once every
-    // wave has passed the barrier below) so that global stores are 16 B per lane.
-    if (G1) {
-      constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
-      float hv[MT][4][2];
+  // Epilogue: results go through LDS (the stage buffers are free once every
+  // wave has passed the barrier below) so that global stores are 16 B per lane.
+  if (G1) {
+    constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
+    float hv[MTW][4][2];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float am = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        float am = 0.0f;
 #pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            hv[m][i][n] = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
-            am = fmaxf(am, fabsf(hv[m][i][n]));
-          }
-          am = row16_max_nonneg(am);
-          if (ln == 0) red[wave][m * 16 + lg * 4 + i] = am;
+        for (int n = 0; n < 2; ++n) {
+          hv[m][i][n] = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
+          am = fmaxf(am, fabsf(hv[m][i][n]));
         }
-      lds_barrier();
-      float* Hs = static_cast<float*>(p.out_scale);
+        am = row16_max_nonneg(am);
+        if (m < nmb && ln == 0) red[wc][(mb0 + m) * 16 + lg * 4 + i] = am;
+      }
+    lds_barrier();
+    float* Hs = static_cast<float*>(p.out_scale);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
+      if (m < nmb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + lg * 4 + i;
+          const int row = (mb0 + m) * 16 + lg * 4 + i;
           const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
           // the row's [1,128] block scale amax/448; codes h/s with the hardware reciprocal
           const float sc = amax == 0.0f ? 1.0f : amax * (1.0f / 448.0f);
           const float inv = __builtin_amdgcn_rcpf(sc);
           const uint32_t c2 = cvt_e4m3x2(hv[m][i][0] * inv, hv[m][i][1] * inv);
-          smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
-          smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
-          if (wave == 0 && ln == 0 && row < tl.nrows)
+          smem[row * HS + wc * 32 + ln] = (uint8_t)(c2 & 0xFF);
+          smem[row * HS + wc * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+          if (wc == 0 && ln == 0 && row < tl.nrows)
             Hs[(int64_t)(tl.rbase + row) * (p.inter / 128) + tl.nb] = sc;
         }
-      lds_barrier();
-      uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
-      for (int c = threadIdx.x; c < BM * 8; c += 256) {
-        const int row = c >> 3, part = c & 7;
-        if (row < tl.nrows)
-          *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
-              *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
       }
-    } else {
-      constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
-      lds_barrier();
+    lds_barrier();
+    uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
+    for (int c = threadIdx.x; c < BM * 8; c += FP8_THREADS) {
+      const int row = c >> 3, part = c & 7;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
+    }
+  } else {
+    constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
+    lds_barrier();
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
+      if (m < nmb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + lg * 4 + i;
+          const int row = (mb0 + m) * 16 + lg * 4 + i;
 #pragma unroll
           for (int n = 0; n < 4; ++n)
-            *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+            *reinterpret_cast<uint16_t*>(smem + row * YS + (wc * 64 + n * 16 + ln) * 2) =
                 (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
         }
-      lds_barrier();
-      char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
-      for (int c = threadIdx.x; c < BM * 32; c += 256) {
-        const int row = c >> 5, part = c & 31;
-        if (row < tl.nrows)
-          *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
-              *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
       }
+    lds_barrier();
+    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
+    for (int c = threadIdx.x; c < BM * 32; c += FP8_THREADS) {
+      const int row = c >> 5, part = c & 31;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
     }
   }
 }
@@ -256,7 +273,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
 // its range through an atomic counter, so every workgroup exits once the
 // range is used up.
 template <int BM>
-__global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+__global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmArgs p2, int32_t* queue) {
   using ST = Fp8Stage<BM>;
   constexpr int S = ST::S;
   static_assert(S >= 2 && S <= 5, "LDS stages");
@@ -289,13 +306,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8(GemmArgs p1, GemmArgs p2, i
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                           hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent2<k_gemm_fp8<16>>(g1, g2, queue, grid, s); break;
-    case 32: launch_persistent2<k_gemm_fp8<32>>(g1, g2, queue, grid, s); break;
-    case 64: launch_persistent2<k_gemm_fp8<64>>(g1, g2, queue, grid, s); break;
-    case 48: launch_persistent2<k_gemm_fp8<48>>(g1, g2, queue, grid, s); break;
-    case 96: launch_persistent2<k_gemm_fp8<96>>(g1, g2, queue, grid, s); break;
-    case 128: launch_persistent2<k_gemm_fp8<128>>(g1, g2, queue, grid, s); break;
-    default: launch_persistent2<k_gemm_fp8<192>>(g1, g2, queue, grid, s); break;
+    case 16: launch_persistent2<k_gemm_fp8<16>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_fp8<32>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_fp8<64>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_fp8<48>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_fp8<96>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_fp8<128>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_fp8<192>, FP8_THREADS>(g1, g2, queue, grid, s); break;
   }
 }
 

@@ -80,20 +80,20 @@ inline int device_cus(int dev) {
   return cache[dev];
 }
 template <typename F>
-inline int resident_grid(F kernel, int grid) {
+inline int resident_grid(F kernel, int grid, int threads) {
   int o = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, 256, 0) != hipSuccess || o <= 0) o = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, threads, 0) != hipSuccess || o <= 0) o = 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   int cap = o * device_cus(dev) / 8 * 8;
   if (cap < 8) cap = 8;
   return grid > cap ? cap : grid;
 }
-template <void (*K)(GemmArgs, GemmArgs, int32_t*)>
+template <void (*K)(GemmArgs, GemmArgs, int32_t*), int THREADS = 256>
 inline void launch_persistent2(const GemmArgs& a, const GemmArgs& b, int32_t* q, int grid, hipStream_t s) {
   static int cap = 0;
-  if (cap == 0) cap = resident_grid(K, 1 << 30);
-  hipLaunchKernelGGL(K, dim3(grid < cap ? grid : cap), dim3(256), 0, s, a, b, q);
+  if (cap == 0) cap = resident_grid(K, 1 << 30, THREADS);
+  hipLaunchKernelGGL(K, dim3(grid < cap ? grid : cap), dim3(THREADS), 0, s, a, b, q);
 }
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
