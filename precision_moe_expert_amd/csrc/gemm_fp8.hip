@@ -289,12 +289,14 @@ __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmAr
   const int b1 = x * per1, b2 = x * per2;
   const int len1 = max(0, min(n1, b1 + per1) - b1), len2 = max(0, min(n2, b2 + per2) - b2);
   int32_t* q = queue + x;
-  if (threadIdx.x == 0) s_item = atomicAdd(q, 1);
-  __syncthreads();
-  int cur = s_item;
+  // the first item of each workgroup is its slot in the XCD; later ones come
+  // from the counter (offset by the workgroups per XCD), so the launch does
+  // not start with every workgroup contending for the same counter
+  const int wpx = gridDim.x >> 3;
+  int cur = blockIdx.x >> 3;
   while (cur < len1 + len2) {
     int nxt = 0;
-    if (threadIdx.x == 0) nxt = atomicAdd(q, 1);  // claimed now, read after the item
+    if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
     if (cur < len1) fp8_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, red);
     else fp8_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, red);
     if (threadIdx.x == 0) s_item = nxt;
