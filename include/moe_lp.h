@@ -66,7 +66,7 @@ typedef enum {
 typedef struct {
   int32_t num_tokens;  /* T >= 0 (T = 0 is a no-op) */
   int32_t hidden;      /* H: multiple of 256                                */
-  int32_t inter;       /* I: multiple of 128 (expert intermediate size)     */
+  int32_t inter;       /* I: multiple of 128 (256 for INT4 weights)         */
   int32_t num_experts; /* E: 1..1024                                        */
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */

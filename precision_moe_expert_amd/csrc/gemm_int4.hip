@@ -47,15 +47,17 @@ MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 
 
 // LDS bytes of one pipeline stage: activation rows (256 B = 128 fp16 each,
 // 16-byte parts XOR-swizzled by row), each wave's weight fragments (4
-// subtiles x 1 KB of nibbles) and two dwords of bf16 group scales per
-// weight row.
+// subtiles x 1 KB of nibbles) and 16 bytes of bf16 group scales per weight
+// row: the 8 scales of the aligned pair of K steps that holds this one (one
+// 16-byte request per row instead of two 4-byte ones; scattered small
+// requests were measured to cost more than the nibbles themselves).
 template <int BM>
 struct I4Stage {
   static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
   static constexpr int A_BYTES = BM * 256;
   static constexpr int B_OFF = A_BYTES;
   static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
-  static constexpr int BYTES = BS_OFF + 4 * 2 * 256;
+  static constexpr int BYTES = BS_OFF + 4 * 1024;
   // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
   // a second resident workgroup covers one's item start-up and waits; one at
   // 32 rows (a deeper ring wins there) and above 64 rows, where the
@@ -63,7 +65,7 @@ struct I4Stage {
   static constexpr int WPC = (BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
   static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
-  static constexpr int NPER = NA + 4 + 2;             // DMA instructions per wave per stage
+  static constexpr int NPER = NA + 4 + 1;             // DMA instructions per wave per stage
 };
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
@@ -119,8 +121,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) dma_b32(bssrc + kt * 8 + h * 4, sb + ST::BS_OFF + (wave * 2 + h) * 256);
+    dma_b128(bssrc + (kt & ~1) * 8, sb + ST::BS_OFF + wave * 1024);
   };
   f32x4 acc[MT][4];
 #pragma unroll
@@ -141,7 +142,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + (wave * 2 + (lg >> 1)) * 256 + (i * 16 + ln) * 4);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + wave * 1024 + (i * 16 + ln) * 16 +
+                                                             (kt & 1) * 8 + (lg >> 1) * 4);
       const float sf = bf16_bits_to_f32((uint16_t)((lg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
       const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
       s2[i] = (f16x2){sh, sh};

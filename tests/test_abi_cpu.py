@@ -70,6 +70,8 @@ def _fwd(layer, x=FAKE, lg=FAKE, w=FAKE, adapter=None, chunk=1, out=FAKE, ws=FAK
 @pytest.mark.parametrize("case,expect", [
     (dict(H=200), binding.MOE_ERR_UNSUPPORTED),
     (dict(I=100), binding.MOE_ERR_UNSUPPORTED),
+    (dict(I=384), binding.MOE_ERR_UNSUPPORTED),          # INT4 group scales need I % 256 == 0
+    (dict(I=384, fmt=2), None),
     (dict(E=2000), binding.MOE_ERR_UNSUPPORTED),
     (dict(k=17, E=32), binding.MOE_ERR_UNSUPPORTED),
     (dict(k=9, E=8), binding.MOE_ERR_INVALID_ARGUMENT),
@@ -81,7 +83,10 @@ def test_forward_rejects_bad_layer(case, expect):
     p = dict(T=64, H=256, I=512, E=8, k=2, fmt=1)
     p.update(case)
     L = binding.make_layer(p["T"], p["H"], p["I"], p["E"], p["k"], p["fmt"])
-    assert _fwd(L) == expect
+    if expect is None:  # a valid layer: validation passes and the fake workspace size is what fails
+        assert _fwd(L, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    else:
+        assert _fwd(L) == expect
 
 
 def test_forward_rejects_bad_pointers_and_workspace():

@@ -15,14 +15,16 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def small(fmt, T=77, H=256, I=384, E=12, k=3, oft=False, zipf=0.0, chunk=4, cfg_id=None):
+def small(fmt, T=77, H=256, I=None, E=12, k=3, oft=False, zipf=0.0, chunk=4, cfg_id=None):
+    # three 128-column h blocks (INT4 weights need I % 256 == 0: three 256-wide K pairs)
+    I = I or (768 if fmt == 1 else 384)
     return synth.LayerConfig(f"small_f{fmt}", cfg_id or (40 + fmt + (5 if oft else 0)), T=T, H=H, E=E, k=k, I=I,
                              fmt=fmt, chunk=chunk, oft=oft, zipf_alpha=zipf)
 
 
 def check_route(logits: np.ndarray, k: int, E: int):
     T = logits.shape[0]
-    layer = binding.make_layer(T, 256, 128, E, k, 1)
+    layer = binding.make_layer(T, 256, 256, E, k, 1)
     got = binding.route_permute(gu.dev(np.ascontiguousarray(logits, np.float32)), layer)
     torch.cuda.synchronize()
     ids, w = oracle.route(logits, k)
@@ -128,7 +130,7 @@ def test_combine_vs_oracle():
     ids, w = oracle.route(lg, k)
     P = oracle.permute(ids, E)
     y = synth._to_bf16_bits((r.standard_normal((T * k, H)) * 3).astype(np.float32))
-    layer = binding.make_layer(T, H, 128, E, k, 1)
+    layer = binding.make_layer(T, H, 256, E, k, 1)
     out = binding.combine(layer, gu.dev(y, "bf16"), gu.dev(w), gu.dev(P["row_of"]))
     got = gu.bf16_to_np(out)
     ref = oracle.combine(y, w, P["row_of"])
@@ -150,7 +152,7 @@ def test_lm_head_logprob_vs_oracle():
 
 
 def test_t0_is_noop():
-    layer = binding.make_layer(0, 256, 128, 8, 2, 1)
+    layer = binding.make_layer(0, 256, 256, 8, 2, 1)
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     lg = torch.empty((0, 8), dtype=torch.float32, device="cuda")
     z = torch.zeros(16, dtype=torch.uint8, device="cuda")
