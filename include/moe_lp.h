@@ -66,7 +66,7 @@ typedef enum {
 typedef struct {
   int32_t num_tokens;  /* T >= 0 (T = 0 is a no-op) */
   int32_t hidden;      /* H: multiple of 256                                */
-  int32_t inter;       /* I: multiple of 128 (256 for INT4 weights)         */
+  int32_t inter;       /* I: multiple of 128 (expert intermediate size)     */
   int32_t num_experts; /* E: 1..1024                                        */
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */
@@ -83,10 +83,12 @@ typedef struct {
   const void* w2;
 } moe_qweights;
 
-/* Scales, layouts per format:
- *   INT4 : s13 bf16 [E][2I][H/32],   s2 bf16 [E][H][I/32]
+/* Scales, layouts per format.  Group scales (one per output row n and 32
+ * consecutive k) are stored group-major, [K/32][N] per expert, so that the
+ * scales of one K step for a block of output rows are contiguous:
+ *   INT4 : s13 bf16 [E][H/32][2I],   s2 bf16 [E][I/32][H]
  *   FP8  : s13 fp32 [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]
- *   MXFP4: s13 u8   [E][2I][H/32],   s2 u8   [E][H][I/32]  (E8M0) */
+ *   MXFP4: s13 u8   [E][H/32][2I],   s2 u8   [E][I/32][H]  (E8M0) */
 typedef struct {
   const void* s13;
   const void* s2;

@@ -232,9 +232,10 @@ int oracle_permute(int T, int E, int k, const int32_t* ids, int32_t* counts, int
 /* ----------------------------------------------------------- dequantizers */
 
 /* Dequantize the N x K weight matrix of one expert to fp32 (w = q * s).
- *   INT4 : q two's-complement nibble, s bf16 per (n, 32 along K)
+ *   INT4 : q two's-complement nibble, s bf16 per (n, 32 along K), stored
+ *          group-major: s[(k/32) * N + n]
  *   FP8  : q E4M3FN, s fp32 per [128,128] block (n/128, k/128)
- *   MXFP4: q E2M1 nibble, s E8M0 per (n, 32 along K) */
+ *   MXFP4: q E2M1 nibble, s E8M0 per (n, 32 along K), group-major as INT4 */
 static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < N; ++n) {
@@ -242,13 +243,13 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
       double v;
       if (fmt == OR_INT4) {
         v = (double)int4_value(nibble_at(q, (int64_t)n * K + kk)) *
-            (double)bf16_value(((const uint16_t*)s)[(int64_t)n * (K / 32) + kk / 32]);
+            (double)bf16_value(((const uint16_t*)s)[(int64_t)(kk / 32) * N + n]);
       } else if (fmt == OR_FP8) {
         v = e4m3_value(q[(int64_t)n * K + kk]) *
             (double)((const float*)s)[(int64_t)(n / 128) * (K / 128) + kk / 128];
       } else {
         v = e2m1_value(nibble_at(q, (int64_t)n * K + kk)) *
-            e8m0_value(((const uint8_t*)s)[(int64_t)n * (K / 32) + kk / 32]);
+            e8m0_value(((const uint8_t*)s)[(int64_t)(kk / 32) * N + n]);
       }
       out[(int64_t)n * K + kk] = (float)v;
     }

@@ -47,17 +47,18 @@ MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 
 
 // LDS bytes of one pipeline stage: activation rows (256 B = 128 fp16 each,
 // 16-byte parts XOR-swizzled by row), each wave's weight fragments (4
-// subtiles x 1 KB of nibbles) and 16 bytes of bf16 group scales per weight
-// row: the 8 scales of the aligned pair of K steps that holds this one (one
-// 16-byte request per row instead of two 4-byte ones; scattered small
-// requests were measured to cost more than the nibbles themselves).
+// subtiles x 1 KB of nibbles) and the bf16 group scales of the wave's 64
+// weight rows for the step's 4 groups (512 B).  Scales are stored
+// group-major, so those are 4 (GEMM2) or 8 (GEMM1: gate and up) contiguous
+// runs: 32 lanes x 16 B.  (Per-row scale requests, 64 per wave per step,
+// were measured to cost more time than the weight nibbles themselves.)
 template <int BM>
 struct I4Stage {
   static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
   static constexpr int A_BYTES = BM * 256;
   static constexpr int B_OFF = A_BYTES;
   static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
-  static constexpr int BYTES = BS_OFF + 4 * 1024;
+  static constexpr int BYTES = BS_OFF + 4 * 512;
   // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
   // a second resident workgroup covers one's item start-up and waits; one at
   // 32 rows (a deeper ring wins there) and above 64 rows, where the
@@ -96,13 +97,12 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   const char* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  // group scales: lane l < 32 takes 8 consecutive weight rows of group l/8
   const char* bssrc;
   {
-    int cc = col[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if ((lane >> 4) == i) cc = col[i];
-    bssrc = sexp + (int64_t)(cc + (lane & 15)) * (K / 32) * 2;
+    const int g = (lane >> 3) & 3, pc = lane & 7;
+    const int c = G1 ? (pc < 4 ? col[0] + pc * 8 : col[2] + (pc - 4) * 8) : col[0] + pc * 8;
+    bssrc = sexp + ((int64_t)g * p.N + c) * 2;
   }
   const char* asrc[ST::NA];
 #pragma unroll
@@ -121,7 +121,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-    dma_b128(bssrc + (kt & ~1) * 8, sb + ST::BS_OFF + wave * 1024);
+    if (lane < 32) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * 512);
   };
   f32x4 acc[MT][4];
 #pragma unroll
@@ -142,9 +142,9 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + wave * 1024 + (i * 16 + ln) * 16 +
-                                                             (kt & 1) * 8 + (lg >> 1) * 4);
-      const float sf = bf16_bits_to_f32((uint16_t)((lg & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+      const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * 512 + lg * 128 +
+                                                             (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
+      const float sf = bf16_bits_to_f32(sw);
       const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
       s2[i] = (f16x2){sh, sh};
       s2_16[i] = (f16x2){sh16, sh16};

@@ -26,7 +26,8 @@ MOE_DEV float floor_log2_pos_mx(float a) {
 // LDS bytes of one pipeline stage: activation rows (128 B of E4M3 codes each,
 // whole DMA groups of 8 rows per wave), one dword of four E8M0 activation
 // scales per row slot, each wave's weight fragments (4 subtiles x 1 KB of
-// E2M1) and one dword of four E8M0 weight scales per weight row.
+// E2M1) and the E8M0 scales of its 64 weight rows for the step's 4 groups
+// (group-major storage: 16 contiguous runs of 16 bytes).
 template <int BM>
 struct MxStage {
   static constexpr int NA = (BM * 8 + 255) / 256;  // activation DMA groups per wave
@@ -73,13 +74,13 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   const char* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  // E8M0 weight scales (group-major): lane l < 16 takes 16 consecutive
+  // weight rows of group l/4, i.e. one subtile
   const char* bssrc;
   {
-    int cc = col[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if ((lane >> 4) == i) cc = col[i];
-    bssrc = wsexp + (int64_t)(cc + (lane & 15)) * (K / 32);
+    const int g = (lane >> 2) & 3, pc = lane & 3;
+    const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
+    bssrc = wsexp + (int64_t)g * p.N + c;
   }
   const char* asrc[ST::NA];
 #pragma unroll
@@ -107,7 +108,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-    dma_b32(bssrc + kt * 4, sb + ST::BS_OFF + wave * 256);
+    if (lane < 16) dma_b128(bssrc + (int64_t)kt * 4 * p.N, sb + ST::BS_OFF + wave * 256);
   };
   f32x4 acc[MT][4];
 #pragma unroll
@@ -128,7 +129,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf[i] = *reinterpret_cast<const i32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
-      sb[i] = (int)((*reinterpret_cast<const uint32_t*>(st + ST::BS_OFF + wave * 256 + (i * 16 + ln) * 4) >> (8 * lg)) & 0xFFu);
+      sb[i] = (int)st[ST::BS_OFF + wave * 256 + lg * 64 + i * 16 + ln];
     }
     auto read_a = [&](int m, i32x8& af, int& sa) {
       const int r = m * 16 + ln;

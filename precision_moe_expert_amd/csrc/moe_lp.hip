@@ -43,8 +43,6 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if (L->oft_block != 0 && L->oft_block != 32) return MOE_ERR_UNSUPPORTED;
   if (L->adapter_expert_stride < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (L->hidden % 256 != 0 || L->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  // INT4 group scales of a weight row are read 16 bytes (two K steps) at a time
-  if (L->wformat == MOE_W_INT4_G32_BF16 && L->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
   if (L->num_experts > MAX_EXPERTS || L->top_k > MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;

@@ -123,11 +123,11 @@ def gen_logits(cfg: LayerConfig) -> np.ndarray:
 def _gen_int4(cfg, N, K, tensor, stensor):
     E = cfg.E
     q = np.empty((E, N, K // 2), np.uint8)
-    s = np.empty((E, N, K // 32), np.uint16)
+    s = np.empty((E, K // 32, N), np.uint16)  # group-major: s[e][g][n] scales row n, k in [32g, 32g+32)
     for e in range(E):
         # uniform bytes = two independent uniform nibbles over all 16 codes
         q[e] = _rng(cfg.cfg_id, tensor, e).integers(0, 256, (N, K // 2), dtype=np.uint8)
-        s[e] = _to_bf16_bits(_rng(cfg.cfg_id, stensor, e).uniform(0.005, 0.02, (N, K // 32)).astype(np.float32))
+        s[e] = _to_bf16_bits(_rng(cfg.cfg_id, stensor, e).uniform(0.005, 0.02, (N, K // 32)).astype(np.float32)).T
     return q, s
 
 
@@ -152,14 +152,14 @@ def _gen_mxfp4(cfg, N, K, tensor, stensor):
     lut16[:256] = mag
     lut16[256:] = mag | 8
     q = np.empty((E, N, K // 2), np.uint8)
-    s = np.empty((E, N, K // 32), np.uint8)
+    s = np.empty((E, K // 32, N), np.uint8)  # group-major, as for INT4
     for e in range(E):
         r = _rng(cfg.cfg_id, tensor, e)
         lo = lut16[r.integers(0, 512, (N, K // 2), dtype=np.uint16)]
         hi = lut16[r.integers(0, 512, (N, K // 2), dtype=np.uint16)]
         q[e] = lo | (hi << 4)
         # E8M0 scale bytes 2^-8 .. 2^-6 -> weights of magnitude ~0.02
-        s[e] = _rng(cfg.cfg_id, stensor, e).integers(119, 122, (N, K // 32), dtype=np.uint8)
+        s[e] = _rng(cfg.cfg_id, stensor, e).integers(119, 122, (N, K // 32), dtype=np.uint8).T
     return q, s
 
 

@@ -44,14 +44,14 @@ def int4_values(nibbles):
 def dequant(fmt, q, s, N, K):
     if fmt == 1:
         v = int4_values(unpack_nibbles(q)).reshape(N, K)
-        sc = np.repeat(bf16_to_f32(s).astype(np.float64).reshape(N, K // 32), 32, axis=1)
+        sc = np.repeat(bf16_to_f32(s).astype(np.float64).reshape(K // 32, N).T, 32, axis=1)  # group-major
         return v * sc
     if fmt == 2:
         v = e4m3_to_f64(q).reshape(N, K)
         sc = np.kron(np.asarray(s, np.float64).reshape(N // 128, K // 128), np.ones((128, 128)))
         return v * sc
     v = E2M1_TABLE[unpack_nibbles(q)].reshape(N, K)
-    sc = np.repeat(np.ldexp(1.0, np.asarray(s, np.int64).reshape(N, K // 32) - 127), 32, axis=1)
+    sc = np.repeat(np.ldexp(1.0, np.asarray(s, np.int64).reshape(K // 32, N).T - 127), 32, axis=1)
     return v * sc
 
 

@@ -15,9 +15,7 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def small(fmt, T=77, H=256, I=None, E=12, k=3, oft=False, zipf=0.0, chunk=4, cfg_id=None):
-    # three 128-column h blocks (INT4 weights need I % 256 == 0: three 256-wide K pairs)
-    I = I or (768 if fmt == 1 else 384)
+def small(fmt, T=77, H=256, I=384, E=12, k=3, oft=False, zipf=0.0, chunk=4, cfg_id=None):
     return synth.LayerConfig(f"small_f{fmt}", cfg_id or (40 + fmt + (5 if oft else 0)), T=T, H=H, E=E, k=k, I=I,
                              fmt=fmt, chunk=chunk, oft=oft, zipf_alpha=zipf)
 
