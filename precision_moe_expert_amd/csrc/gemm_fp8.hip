@@ -23,8 +23,8 @@ constexpr int FP8_THREADS = 512;
 
 // LDS bytes of one pipeline stage: activation rows (128 B each, whole DMA
 // groups of 8 rows per wave), one fp32 activation scale per slot (512 slots,
-// one DMA per wave), and the weight fragments (4 column groups x 4 subtiles
-// x 2 halves x 1 KB, each half loaded by one of the group's two waves).
+// one DMA per wave), and the weight rows (4 column groups x 64 rows x 128 B,
+// each group loaded half by each of its two waves).
 template <int BM>
 struct Fp8Stage {
   static constexpr int NA = (BM * 8 + 511) / 512;  // activation DMA groups per wave
@@ -67,9 +67,19 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
   // per-lane global sources of this item's DMA pieces (K offset added per step)
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
   const float* wsexp = WS + tl.e * p.ws_expert_elems;
-  const char* bsrc[4];  // half wr of each subtile's fragment
+  // Weight rows go to LDS as whole 128-byte lines (8 lanes per row, so every
+  // request is a full line), 16-byte parts XOR-swizzled by row as for the
+  // activations: column group wc's 64 rows take 8 DMAs, 4 from each of its
+  // two waves.  Local row r < 32 is gate/first-half row col[0] + r, r >= 32
+  // is col[2] + r - 32 (GEMM2: col[0] + r).
+  const char* bsrc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * K + (lg + 4 * wr) * 16;
+  for (int j = 0; j < 4; ++j) {
+    const int c = (wr * 4 + j) * 64 + lane;
+    const int r = c >> 3, part = (c & 7) ^ (r & 7);
+    const int n = G1 ? (r < 32 ? col[0] + r : col[2] + r - 32) : col[0] + r;
+    bsrc[j] = wexp + (int64_t)n * K + part * 16;
+  }
   const char* asrc[ST::NA];
 #pragma unroll
   for (int j = 0; j < ST::NA; ++j) {
@@ -95,7 +105,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
     dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 128, sb + ST::B_OFF + (wc * 8 + i * 2 + wr) * 1024);
+    for (int j = 0; j < 4; ++j) dma_b128(bsrc[j] + kt * 128, sb + ST::B_OFF + (wc * 8 + wr * 4 + j) * 1024);
   };
   f32x4 acc[MTW][4];
 #pragma unroll
@@ -124,8 +134,10 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     i32x8 bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wc * 8 + i * 2) * 1024 + lane * 16);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wc * 8 + i * 2 + 1) * 1024 + lane * 16);
+      const int r = i * 16 + ln;
+      const uint8_t* brow = st + ST::B_OFF + wc * 8192 + r * 128;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(brow + ((lg ^ (r & 7)) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(brow + (((lg + 4) ^ (r & 7)) << 4));
       bf[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
