@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_act_f16(const uint16_t* __restrict__ x,
 // 0), codes = E4M3(v / s).  One wave per token; a lane owns 32 elements, four
 // lanes a block.
 __global__ __launch_bounds__(256) void k_act_fp8(const uint16_t* __restrict__ x, int T, int H,
-                                                 uint8_t* __restrict__ q, float* __restrict__ sc) {
+                                                 uint8_t* __restrict__ q, float* __restrict__ sc, int sc_stride) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (t >= T) return;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_act_fp8(const uint16_t* __restrict__ x,
     uint4* dst = reinterpret_cast<uint4*>(q + (int64_t)t * H + c0);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    if ((lane & 3) == 0) sc[(int64_t)t * (H / 128) + c0 / 128] = s;
+    if ((lane & 3) == 0) sc[(int64_t)t * (sc_stride / 4) + c0 / 128] = s;
   }
 }
 
@@ -100,7 +100,7 @@ MOE_DEV uint32_t mx_quant32(const float* v, float amax, uint32_t* packed) {
 
 // MXFP8 activation quantization per token: a lane owns one 32-block.
 __global__ __launch_bounds__(256) void k_act_mxfp8(const uint16_t* __restrict__ x, int T, int H,
-                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ e8, int e8_stride) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (t >= T) return;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_act_mxfp8(const uint16_t* __restrict__ 
     uint4* dst = reinterpret_cast<uint4*>(q + (int64_t)t * H + c0);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    e8[(int64_t)t * (H / 32) + c0 / 32] = (uint8_t)eb;
+    e8[(int64_t)t * e8_stride + c0 / 32] = (uint8_t)eb;
   }
 }
 
@@ -194,11 +194,11 @@ void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t 
   if (n8 == 0) return;
   hipLaunchKernelGGL(k_act_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
 }
-void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, hipStream_t s) {
-  hipLaunchKernelGGL(k_act_fp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc);
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_fp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc, sc_stride);
 }
-void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, hipStream_t s) {
-  hipLaunchKernelGGL(k_act_mxfp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, e8);
+void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_mxfp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, e8, e8_stride);
 }
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,

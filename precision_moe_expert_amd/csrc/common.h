@@ -151,6 +151,22 @@ MOE_DEV void wait_vmcnt() {
 // waits longer.
 template <int N>
 MOE_DEV void wait_vmcnt_clamped() { wait_vmcnt<(N > 63 ? 63 : N)>(); }
+// As wait_stages, when the stages in flight also hold `extra` (0 or 1) more
+// loads of this wave.
+template <int NPER>
+MOE_DEV void wait_stages_x(int n, int extra) {
+  if (extra == 0) {
+    if (n >= 3) wait_vmcnt_clamped<3 * NPER>();
+    else if (n == 2) wait_vmcnt_clamped<2 * NPER>();
+    else if (n == 1) wait_vmcnt_clamped<NPER>();
+    else wait_vmcnt<0>();
+  } else {
+    if (n >= 3) wait_vmcnt_clamped<3 * NPER + 1>();
+    else if (n == 2) wait_vmcnt_clamped<2 * NPER + 1>();
+    else if (n == 1) wait_vmcnt_clamped<NPER + 1>();
+    else wait_vmcnt<0>();
+  }
+}
 template <int NPER>
 MOE_DEV void wait_stages(int n) {
   if (n >= 5) wait_vmcnt_clamped<5 * NPER>();

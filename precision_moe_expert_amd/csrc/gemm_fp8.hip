@@ -22,26 +22,30 @@ namespace moe {
 constexpr int FP8_THREADS = 512;
 
 // LDS bytes of one pipeline stage: activation rows (128 B each, whole DMA
-// groups of 8 rows per wave), one fp32 activation scale per slot (512 slots,
-// one DMA per wave), and the weight rows (4 column groups x 64 rows x 128 B,
-// each group loaded half by each of its two waves).
+// groups of 8 rows per wave) and the weight rows (4 column groups x 64 rows
+// x 128 B, each group loaded half by each of its two waves).
 template <int BM>
 struct Fp8Stage {
   static constexpr int NA = (BM * 8 + 511) / 512;  // activation DMA groups per wave
   static constexpr int A_BYTES = NA * 8 * 1024;
-  static constexpr int AS_OFF = A_BYTES;
-  static constexpr int B_OFF = AS_OFF + 2048;
+  static constexpr int B_OFF = A_BYTES;
   static constexpr int BYTES = B_OFF + 4 * 8 * 1024;
   static constexpr int S = (152 * 1024) / BYTES > 4 ? 4 : (152 * 1024) / BYTES;  // stages
-  static constexpr int NPER = NA + 1 + 4;           // DMA instructions per wave per stage
+  static constexpr int NPER = NA + 4;               // DMA instructions per wave per stage
   static constexpr int MT = BM / 16;                // row blocks of the tile
   static constexpr int MTW = (MT + 1) / 2;          // row blocks per wave (row group 0 takes the extra one)
+  // Activation scales travel in blocks of 4 K steps (16 B per row, one
+  // aligned piece of the padded scale row), double-buffered outside the
+  // ring: waves 0..NASW-1 load 64 rows each with every 4th stage.
+  static constexpr int NASW = (BM + 63) / 64;
+  static constexpr int AS_BLOCK = NASW * 64 * 16;
 };
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
 // 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
-__device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, float (*red)[BM]) {
+__device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, uint8_t* asb,
+                                         float (*red)[BM]) {
   using ST = Fp8Stage<BM>;
   constexpr int S = ST::S, MT = ST::MT, MTW = ST::MTW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -53,7 +57,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
   const char* Abase = static_cast<const char*>(p.a);
   const char* ASbase = static_cast<const char*>(p.a_scale);
   const float* WS = static_cast<const float*>(p.w_scale);
-  const uint32_t smem0 = lds_u32(smem);
+  const uint32_t smem0 = lds_u32(smem), asb0 = lds_u32(asb);
   lds_barrier();  // every wave is done with the previous item's stages
   int col[4];
   if (G1) {
@@ -97,13 +101,14 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
     const int sr = p.sorted_rows[rr];
     const int src = p.a_per_token ? sr / p.top_k : rr;
-    ssrc = ASbase + (int64_t)src * KT * 4;
+    ssrc = ASbase + (int64_t)src * p.a_scale_stride;
   }
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * ST::BYTES;
 #pragma unroll
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
-    dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
+    if (wave < ST::NASW && (kt & 3) == 0)
+      dma_b128(ssrc + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma_b128(bsrc[j] + kt * 128, sb + ST::B_OFF + (wc * 8 + wr * 4 + j) * 1024);
   };
@@ -120,7 +125,12 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
   const float* ws2 = wsexp + (col[2] / 128) * KT;
   float wnext[2] = {ld_uniform_f32(ws0), ld_uniform_f32(ws2)};
   for (int kt = 0; kt < KT; ++kt) {
-    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    {
+      // this wave's pieces of stage kt have landed (later stages in flight
+      // hold one more load if a scale block starts among them)
+      const int n = min(S - 2, KT - 1 - kt);
+      wait_stages_x<ST::NPER>(n, (wave < ST::NASW && ((kt + n) >> 2) > (kt >> 2)) ? 1 : 0);
+    }
     lds_barrier();                                    // ... and every other wave's
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const float wc0 = wnext[0], wc2 = wnext[1];
@@ -130,7 +140,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     }
     if (nmb == 0) continue;  // a 16-row tile leaves row group 1 without work
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
-    const float* As = reinterpret_cast<const float*>(st + ST::AS_OFF);
+    const float* As = reinterpret_cast<const float*>(asb + ((kt >> 2) & 1) * ST::AS_BLOCK) + (kt & 3);
     i32x8 bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -147,7 +157,8 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
       const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
       af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa = *reinterpret_cast<const f32x4*>(As + (mb0 + m) * 16 + lg * 4);
+      const int r0 = (mb0 + m) * 16 + lg * 4;
+      sa = (f32x4){As[r0 * 4], As[(r0 + 1) * 4], As[(r0 + 2) * 4], As[(r0 + 3) * 4]};
     };
     // Software pipeline over row blocks: the MFMAs of block m run while the
     // VALU folds block m-1's partial products into the accumulators with
@@ -238,7 +249,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
           smem[row * HS + wc * 32 + ln] = (uint8_t)(c2 & 0xFF);
           smem[row * HS + wc * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
           if (wc == 0 && ln == 0 && row < tl.nrows)
-            Hs[(int64_t)(tl.rbase + row) * (p.inter / 128) + tl.nb] = sc;
+            Hs[(int64_t)(tl.rbase + row) * (p.out_scale_stride / 4) + tl.nb] = sc;
         }
       }
     lds_barrier();
@@ -291,6 +302,7 @@ __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmAr
   static_assert(S >= 2 && S <= 5, "LDS stages");
   __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
   static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ __align__(16) uint8_t asb[2 * ST::AS_BLOCK];
   __shared__ float red[4][BM];
   __shared__ int s_item;
   ChunkWork c1, c2;
@@ -309,8 +321,8 @@ __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmAr
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) fp8_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, red);
-    else fp8_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, red);
+    if (cur < len1) fp8_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, asb, red);
+    else fp8_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, asb, red);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;

@@ -24,16 +24,14 @@ MOE_DEV float floor_log2_pos_mx(float a) {
 }
 
 // LDS bytes of one pipeline stage: activation rows (128 B of E4M3 codes each,
-// whole DMA groups of 8 rows per wave), one dword of four E8M0 activation
-// scales per row slot, each wave's weight fragments (4 subtiles x 1 KB of
-// E2M1) and the E8M0 scales of its 64 weight rows for the step's 4 groups
-// (group-major storage: 16 contiguous runs of 16 bytes).
+// whole DMA groups of 8 rows per wave), each wave's weight fragments (4
+// subtiles x 1 KB of E2M1) and the E8M0 scales of its 64 weight rows for the
+// step's 4 groups (group-major storage: 16 contiguous runs of 16 bytes).
 template <int BM>
 struct MxStage {
   static constexpr int NA = (BM * 8 + 255) / 256;  // activation DMA groups per wave
   static constexpr int A_BYTES = NA * 32 * 128;
-  static constexpr int AS_OFF = A_BYTES;
-  static constexpr int B_OFF = AS_OFF + 1024;
+  static constexpr int B_OFF = A_BYTES;
   static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
   static constexpr int BYTES = BS_OFF + 4 * 256;
   // Two workgroups per CU (up to 128-row tiles): with no per-block rescale
@@ -42,13 +40,18 @@ struct MxStage {
   // MI355X: 19% faster than one workgroup with a deeper ring).
   static constexpr int WPC = BM <= 128 ? 2 : 1;
   static constexpr int S = (152 * 1024 / WPC) / BYTES > 5 ? 5 : (152 * 1024 / WPC) / BYTES;  // stages
-  static constexpr int NPER = NA + 1 + 4 + 1;        // DMA instructions per wave per stage
+  static constexpr int NPER = NA + 4 + 1;            // DMA instructions per wave per stage
+  // Activation scales travel in blocks of 4 K steps (16 B per row), double-
+  // buffered outside the ring: waves 0..NASW-1 load 64 rows each with
+  // every 4th stage.
+  static constexpr int NASW = (BM + 63) / 64;
+  static constexpr int AS_BLOCK = NASW * 64 * 16;
 };
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
 // 128 gate + 128 up weight rows; GEMM2: 256 output columns).
 template <int BM, bool G1>
-__device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
+__device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, uint8_t* asb) {
   constexpr int MT = BM / 16;
   using ST = MxStage<BM>;
   constexpr int S = ST::S;
@@ -57,7 +60,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
   const char* ASbase = static_cast<const char*>(p.a_scale);
-  const uint32_t smem0 = lds_u32(smem);
+  const uint32_t smem0 = lds_u32(smem), asb0 = lds_u32(asb);
   lds_barrier();  // every wave is done with the previous item's stages
   int col[4];
   if (G1) {
@@ -99,13 +102,14 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
     const int sr = p.sorted_rows[rr];
     const int src = p.a_per_token ? sr / p.top_k : rr;
-    ssrc = ASbase + (int64_t)src * (K / 32);
+    ssrc = ASbase + (int64_t)src * p.a_scale_stride;
   }
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * ST::BYTES;
 #pragma unroll
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
-    dma_b32(ssrc + kt * 4, sb + ST::AS_OFF + wave * 256);
+    if (wave < ST::NASW && (kt & 3) == 0)
+      dma_b128(ssrc + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
     if (lane < 16) dma_b128(bssrc + (int64_t)kt * 4 * p.N, sb + ST::BS_OFF + wave * 256);
@@ -120,7 +124,12 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   for (int s = 0; s + 1 < S; ++s)
     if (s < KT) issue(s, s);
   for (int kt = 0; kt < KT; ++kt) {
-    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    {
+      // this wave's pieces of stage kt have landed (later stages in flight
+      // hold one more load if a scale block starts among them)
+      const int n = min(S - 2, KT - 1 - kt);
+      wait_stages_x<ST::NPER>(n, (wave < ST::NASW && ((kt + n) >> 2) > (kt >> 2)) ? 1 : 0);
+    }
     lds_barrier();                                    // ... and every other wave's
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
@@ -137,7 +146,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
       const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
       af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa = (int)((*reinterpret_cast<const uint32_t*>(st + ST::AS_OFF + r * 4) >> (8 * lg)) & 0xFFu);
+      sa = (int)asb[((kt >> 2) & 1) * ST::AS_BLOCK + r * 16 + (kt & 3) * 4 + lg];
     };
     i32x8 afc;
     int sac;
@@ -181,7 +190,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
         smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
         smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
         if (ln == 0 && row < tl.nrows)
-          He[(int64_t)(tl.rbase + row) * (p.inter / 32) + col[0] / 32] = (uint8_t)(X + 127);
+          He[(int64_t)(tl.rbase + row) * p.out_scale_stride + col[0] / 32] = (uint8_t)(X + 127);
       }
     lds_barrier();
     uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(256, MxStage<BM>::WPC) void k_gemm_mxfp4(GemmArgs p
   static_assert(S >= 2 && S <= 5, "LDS stages");
   __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
   static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ __align__(16) uint8_t asb[2 * ST::AS_BLOCK];
   __shared__ int s_item;
   ChunkWork c1, c2;
   const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
@@ -242,8 +252,8 @@ __global__ __launch_bounds__(256, MxStage<BM>::WPC) void k_gemm_mxfp4(GemmArgs p
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) mx_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
-    else mx_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (cur < len1) mx_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, asb);
+    else mx_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, asb);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;

@@ -14,6 +14,7 @@ struct GemmArgs {
   // A operand: activation rows.  a_per_token: row r reads token sorted_rows[r]/k.
   const void* a;            // codes / fp16 values, [rows][K]
   const void* a_scale;      // FP8: fp32 [rows][K/128]; MXFP4 path: E8M0 [rows][K/32]
+  int a_scale_stride;       // bytes between rows of a_scale (scale_row_bytes(K))
   int a_per_token;
   // B operand: packed expert weights [E][N][K] and their scales.
   const uint8_t* w;
@@ -25,6 +26,7 @@ struct GemmArgs {
   // output
   void* out;                   // GEMM1: activation-format h [R][I]; GEMM2: bf16 y [R][N]
   void* out_scale;             // GEMM1 FP8: fp32 [R][I/128]; MXFP4: E8M0 [R][I/32]
+  int out_scale_stride;        // bytes between rows of out_scale (scale_row_bytes(I))
   // routing / schedule (device)
   const int32_t* offsets;
   const int32_t* sorted_rows;
@@ -47,8 +49,13 @@ inline int64_t max_row_tiles(int64_t R, int E) { return R / 16 + E; }
 
 // Activation preparation (per token rows, no adapter).
 void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
-void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, hipStream_t s);
-void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, hipStream_t s);
+// Activation scale rows (FP8: fp32 per 128, MXFP8: E8M0 per 32, i.e. 4 bytes
+// per 128-wide K step either way) are padded to a multiple of 16 bytes, so a
+// GEMM can fetch the scales of 4 consecutive K steps of a row as one
+// aligned 16-byte piece.
+inline int scale_row_bytes(int K) { return ((K / 128) * 4 + 15) / 16 * 16; }
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, hipStream_t s);
+void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s);
 // OFT rotation of every permuted row into the INT4-path activation layout.
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,

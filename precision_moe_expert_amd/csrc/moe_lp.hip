@@ -98,14 +98,14 @@ WsLayout layout(const Dims& d) {
     w.h_scale = take(0);
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
     w.act = take(arows * H);
-    w.act_scale = take(arows * (H / 128) * 4);
+    w.act_scale = take(arows * scale_row_bytes((int)H));
     w.h = take(R * I);
-    w.h_scale = take(R * (I / 128) * 4);
+    w.h_scale = take(R * scale_row_bytes((int)I));
   } else {
     w.act = take(arows * H);
-    w.act_scale = take(arows * (H / 32));
+    w.act_scale = take(arows * scale_row_bytes((int)H));
     w.h = take(R * I);
-    w.h_scale = take(R * (I / 32));
+    w.h_scale = take(R * scale_row_bytes((int)I));
   }
   w.y = take(R * H * 2);
   w.total = o;
@@ -322,9 +322,10 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     else
       launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
-    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), s);
+    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H), s);
   } else {
-    launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), s);
+    launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), scale_row_bytes(d.H),
+                     s);
   }
   }
 
@@ -333,6 +334,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   GemmArgs g1{}, g2{};
   g1.a = act;
   g1.a_scale = act_scale;
+  g1.a_scale_stride = scale_row_bytes(d.H);
+  g1.out_scale_stride = scale_row_bytes(d.I);
   g1.a_per_token = d.oft ? 0 : 1;
   g1.w = static_cast<const uint8_t*>(qw->w13);
   g1.w_scale = sc->s13;
@@ -343,6 +346,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   g1.out_scale = h_scale;
   g2.a = h;
   g2.a_scale = h_scale;
+  g2.a_scale_stride = scale_row_bytes(d.I);
   g2.a_per_token = 0;
   g2.w = static_cast<const uint8_t*>(qw->w2);
   g2.w_scale = sc->s2;
