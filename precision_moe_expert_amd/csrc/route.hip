@@ -80,21 +80,30 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, i
   for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Exclusive scan of 1024 values held one per thread (blockDim = 1024).
-MOE_DEV int block_excl_scan_1024(int v, int* sh, int* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int a = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += a;
-    __syncthreads();
+// Exclusive scan, over the 1024 threads of the block, of four independent
+// ints per thread: a shuffle scan inside each wave, then each thread adds the
+// totals of the waves before it (two barriers instead of twenty per scan).
+MOE_DEV i32x4 block_excl_scan4_1024(i32x4 v, i32x4* sh, i32x4* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  i32x4 incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    i32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = __shfl_up(incl[c], off, 64);
+    if (lane >= off) incl += o;
   }
-  int incl = sh[tid];
-  *total = sh[1023];
+  if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  return incl - v;
+  i32x4 before = {0, 0, 0, 0}, all = {0, 0, 0, 0};
+  for (int w = 0; w < 16; ++w) {
+    const i32x4 t = sh[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  __syncthreads();
+  return before + incl - v;
 }
 
 // One workgroup of 1024 threads (thread = expert).  Turns the per-block
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
                                                int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
                                                int32_t* __restrict__ tile_16, int32_t* __restrict__ tile_desc,
                                                int32_t* __restrict__ queue, int nqueue) {
-  __shared__ int sh[1024];
+  __shared__ i32x4 sh4[16];
   __shared__ int s_tstart[MAX_EXPERTS + 1], s_exp[MAX_EXPERTS], s_off[MAX_EXPERTS], s_cnt[MAX_EXPERTS];
   const int e = threadIdx.x;
   int cnt = 0;
@@ -121,19 +130,18 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
         cnt += h[i];
       }
     }
-  int total;
-  const int off = block_excl_scan_1024(e < E ? cnt : 0, sh, &total);
+  // one scan for: row offsets, active positions, bm_a-row tiles, 16-row tiles
+  const int act = (e < E && cnt > 0) ? 1 : 0;
+  const i32x4 v = {e < E ? cnt : 0, act, act ? (cnt + bm_a - 1) / bm_a : 0, act ? (cnt + 15) / 16 : 0};
+  i32x4 tot;
+  const i32x4 ex = block_excl_scan4_1024(v, sh4, &tot);
+  const int off = ex[0], pos = ex[1], ta = ex[2], t16 = ex[3];
+  const int na = tot[1], nta = tot[2], nt16 = tot[3];
   if (e < E) {
     offsets[e] = off;
     for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;  // independent updates, pipelined
   }
-  if (e == 0) offsets[E] = total;
-  const int act = (e < E && cnt > 0) ? 1 : 0;
-  int na;
-  const int pos = block_excl_scan_1024(act, sh, &na);
-  int nta, nt16;
-  const int ta = block_excl_scan_1024(act ? (cnt + bm_a - 1) / bm_a : 0, sh, &nta);
-  const int t16 = block_excl_scan_1024(act ? (cnt + 15) / 16 : 0, sh, &nt16);
+  if (e == 0) offsets[E] = tot[0];
   if (act) {
     active[pos] = e;
     tile_a[pos] = ta;
