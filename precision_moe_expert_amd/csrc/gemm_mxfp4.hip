@@ -189,8 +189,8 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
         const uint32_t c2 = cvt_e4m3x2(h0 * mul, h1 * mul);
         smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
         smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
-        if (ln == 0 && row < tl.nrows)
-          He[(int64_t)(tl.rbase + row) * p.out_scale_stride + col[0] / 32] = (uint8_t)(X + 127);
+        // the row's four block scales (one per wave) are staged as one dword
+        if (ln == 0) smem[BM * HS + row * 4 + wave] = (uint8_t)(X + 127);
       }
     lds_barrier();
     uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
@@ -200,6 +200,9 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
         *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
             *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
     }
+    for (int row = threadIdx.x; row < tl.nrows; row += 256)
+      *reinterpret_cast<uint32_t*>(He + (int64_t)(tl.rbase + row) * p.out_scale_stride + tl.nb * 4) =
+          *reinterpret_cast<const uint32_t*>(smem + BM * HS + row * 4);
   } else {
     constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
     lds_barrier();
