@@ -26,14 +26,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE expert-layer tokens/s + TFLOP/s (% MFMA peak) / HBM GB/s per weight format"
 HBM_PEAK = 8.0e12
-MFMA_PEAK = {1: 2.5e15, 2: 5.0e15, 3: 5.0e15}  # fp16 MFMA (INT4 path), fp8, fp8 x fp4 (issued at the fp8 rate)
-DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a"}
+# fp16 MFMA (INT4 path), fp8, fp8 x fp4 (issued at the fp8 rate), fp8 with E8M0 block scales
+MFMA_PEAK = {1: 2.5e15, 2: 5.0e15, 3: 5.0e15, 4: 5.0e15}
+DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a", 4: "fp8_e4m3_pow2"}
 
 
 def weight_bytes_per_expert(fmt: int, N: int, K: int) -> float:
     if fmt == 1:
         return N * K / 2 + N * (K // 32) * 2
-    if fmt == 2:
+    if fmt in (2, 4):
         return N * K + (N // 128) * (K // 128) * 4
     return N * K / 2 + N * (K // 32)
 
@@ -42,7 +43,7 @@ def act_bytes(fmt: int, rows: int, K: int) -> float:
     """Bytes of one activation matrix in the GEMM input format."""
     if fmt == 1:
         return rows * K * 2
-    if fmt == 2:
+    if fmt in (2, 4):
         return rows * K + rows * (K // 128) * 4
     return rows * K + rows * (K // 32)
 
@@ -138,21 +139,17 @@ def main():
 
     sec = ms_per_step / 1e3
     peak = MFMA_PEAK[cfg.fmt]
-    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4"}[cfg.fmt]
+    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4", 4: "fp8"}[cfg.fmt]
     bm = binding.tile_rows(layer)
-    if True:
-        # every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
-        dom = "gemm"
-        launches = stage_n["gemm1"] + stage_n["gemm2"]
-        launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
-        f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
-        kname = f"k_gemm_{fmt_name}<{bm}>"
+    # every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
+    dom = "gemm"
+    launches = stage_n["gemm1"] + stage_n["gemm2"]
+    launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
+    f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
+    if cfg.fmt in (2, 4):
+        kname = f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>"
     else:
-        dom = max(("gemm1", "gemm2"), key=lambda s: stage_ms[s])
-        launches = stage_n[dom]
-        launch_ms = stage_ms[dom] / max(launches, 1)
-        f_dom, b_dom = acc[dom]
-        kname = f"k_gemm_{fmt_name}<{bm}, {'true' if dom == 'gemm1' else 'false'}>"
+        kname = f"k_gemm_{fmt_name}<{bm}>"
     launches_per_step = launches / args.steps
     f_launch, b_launch = f_dom / launches_per_step, b_dom / launches_per_step
     if b_launch / HBM_PEAK >= f_launch / peak:

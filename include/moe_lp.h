@@ -59,7 +59,13 @@ typedef enum {
   /* OCP MXFP4: E2M1 codes (low nibble first) with an E8M0 scale byte per
    * (n, 32 consecutive k).  Activations are quantized to MXFP8: E4M3 codes
    * with an E8M0 scale per 32, shared exponent floor(log2 amax) - 8. */
-  MOE_W_MXFP4 = 3
+  MOE_W_MXFP4 = 3,
+  /* As MOE_W_FP8_E4M3_B128 with power-of-two scales (the FP8 recipe's
+   * power-of-two scaling-factor switches, NeMo RL FP8 post): weight block
+   * scales must be exact powers of two (fp32, only their exponent is used);
+   * activation scales are the smallest power of two >= fl32(amax/448).  The
+   * GEMMs then apply both scales inside the block-scaled MFMA. */
+  MOE_W_FP8_E4M3_B128_POW2 = 4
 } moe_wformat;
 
 /* Layer description (host memory). */
@@ -87,7 +93,7 @@ typedef struct {
  * consecutive k) are stored group-major, [K/32][N] per expert, so that the
  * scales of one K step for a block of output rows are contiguous:
  *   INT4 : s13 bf16 [E][H/32][2I],   s2 bf16 [E][I/32][H]
- *   FP8  : s13 fp32 [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]
+ *   FP8, FP8_POW2: s13 fp32 [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]
  *   MXFP4: s13 u8   [E][H/32][2I],   s2 u8   [E][I/32][H]  (E8M0) */
 typedef struct {
   const void* s13;

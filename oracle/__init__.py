@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
+FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
 
 
 def build(force: bool = False) -> str:
@@ -119,6 +119,16 @@ def quant_fp8(v: np.ndarray):
     q = np.empty((R, K), np.uint8)
     s = np.empty((R, K // 128), np.float32)
     lib().oracle_quant_fp8(R, K, _p(v), _p(q), _p(s))
+    return q, s
+
+
+def quant_fp8_pow2(v: np.ndarray):
+    """[R][K] fp32 -> (codes [R][K] uint8, power-of-two scales [R][K/128] fp32)."""
+    v = _c(v, np.float32)
+    R, K = v.shape
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R, K // 128), np.float32)
+    lib().oracle_quant_fp8_pow2(R, K, _p(v), _p(q), _p(s))
     return q, s
 
 

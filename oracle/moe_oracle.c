@@ -39,7 +39,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_INT4 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
+enum { OR_INT4 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_FP8_POW2 = 4 };
 
 /* ------------------------------------------------------------------ codecs */
 
@@ -129,6 +129,31 @@ static void quant_fp8_row(int K, const float* v, uint8_t* q, float* s) {
     s[b] = sc;
     for (int i = 0; i < 128; ++i) {
       volatile float r = v[b * 128 + i] / sc; /* fp32 division */
+      q[b * 128 + i] = e4m3_encode(r);
+    }
+  }
+}
+
+/* FP8 [1,128] with power-of-two scales (NeMo RL FP8 post, recipe switches
+ * for power-of-two weight and activation scaling factors): as above, but
+ * the scale is the smallest power of two >= fl32(amax / 448), so no element
+ * saturates and v / s is exact scaling.  s = 1 when amax = 0. */
+static float pow2_at_least(float x) {
+  int e;
+  const float m = frexpf(x, &e); /* x = m * 2^e, m in [0.5, 1) */
+  return m == 0.5f ? x : ldexpf(1.0f, e);
+}
+static void quant_fp8_row_pow2(int K, const float* v, uint8_t* q, float* s) {
+  for (int b = 0; b < K / 128; ++b) {
+    float amax = 0.0f, sc;
+    for (int i = 0; i < 128; ++i) {
+      float a = fabsf(v[b * 128 + i]);
+      if (a > amax) amax = a;
+    }
+    sc = (amax == 0.0f) ? 1.0f : pow2_at_least(amax / 448.0f);
+    s[b] = sc;
+    for (int i = 0; i < 128; ++i) {
+      volatile float r = v[b * 128 + i] / sc; /* exact: sc is a power of two */
       q[b * 128 + i] = e4m3_encode(r);
     }
   }
@@ -244,7 +269,7 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
       if (fmt == OR_INT4) {
         v = (double)int4_value(nibble_at(q, (int64_t)n * K + kk)) *
             (double)bf16_value(((const uint16_t*)s)[(int64_t)(kk / 32) * N + n]);
-      } else if (fmt == OR_FP8) {
+      } else if (fmt == OR_FP8 || fmt == OR_FP8_POW2) {
         v = e4m3_value(q[(int64_t)n * K + kk]) *
             (double)((const float*)s)[(int64_t)(n / 128) * (K / 128) + kk / 128];
       } else {
@@ -261,8 +286,9 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
  * as they are. */
 static void act_quant_row(int fmt, int K, const float* v, double* out, uint8_t* qtmp, float* stmp,
                           uint8_t* etmp) {
-  if (fmt == OR_FP8) {
-    quant_fp8_row(K, v, qtmp, stmp);
+  if (fmt == OR_FP8 || fmt == OR_FP8_POW2) {
+    if (fmt == OR_FP8) quant_fp8_row(K, v, qtmp, stmp);
+    else quant_fp8_row_pow2(K, v, qtmp, stmp);
     for (int i = 0; i < K; ++i) out[i] = e4m3_value(qtmp[i]) * (double)stmp[i / 128];
   } else if (fmt == OR_MXFP4) {
     quant_mxfp8_row(K, v, qtmp, etmp);
@@ -326,10 +352,10 @@ static void expert_row(const oracle_layer* L, const uint16_t* xrow, const uint16
   }
 }
 
-static int64_t packed_bytes(int fmt, int64_t n) { return fmt == OR_FP8 ? n : n / 2; }
+static int64_t packed_bytes(int fmt, int64_t n) { return (fmt == OR_FP8 || fmt == OR_FP8_POW2) ? n : n / 2; }
 static int64_t scale_bytes(int fmt, int N, int K) {
   if (fmt == OR_INT4) return (int64_t)N * (K / 32) * 2;
-  if (fmt == OR_FP8) return (int64_t)(N / 128) * (K / 128) * 4;
+  if (fmt == OR_FP8 || fmt == OR_FP8_POW2) return (int64_t)(N / 128) * (K / 128) * 4;
   return (int64_t)N * (K / 32);
 }
 
@@ -351,7 +377,7 @@ int oracle_forward(const oracle_layer* L, const uint16_t* x, const float* logits
   float *wts, *ybuf;
   int rc = 0;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || chunk_experts < 1) return 1;
-  if (H % 32 || I % 32 || (fmt == OR_FP8 && (H % 128 || I % 128))) return 1;
+  if (H % 32 || I % 32 || ((fmt == OR_FP8 || fmt == OR_FP8_POW2) && (H % 128 || I % 128))) return 1;
   if (oft != NULL && (L->oft_block != 32 || H % 32)) return 1;
   if (tokens == NULL) n_tokens = T;
   if (T == 0 || n_tokens == 0) return 0;
@@ -510,6 +536,11 @@ void oracle_encode_e4m3(int64_t n, const float* v, uint8_t* out) {
 void oracle_quant_fp8(int R, int K, const float* v, uint8_t* q, float* s) {
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < R; ++r) quant_fp8_row(K, v + (int64_t)r * K, q + (int64_t)r * K, s + (int64_t)r * (K / 128));
+}
+void oracle_quant_fp8_pow2(int R, int K, const float* v, uint8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < R; ++r)
+    quant_fp8_row_pow2(K, v + (int64_t)r * K, q + (int64_t)r * K, s + (int64_t)r * (K / 128));
 }
 void oracle_quant_mxfp8(int R, int K, const float* v, uint8_t* q, uint8_t* e8) {
 #pragma omp parallel for schedule(static)

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void k_act_f16(const uint16_t* __restrict__ x,
 // activations): per 128-block s = amax/448 (IEEE fp32 division; 1 if amax =
 // 0), codes = E4M3(v / s).  One wave per token; a lane owns 32 elements, four
 // lanes a block.
+template <bool POW2>
 __global__ __launch_bounds__(256) void k_act_fp8(const uint16_t* __restrict__ x, int T, int H,
                                                  uint8_t* __restrict__ q, float* __restrict__ sc, int sc_stride) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -59,10 +60,21 @@ __global__ __launch_bounds__(256) void k_act_fp8(const uint16_t* __restrict__ x,
     amax = fmaxf(amax, shfl_xor(amax, 1));
     amax = fmaxf(amax, shfl_xor(amax, 2));
     if (!valid) continue;
-    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
     uint32_t packed[8];
+    float s;
+    if (POW2) {
+      // the power of two at or above amax/448; codes v * 2^-e, exact scaling
+      s = (amax == 0.0f) ? 1.0f : pow2_at_least(amax / 448.0f);
+      const float inv = pow2_reciprocal(s);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) packed[j] = cvt_e4m3x4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+      for (int j = 0; j < 8; ++j)
+        packed[j] = cvt_e4m3x4(v[4 * j] * inv, v[4 * j + 1] * inv, v[4 * j + 2] * inv, v[4 * j + 3] * inv);
+    } else {
+      s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        packed[j] = cvt_e4m3x4(v[4 * j] / s, v[4 * j + 1] / s, v[4 * j + 2] / s, v[4 * j + 3] / s);
+    }
     uint4* dst = reinterpret_cast<uint4*>(q + (int64_t)t * H + c0);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -194,8 +206,10 @@ void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t 
   if (n8 == 0) return;
   hipLaunchKernelGGL(k_act_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
 }
-void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, hipStream_t s) {
-  hipLaunchKernelGGL(k_act_fp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc, sc_stride);
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, bool pow2,
+                    hipStream_t s) {
+  if (pow2) hipLaunchKernelGGL(k_act_fp8<true>, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc, sc_stride);
+  else hipLaunchKernelGGL(k_act_fp8<false>, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, sc, sc_stride);
 }
 void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s) {
   hipLaunchKernelGGL(k_act_mxfp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, e8, e8_stride);

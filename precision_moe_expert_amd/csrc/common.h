@@ -52,6 +52,16 @@ MOE_DEV uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)r;
 }
 
+// Smallest power of two >= x for a positive normal float x (x itself when it
+// is one), and the exact reciprocal of a power of two.
+MOE_DEV float pow2_at_least(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x7FFFFFu) ? __uint_as_float(((b >> 23) + 1) << 23) : x;
+}
+MOE_DEV float pow2_reciprocal(float p) { return __uint_as_float((254u - (__float_as_uint(p) >> 23)) << 23); }
+// E8M0 byte (biased exponent) of a power-of-two float.
+MOE_DEV int e8m0_of_pow2(float p) { return (int)((__float_as_uint(p) >> 23) & 0xFFu); }
+
 // silu(g) = g * sigmoid(g); the reciprocal is the hardware one (1 ulp).
 MOE_DEV float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 

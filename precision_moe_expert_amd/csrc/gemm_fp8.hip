@@ -8,6 +8,9 @@
 // [1,128] scale: the workgroup's 128 h columns are one scale block, so the
 // row maximum is reduced across the column waves through LDS.
 //
+// Power-of-two scales (the recipe's pow2 switches) instead go into the
+// block-scaled MFMA as E8M0 exponents: no VALU rescale at all.
+//
 // Workgroup: 8 waves, two per SIMD.  Wave (wr, wc) computes the 64 output
 // columns of column group wc for half wr of the tile's row blocks; the two
 // waves of a SIMD share their weight fragments in LDS, and while one waits
@@ -43,7 +46,7 @@ struct Fp8Stage {
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
 // 128 gate + 128 up weight rows; GEMM2: 256 output columns).
-template <int BM, bool G1>
+template <int BM, bool G1, bool P2>
 __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint8_t* smem, uint8_t* asb,
                                          float (*red)[BM]) {
   using ST = Fp8Stage<BM>;
@@ -150,69 +153,90 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
       const u32x4 hi = *reinterpret_cast<const u32x4*>(brow + (((lg + 4) ^ (r & 7)) << 4));
       bf[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto read_a = [&](int m, i32x8& af, f32x4& sa) {
-      const int r = (mb0 + m) * 16 + ln;
-      const uint8_t* arow = st + r * 128;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
-      af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const int r0 = (mb0 + m) * 16 + lg * 4;
-      sa = (f32x4){As[r0 * 4], As[(r0 + 1) * 4], As[(r0 + 2) * 4], As[(r0 + 3) * 4]};
-    };
-    // Software pipeline over row blocks: the MFMAs of block m run while the
-    // VALU folds block m-1's partial products into the accumulators with
-    // their (activation x weight) block scales.
-    i32x8 afc;
-    f32x4 sac;
-    read_a(0, afc, sac);
-    f32x4 prev[4], psc01, psc23;
+    if constexpr (P2) {
+      // power-of-two scales: the block-scaled MFMA applies 2^ea (the row's
+      // activation scale) and 2^ew (the weight block's) exactly, so the
+      // partials accumulate directly
+      const int ew0 = e8m0_of_pow2(wc0), ew2 = e8m0_of_pow2(wc2);
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      if (m < nmb) {
-        i32x8 afn;
-        f32x4 san;
-        if (m + 1 < nmb) read_a(m + 1, afn, san);
-        // one MFMA of block m per group, with the VALU work of block m-1
-        // (sched_barrier keeps the compiler from bunching the MFMAs, which
-        // would leave the VALU work waiting behind them)
-        f32x4 part[4];
+      for (int m = 0; m < MTW; ++m)
+        if (m < nmb) {
+          const int r = (mb0 + m) * 16 + ln;
+          const uint8_t* arow = st + r * 128;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+          const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          const int ea = e8m0_of_pow2(As[r * 4]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          part[i] = mfma_fp8_16x16x128(afc, bf[i], zero);
-          if (m > 0) {
+          for (int i = 0; i < 4; ++i)
+            acc[m][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[i], acc[m][i], 0, 0, 0, ea, 0,
+                                                                          i < 2 ? ew0 : ew2);
+        }
+    } else {
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      auto read_a = [&](int m, i32x8& af, f32x4& sa) {
+        const int r = (mb0 + m) * 16 + ln;
+        const uint8_t* arow = st + r * 128;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+        af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const int r0 = (mb0 + m) * 16 + lg * 4;
+        sa = (f32x4){As[r0 * 4], As[(r0 + 1) * 4], As[(r0 + 2) * 4], As[(r0 + 3) * 4]};
+      };
+      // Software pipeline over row blocks: the MFMAs of block m run while the
+      // VALU folds block m-1's partial products into the accumulators with
+      // their (activation x weight) block scales.
+      i32x8 afc;
+      f32x4 sac;
+      read_a(0, afc, sac);
+      f32x4 prev[4], psc01, psc23;
+#pragma unroll
+      for (int m = 0; m < MTW; ++m) {
+        if (m < nmb) {
+          i32x8 afn;
+          f32x4 san;
+          if (m + 1 < nmb) read_a(m + 1, afn, san);
+          // one MFMA of block m per group, with the VALU work of block m-1
+          // (sched_barrier keeps the compiler from bunching the MFMAs, which
+          // would leave the VALU work waiting behind them)
+          f32x4 part[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            part[i] = mfma_fp8_16x16x128(afc, bf[i], zero);
+            if (m > 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[m - 1][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m - 1][i][q]);
+            }
+            // subtiles 0,1 share one weight-scale block and 2,3 another (GEMM1: gate, up)
+            if (i == 1) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) psc01[q] = sac[q] * wc0;
+            }
+            if (i == 3) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) psc23[q] = sac[q] * wc2;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) prev[i] = part[i];
+          if (m + 1 < nmb) {
+            afc = afn;
+            sac = san;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MTW; ++m)
+        if (m + 1 == nmb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[m - 1][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m - 1][i][q]);
-          }
-          // subtiles 0,1 share one weight-scale block and 2,3 another (GEMM1: gate, up)
-          if (i == 1) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) psc01[q] = sac[q] * wc0;
-          }
-          if (i == 3) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) psc23[q] = sac[q] * wc2;
-          }
-          __builtin_amdgcn_sched_barrier(0);
+              acc[m][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m][i][q]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) prev[i] = part[i];
-        if (m + 1 < nmb) {
-          afc = afn;
-          sac = san;
-        }
-      }
     }
-#pragma unroll
-    for (int m = 0; m < MTW; ++m)
-      if (m + 1 == nmb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[m][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m][i][q]);
-      }
   }
 
   // Epilogue: results go through LDS (the stage buffers are free once every
@@ -242,9 +266,16 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         for (int i = 0; i < 4; ++i) {
           const int row = (mb0 + m) * 16 + lg * 4 + i;
           const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
-          // the row's [1,128] block scale amax/448; codes h/s with the hardware reciprocal
-          const float sc = amax == 0.0f ? 1.0f : amax * (1.0f / 448.0f);
-          const float inv = __builtin_amdgcn_rcpf(sc);
+          // the row's [1,128] block scale: amax/448 (codes h/s with the hardware
+          // reciprocal), or the power of two at or above it (exact scaling)
+          float sc, inv;
+          if constexpr (P2) {
+            sc = amax == 0.0f ? 1.0f : pow2_at_least(amax / 448.0f);
+            inv = pow2_reciprocal(sc);
+          } else {
+            sc = amax == 0.0f ? 1.0f : amax * (1.0f / 448.0f);
+            inv = __builtin_amdgcn_rcpf(sc);
+          }
           const uint32_t c2 = cvt_e4m3x2(hv[m][i][0] * inv, hv[m][i][1] * inv);
           smem[row * HS + wc * 32 + ln] = (uint8_t)(c2 & 0xFF);
           smem[row * HS + wc * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
@@ -295,7 +326,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
 // that XCD's L2), GEMM1 items first; the workgroups of an XCD take items from
 // its range through an atomic counter, so every workgroup exits once the
 // range is used up.
-template <int BM>
+template <int BM, bool P2>
 __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmArgs p2, int32_t* queue) {
   using ST = Fp8Stage<BM>;
   constexpr int S = ST::S;
@@ -321,25 +352,35 @@ __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmAr
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) fp8_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem, asb, red);
-    else fp8_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, asb, red);
+    if (cur < len1) fp8_item<BM, true, P2>(p1, tile_of(p1, c1, b1 + cur, BM), smem, asb, red);
+    else fp8_item<BM, false, P2>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem, asb, red);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;
   }
 }
 
+template <bool P2>
+static void launch_fp8(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid, hipStream_t s) {
+  switch (bm) {
+    case 16: launch_persistent2<k_gemm_fp8<16, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_fp8<32, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_fp8<64, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_fp8<48, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_fp8<96, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_fp8<128, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_fp8<192, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+  }
+}
+
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                           hipStream_t s) {
-  switch (bm) {
-    case 16: launch_persistent2<k_gemm_fp8<16>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    case 32: launch_persistent2<k_gemm_fp8<32>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    case 64: launch_persistent2<k_gemm_fp8<64>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    case 48: launch_persistent2<k_gemm_fp8<48>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    case 96: launch_persistent2<k_gemm_fp8<96>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    case 128: launch_persistent2<k_gemm_fp8<128>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-    default: launch_persistent2<k_gemm_fp8<192>, FP8_THREADS>(g1, g2, queue, grid, s); break;
-  }
+  launch_fp8<false>(g1, g2, queue, bm, grid, s);
+}
+
+void launch_gemm_fp8_pow2_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                               hipStream_t s) {
+  launch_fp8<true>(g1, g2, queue, bm, grid, s);
 }
 
 }  // namespace moe

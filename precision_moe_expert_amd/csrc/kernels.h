@@ -54,7 +54,9 @@ void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t 
 // GEMM can fetch the scales of 4 consecutive K steps of a row as one
 // aligned 16-byte piece.
 inline int scale_row_bytes(int K) { return ((K / 128) * 4 + 15) / 16 * 16; }
-void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, hipStream_t s);
+// pow2: scales are the power of two at or above amax/448 (else amax/448).
+void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, bool pow2,
+                    hipStream_t s);
 void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s);
 // OFT rotation of every permuted row into the INT4-path activation layout.
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
@@ -68,6 +70,9 @@ void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queu
                            hipStream_t s);
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                           hipStream_t s);
+// FP8 with power-of-two scales: both scales applied inside the block-scaled MFMA.
+void launch_gemm_fp8_pow2_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                               hipStream_t s);
 void launch_gemm_mxfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                             hipStream_t s);
 

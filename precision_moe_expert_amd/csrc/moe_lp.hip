@@ -23,7 +23,8 @@ struct WsLayout {
 };
 
 struct Dims {
-  int T, H, I, E, k, fmt;
+  int T, H, I, E, k, fmt;  // fmt: the kernel family (the pow2 FP8 variant runs the FP8 kernels)
+  bool pow2;               // FP8 with power-of-two scales
   bool oft;
   int64_t R;
   int nblk;
@@ -38,7 +39,8 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if (L->num_tokens < 0 || L->hidden <= 0 || L->inter <= 0 || L->num_experts <= 0 || L->top_k <= 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (L->top_k > L->num_experts) return MOE_ERR_INVALID_ARGUMENT;
-  if (L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_FP8_E4M3_B128 && L->wformat != MOE_W_MXFP4)
+  if (L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_FP8_E4M3_B128 && L->wformat != MOE_W_MXFP4 &&
+      L->wformat != MOE_W_FP8_E4M3_B128_POW2)
     return MOE_ERR_INVALID_ARGUMENT;
   if (L->oft_block != 0 && L->oft_block != 32) return MOE_ERR_UNSUPPORTED;
   if (L->adapter_expert_stride < 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -58,6 +60,8 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   d->E = L->num_experts;
   d->k = L->top_k;
   d->fmt = L->wformat;
+  d->pow2 = L->wformat == MOE_W_FP8_E4M3_B128_POW2;
+  if (d->pow2) d->fmt = MOE_W_FP8_E4M3_B128;  // same layouts and kernels, power-of-two scale path
   d->oft = L->oft_block != 0;
   d->R = (int64_t)d->T * d->k;
   d->nblk = (int)((d->R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK);
@@ -322,7 +326,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     else
       launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
-    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H), s);
+    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H),
+                   d.pow2, s);
   } else {
     launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), scale_row_bytes(d.H),
                      s);
@@ -386,7 +391,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   // launch c runs chunk c's GEMM1 together with chunk c-1's GEMM2
   const int grid = grid1 > grid2 ? grid1 : grid2;
   auto pair = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4_pair
-            : d.fmt == MOE_W_FP8_E4M3_B128 ? launch_gemm_fp8_pair : launch_gemm_mxfp4_pair;
+            : d.fmt == MOE_W_FP8_E4M3_B128 ? (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)
+                                           : launch_gemm_mxfp4_pair;
   for (int c = 0; c <= nchunks; ++c) {
     g1.chunk = c < nchunks ? c : -1;
     g2.chunk = c - 1;

@@ -27,8 +27,9 @@ import numpy as np
 import torch
 
 SEED_ROOT = 20261202
-FMT_INT4, FMT_FP8, FMT_MXFP4 = 1, 2, 3
-FMT_NAMES = {FMT_INT4: "int4_g32_bf16", FMT_FP8: "fp8_e4m3_b128", FMT_MXFP4: "mxfp4"}
+FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
+FMT_NAMES = {FMT_INT4: "int4_g32_bf16", FMT_FP8: "fp8_e4m3_b128", FMT_MXFP4: "mxfp4",
+             FMT_FP8_POW2: "fp8_e4m3_b128_pow2"}
 
 # tensor ids inside one seed sequence
 _T_X, _T_LOGITS, _T_ZIPF, _T_W13, _T_W2, _T_S13, _T_S2, _T_OFT, _T_WLM, _T_TGT = range(10)
@@ -68,6 +69,9 @@ CONFIGS = {
                       fmt=FMT_MXFP4, chunk=32, zipf_alpha=1.2),
     "c5": LayerConfig("kimi_k2_decode_int4_oft_lmhead", 5, T=64, H=7168, E=384, k=8, I=2048,
                       fmt=FMT_INT4, chunk=32, oft=True, lm_vocab=32000),
+    # the Qwen3-30B-A3B shape with the power-of-two scale variant of the FP8 recipe
+    "c2p": LayerConfig("qwen3_30b_a3b_fp8_pow2", 6, T=4096, H=2048, E=128, k=8, I=768,
+                       fmt=FMT_FP8_POW2, chunk=16),
 }
 
 
@@ -144,6 +148,13 @@ def _gen_fp8(cfg, N, K, tensor, stensor):
     return q, s
 
 
+def _gen_fp8_pow2(cfg, N, K, tensor, stensor):
+    """FP8 weights whose [128,128] block scales are powers of two (the
+    block scales of _gen_fp8 rounded down to a power of two)."""
+    q, s = _gen_fp8(cfg, N, K, tensor, stensor)
+    return q, np.ldexp(np.float32(1.0), np.floor(np.log2(s)).astype(np.int32)).astype(np.float32)
+
+
 def _gen_mxfp4(cfg, N, K, tensor, stensor):
     E = cfg.E
     mag = _e2m1_nibble_lut()
@@ -166,7 +177,7 @@ def _gen_mxfp4(cfg, N, K, tensor, stensor):
 def gen_weights(cfg: LayerConfig):
     """Returns (w13, w2, s13, s2) as numpy arrays in the storage layouts above."""
     H, I = cfg.H, cfg.I
-    gen = {FMT_INT4: _gen_int4, FMT_FP8: _gen_fp8, FMT_MXFP4: _gen_mxfp4}[cfg.fmt]
+    gen = {FMT_INT4: _gen_int4, FMT_FP8: _gen_fp8, FMT_MXFP4: _gen_mxfp4, FMT_FP8_POW2: _gen_fp8_pow2}[cfg.fmt]
     w13, s13 = gen(cfg, 2 * I, H, _T_W13, _T_S13)
     w2, s2 = gen(cfg, H, I, _T_W2, _T_S2)
     return w13, w2, s13, s2

@@ -46,7 +46,7 @@ def dequant(fmt, q, s, N, K):
         v = int4_values(unpack_nibbles(q)).reshape(N, K)
         sc = np.repeat(bf16_to_f32(s).astype(np.float64).reshape(K // 32, N).T, 32, axis=1)  # group-major
         return v * sc
-    if fmt == 2:
+    if fmt in (2, 4):
         v = e4m3_to_f64(q).reshape(N, K)
         sc = np.kron(np.asarray(s, np.float64).reshape(N // 128, K // 128), np.ones((128, 128)))
         return v * sc
@@ -63,6 +63,21 @@ def quant_fp8_rows(v):
     amax = np.abs(blk).max(axis=2)
     s = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
     q = f32_to_e4m3_sat((blk / s[:, :, None]).astype(np.float32)).reshape(R, K)
+    return q, s
+
+
+def quant_fp8_pow2_rows(v):
+    """[R][K] fp32 -> codes, power-of-two scales (the power of two at or above
+    fl32(amax/448); amax = 0 -> 1)."""
+    v = np.asarray(v, np.float32)
+    R, K = v.shape
+    blk = v.reshape(R, K // 128, 128)
+    amax = np.abs(blk).max(axis=2)
+    x = (amax / np.float32(448.0)).astype(np.float32)
+    m, e = np.frexp(x.astype(np.float64))
+    p2 = np.where(m == 0.5, x.astype(np.float64), np.ldexp(1.0, e))
+    s = np.where(amax == 0, 1.0, p2).astype(np.float32)
+    q = f32_to_e4m3_sat((blk.astype(np.float64) / s[:, :, None].astype(np.float64)).astype(np.float32)).reshape(R, K)
     return q, s
 
 
@@ -84,6 +99,9 @@ def act_values(fmt, v32):
         return np.asarray(v32, np.float64)
     if fmt == 2:
         q, s = quant_fp8_rows(v32)
+        return e4m3_to_f64(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+    if fmt == 4:
+        q, s = quant_fp8_pow2_rows(v32)
         return e4m3_to_f64(q) * np.repeat(s.astype(np.float64), 128, axis=1)
     q, e = quant_mxfp8_rows(v32)
     return e4m3_to_f64(q) * np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)

@@ -43,6 +43,10 @@ def test_qwen3_30b_a3b_fp8_full():
     run_full("c2", 64)
 
 
+def test_qwen3_30b_a3b_fp8_pow2_full():
+    run_full("c2p", 64)
+
+
 def test_kimi_k2_int4_oft_full():
     run_full("c3", 16)
 

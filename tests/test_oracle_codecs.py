@@ -112,6 +112,35 @@ def test_fp8_act_quant_bitexact_vs_numpy(seed):
 
 
 @pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_pow2_act_quant_properties(seed):
+    """Power-of-two [1,128] scales (NeMo RL FP8 post, pow2 scaling-factor switches):
+    s is an exact power of two with s/2 < fl32(amax/448) <= s (the smallest
+    power of two that keeps every |v|/s <= 448), codes are E4M3 of the exact
+    quotient, an all-zero block has scale 1."""
+    r = np.random.default_rng(seed + 10)
+    v = (r.standard_normal((41, 512)) * np.exp(r.uniform(-12, 12, (41, 1)))).astype(np.float32)
+    v[2, 256:384] = 0.0
+    v[4, :128] = 0.0
+    v[4, 7] = 448.0 * 2.0 ** -3   # amax/448 exactly a power of two: s = 2^-3
+    q, s = oracle.quant_fp8_pow2(v)
+    blk = np.abs(v.reshape(41, 4, 128)).max(axis=2)
+    x = (blk / np.float32(448.0)).astype(np.float32)          # fl32(amax/448)
+    nz = blk > 0
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)                                    # powers of two
+    assert np.all(s[nz] >= x[nz]) and np.all(s[nz] / 2 < x[nz])
+    assert s[2, 2] == 1.0 and not q[2, 256:384].any()
+    assert s[4, 0] == np.float32(2.0 ** -3)
+    sc = np.repeat(s.astype(np.float64), 128, axis=1)
+    quot = (v.astype(np.float64) / sc).astype(np.float32)      # exact: power-of-two divisor
+    assert np.all(np.abs(quot) <= 448.0)
+    assert np.array_equal(q, refimpl.f32_to_e4m3_sat(quot))
+    # the same blocks quantized with amax/448 scales: s_pow2 is the power of two at or above
+    _, s1 = oracle.quant_fp8(v)
+    assert np.all(s[nz] >= s1[nz]) and np.all(s[nz] < 2 * s1[nz])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
 def test_mxfp8_act_quant_bitexact_vs_numpy(seed):
     r = np.random.default_rng(seed)
     v = (r.standard_normal((29, 256)) * np.exp(r.uniform(-20, 20, (29, 1)))).astype(np.float32)
@@ -126,16 +155,18 @@ def test_mxfp8_act_quant_bitexact_vs_numpy(seed):
     assert np.all((mags[nz] >> 3) == 15)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
 def test_dequant_matches_reference(fmt):
     r = np.random.default_rng(fmt)
     N, K = 256, 384
     if fmt == 1:
         q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
         s = refimpl.torch.from_numpy(r.uniform(0.005, 0.02, (N, K // 32)).astype(np.float32)).to(refimpl.torch.bfloat16).view(refimpl.torch.int16).numpy().view(np.uint16)
-    elif fmt == 2:
+    elif fmt in (2, 4):
         q = refimpl.f32_to_e4m3_sat(r.standard_normal((N, K)).astype(np.float32) * 100)
         s = r.uniform(1e-4, 1e-3, (N // 128, K // 128)).astype(np.float32)
+        if fmt == 4:
+            s = np.ldexp(np.float32(1.0), np.floor(np.log2(s)).astype(np.int32)).astype(np.float32)
     else:
         q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
         s = r.integers(110, 130, (N, K // 32), dtype=np.uint8)

@@ -67,7 +67,7 @@ def test_permute_bruteforce(T, E, k):
 
 
 # ----------------------------------------------------------- expert FFN: brute force
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
 @pytest.mark.parametrize("oft", [False, True])
 def test_forward_vs_dense_bruteforce(fmt, oft):
     cfg = tiny(fmt=fmt, oft=oft)
