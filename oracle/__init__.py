@@ -38,7 +38,8 @@ def build(force: bool = False) -> str:
 class _Layer(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("fmt", ctypes.c_int32),
-                ("oft_block", ctypes.c_int32), ("adapter_expert_stride", ctypes.c_int64)]
+                ("oft_block", ctypes.c_int32), ("adapter_expert_stride", ctypes.c_int64),
+                ("materialized", ctypes.c_int32)]
 
 
 def lib():
@@ -149,15 +150,34 @@ def dequant(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray) -> np.ndarra
     return out
 
 
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 values -> nearest bf16 value (ties to even), as float64."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.float64)
+    lib().oracle_round_bf16(ctypes.c_int64(v.size), _p(v), _p(out))
+    return out
+
+
+def dequant_bf16(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One expert's packed [N][K] weights -> the BF16 temporary copy's values (fp32)."""
+    out = np.empty((N, K), np.float32)
+    lib().oracle_dequant_bf16(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), _p(out))
+    return out
+
+
 def forward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, chunk_experts=1,
-            tokens=None, adapter_expert_stride=None, return_y=False, return_routing=False):
+            tokens=None, adapter_expert_stride=None, return_y=False, return_routing=False,
+            materialized=False):
     """Oracle MoE expert forward.  x: [T][H] bf16 bits (uint16); logits [T][E] fp32;
     weights/scales in the packed storage layouts; oft [E][H/32][32][32] bf16 bits
     (or [H/32][32][32] with adapter_expert_stride=0) or None.
     tokens: optional int array of token indices to compute (default: all).
+    materialized: BF16 temporary weights and bf16 GEMM inputs instead of the
+    format's activation quantizers (the chunk dequantized to a BF16 copy).
     Returns out [n][H] fp32 (+ y [n][k][H], + (ids, w) when requested)."""
     layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0,
-                   (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride)
+                   (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride,
+                   1 if materialized else 0)
     x = _c(x, np.uint16)
     logits = _c(logits, np.float32)
     w13 = _c(w13, np.uint8)

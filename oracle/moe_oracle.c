@@ -28,6 +28,14 @@
  * Precision: dequantized weights are fp32, dot products accumulate in fp64,
  * stored results are fp32.  Quantizer decisions are taken in fp32.
  *
+ * Materialized numerics (layer flag `materialized`): the same announcement
+ * paragraph read literally -- each chunk's experts are dequantized into a
+ * temporary BF16 copy and an ordinary BF16 grouped GEMM runs on it.  Then
+ * every dequantized weight is rounded once to bf16 (nearest, ties to even),
+ * the GEMM inputs are bf16 (the token row; after the OFT rotation x R_e
+ * rounded to bf16), there is no activation quantizer, and h = silu(g) * u is
+ * rounded to bf16 before the down projection.  Accumulation stays fp64.
+ *
  * Build: gcc -O2 -fopenmp -fPIC -shared (no -ffast-math: IEEE fp32 division
  * and rounding are relied on).
  */
@@ -42,6 +50,17 @@
 enum { OR_INT4 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_FP8_POW2 = 4 };
 
 /* ------------------------------------------------------------------ codecs */
+
+/* v rounded to the nearest value with 8 significant bits (bf16), ties to
+ * even, for v in bf16's normal range (or 0): v = m 2^e with 0.5 <= |m| < 1,
+ * so m 2^8 is rounded to an integer in the default rounding mode. */
+static double bf16_round(double v) {
+  int e;
+  double m;
+  if (v == 0.0 || !isfinite(v)) return v;
+  m = frexp(v, &e);
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
 
 /* bf16 bit pattern -> float: the upper 16 bits of an IEEE binary32. */
 static float bf16_value(uint16_t b) {
@@ -261,7 +280,7 @@ int oracle_permute(int T, int E, int k, const int32_t* ids, int32_t* counts, int
  *          group-major: s[(k/32) * N + n]
  *   FP8  : q E4M3FN, s fp32 per [128,128] block (n/128, k/128)
  *   MXFP4: q E2M1 nibble, s E8M0 per (n, 32 along K), group-major as INT4 */
-static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
+static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* s, int to_bf16, float* out) {
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < N; ++n) {
     for (int kk = 0; kk < K; ++kk) {
@@ -276,7 +295,7 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
         v = e2m1_value(nibble_at(q, (int64_t)n * K + kk)) *
             e8m0_value(((const uint8_t*)s)[(int64_t)(kk / 32) * N + n]);
       }
-      out[(int64_t)n * K + kk] = (float)v;
+      out[(int64_t)n * K + kk] = (float)(to_bf16 ? bf16_round(v) : v);
     }
   }
 }
@@ -304,6 +323,7 @@ typedef struct {
   int32_t T, H, I, E, k, fmt;
   int32_t oft_block;             /* 0: no adapter; 32: block-diagonal 32x32 R */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = shared */
+  int32_t materialized;          /* 1: BF16 temporary weights (see the header) */
 } oracle_layer;
 
 /* One expert FFN row: x (bf16 token row) -> y (fp32, length H).
@@ -324,13 +344,16 @@ static void expert_row(const oracle_layer* L, const uint16_t* xrow, const uint16
         double acc = 0.0;
         for (int i = 0; i < B; ++i)
           acc += (double)bf16_value(xrow[b * B + i]) * (double)bf16_value(R_e[(int64_t)b * B * B + i * B + j]);
-        xr[b * B + j] = (float)acc;
+        xr[b * B + j] = (float)(L->materialized ? bf16_round(acc) : acc);
       }
   } else {
     for (int i = 0; i < H; ++i) xr[i] = bf16_value(xrow[i]);
   }
-  /* 2. input activation format */
-  act_quant_row(L->fmt, H, xr, xq, qtmp, stmp, etmp);
+  /* 2. input activation format (BF16 temporaries: the bf16 row as it is) */
+  if (L->materialized)
+    for (int i = 0; i < H; ++i) xq[i] = (double)xr[i];
+  else
+    act_quant_row(L->fmt, H, xr, xq, qtmp, stmp, etmp);
   /* 3. gate and up projections, SwiGLU */
   for (int n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
@@ -340,10 +363,14 @@ static void expert_row(const oracle_layer* L, const uint16_t* xrow, const uint16
       g += xq[kk] * (double)wg[kk];
       u += xq[kk] * (double)wu[kk];
     }
-    hf[n] = (float)(silu((double)(float)g) * (double)(float)u);
+    const double hv = silu((double)(float)g) * (double)(float)u;
+    hf[n] = (float)(L->materialized ? bf16_round(hv) : hv);
   }
   /* 4. down-projection input format, then the down projection */
-  act_quant_row(L->fmt, I, hf, hq, qtmp, stmp, etmp);
+  if (L->materialized)
+    for (int i = 0; i < I; ++i) hq[i] = (double)hf[i];
+  else
+    act_quant_row(L->fmt, I, hf, hq, qtmp, stmp, etmp);
   for (int n = 0; n < H; ++n) {
     double acc = 0.0;
     const float* wd = W2 + (int64_t)n * I;
@@ -418,9 +445,9 @@ int oracle_forward(const oracle_layer* L, const uint16_t* x, const float* logits
       W13c[a] = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
       W2c[a] = (float*)malloc(sizeof(float) * (size_t)H * I);
       dequant_matrix(fmt, 2 * I, H, w13 + packed_bytes(fmt, (int64_t)e * 2 * I * H),
-                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), W13c[a]);
+                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), L->materialized, W13c[a]);
       dequant_matrix(fmt, H, I, w2 + packed_bytes(fmt, (int64_t)e * H * I),
-                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), W2c[a]);
+                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), L->materialized, W2c[a]);
     }
     /* the chunk's grouped GEMM, row by row */
     rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(offsets[active[c0 + nc - 1] + 1] - offsets[active[c0]] + 1));
@@ -549,7 +576,16 @@ void oracle_quant_mxfp8(int R, int K, const float* v, uint8_t* q, uint8_t* e8) {
 
 /* One expert's N x K weights dequantized to fp32 (format codes as above). */
 void oracle_dequant(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
-  dequant_matrix(fmt, N, K, q, s, out);
+  dequant_matrix(fmt, N, K, q, s, 0, out);
+}
+
+/* One expert's weights as the BF16 temporary copy holds them. */
+void oracle_dequant_bf16(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
+  dequant_matrix(fmt, N, K, q, s, 1, out);
+}
+
+void oracle_round_bf16(int64_t n, const double* v, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
 }
 
 int oracle_num_threads(void) {

@@ -55,6 +55,22 @@ def dequant(fmt, q, s, N, K):
     return v * sc
 
 
+def bf16_round_rto(v):
+    """float64 -> nearest bf16 value (ties to even), by round-to-odd to fp32
+    followed by torch's fp32 -> bf16 cast.  Rounding to odd at 24 bits then
+    to nearest at 8 bits equals one rounding to nearest (Boldo & Melquiond,
+    "When double rounding is odd", 2005: at least two extra bits suffice)."""
+    v = np.asarray(v, np.float64)
+    t = v.astype(np.float32)
+    over = np.abs(t.astype(np.float64)) > np.abs(v)
+    t = np.where(over, np.nextafter(t, np.float32(0.0)), t)      # truncate toward zero
+    inexact = t.astype(np.float64) != v
+    bits = t.view(np.uint32) | inexact.astype(np.uint32)         # sticky bit -> odd
+    t = bits.view(np.float32)
+    b = torch.from_numpy(np.ascontiguousarray(t)).to(torch.bfloat16).float().numpy()
+    return b.astype(np.float64)
+
+
 def quant_fp8_rows(v):
     """[R][K] fp32 -> codes, scales (s = amax/448 in fp32; amax = 0 -> 1)."""
     v = np.asarray(v, np.float32)
@@ -121,9 +137,12 @@ def route_bruteforce(logits, k):
     return ids, w
 
 
-def dense_moe(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, adapter_stride_zero=False):
+def dense_moe(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, adapter_stride_zero=False,
+              materialized=False):
     """Dense MoE in float64: every expert runs on every token; the routing mask
-    (softmax over the top-k, zero elsewhere) weights the sum."""
+    (softmax over the top-k, zero elsewhere) weights the sum.  materialized:
+    weights rounded to bf16, bf16 GEMM inputs, h rounded to bf16, no
+    activation quantizer."""
     xf = bf16_to_f32(x).reshape(T, H).astype(np.float32)
     ids, w = route_bruteforce(logits, k)
     mask = np.zeros((T, E))
@@ -132,18 +151,25 @@ def dense_moe(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, adapter
             mask[t, ids[t, j]] = np.float32(w[t, j])
     out = np.zeros((T, H))
     for e in range(E):
-        W13 = dequant(fmt, w13[e], s13[e], 2 * I, H).astype(np.float32).astype(np.float64)
-        W2 = dequant(fmt, w2[e], s2[e], H, I).astype(np.float32).astype(np.float64)
+        if materialized:
+            W13 = bf16_round_rto(dequant(fmt, w13[e], s13[e], 2 * I, H))
+            W2 = bf16_round_rto(dequant(fmt, w2[e], s2[e], H, I))
+        else:
+            W13 = dequant(fmt, w13[e], s13[e], 2 * I, H).astype(np.float32).astype(np.float64)
+            W2 = dequant(fmt, w2[e], s2[e], H, I).astype(np.float32).astype(np.float64)
         xin = xf.astype(np.float64)
         if oft is not None:
             R = bf16_to_f32(oft if adapter_stride_zero else oft[e]).astype(np.float64).reshape(H // 32, 32, 32)
             xr = np.einsum("tbi,bij->tbj", xin.reshape(T, H // 32, 32), R).reshape(T, H)
-            xin = xr.astype(np.float32).astype(np.float64)
-        xq = act_values(fmt, xin.astype(np.float32))
+            xin = bf16_round_rto(xr) if materialized else xr.astype(np.float32).astype(np.float64)
+        xq = xin if materialized else act_values(fmt, xin.astype(np.float32))
         g = (xq @ W13[:I].T).astype(np.float32).astype(np.float64)
         u = (xq @ W13[I:].T).astype(np.float32).astype(np.float64)
-        h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
-        hq = act_values(fmt, h)
+        if materialized:
+            hq = bf16_round_rto(g / (1.0 + np.exp(-g)) * u)
+        else:
+            h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+            hq = act_values(fmt, h)
         y = (hq @ W2.T).astype(np.float32).astype(np.float64)
         out += mask[:, e:e + 1] * y
     return out, ids, w
