@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_LP_ABI_VERSION 1
+#define MOE_LP_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -161,7 +161,8 @@ enum {
   MOE_STAGE_GEMM1 = 3,   /* dequant + gate/up GEMM + SwiGLU                  */
   MOE_STAGE_GEMM2 = 4,   /* dequant + down GEMM (launch pairing: see below)  */
   MOE_STAGE_COMBINE = 5, /* weighted combine                                 */
-  MOE_NUM_STAGES = 6
+  MOE_STAGE_DEQUANT = 6, /* materialized scheme only: chunk -> BF16 copy     */
+  MOE_NUM_STAGES = 7
 };
 
 /* moe_expert_forward with per-stage timing, for measurement: a HIP event is
@@ -179,6 +180,37 @@ moe_status moe_expert_forward_timed(const moe_layer* layer, const void* x_bf16, 
                                     const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
                                     void* ws, size_t ws_bytes, void* stream, float* stage_ms,
                                     int32_t* stage_launches);
+
+/* Workspace bytes moe_expert_forward_materialized needs: the routing arrays,
+ * bf16 h [R][I] and y [R][H], the rotated input [R][H] bf16 when an adapter is
+ * used, and one chunk's BF16 weight copy, min(chunk_experts, E) * 3*H*I * 2
+ * bytes.  Returns 0 for an invalid descriptor or chunk_experts < 1. */
+size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
+
+/* The materialized-chunk scheme (Orbit announcement, 技术细节: the chunk's
+ * experts are dequantized temporarily to high precision, a grouped GEMM runs,
+ * and the high-precision weights are released), for comparison with
+ * moe_expert_forward.  Routing, permutation and combine are the same; then for
+ * each chunk of chunk_experts consecutive active experts:
+ *   1. dequantize the chunk's W13 and W2 into a BF16 copy in ws (each weight
+ *      rounded once to bf16, nearest even),
+ *   2. GEMM1 on bf16 MFMA: g, u = x~ W^T in fp32, h = silu(g) * u rounded to bf16,
+ *   3. GEMM2: y = h W2^T in fp32, rounded to bf16,
+ * and the next chunk overwrites the copy.  x~ is the bf16 token row, or x R_e
+ * rounded to bf16 with the adapter; no activation quantizer is applied (the
+ * copy is BF16, so the GEMMs are BF16 GEMMs for every weight format).
+ * The copy's size, and so ws, grows with chunk_experts.
+ * Same arguments and errors as moe_expert_forward, with
+ * ws >= moe_materialized_workspace_bytes(layer, chunk_experts).  stage_ms and
+ * stage_launches: both NULL (asynchronous, no host synchronisation), or both
+ * HOST arrays of MOE_NUM_STAGES entries filled as by moe_expert_forward_timed
+ * (the call then synchronises the stream); dequant launches are reported under
+ * MOE_STAGE_DEQUANT, each chunk's GEMM1 and GEMM2 launch under GEMM1 and GEMM2. */
+moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                           const moe_qweights* qweights, const moe_scales* scales,
+                                           const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                                           void* ws, size_t ws_bytes, void* stream, float* stage_ms,
+                                           int32_t* stage_launches);
 
 /* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
  * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:

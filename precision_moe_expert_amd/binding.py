@@ -19,8 +19,9 @@ FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_rows",
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
-            "moe_lm_head_workspace_bytes", "moe_lm_head_logprob")
-STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine")
+            "moe_lm_head_workspace_bytes", "moe_lm_head_logprob", "moe_materialized_workspace_bytes",
+            "moe_expert_forward_materialized")
+STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine", "dequant")
 
 
 class MoeLayer(ctypes.Structure):
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_forward_timed.restype = ctypes.c_int
         L.moe_expert_forward_timed.argtypes = L.moe_expert_forward.argtypes + [ctypes.POINTER(ctypes.c_float),
                                                                                 ctypes.POINTER(ctypes.c_int32)]
+        L.moe_materialized_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_materialized_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_int32]
+        L.moe_expert_forward_materialized.restype = ctypes.c_int
+        L.moe_expert_forward_materialized.argtypes = L.moe_expert_forward_timed.argtypes
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -180,6 +185,31 @@ def expert_forward_timed(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=N
                                           ctypes.byref(sc), _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws),
                                           ws.numel(), _stream(), ms, n), "moe_expert_forward_timed")
     return out, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
+
+
+def materialized_workspace_bytes(layer: MoeLayer, chunk_experts: int) -> int:
+    return lib().moe_materialized_workspace_bytes(ctypes.byref(layer), int(chunk_experts))
+
+
+def expert_forward_materialized(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=None, chunk_experts: int = 1,
+                                out=None, ws=None, timed: bool = False):
+    """moe_expert_forward_materialized: per chunk, the experts' BF16 copy in ws,
+    then BF16 GEMMs.  Returns out, or (out, {stage: (ms, launches)}) if timed."""
+    if out is None:
+        out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(materialized_workspace_bytes(layer, chunk_experts), x.device)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2))
+    ms = (ctypes.c_float * len(STAGES))() if timed else None
+    n = (ctypes.c_int32 * len(STAGES))() if timed else None
+    _check(lib().moe_expert_forward_materialized(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
+                                                 ctypes.byref(sc), _ptr(adapter), int(chunk_experts), _ptr(out),
+                                                 _ptr(ws), ws.numel(), _stream(), ms, n),
+           "moe_expert_forward_materialized")
+    if timed:
+        return out, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
+    return out
 
 
 def combine(layer: MoeLayer, y_perm: torch.Tensor, topk_w: torch.Tensor, row_of: torch.Tensor,

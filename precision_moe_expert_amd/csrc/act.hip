@@ -143,9 +143,11 @@ __global__ __launch_bounds__(256) void k_act_mxfp8(const uint16_t* __restrict__ 
 
 // OFT rotation x' = x R_e (R_e block-diagonal, 32x32 bf16 blocks; row i of a
 // block indexes the input dim) for every permuted row, on bf16 MFMA with fp32
-// accumulation, written as fp16 in the INT4-path layout.  Work item = 16 rows
-// of one expert (the 16-row tile list); the 4 waves split the H/32 blocks.
-__global__ __launch_bounds__(256) void k_oft_f16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
+// accumulation, written as fp16 in the INT4-path layout (BF16OUT: bf16 in
+// natural order, the BF16 GEMMs' input).  Work item = 16 rows of one expert
+// (the 16-row tile list); the 4 waves split the H/32 blocks.
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
                                                  int64_t r_stride, int H, int k, const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ sorted_rows,
                                                  const int32_t* __restrict__ active,
@@ -186,13 +188,14 @@ __global__ __launch_bounds__(256) void k_oft_f16(const uint16_t* __restrict__ x,
         const bf16x8 bb = __builtin_bit_cast(bf16x8, bv);
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         acc = mfma_bf16_16x16x32(a, bb, acc);
-        const int col = i4act_pos(b * 32 + half * 16 + ln);
+        const int col = BF16OUT ? b * 32 + half * 16 + ln : i4act_pos(b * 32 + half * 16 + ln);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = lg * 4 + i;
           if (m < nrows) {
             const _Float16 hv = (_Float16)acc[i];
-            out[(int64_t)(r0 + m) * H + col] = __builtin_bit_cast(uint16_t, hv);
+            out[(int64_t)(r0 + m) * H + col] =
+                BF16OUT ? (uint16_t)f32_to_bf16_bits(acc[i]) : __builtin_bit_cast(uint16_t, hv);
           }
         }
       }
@@ -218,8 +221,15 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                     const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s) {
   (void)E;
-  hipLaunchKernelGGL(k_oft_f16, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows, active,
-                     num_active, tile16, out);
+  hipLaunchKernelGGL(k_oft<false>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows,
+                     active, num_active, tile16, out);
+}
+
+void launch_oft_bf16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                     const int32_t* num_active, const int32_t* tile16, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_oft<true>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows,
+                     active, num_active, tile16, out);
 }
 
 }  // namespace moe

@@ -63,6 +63,22 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                     const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s);
 
+// The same rotation written as bf16 rows in natural order (BF16 GEMM input).
+void launch_oft_bf16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
+                     const int32_t* num_active, const int32_t* tile16, uint16_t* out, hipStream_t s);
+
+// Materialized-chunk scheme: dequantize chunk `chunk`'s experts (active order)
+// into scratch [C][2I*H + H*I] bf16 (W13 rows then W2 rows per expert), then
+// BF16 grouped GEMMs that read the copy (GemmArgs.w = the copy, w_expert_bytes
+// = 2 * (2I*H + H*I), the W2 copy at an offset of 2I*H elements); bm in
+// {16, 32, 64, 128}.
+void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
+                          const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
+                          uint16_t* scratch, hipStream_t s);
+void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                           hipStream_t s);
+
 // Grouped GEMMs; bm = rows per tile (16, 32, 48, 64, 96, 128 or 192).  One
 // launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2 (either may
 // be empty); queue: 8 zeroed per-XCD item counters for this launch.

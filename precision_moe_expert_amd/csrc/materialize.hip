@@ -1,0 +1,323 @@
+// The materialized-chunk scheme, as the Orbit announcement (技术细节,
+// active-expert-chunked dequantization) describes it literally: the experts of
+// one chunk are dequantized into a temporary BF16 copy in device memory, an
+// ordinary BF16 grouped GEMM runs on that copy, and the copy is overwritten by
+// the next chunk.  It exists to measure what the fused kernels save (the copy
+// costs 2 bytes written and read back per weight, and its size grows with the
+// chunk) and to compare the two numerics.
+//
+// k_dequant_chunk: one pass over the chunk's packed experts, 16 weights per
+// thread per iteration, bf16 written with round-to-nearest-even.
+// k_gemm_bf16<BM>: BM rows x 256 weight rows per item (GEMM1: 128 gate + 128
+// up rows, h = silu(gate) * up rounded to bf16; GEMM2: 256 output columns),
+// K step 64, operands streamed into an LDS stage ring by global_load_lds DMA
+// and consumed by bf16 16x16x32 MFMA.
+#include "common.h"
+#include "kernels.h"
+#include "moe_sched.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ dequant
+
+// E4M3FN byte -> fp32 (exact; the NaN code is not expected in weights).
+MOE_DEV float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0) {  // subnormal: m * 2^-9
+    const float v = (float)m * 0x1p-9f;
+    return s ? -v : v;
+  }
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 nibble -> fp32 (exact): 0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign bit 3.
+MOE_DEV float e2m1_to_f32(uint32_t nib) {
+  const uint32_t s = (nib & 8u) << 28, e = (nib >> 1) & 3u, m = nib & 1u;
+  const uint32_t mag = e == 0 ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+  return __uint_as_float(s | mag);
+}
+
+// bf16 bits of the exact product a * s, rounded to nearest even.  The fp32
+// product is turned into its round-to-odd form (truncate, then set the last
+// bit if anything was lost; the FMA gives the exact remainder), and rounding
+// that to nearest at 8 bits equals one rounding of the exact product, since
+// fp32 keeps more than two extra bits.
+MOE_DEV uint32_t bf16_of_product(float a, float s) {
+  const float p = a * s;
+  const float err = __builtin_fmaf(a, s, -p);
+  uint32_t pb = __float_as_uint(p);
+  if (err != 0.0f) {
+    if ((__float_as_uint(err) ^ pb) >> 31) pb -= 1;  // |p| above the exact value: step toward zero
+    pb |= 1u;
+  }
+  return f32_to_bf16_bits(__uint_as_float(pb));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict__ w13, const void* __restrict__ s13,
+                                                       const uint8_t* __restrict__ w2, const void* __restrict__ s2,
+                                                       const int32_t* __restrict__ active,
+                                                       const int32_t* __restrict__ num_active, int chunk, int C,
+                                                       int H, int I, uint16_t* __restrict__ scratch) {
+  const int na = *num_active;
+  const int a0 = chunk * C;
+  if (a0 >= na) return;
+  const int nc = min(C, na - a0);
+  const int64_t n13 = (int64_t)2 * I * H, n2 = (int64_t)H * I;
+  const int64_t u13 = n13 / 16, U = (n13 + n2) / 16;
+  const int64_t total = (int64_t)nc * U;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
+    const int slot = (int)(u / U);
+    int64_t r = u - (int64_t)slot * U;
+    const int e = active[a0 + slot];
+    const bool first = r < u13;
+    if (!first) r -= u13;
+    const int N = first ? 2 * I : H, K = first ? H : I;
+    const uint8_t* w = first ? w13 : w2;
+    const void* sc = first ? s13 : s2;
+    const int64_t nel = first ? n13 : n2;
+    const int n = (int)(r / (K / 16)), k0 = (int)(r % (K / 16)) * 16;
+    uint32_t o[8];
+    if (FMT == FMT_FP8) {
+      const uint4 q = *reinterpret_cast<const uint4*>(w + (int64_t)e * nel + (int64_t)n * K + k0);
+      const float s = static_cast<const float*>(sc)[(int64_t)e * (nel / (128 * 128)) + (n / 128) * (K / 128) + k0 / 128];
+      const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t d = qs[i >> 1] >> ((i & 1) * 16);
+        o[i] = bf16_of_product(e4m3_to_f32(d & 0xFFu), s) | (bf16_of_product(e4m3_to_f32((d >> 8) & 0xFFu), s) << 16);
+      }
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(w + (int64_t)e * (nel / 2) + ((int64_t)n * K + k0) / 2);
+      const int64_t si = (int64_t)e * (nel / 32) + (int64_t)(k0 / 32) * N + n;  // group-major [K/32][N]
+      const uint32_t qs[2] = {q.x, q.y};
+      if (FMT == FMT_INT4) {
+        const float s = bf16_bits_to_f32(static_cast<const uint16_t*>(sc)[si]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t d = qs[i >> 2] >> ((i & 3) * 8);
+          const float lo = (float)((int32_t)(d << 28) >> 28), hi = (float)((int32_t)(d << 24) >> 28);
+          // a 4-bit integer times a bf16 scale is exact in fp32
+          o[i] = f32_to_bf16_bits(lo * s) | (f32_to_bf16_bits(hi * s) << 16);
+        }
+      } else {
+        const uint32_t eb = static_cast<const uint8_t*>(sc)[si];
+        const float s = __uint_as_float(eb ? eb << 23 : 0x00400000u);  // 2^(eb - 127)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t d = qs[i >> 2] >> ((i & 3) * 8);
+          // E2M1 times a power of two is exact in bf16
+          o[i] = f32_to_bf16_bits(e2m1_to_f32(d & 15u) * s) | (f32_to_bf16_bits(e2m1_to_f32((d >> 4) & 15u) * s) << 16);
+        }
+      }
+    }
+    uint16_t* dst = scratch + (int64_t)slot * (n13 + n2) + (first ? 0 : n13) + (int64_t)n * K + k0;
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
+                          const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
+                          uint16_t* scratch, hipStream_t s) {
+  const dim3 grid(2048), block(256);
+  if (fmt == FMT_INT4)
+    hipLaunchKernelGGL(k_dequant_chunk<FMT_INT4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
+                       H, I, scratch);
+  else if (fmt == FMT_FP8)
+    hipLaunchKernelGGL(k_dequant_chunk<FMT_FP8>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
+                       H, I, scratch);
+  else
+    hipLaunchKernelGGL(k_dequant_chunk<FMT_MXFP4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk,
+                       C, H, I, scratch);
+}
+
+// ------------------------------------------------------------- BF16 GEMM
+
+// LDS of one stage: BM activation rows and the 4 waves' 4 x 16 weight rows,
+// 64 bf16 (128 bytes) each, 16-byte parts XOR-swizzled by (row & 7).
+template <int BM>
+struct BfStage {
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_OFF = A_BYTES;
+  static constexpr int BYTES = B_OFF + 256 * 128;
+  static constexpr int APW = BM * 2;              // activation 16-byte pieces per wave
+  static constexpr int NA = (APW + 63) / 64;      // activation DMA instructions per wave
+  static constexpr int SR = (152 * 1024) / BYTES;
+  static constexpr int S = SR > 5 ? 5 : SR;       // stages
+  static constexpr int NPER = NA + 8;             // DMA instructions per wave per stage
+};
+
+template <int BM, bool G1>
+__device__ __forceinline__ void bf_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
+  constexpr int MT = BM / 16;
+  using ST = BfStage<BM>;
+  constexpr int S = ST::S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int K = p.K, KT = K / 64;
+  const uint32_t smem0 = lds_u32(smem);
+  lds_barrier();  // every wave is done with the previous item's stages
+  int col[4];
+  if (G1) {
+    const int g0 = tl.nb * 128 + wave * 32;
+    col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
+  } else {
+    const int c0 = tl.nb * 256 + wave * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
+  }
+  // the chunk's BF16 copy holds its experts in active order
+  const int slot = tl.a - p.chunk * p.chunk_experts;
+  const char* wexp = reinterpret_cast<const char*>(p.w) + (int64_t)slot * p.w_expert_bytes;
+  const char* bsrc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * 64 + lane, rr = c >> 3, part = c & 7;
+      bsrc[i][h] = wexp + (int64_t)(col[i] + rr) * K * 2 + ((part ^ (rr & 7)) << 4);
+    }
+  const char* asrc[ST::NA];
+#pragma unroll
+  for (int j = 0; j < ST::NA; ++j) {
+    const int c = min(wave * ST::APW + j * 64 + lane, BM * 8 - 1);
+    const int row = c >> 3, part = c & 7;
+    const int rr = tl.rbase + min(row, tl.nrows - 1);
+    const int src = p.a_per_token ? p.sorted_rows[rr] / p.top_k : rr;
+    asrc[j] = static_cast<const char*>(p.a) + (int64_t)src * K * 2 + ((part ^ (row & 7)) << 4);
+  }
+  auto issue = [&](int kt, int s) {
+    const uint32_t sb = smem0 + s * ST::BYTES;
+#pragma unroll
+    for (int j = 0; j < ST::NA; ++j)
+      if (ST::APW >= 64 || lane < ST::APW) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::APW + j * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dma_b128(bsrc[i][h] + kt * 128, sb + ST::B_OFF + (wave * 4 + i) * 2048 + h * 1024);
+  };
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int s = 0; s + 1 < S; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<ST::NPER>(min(S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    lds_barrier();                                    // ... and every other wave's
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const uint8_t* st = smem + (kt % S) * ST::BYTES;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int lp = 4 * s + lg;  // logical 16-byte part of this lane's 8 K values
+      bf16x8 bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bfr[i] = *reinterpret_cast<const bf16x8*>(st + ST::B_OFF + (wave * 4 + i) * 2048 + ln * 128 +
+                                                  ((lp ^ (ln & 7)) << 4));
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int r = m * 16 + ln;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + r * 128 + ((lp ^ (r & 7)) << 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_bf16_16x16x32(af, bfr[i], acc[m][i]);
+      }
+    }
+  }
+
+  // Epilogue through LDS (stage buffers are free after the barrier) so that
+  // global stores are 16 bytes per lane.
+  lds_barrier();
+  if (G1) {
+    constexpr int HS = 272;  // staged row stride (bytes) of the 128 bf16 h values
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float hv = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
+          *reinterpret_cast<uint16_t*>(smem + row * HS + (wave * 32 + n * 16 + ln) * 2) =
+              (uint16_t)f32_to_bf16_bits(hv);
+        }
+      }
+    lds_barrier();
+    char* Hh = static_cast<char*>(p.out) + (int64_t)tl.nb * 256;
+    for (int c = threadIdx.x; c < BM * 16; c += 256) {
+      const int row = c >> 4, part = c & 15;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Hh + (int64_t)(tl.rbase + row) * p.inter * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
+    }
+  } else {
+    constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+              (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
+      }
+    lds_barrier();
+    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
+    for (int c = threadIdx.x; c < BM * 32; c += 256) {
+      const int row = c >> 5, part = c & 31;
+      if (row < tl.nrows)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
+            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
+    }
+  }
+}
+
+// Persistent launch over chunk p1.chunk's GEMM1 items and chunk p2.chunk's
+// GEMM2 items (either may be empty), dealt through per-XCD atomic counters as
+// in the fused kernels.
+template <int BM>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  using ST = BfStage<BM>;
+  constexpr int S = ST::S;
+  static_assert(S >= 2 && S <= 5, "LDS stages");
+  static_assert(ST::NA * 64 >= ST::APW, "activation pieces");
+  __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
+  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  __shared__ int s_item;
+  ChunkWork c1, c2;
+  const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
+  const int n2 = chunk_work(p2, p2.N / 256, c2) ? c2.nwork : 0;
+  const int x = blockIdx.x & 7;
+  const int per1 = (n1 + 7) >> 3, per2 = (n2 + 7) >> 3;
+  const int b1 = x * per1, b2 = x * per2;
+  const int len1 = max(0, min(n1, b1 + per1) - b1), len2 = max(0, min(n2, b2 + per2) - b2);
+  int32_t* q = queue + x;
+  const int wpx = gridDim.x >> 3;
+  int cur = blockIdx.x >> 3;
+  while (cur < len1 + len2) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;
+    if (cur < len1) bf_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else bf_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (threadIdx.x == 0) s_item = nxt;
+    lds_barrier();
+    cur = s_item;
+  }
+}
+
+void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                           hipStream_t s) {
+  switch (bm) {
+    case 16: launch_persistent2<k_gemm_bf16<16>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_bf16<32>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_bf16<64>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_bf16<128>>(g1, g2, queue, grid, s); break;
+  }
+}
+
+}  // namespace moe

@@ -405,6 +405,160 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s); }
   return launch_status();
 }
+
+// ---------------------------------------------------------------------------
+// Materialized-chunk scheme: per chunk, dequantize its experts into a BF16
+// copy in the workspace, then BF16 GEMM1 and GEMM2 over that copy.
+
+// Workspace of the materialized scheme: the routing arrays, the bf16 GEMM1
+// input (OFT only; otherwise x is read directly), h and y in bf16, work
+// counters for two launches per chunk, and one chunk's BF16 weight copy.
+struct MatLayout {
+  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
+  size_t act, h, y, copy;
+  size_t total;
+};
+
+int mat_queue_ints(const Dims& d) { return 16 * (d.E + 1); }
+int64_t mat_copy_elems(const Dims& d) { return (int64_t)3 * d.H * d.I; }  // W13 + W2 of one expert
+
+MatLayout mat_layout(const Dims& d, int chunk) {
+  MatLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t R = (size_t)d.R, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+  w.ids = take(R * 4);
+  w.wts = take(R * 4);
+  w.offsets = take((E + 1) * 4);
+  w.sorted_rows = take(R * 4);
+  w.row_of = take(R * 4);
+  w.active = take(E * 4);
+  w.num_active = take(16);
+  w.tile_a = take((E + 1) * 4);
+  w.tile_16 = take((E + 1) * 4);
+  w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
+  w.queue = take((size_t)mat_queue_ints(d) * 4);
+  w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
+  w.act = take(d.oft ? R * H * 2 : 0);
+  w.h = take(R * I * 2);
+  w.y = take(R * H * 2);
+  w.copy = take((size_t)chunk * (size_t)mat_copy_elems(d) * 2);
+  w.total = o;
+  return w;
+}
+
+// BF16 GEMM tile rows: 16, 32, 64 or 128 (layer->tile_rows if one of these).
+int choose_bm_mat(const Dims& d) {
+  if (d.tile_rows == 16 || d.tile_rows == 32 || d.tile_rows == 64 || d.tile_rows == 128) return d.tile_rows;
+  const int64_t mean = d.R / d.E;
+  if (mean <= 16) return 16;
+  if (mean <= 32) return 32;
+  if (mean <= 96) return 64;
+  return 128;
+}
+
+moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                     const moe_qweights* qw, const moe_scales* sc, const void* adapter_bf16,
+                                     int32_t chunk_experts, void* out_bf16, void* ws, size_t ws_bytes, void* stream,
+                                     StageTimer* tm) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.T == 0) return MOE_OK;
+  const void* ptrs[] = {x_bf16, logits, qw->w13, qw->w2, sc->s13, sc->s2, out_bf16, ws};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.oft && !aligned16(adapter_bf16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.oft && (layer->adapter_expert_stride % 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  const int C = chunk_experts < d.E ? chunk_experts : d.E;  // a chunk never holds more than E experts
+  const MatLayout wl = mat_layout(d, C);
+  if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  int32_t* ids = I32(wl.ids);
+  float* wts = reinterpret_cast<float*>(base + wl.wts);
+  int32_t* offsets = I32(wl.offsets);
+  int32_t* sorted_rows = I32(wl.sorted_rows);
+  int32_t* row_of = I32(wl.row_of);
+  int32_t* active = I32(wl.active);
+  int32_t* num_active = I32(wl.num_active);
+  int32_t* tile_a = I32(wl.tile_a);
+  int32_t* tile_16 = I32(wl.tile_16);
+  int32_t* tiles = I32(wl.tiles);
+  int32_t* queue = I32(wl.queue);
+  int32_t* hist = I32(wl.hist);
+  uint16_t* act = reinterpret_cast<uint16_t*>(base + wl.act);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + wl.h);
+  uint16_t* y = reinterpret_cast<uint16_t*>(base + wl.y);
+  uint16_t* copy = reinterpret_cast<uint16_t*>(base + wl.copy);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const int bm = choose_bm_mat(d);
+
+  { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
+  { Scope sc_(tm, MOE_STAGE_PERMUTE);
+    launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
+                   tiles, queue, mat_queue_ints(d), s); }
+  if (d.oft) {
+    Scope sc_(tm, MOE_STAGE_ACT);
+    launch_oft_bf16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
+                    sorted_rows, active, num_active, tile_16, act, s);
+  }
+
+  const int64_t copy_bytes = mat_copy_elems(d) * 2;
+  GemmArgs g1{}, g2{};
+  g1.a = d.oft ? static_cast<const void*>(act) : static_cast<const void*>(x);
+  g1.a_per_token = d.oft ? 0 : 1;
+  g1.w = reinterpret_cast<const uint8_t*>(copy);
+  g1.w_expert_bytes = copy_bytes;
+  g1.N = 2 * d.I;
+  g1.K = d.H;
+  g1.inter = d.I;
+  g1.out = h;
+  g2.a = h;
+  g2.a_per_token = 0;
+  g2.w = reinterpret_cast<const uint8_t*>(copy + (int64_t)2 * d.I * d.H);
+  g2.w_expert_bytes = copy_bytes;
+  g2.N = d.H;
+  g2.K = d.I;
+  g2.inter = d.I;
+  g2.out = y;
+  for (GemmArgs* g : {&g1, &g2}) {
+    g->offsets = offsets;
+    g->sorted_rows = sorted_rows;
+    g->active = active;
+    g->num_active = num_active;
+    g->tile_start = tile_a;
+    g->tiles = tiles;
+    g->top_k = d.k;
+    g->chunk_experts = C;
+    g->nb_fastest = 1;
+  }
+  const int grid1 = gemm_grid(d, bm, C, d.I / 128);
+  const int grid2 = gemm_grid(d, bm, C, d.H / 256);
+  const int nchunks = (d.E + C - 1) / C;
+  for (int c = 0; c < nchunks; ++c) {
+    { Scope sc_(tm, MOE_STAGE_DEQUANT);
+      launch_dequant_chunk(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13,
+                           static_cast<const uint8_t*>(qw->w2), sc->s2, active, num_active, c, C, d.H, d.I, copy, s); }
+    g1.chunk = c;
+    g2.chunk = -1;
+    { Scope sc_(tm, MOE_STAGE_GEMM1); launch_gemm_bf16_pair(g1, g2, queue + 16 * c, bm, grid1, s); }
+    g1.chunk = -1;
+    g2.chunk = c;
+    { Scope sc_(tm, MOE_STAGE_GEMM2); launch_gemm_bf16_pair(g1, g2, queue + 16 * c + 8, bm, grid2, s); }
+  }
+  { Scope sc_(tm, MOE_STAGE_COMBINE);
+    launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s); }
+  return launch_status();
+}
 }  // namespace
 
 extern "C" {
@@ -443,6 +597,31 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
   launch_lm_head(static_cast<const uint16_t*>(h_bf16), static_cast<const uint16_t*>(w_lm_bf16), targets, T, H, V,
                  logits, inv_rms, logprob, static_cast<hipStream_t>(stream));
   return launch_status();
+}
+
+size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
+  Dims d;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
+  return mat_layout(d, chunk_experts < d.E ? chunk_experts : d.E).total;
+}
+
+moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                           const moe_qweights* qw, const moe_scales* sc, const void* adapter_bf16,
+                                           int32_t chunk_experts, void* out_bf16, void* ws, size_t ws_bytes,
+                                           void* stream, float* stage_ms, int32_t* stage_launches) {
+  if ((stage_ms == nullptr) != (stage_launches == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage_ms == nullptr)
+    return forward_materialized_impl(layer, x_bf16, logits, qw, sc, adapter_bf16, chunk_experts, out_bf16, ws,
+                                     ws_bytes, stream, nullptr);
+  StageTimer* tm = new StageTimer();
+  tm->s = static_cast<hipStream_t>(stream);
+  moe_status st = forward_materialized_impl(layer, x_bf16, logits, qw, sc, adapter_bf16, chunk_experts, out_bf16,
+                                            ws, ws_bytes, stream, tm);
+  tm->finish(stage_ms, stage_launches);
+  const bool ok = tm->ok;
+  delete tm;
+  if (st == MOE_OK && !ok) st = MOE_ERR_DEVICE;
+  return st;
 }
 
 }  // extern "C"

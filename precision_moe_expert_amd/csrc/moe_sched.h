@@ -34,6 +34,7 @@ struct Tile {
   int rbase;   // first permuted row
   int nrows;   // valid rows (1..BM)
   int nb;      // N block
+  int a;       // index of the expert in the active list
 };
 
 // Item wk -> (tile, N block).  With tiles fastest, workgroups that run at
@@ -55,6 +56,7 @@ MOE_DEV Tile tile_of(const GemmArgs& p, const ChunkWork& cw, int wk, int bm) {
   t.e = d[0];
   t.rbase = d[1];
   t.nrows = d[2];
+  t.a = d[3];
   (void)bm;
   return t;
 }

@@ -39,6 +39,12 @@ class DevInputs:
                                       adapter=self.oft, chunk_experts=c.chunk if chunk is None else chunk,
                                       out=out, ws=ws)
 
+    def forward_materialized(self, chunk=None, out=None, ws=None):
+        c = self.li.cfg
+        return binding.expert_forward_materialized(self.layer, self.x, self.logits, self.w13, self.w2, self.s13,
+                                                   self.s2, adapter=self.oft,
+                                                   chunk_experts=c.chunk if chunk is None else chunk, out=out, ws=ws)
+
 
 def bf16_to_np(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy()

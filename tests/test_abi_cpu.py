@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     fns = declared_functions()
     for name in ("moe_route_permute", "moe_expert_forward", "moe_combine", "moe_workspace_bytes",
-                 "moe_lm_head_logprob", "moe_status_str", "moe_abi_version"):
+                 "moe_lm_head_logprob", "moe_status_str", "moe_abi_version", "moe_expert_forward_materialized",
+                 "moe_materialized_workspace_bytes"):
         assert name in fns
 
 
@@ -30,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = binding.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -118,3 +119,34 @@ def test_other_entry_points_reject_bad_args():
         binding.MOE_ERR_UNSUPPORTED
     assert lib.moe_lm_head_logprob(4, 128, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == \
         binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def _mat(layer, chunk=1, ws_bytes=1 << 40, ms=None, n=None, x=FAKE):
+    qw = binding.MoeQWeights(FAKE, FAKE)
+    sc = binding.MoeScales(FAKE, FAKE)
+    return binding.lib().moe_expert_forward_materialized(ctypes.byref(layer), x, FAKE, ctypes.byref(qw),
+                                                         ctypes.byref(sc), None, chunk, FAKE, FAKE, ws_bytes, None,
+                                                         ms, n)
+
+
+def test_materialized_workspace_grows_with_the_chunk():
+    H, I, E = 7168, 2048, 384
+    L = binding.make_layer(8192, H, I, E, 8, binding.FMT_INT4)
+    sizes = {c: binding.materialized_workspace_bytes(L, c) for c in (1, 8, 32, 64)}
+    for a, b in ((1, 8), (8, 32), (32, 64)):
+        # exactly (b - a) more experts' BF16 copies, up to alignment
+        assert abs(sizes[b] - sizes[a] - (b - a) * 3 * H * I * 2) <= 256
+    assert binding.materialized_workspace_bytes(L, 10 ** 6) == binding.materialized_workspace_bytes(L, E)
+    assert binding.materialized_workspace_bytes(L, 0) == 0
+
+
+def test_materialized_rejects_bad_args():
+    L = binding.make_layer(64, 256, 512, 8, 2, 1)
+    ms = (ctypes.c_float * len(binding.STAGES))()
+    n = (ctypes.c_int32 * len(binding.STAGES))()
+    assert _mat(L, chunk=0) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _mat(L, x=None) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _mat(L, ms=ms) == binding.MOE_ERR_INVALID_ARGUMENT              # one timing array without the other
+    assert _mat(L, ws_bytes=binding.materialized_workspace_bytes(L, 2) - 1, chunk=2) == \
+        binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert _mat(L, ws_bytes=0, ms=ms, n=n) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
