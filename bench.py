@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--tile-rows", type=int, default=0, help="grouped-GEMM tile rows (0: automatic)")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle token sample (default: sized per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialized", action="store_true",
+                    help="time the materialized-chunk scheme (per-chunk BF16 weight copy + BF16 GEMMs) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the expert-parallel split "
@@ -100,12 +102,18 @@ def main():
     oft = dev(li.oft, True) if li.oft is not None else None
     layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
                                tile_rows=args.tile_rows)
-    ws = binding.alloc_workspace(binding.workspace_bytes(layer, cfg.chunk))
+    mat = args.materialized
+    ws_bytes = (binding.materialized_workspace_bytes if mat else binding.workspace_bytes)(layer, cfg.chunk)
+    ws = binding.alloc_workspace(ws_bytes)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
 
     def step():
-        binding.expert_forward(layer, x, logits, w13, w2, s13, s2, adapter=oft, chunk_experts=cfg.chunk, out=out,
-                               ws=ws)
+        if mat:
+            binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
+                                                chunk_experts=cfg.chunk, out=out, ws=ws)
+        else:
+            binding.expert_forward(layer, x, logits, w13, w2, s13, s2, adapter=oft, chunk_experts=cfg.chunk,
+                                   out=out, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -125,8 +133,12 @@ def main():
     stage_ms = {s: 0.0 for s in binding.STAGES}
     stage_n = {s: 0 for s in binding.STAGES}
     for _ in range(args.steps):
-        _, st = binding.expert_forward_timed(layer, x, logits, w13, w2, s13, s2, adapter=oft,
-                                             chunk_experts=cfg.chunk, out=out, ws=ws)
+        if mat:
+            _, st = binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
+                                                        chunk_experts=cfg.chunk, out=out, ws=ws, timed=True)
+        else:
+            _, st = binding.expert_forward_timed(layer, x, logits, w13, w2, s13, s2, adapter=oft,
+                                                 chunk_experts=cfg.chunk, out=out, ws=ws)
         for s, (ms, n) in st.items():
             stage_ms[s] += ms
             stage_n[s] += n
@@ -141,18 +153,38 @@ def main():
     peak = MFMA_PEAK[cfg.fmt]
     fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4", 4: "fp8"}[cfg.fmt]
     bm = binding.tile_rows(layer)
-    # every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
-    dom = "gemm"
-    launches = stage_n["gemm1"] + stage_n["gemm2"]
-    launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
-    f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
-    if cfg.fmt in (2, 4):
-        kname = f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>"
+    if mat:
+        # the BF16 copy: packed weights read and 2 bytes per weight written by the
+        # dequant kernel, then read back by the BF16 GEMMs with bf16 activations
+        nw = acc["active"] * 3 * cfg.H * cfg.I
+        R = cfg.T * cfg.k
+        deq_b = nw * 2 + acc["active"] * (weight_bytes_per_expert(cfg.fmt, 2 * cfg.I, cfg.H) +
+                                          weight_bytes_per_expert(cfg.fmt, cfg.H, cfg.I))
+        gemm_b = nw * 2 + (R if cfg.oft else cfg.T) * cfg.H * 2 + 2 * R * cfg.I * 2 + R * cfg.H * 2
+        peak = MFMA_PEAK[1]  # bf16 MFMA, same peak as fp16
+        g_ms = stage_ms["gemm1"] + stage_ms["gemm2"]
+        if stage_ms["dequant"] > g_ms:
+            dom, launches, f_dom, b_dom = "dequant", stage_n["dequant"], 0.0, deq_b
+            launch_ms = stage_ms["dequant"] / max(launches, 1)
+            kname = f"k_dequant_chunk<{ {1: 1, 2: 2, 3: 3, 4: 2}[cfg.fmt] }>"
+        else:
+            dom, launches = "gemm", stage_n["gemm1"] + stage_n["gemm2"]
+            launch_ms = g_ms / max(launches, 1)
+            f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], gemm_b
+            kname = "k_gemm_bf16"
     else:
-        kname = f"k_gemm_{fmt_name}<{bm}>"
+        # every launch is one kernel running chunk c's GEMM1 with chunk c-1's GEMM2
+        dom = "gemm"
+        launches = stage_n["gemm1"] + stage_n["gemm2"]
+        launch_ms = (stage_ms["gemm1"] + stage_ms["gemm2"]) / max(launches, 1)
+        f_dom, b_dom = acc["gemm1"][0] + acc["gemm2"][0], acc["gemm1"][1] + acc["gemm2"][1]
+        if cfg.fmt in (2, 4):
+            kname = f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>"
+        else:
+            kname = f"k_gemm_{fmt_name}<{bm}>"
     launches_per_step = launches / args.steps
     f_launch, b_launch = f_dom / launches_per_step, b_dom / launches_per_step
-    if b_launch / HBM_PEAK >= f_launch / peak:
+    if f_launch == 0 or b_launch / HBM_PEAK >= f_launch / peak:
         roof = dict(bound="hbm", achieved=b_launch / (launch_ms / 1e3) / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s")
     else:
         roof = dict(bound="mfma", achieved=f_launch / (launch_ms / 1e3) / 1e12, peak=peak / 1e12, unit="TFLOP/s")
@@ -162,7 +194,7 @@ def main():
     # valid only while the kernel source is unchanged
     from precision_moe_expert_amd import profiling
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{fmt_name}_{cfg.name}_traffic.txt"))
-    roof["traffic"] = tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname else None
+    roof["traffic"] = tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname and not mat else None
     roof["launch_ms"] = launch_ms
     roof["algorithmic_bytes_per_launch"] = b_launch
     roof["algorithmic_flops_per_launch"] = f_launch
@@ -178,18 +210,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPE[cfg.fmt],
+        "dtype": "bf16_from_" + DTYPE[cfg.fmt] if mat else DTYPE[cfg.fmt],
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE expert layer", "tokens": cfg.T, "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I, "weight_format": synth.FMT_NAMES[cfg.fmt],
-                   "chunk_experts": cfg.chunk, "tile_rows": args.tile_rows or "auto", "oft_adapter": cfg.oft, "active_experts": acc["active"]},
+                   "chunk_experts": cfg.chunk, "tile_rows": args.tile_rows or "auto", "oft_adapter": cfg.oft,
+                   "active_experts": acc["active"], "mode": "materialized_bf16_copy" if mat else "fused"},
         "tflops": acc["flops"] / sec / 1e12,
         "pct_mfma_peak": 100.0 * acc["flops"] / sec / peak,
         "hbm_gbps_algorithmic": acc["bytes"] / sec / 1e9,
         "pct_hbm_peak": 100.0 * acc["bytes"] / sec / HBM_PEAK,
         "stages_ms_per_step": {s: stage_ms[s] / args.steps for s in binding.STAGES},
-        "temp_dequant_bytes": {"materialized_chunk_scheme": cfg.chunk * 3 * cfg.H * cfg.I * 2,
-                               "this_build_global": 0},
+        "temp_dequant_bytes": {"materialized_chunk_scheme": min(cfg.chunk, cfg.E) * 3 * cfg.H * cfg.I * 2,
+                               "this_run": min(cfg.chunk, cfg.E) * 3 * cfg.H * cfg.I * 2 if mat else 0},
+        "workspace_bytes": ws_bytes,
         "roofline": roof,
     }
 
@@ -201,7 +235,7 @@ def main():
         # repeat short samples until about 10 s of oracle work has been timed
         passes, c0 = 0, time.perf_counter()
         while passes == 0 or (time.perf_counter() - c0 < 10.0 and passes < 8):
-            oracle.forward_inputs(li, tokens=toks)
+            oracle.forward_inputs(li, tokens=toks, materialized=mat)
             passes += 1
         csec = time.perf_counter() - c0
         result["cpu_baseline"] = {"value": n * passes / csec, "unit": "tokens/s", "cores": oracle.num_threads(),

@@ -6,7 +6,7 @@
 // costs 2 bytes written and read back per weight, and its size grows with the
 // chunk) and to compare the two numerics.
 //
-// k_dequant_chunk: one pass over the chunk's packed experts, 16 weights per
+// k_dequant_chunk: one pass over the chunk's packed experts, 8 weights per
 // thread per iteration, bf16 written with round-to-nearest-even.
 // k_gemm_bf16<BM>: BM rows x 256 weight rows per item (GEMM1: 128 gate + 128
 // up rows, h = silu(gate) * up rounded to bf16; GEMM2: 256 output columns),
@@ -53,6 +53,64 @@ MOE_DEV uint32_t bf16_of_product(float a, float s) {
   return f32_to_bf16_bits(__uint_as_float(pb));
 }
 
+// One unit: 8 consecutive weights of one row (16 bytes of bf16), so that a
+// wave's loads and stores are contiguous.  Each thread loads four units
+// before converting any, to keep four loads in flight per wave.
+struct Raw8 {
+  uint2 q;       // FP8: 8 codes; INT4 / MXFP4: 8 nibbles in q.x
+  uint32_t s;    // scale bits (fp32, bf16 or E8M0)
+};
+
+template <int FMT>
+MOE_DEV Raw8 load8(const uint8_t* __restrict__ w, const void* __restrict__ sc, int N, int K, int n, int k0) {
+  Raw8 r;
+  if (FMT == FMT_FP8) {
+    r.q = *reinterpret_cast<const uint2*>(w + (int64_t)n * K + k0);
+    r.s = static_cast<const uint32_t*>(sc)[(n / 128) * (K / 128) + k0 / 128];
+  } else {
+    r.q.x = *reinterpret_cast<const uint32_t*>(w + ((int64_t)n * K + k0) / 2);
+    r.q.y = 0;
+    const int si = (k0 / 32) * N + n;  // group-major [K/32][N]
+    r.s = FMT == FMT_INT4 ? (uint32_t) static_cast<const uint16_t*>(sc)[si]
+                          : (uint32_t) static_cast<const uint8_t*>(sc)[si];
+  }
+  return r;
+}
+
+template <int FMT>
+MOE_DEV uint4 cvt8(const Raw8& r) {
+  uint32_t o[4];
+  if (FMT == FMT_FP8) {
+    const float s = __uint_as_float(r.s);
+    const uint32_t qs[2] = {r.q.x, r.q.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = qs[i >> 1] >> ((i & 1) * 16);
+      o[i] = bf16_of_product(e4m3_to_f32(d & 0xFFu), s) | (bf16_of_product(e4m3_to_f32((d >> 8) & 0xFFu), s) << 16);
+    }
+  } else if (FMT == FMT_INT4) {
+    const float s = bf16_bits_to_f32(r.s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = r.q.x >> (i * 8);
+      const float lo = (float)((int32_t)(b << 28) >> 28), hi = (float)((int32_t)(b << 24) >> 28);
+      // a 4-bit integer times a bf16 scale is exact in fp32
+      o[i] = f32_to_bf16_bits(lo * s) | (f32_to_bf16_bits(hi * s) << 16);
+    }
+  } else {
+    const float s = __uint_as_float(r.s ? r.s << 23 : 0x00400000u);  // 2^(s - 127)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = r.q.x >> (i * 8);
+      // E2M1 times a power of two is exact in bf16
+      o[i] = f32_to_bf16_bits(e2m1_to_f32(b & 15u) * s) | (f32_to_bf16_bits(e2m1_to_f32((b >> 4) & 15u) * s) << 16);
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// grid.y = chunk slot (slots past the chunk's last active expert exit).
+// Units u < u13 are W13's, the rest W2's, both in row-major order.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict__ w13, const void* __restrict__ s13,
                                                        const uint8_t* __restrict__ w2, const void* __restrict__ s2,
@@ -60,67 +118,50 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
                                                        const int32_t* __restrict__ num_active, int chunk, int C,
                                                        int H, int I, uint16_t* __restrict__ scratch) {
   const int na = *num_active;
-  const int a0 = chunk * C;
-  if (a0 >= na) return;
-  const int nc = min(C, na - a0);
+  const int slot = blockIdx.y;
+  const int a = chunk * C + slot;
+  if (slot >= C || a >= na) return;
+  const int e = active[a];
   const int64_t n13 = (int64_t)2 * I * H, n2 = (int64_t)H * I;
-  const int64_t u13 = n13 / 16, U = (n13 + n2) / 16;
-  const int64_t total = (int64_t)nc * U;
-  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
-    const int slot = (int)(u / U);
-    int64_t r = u - (int64_t)slot * U;
-    const int e = active[a0 + slot];
-    const bool first = r < u13;
-    if (!first) r -= u13;
-    const int N = first ? 2 * I : H, K = first ? H : I;
-    const uint8_t* w = first ? w13 : w2;
-    const void* sc = first ? s13 : s2;
-    const int64_t nel = first ? n13 : n2;
-    const int n = (int)(r / (K / 16)), k0 = (int)(r % (K / 16)) * 16;
-    uint32_t o[8];
-    if (FMT == FMT_FP8) {
-      const uint4 q = *reinterpret_cast<const uint4*>(w + (int64_t)e * nel + (int64_t)n * K + k0);
-      const float s = static_cast<const float*>(sc)[(int64_t)e * (nel / (128 * 128)) + (n / 128) * (K / 128) + k0 / 128];
-      const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+  constexpr int64_t WB = FMT == FMT_FP8 ? 1 : 2;                 // weights per byte
+  constexpr int64_t SB = FMT == FMT_FP8 ? 128 * 128 : 32;        // weights per scale
+  constexpr int64_t SZ = FMT == FMT_FP8 ? 4 : FMT == FMT_INT4 ? 2 : 1;  // scale bytes
+  const int u13 = (int)(n13 / 8), total = (int)((n13 + n2) / 8);
+  const int KU1 = H / 8, KU2 = I / 8;
+  const uint8_t* w13e = w13 + (int64_t)e * (n13 / WB);
+  const uint8_t* w2e = w2 + (int64_t)e * (n2 / WB);
+  const char* s13e = static_cast<const char*>(s13) + (int64_t)e * (n13 / SB) * SZ;
+  const char* s2e = static_cast<const char*>(s2) + (int64_t)e * (n2 / SB) * SZ;
+  uint16_t* dst = scratch + (int64_t)slot * (n13 + n2);
+  const int stride = gridDim.x * 256;
+  constexpr int U = 4;
+  for (int u0 = blockIdx.x * 256 + threadIdx.x; u0 < total; u0 += U * stride) {
+    Raw8 r[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t d = qs[i >> 1] >> ((i & 1) * 16);
-        o[i] = bf16_of_product(e4m3_to_f32(d & 0xFFu), s) | (bf16_of_product(e4m3_to_f32((d >> 8) & 0xFFu), s) << 16);
-      }
-    } else {
-      const uint2 q = *reinterpret_cast<const uint2*>(w + (int64_t)e * (nel / 2) + ((int64_t)n * K + k0) / 2);
-      const int64_t si = (int64_t)e * (nel / 32) + (int64_t)(k0 / 32) * N + n;  // group-major [K/32][N]
-      const uint32_t qs[2] = {q.x, q.y};
-      if (FMT == FMT_INT4) {
-        const float s = bf16_bits_to_f32(static_cast<const uint16_t*>(sc)[si]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t d = qs[i >> 2] >> ((i & 3) * 8);
-          const float lo = (float)((int32_t)(d << 28) >> 28), hi = (float)((int32_t)(d << 24) >> 28);
-          // a 4-bit integer times a bf16 scale is exact in fp32
-          o[i] = f32_to_bf16_bits(lo * s) | (f32_to_bf16_bits(hi * s) << 16);
-        }
-      } else {
-        const uint32_t eb = static_cast<const uint8_t*>(sc)[si];
-        const float s = __uint_as_float(eb ? eb << 23 : 0x00400000u);  // 2^(eb - 127)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t d = qs[i >> 2] >> ((i & 3) * 8);
-          // E2M1 times a power of two is exact in bf16
-          o[i] = f32_to_bf16_bits(e2m1_to_f32(d & 15u) * s) | (f32_to_bf16_bits(e2m1_to_f32((d >> 4) & 15u) * s) << 16);
-        }
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * stride;
+      if (u < u13) {
+        const int n = u / KU1;
+        r[j] = load8<FMT>(w13e, s13e, 2 * I, H, n, (u - n * KU1) * 8);
+      } else if (u < total) {
+        const int v = u - u13, n = v / KU2;
+        r[j] = load8<FMT>(w2e, s2e, H, I, n, (v - n * KU2) * 8);
       }
     }
-    uint16_t* dst = scratch + (int64_t)slot * (n13 + n2) + (first ? 0 : n13) + (int64_t)n * K + k0;
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * stride;
+      if (u < total) *reinterpret_cast<uint4*>(dst + (int64_t)u * 8) = cvt8<FMT>(r[j]);
+    }
   }
 }
 
 void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
                           const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
                           uint16_t* scratch, hipStream_t s) {
-  const dim3 grid(2048), block(256);
+  // about 4096 workgroups over the chunk's slots, at least 16 per slot
+  const int gx = C >= 256 ? 16 : 4096 / C;
+  const dim3 grid(gx, C), block(256);
   if (fmt == FMT_INT4)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_INT4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
                        H, I, scratch);
