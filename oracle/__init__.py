@@ -53,6 +53,7 @@ def lib():
             _lib.oracle_combine.restype = ctypes.c_int
             _lib.oracle_lm_head_logprob.restype = ctypes.c_int
             _lib.oracle_num_threads.restype = ctypes.c_int
+            _lib.oracle_backward.restype = ctypes.c_int
         return _lib
 
 
@@ -209,6 +210,40 @@ def forward_inputs(li, chunk_experts=None, tokens=None, **kw):
     return forward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2,
                    oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts,
                    tokens=tokens, **kw)
+
+
+def backward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, dout, oft=None, chunk_experts=1, tokens=None,
+             adapter_expert_stride=None):
+    """Frozen-base backward of the oracle forward.  dout: [n][H] fp32 gradient of
+    the requested tokens' outputs (all tokens if tokens is None).
+    Returns (dx [n][H] fp32, dlogits [n][E] fp32, doft or None), doft float64
+    shaped like the adapter, summed over the requested tokens' rows."""
+    stride = (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride
+    layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0, stride, 0)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tok is None else len(tok)
+    dout = _c(dout, np.float32).reshape(n, H)
+    dx = np.empty((n, H), np.float32)
+    dl = np.empty((n, E), np.float32)
+    doft = None
+    if oft is not None:
+        doft = np.zeros((E * stride if stride else H * 32,), np.float64)
+    rc = lib().oracle_backward(ctypes.byref(layer), _p(_c(x, np.uint16)), _p(_c(logits, np.float32)),
+                               _p(_c(w13, np.uint8)), _p(_c(w2, np.uint8)), _p(np.ascontiguousarray(s13)),
+                               _p(np.ascontiguousarray(s2)), _p(None if oft is None else _c(oft, np.uint16)),
+                               _p(dout), int(chunk_experts), _p(tok), int(n), _p(dx), _p(dl), _p(doft))
+    if rc != 0:
+        raise ValueError("oracle_backward: invalid arguments")
+    if doft is not None:
+        doft = doft.reshape((E, H // 32, 32, 32) if stride else (H // 32, 32, 32))
+    return dx, dl, doft
+
+
+def backward_inputs(li, dout, chunk_experts=None, tokens=None):
+    """oracle backward on a synth.LayerInputs bundle."""
+    c = li.cfg
+    return backward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2, dout,
+                    oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts, tokens=tokens)
 
 
 def combine(y_perm_bf16: np.ndarray, w: np.ndarray, row_of: np.ndarray) -> np.ndarray:

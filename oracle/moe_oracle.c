@@ -498,6 +498,211 @@ done:
   return rc;
 }
 
+/* ---------------------------------------------------------------- backward
+ *
+ * Frozen-base backward (Orbit announcement, 技术细节: the GEMM backward that
+ * bypasses the base weight gradient, so nothing is computed for the frozen
+ * base; Orbit analysis page, 机制拆解: the base takes part in the forward but
+ * carries no backward update, the adapter's parameters get the gradients).
+ * Given dL/dout, it returns dL/dx, dL/dlogits and, with an adapter, dL/dR;
+ * no gradient for W13 or W2.  The forward is the oracle's own (exactly
+ * dequantized weights; activation quantizers of the FP8 / MXFP4 formats are
+ * passed straight through in the backward).  All arithmetic in fp64.
+ *
+ *   per selected (t, j), expert e = ids_tj, w = w_tj:
+ *     x' = x_t R_e;  a = Q(x') Wg^T;  b = Q(x') Wu^T;  h = silu(a) b
+ *     u  = dout_t W2                 (the gradient reaching Q(h), before w)
+ *     g_tj = <u, Q(h)> = <dout_t, y_tj>
+ *     dh = w u;  da = dh b silu'(a);  db = dh silu(a)
+ *     dx' = da Wg + db Wu
+ *     dR_e += x_t^T dx'  on each 32x32 diagonal block
+ *     dx_tj = dx' R_e^T
+ *   dx_t = sum_j dx_tj
+ *   dlogits[t][ids_tj] = w_tj (g_tj - sum_i w_ti g_ti)  (softmax over the k
+ *   selected logits); 0 for experts not selected.
+ *
+ * silu'(a) = s (1 + a (1 - s)) with s = 1 / (1 + e^-a). */
+static void expert_row_backward(const oracle_layer* L, const uint16_t* xrow, const uint16_t* R_e, const float* W13,
+                                const float* W2, const float* dout, double w, double* dx, double* dR_e, double* g,
+                                double* buf, uint8_t* qtmp, float* stmp, uint8_t* etmp) {
+  const int H = L->H, I = L->I;
+  float* xr = (float*)buf;                 /* H floats (in the first H/2 doubles) */
+  double* xq = buf + H;                    /* H */
+  double* a = xq + H;                      /* I */
+  double* b = a + I;                       /* I */
+  double* hq = b + I;                      /* I */
+  double* u = hq + I;                      /* I */
+  double* dxr = u + I;                     /* H: dL/dx' */
+  float* hf = (float*)(dxr + H);           /* I floats */
+  int B = L->oft_block;
+  /* forward of this row, as the oracle's forward computes it */
+  if (R_e != NULL) {
+    for (int bb = 0; bb < H / B; ++bb)
+      for (int j = 0; j < B; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < B; ++i)
+          acc += (double)bf16_value(xrow[bb * B + i]) * (double)bf16_value(R_e[(int64_t)bb * B * B + i * B + j]);
+        xr[bb * B + j] = (float)acc;
+      }
+  } else {
+    for (int i = 0; i < H; ++i) xr[i] = bf16_value(xrow[i]);
+  }
+  act_quant_row(L->fmt, H, xr, xq, qtmp, stmp, etmp);
+  for (int n = 0; n < I; ++n) {
+    double ga = 0.0, ub = 0.0;
+    const float* wg = W13 + (int64_t)n * H;
+    const float* wu = W13 + (int64_t)(I + n) * H;
+    for (int kk = 0; kk < H; ++kk) {
+      ga += xq[kk] * (double)wg[kk];
+      ub += xq[kk] * (double)wu[kk];
+    }
+    a[n] = ga;
+    b[n] = ub;
+    hf[n] = (float)(silu((double)(float)ga) * (double)(float)ub);
+  }
+  act_quant_row(L->fmt, I, hf, hq, qtmp, stmp, etmp);
+  /* u = dout W2 (W2 is [H][I]) and g = <u, Q(h)> */
+  for (int i = 0; i < I; ++i) u[i] = 0.0;
+  for (int n = 0; n < H; ++n) {
+    const double d = (double)dout[n];
+    const float* wd = W2 + (int64_t)n * I;
+    for (int i = 0; i < I; ++i) u[i] += d * (double)wd[i];
+  }
+  double gg = 0.0;
+  for (int i = 0; i < I; ++i) gg += u[i] * hq[i];
+  *g = gg;
+  /* SwiGLU backward, then dx' = da Wg + db Wu */
+  for (int kk = 0; kk < H; ++kk) dxr[kk] = 0.0;
+  for (int n = 0; n < I; ++n) {
+    const double sg = 1.0 / (1.0 + exp(-a[n]));
+    const double dh = w * u[n];
+    const double da = dh * b[n] * sg * (1.0 + a[n] * (1.0 - sg));
+    const double db = dh * a[n] * sg;
+    const float* wg = W13 + (int64_t)n * H;
+    const float* wu = W13 + (int64_t)(I + n) * H;
+    for (int kk = 0; kk < H; ++kk) dxr[kk] += da * (double)wg[kk] + db * (double)wu[kk];
+  }
+  /* adapter: dR_e += x^T dx' per diagonal block; dx = dx' R_e^T */
+  if (R_e != NULL) {
+    for (int bb = 0; bb < H / B; ++bb)
+      for (int i = 0; i < B; ++i) {
+        const double xi = (double)bf16_value(xrow[bb * B + i]);
+        double acc = 0.0;
+        for (int j = 0; j < B; ++j) {
+          dR_e[(int64_t)bb * B * B + i * B + j] += xi * dxr[bb * B + j];
+          acc += dxr[bb * B + j] * (double)bf16_value(R_e[(int64_t)bb * B * B + i * B + j]);
+        }
+        dx[bb * B + i] = acc;
+      }
+  } else {
+    for (int kk = 0; kk < H; ++kk) dx[kk] = dxr[kk];
+  }
+}
+
+/* dout: [n_tokens][H] fp32 (rows of the requested tokens, in request order).
+ * Outputs for the requested tokens: dx [n][H] fp32, dlogits [n][E] fp32;
+ * doft (optional, with an adapter): fp64, shaped like the adapter (per-expert
+ * blocks at adapter_expert_stride, or one shared block set), accumulated over
+ * the rows of the requested tokens only (zeroed first). */
+int oracle_backward(const oracle_layer* L, const uint16_t* x, const float* logits, const uint8_t* w13,
+                    const uint8_t* w2, const void* s13, const void* s2, const uint16_t* oft, const float* dout,
+                    int chunk_experts, const int32_t* tokens, int n_tokens, float* dx_out, float* dlogits_out,
+                    double* doft_out) {
+  const int T = L->T, H = L->H, I = L->I, E = L->E, k = L->k, fmt = L->fmt;
+  const int64_t R = (int64_t)T * k;
+  int32_t *ids, *counts, *offsets, *sorted_rows, *row_of, *active, *slot, num_active = 0;
+  float* wts;
+  double *dxbuf, *gbuf;
+  int rc = 0;
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || chunk_experts < 1 || L->materialized) return 1;
+  if (H % 32 || I % 32 || ((fmt == OR_FP8 || fmt == OR_FP8_POW2) && (H % 128 || I % 128))) return 1;
+  if (oft != NULL && (L->oft_block != 32 || H % 32)) return 1;
+  if (tokens == NULL) n_tokens = T;
+  if (T == 0 || n_tokens == 0) return 0;
+  const int64_t n_oft = oft ? (L->adapter_expert_stride ? (int64_t)E * L->adapter_expert_stride : (int64_t)H * 32) : 0;
+  if (doft_out && oft) memset(doft_out, 0, sizeof(double) * (size_t)n_oft);
+
+  ids = (int32_t*)malloc(sizeof(int32_t) * R);
+  wts = (float*)malloc(sizeof(float) * R);
+  counts = (int32_t*)malloc(sizeof(int32_t) * E);
+  offsets = (int32_t*)malloc(sizeof(int32_t) * (E + 1));
+  sorted_rows = (int32_t*)malloc(sizeof(int32_t) * R);
+  row_of = (int32_t*)malloc(sizeof(int32_t) * R);
+  active = (int32_t*)malloc(sizeof(int32_t) * E);
+  slot = (int32_t*)malloc(sizeof(int32_t) * T);
+  dxbuf = (double*)malloc(sizeof(double) * (size_t)n_tokens * k * H);
+  gbuf = (double*)malloc(sizeof(double) * (size_t)n_tokens * k);
+
+  oracle_route(T, E, k, logits, ids, wts);
+  oracle_permute(T, E, k, ids, counts, offsets, sorted_rows, row_of, active, &num_active);
+  for (int t = 0; t < T; ++t) slot[t] = -1;
+  for (int i = 0; i < n_tokens; ++i) {
+    int t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= T) { rc = 1; goto done; }
+    slot[t] = i;
+  }
+
+  for (int c0 = 0; c0 < num_active; c0 += chunk_experts) {
+    int nc = num_active - c0 < chunk_experts ? num_active - c0 : chunk_experts;
+    for (int a = 0; a < nc; ++a) {
+      int e = active[c0 + a], need = 0;
+      for (int32_t r = offsets[e]; r < offsets[e + 1] && !need; ++r) need = slot[sorted_rows[r] / k] >= 0;
+      if (!need) continue;
+      float* W13 = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
+      float* W2 = (float*)malloc(sizeof(float) * (size_t)H * I);
+      dequant_matrix(fmt, 2 * I, H, w13 + packed_bytes(fmt, (int64_t)e * 2 * I * H),
+                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), 0, W13);
+      dequant_matrix(fmt, H, I, w2 + packed_bytes(fmt, (int64_t)e * H * I),
+                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), 0, W2);
+      const uint16_t* R_e = oft ? oft + (int64_t)e * L->adapter_expert_stride : NULL;
+      double* dR_e = (oft && doft_out) ? doft_out + (int64_t)e * L->adapter_expert_stride : NULL;
+      const int32_t r0 = offsets[e], r1 = offsets[e + 1];
+#pragma omp parallel
+      {
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(4 * H + 5 * I));
+        double* dRl = R_e ? (double*)calloc((size_t)H * 32, sizeof(double)) : NULL;
+        uint8_t* qtmp = (uint8_t*)malloc((size_t)(H > I ? H : I));
+        float* stmp = (float*)malloc(sizeof(float) * (size_t)((H > I ? H : I) / 32 + 1));
+        uint8_t* etmp = (uint8_t*)malloc((size_t)((H > I ? H : I) / 32 + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t r = r0; r < r1; ++r) {
+          int32_t p = sorted_rows[r];
+          int t = p / k, j = p % k;
+          if (slot[t] < 0) continue;
+          const int64_t q = (int64_t)slot[t] * k + j;
+          expert_row_backward(L, x + (int64_t)t * H, R_e, W13, W2, dout + (int64_t)slot[t] * H, (double)wts[p],
+                              dxbuf + q * H, dRl, gbuf + q, buf, qtmp, stmp, etmp);
+        }
+        if (dRl && dR_e) {
+#pragma omp critical
+          for (int64_t i = 0; i < (int64_t)H * 32; ++i) dR_e[i] += dRl[i];
+        }
+        free(buf); free(dRl); free(qtmp); free(stmp); free(etmp);
+      }
+      free(W13); free(W2); /* release */
+    }
+  }
+
+  for (int i = 0; i < n_tokens; ++i) {
+    int t = tokens ? tokens[i] : i;
+    for (int n = 0; n < H; ++n) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += dxbuf[((int64_t)i * k + j) * H + n];
+      dx_out[(int64_t)i * H + n] = (float)acc;
+    }
+    double mean = 0.0;
+    for (int j = 0; j < k; ++j) mean += (double)wts[(int64_t)t * k + j] * gbuf[(int64_t)i * k + j];
+    for (int e = 0; e < E; ++e) dlogits_out[(int64_t)i * E + e] = 0.0f;
+    for (int j = 0; j < k; ++j)
+      dlogits_out[(int64_t)i * E + ids[(int64_t)t * k + j]] =
+          (float)((double)wts[(int64_t)t * k + j] * (gbuf[(int64_t)i * k + j] - mean));
+  }
+done:
+  free(ids); free(wts); free(counts); free(offsets); free(sorted_rows); free(row_of); free(active);
+  free(slot); free(dxbuf); free(gbuf);
+  return rc;
+}
+
 /* Combine on its own: out[t] = sum_j w[t][j] * y_perm[row_of[t*k+j]], with
  * y_perm given as bf16 rows; fp64 sum, fp32 result. */
 int oracle_combine(int T, int k, int H, const uint16_t* y_perm, const float* w, const int32_t* row_of, float* out) {

@@ -1,0 +1,175 @@
+"""Pins of the oracle's frozen-base backward (CPU only).
+
+The backward bypasses the base weight gradient (Orbit announcement, 技术细节):
+it returns dL/dx, dL/dlogits and dL/dR for the OFT adapter, nothing for W13
+or W2.  Pins: torch autograd through a dense float64 re-statement of the
+forward (activation quantizers passed straight through), central finite
+differences of a float64 forward, the softmax-gradient identities, the
+identity-adapter case, chunk-size invariance and token-subset consistency."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_moe_expert_amd import synth
+from tests import refimpl
+
+
+def tiny(fmt=1, oft=False, T=12, H=64, I=64, E=5, k=2, chunk=2, zipf=0.0, cid=0):
+    return synth.LayerConfig("bwd_pin", 200 + fmt + 10 * cid + (5 if oft else 0), T=T, H=H, E=E, k=k, I=I,
+                             fmt=fmt, chunk=chunk, oft=oft, zipf_alpha=zipf)
+
+
+def dout_for(cfg, seed=1):
+    return np.random.default_rng(seed).standard_normal((cfg.T, cfg.H)).astype(np.float32)
+
+
+def autograd_reference(li, dout):
+    """Dense float64 forward in torch (every expert on every token, masked by
+    the routing weights), differentiated by autograd.  Quantizers: value of the
+    format's activation quantizer, gradient of the identity."""
+    c = li.cfg
+    T, H, I, E, k, fmt = c.T, c.H, c.I, c.E, c.k, c.fmt
+    x = torch.tensor(refimpl.bf16_to_f32(li.x).reshape(T, H), dtype=torch.float64, requires_grad=True)
+    lg = torch.tensor(li.logits, dtype=torch.float64, requires_grad=True)
+    ids, _ = refimpl.route_bruteforce(li.logits, k)
+    sel = torch.stack([lg[t, torch.tensor(ids[t], dtype=torch.long)] for t in range(T)])
+    w = torch.softmax(sel, dim=1)
+    Rt = None
+    if li.oft is not None:
+        Rt = torch.tensor(refimpl.bf16_to_f32(li.oft).reshape(E, H // 32, 32, 32), dtype=torch.float64,
+                          requires_grad=True)
+
+    def ste(v64):
+        q = refimpl.act_values(fmt, v64.detach().numpy().astype(np.float32))
+        return v64 + (torch.tensor(q, dtype=torch.float64) - v64).detach()
+
+    out = torch.zeros((T, H), dtype=torch.float64)
+    for e in range(E):
+        W13 = torch.tensor(refimpl.dequant(fmt, li.w13[e], li.s13[e], 2 * I, H), dtype=torch.float64)
+        W2 = torch.tensor(refimpl.dequant(fmt, li.w2[e], li.s2[e], H, I), dtype=torch.float64)
+        xin = x
+        if Rt is not None:
+            xin = torch.einsum("tbi,bij->tbj", x.reshape(T, H // 32, 32), Rt[e]).reshape(T, H)
+            # the forward stores x' in fp32; carry that rounding as a constant offset
+            xin = xin + (xin.detach().float().double() - xin.detach())
+        xq = ste(xin)
+        a = xq @ W13[:I].T
+        b = xq @ W13[I:].T
+        h = torch.nn.functional.silu(a) * b
+        h32 = (torch.nn.functional.silu(a.detach().float().double()) * b.detach().float().double()).float().double()
+        h = h + (h32 - h).detach()  # the forward's fp32 h value, exact gradient
+        y = ste(h) @ W2.T
+        m = torch.zeros((T, 1), dtype=torch.float64)
+        for t in range(T):
+            for j in range(k):
+                if ids[t, j] == e:
+                    m[t, 0] = m[t, 0] + w[t, j]
+        out = out + m * y
+    (out * torch.tensor(dout, dtype=torch.float64)).sum().backward()
+    dR = Rt.grad.numpy() if Rt is not None else None
+    return x.grad.numpy(), lg.grad.numpy(), dR
+
+
+def rel(a, b):
+    return np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False)])
+def test_backward_vs_autograd(fmt, oft):
+    cfg = tiny(fmt, oft, H=128 if fmt in (2, 4) else 64, I=128 if fmt in (2, 4) else 64)
+    li = synth.make_inputs(cfg)
+    dout = dout_for(cfg)
+    dx, dl, dR = oracle.backward_inputs(li, dout)
+    rx, rl, rR = autograd_reference(li, dout)
+    tol = 1e-6 if fmt == 1 else 1e-4   # quantizer decisions taken on fp32 values on both sides
+    assert rel(dx, rx) <= tol, rel(dx, rx)
+    assert rel(dl, rl) <= tol, rel(dl, rl)
+    if oft:
+        assert rel(dR, rR) <= tol, rel(dR, rR)
+
+
+def dense_f64(x, logits_sel_ids, lg, R, W13s, W2s, I, k):
+    """Plain float64 forward without any rounding (INT4 format: no quantizer)."""
+    T, H = x.shape
+    ids = logits_sel_ids
+    out = np.zeros((T, H))
+    for t in range(T):
+        sel = lg[t, ids[t]]
+        w = np.exp(sel - sel.max())
+        w /= w.sum()
+        for j in range(k):
+            e = ids[t, j]
+            xin = x[t]
+            if R is not None:
+                xin = np.einsum("bi,bij->bj", x[t].reshape(H // 32, 32), R[e]).reshape(H)
+            a = W13s[e][:I] @ xin
+            b = W13s[e][I:] @ xin
+            h = a / (1.0 + np.exp(-a)) * b
+            out[t] += w[j] * (W2s[e] @ h)
+    return out
+
+
+def test_backward_vs_finite_differences():
+    cfg = tiny(1, True, T=6, E=4, k=2)
+    li = synth.make_inputs(cfg)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    dout = dout_for(cfg, 3).astype(np.float64)
+    dx, dl, dR = oracle.backward_inputs(li, dout.astype(np.float32))
+    x = refimpl.bf16_to_f32(li.x).reshape(T, H).astype(np.float64)
+    lg = li.logits.astype(np.float64)
+    R = refimpl.bf16_to_f32(li.oft).reshape(E, H // 32, 32, 32).astype(np.float64)
+    W13s = [refimpl.dequant(1, li.w13[e], li.s13[e], 2 * I, H) for e in range(E)]
+    W2s = [refimpl.dequant(1, li.w2[e], li.s2[e], H, I) for e in range(E)]
+    ids, _ = refimpl.route_bruteforce(li.logits, k)
+    f = lambda x_, lg_, R_: float(np.sum(dense_f64(x_, ids, lg_, R_, W13s, W2s, I, k) * dout))
+    r = np.random.default_rng(9)
+    eps = 1e-4
+    for _ in range(3):
+        vx, vl, vR = r.standard_normal(x.shape), r.standard_normal(lg.shape), r.standard_normal(R.shape)
+        fd_x = (f(x + eps * vx, lg, R) - f(x - eps * vx, lg, R)) / (2 * eps)
+        fd_l = (f(x, lg + eps * vl, R) - f(x, lg - eps * vl, R)) / (2 * eps)
+        fd_R = (f(x, lg, R + eps * vR) - f(x, lg, R - eps * vR)) / (2 * eps)
+        for fd, an in ((fd_x, np.sum(dx * vx)), (fd_l, np.sum(dl * vl)), (fd_R, np.sum(dR * vR))):
+            # fp32 storage of x' and h in the oracle's recomputed forward, and of its outputs
+            assert abs(fd - an) <= 1e-5 * (abs(fd) + 1e-3), (fd, an)
+
+
+def test_router_gradient_identities():
+    cfg = tiny(1, E=7, k=3, zipf=1.0)
+    li = synth.make_inputs(cfg)
+    _, dl, _ = oracle.backward_inputs(li, dout_for(cfg))
+    ids, _ = oracle.route(li.logits, cfg.k)
+    for t in range(cfg.T):
+        assert abs(float(np.sum(dl[t].astype(np.float64)))) <= 1e-6 * (np.abs(dl[t]).sum() + 1e-30)
+        unsel = np.setdiff1d(np.arange(cfg.E), ids[t])
+        assert np.all(dl[t, unsel] == 0)
+
+
+def test_identity_adapter_matches_no_adapter():
+    cfg = tiny(1, True)
+    li = synth.make_inputs(cfg)
+    li.oft[:] = 0
+    li.oft[:, :, np.arange(32), np.arange(32)] = 0x3F80
+    dout = dout_for(cfg)
+    dx_a, dl_a, dR = oracle.backward_inputs(li, dout)
+    li2 = synth.make_inputs(tiny(1, True))
+    li2.oft = None
+    li2.x, li2.logits, li2.w13, li2.w2, li2.s13, li2.s2 = li.x, li.logits, li.w13, li.w2, li.s13, li.s2
+    dx_n, dl_n, _ = oracle.backward_inputs(li2, dout)
+    assert np.array_equal(dx_a, dx_n) and np.array_equal(dl_a, dl_n)
+    # with R = I, dR_e is the sum over the expert's rows of x^T dx (block diagonal)
+    assert np.abs(dR).max() > 0
+
+
+def test_backward_chunk_and_token_subset_invariance():
+    cfg = tiny(2, T=16, H=128, I=128, E=6, k=3, zipf=1.2)
+    li = synth.make_inputs(cfg)
+    dout = dout_for(cfg)
+    full = oracle.backward_inputs(li, dout, chunk_experts=1)
+    for c in (2, 6):
+        o = oracle.backward_inputs(li, dout, chunk_experts=c)
+        assert np.array_equal(o[0], full[0]) and np.array_equal(o[1], full[1])
+    toks = np.array([3, 0, 11], np.int32)
+    sub = oracle.backward_inputs(li, dout[toks], tokens=toks)
+    assert np.array_equal(sub[0], full[0][toks]) and np.array_equal(sub[1], full[1][toks])
