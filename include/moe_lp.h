@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_LP_ABI_VERSION 2
+#define MOE_LP_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -211,6 +211,53 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
                                            const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
                                            void* ws, size_t ws_bytes, void* stream, float* stage_ms,
                                            int32_t* stage_launches);
+
+/* ---- Frozen-base backward (INT4 weights) ----------------------------------
+ * The GEMM backward that bypasses the base weight gradient (Orbit
+ * announcement, 技术细节): gradients for the layer inputs and the adapter only.
+ * Its two GEMMs contract over the weights' output dimension, so they read a
+ * transposed copy of the frozen weights, made once per base. */
+
+/* Bytes of the transposed copy: W13^T [E][H][2I] and W2^T [E][I][H] INT4
+ * nibbles plus the group scales as fp16 (same count as the bf16 scales);
+ * 0 if the layer is not supported by the backward (INT4 only, I multiple of
+ * 256, per-expert adapter). */
+size_t moe_backward_weights_bytes(const moe_layer* layer);
+
+/* Writes the transposed copy of (qweights, scales) into bwd_weights (device,
+ * caller-owned, >= moe_backward_weights_bytes).  Values are bit-identical
+ * re-layouts; the scales are converted to fp16 (exact for bf16 scales in
+ * [2^-10, 4096]) and pre-divided by 16 where the unpack needs it. */
+moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweights* qweights,
+                                        const moe_scales* scales, void* bwd_weights, size_t bwd_bytes,
+                                        void* stream);
+
+/* Workspace bytes of moe_expert_backward (routing, recomputed gate/up
+ * pre-activations fp32 [R][2I], their gradients fp16 [R][2I], dx' fp32
+ * [R][H] (twice with an adapter), the fp16 copy of d_out). */
+size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
+
+/* Backward of moe_expert_forward for given d_out = dL/dout [T][H] bf16:
+ *   d_x      [T][H] bf16    dL/dx
+ *   d_logits [T][E] fp32    dL/dlogits: w_tj (g_tj - sum_i w_ti g_ti) for the
+ *                           selected experts, g_tj = <d_out_t, y_tj>; 0 elsewhere
+ *   d_adapter fp32, shaped like the adapter (per-expert R only), dL/dR; NULL
+ *                           exactly when adapter is NULL
+ * No gradient is formed for W13 or W2.  The forward is recomputed per chunk
+ * (routing, gate/up pre-activations); per permuted row (t, j) of expert e:
+ * u = d_out_t W2, dh = w_tj u, da = dh b silu'(a), db = dh silu(a),
+ * dx' = da Wg + db Wu, dR_e += x_t^T dx' (32x32 diagonal blocks),
+ * dx_tj = dx' R_e^T, d_x_t = sum_j dx_tj.  GEMM operands are fp16 (INT4
+ * weights times their scales exactly; d_out and the SwiGLU gradients rounded
+ * to fp16, so their magnitudes must stay below 65504), accumulation fp32.
+ * bwd_weights: from moe_prepare_backward_weights for the same weights.
+ * Unsupported layers return MOE_ERR_UNSUPPORTED; the rest as moe_expert_forward.
+ * Stream-ordered, no host synchronisation, nothing allocated. */
+moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
+                               const moe_qweights* qweights, const moe_scales* scales, const void* bwd_weights,
+                               const void* adapter_bf16, const void* d_out_bf16, int32_t chunk_experts,
+                               void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
  * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:

@@ -20,7 +20,8 @@ FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_rows",
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
             "moe_lm_head_workspace_bytes", "moe_lm_head_logprob", "moe_materialized_workspace_bytes",
-            "moe_expert_forward_materialized")
+            "moe_expert_forward_materialized", "moe_backward_weights_bytes", "moe_prepare_backward_weights",
+            "moe_backward_workspace_bytes", "moe_expert_backward")
 STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine", "dequant")
 
 
@@ -87,6 +88,20 @@ def lib() -> ctypes.CDLL:
         L.moe_materialized_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_int32]
         L.moe_expert_forward_materialized.restype = ctypes.c_int
         L.moe_expert_forward_materialized.argtypes = L.moe_expert_forward_timed.argtypes
+        L.moe_backward_weights_bytes.restype = ctypes.c_size_t
+        L.moe_backward_weights_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
+        L.moe_prepare_backward_weights.restype = ctypes.c_int
+        L.moe_prepare_backward_weights.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoeQWeights),
+                                                   ctypes.POINTER(MoeScales), ctypes.c_void_p, ctypes.c_size_t,
+                                                   ctypes.c_void_p]
+        L.moe_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_backward_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_int32]
+        L.moe_expert_backward.restype = ctypes.c_int
+        L.moe_expert_backward.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -210,6 +225,50 @@ def expert_forward_materialized(layer: MoeLayer, x, logits, w13, w2, s13, s2, ad
     if timed:
         return out, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
     return out
+
+
+def backward_weights_bytes(layer: MoeLayer) -> int:
+    return lib().moe_backward_weights_bytes(ctypes.byref(layer))
+
+
+def prepare_backward_weights(layer: MoeLayer, w13, w2, s13, s2, out: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_prepare_backward_weights: the transposed copy of the frozen weights."""
+    n = backward_weights_bytes(layer)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, "moe_backward_weights_bytes")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w13.device)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2))
+    _check(lib().moe_prepare_backward_weights(ctypes.byref(layer), ctypes.byref(qw), ctypes.byref(sc), _ptr(out),
+                                              out.numel(), _stream()), "moe_prepare_backward_weights")
+    return out
+
+
+def backward_workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(layer), int(chunk_experts))
+
+
+def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d_out, adapter=None,
+                    chunk_experts: int = 1, ws=None, d_x=None, d_logits=None, d_adapter=None):
+    """moe_expert_backward -> (d_x [T][H] bf16, d_logits [T][E] fp32, d_adapter fp32 or None)."""
+    T, H, E = layer.num_tokens, layer.hidden, layer.num_experts
+    dev = x.device
+    if d_x is None:
+        d_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if adapter is not None and d_adapter is None:
+        d_adapter = torch.empty(adapter.shape, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = alloc_workspace(backward_workspace_bytes(layer, chunk_experts), dev)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2))
+    _check(lib().moe_expert_backward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
+                                     _ptr(bwd_weights), _ptr(adapter), _ptr(d_out), int(chunk_experts), _ptr(d_x),
+                                     _ptr(d_logits), _ptr(d_adapter), _ptr(ws), ws.numel(), _stream()),
+           "moe_expert_backward")
+    return d_x, d_logits, d_adapter
 
 
 def combine(layer: MoeLayer, y_perm: torch.Tensor, topk_w: torch.Tensor, row_of: torch.Tensor,

@@ -16,58 +16,9 @@
 #include "common.h"
 #include "kernels.h"
 #include "moe_sched.h"
+#include "int4.h"
 
 namespace moe {
-
-// 8 INT4 codes (one dword, element i in bits 4i..4i+3, two's complement) times
-// scale s -> 8 fp16 values ordered (0,4),(1,5),(2,6),(3,7).  Each pair comes
-// from one bitop3 that keeps the two code fields, flips their sign bit (q + 8)
-// and sets the exponent of 1024, i.e. fp16 1024 + (q + 8) for codes in bits
-// 0-3 / 16-19, or 1024 + 16 (q + 8) for codes in bits 4-7 / 20-23 (still
-// inside the 10-bit mantissa, so no shift is needed).  Subtracting the bias
-// gives q or 16 q exactly; multiplying by s or s/16 gives q s, exact in fp16.
-// bitop3 truth table 0x6A: b ? (c ? ~a : a) : c.
-MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2, f16x2 s2_16) {
-  const f16x2 bias0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 bias1 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const uint32_t v = w >> 8;
-  const uint32_t d0 = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, 0x6A);
-  const uint32_t d1 = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, 0x6A);
-  const uint32_t d2 = __builtin_amdgcn_bitop3_b32(v, 0x000F000Fu, 0x64086408u, 0x6A);
-  const uint32_t d3 = __builtin_amdgcn_bitop3_b32(v, 0x00F000F0u, 0x64806480u, 0x6A);
-  const f16x2 h0 = (__builtin_bit_cast(f16x2, d0) + bias0) * s2;
-  const f16x2 h1 = (__builtin_bit_cast(f16x2, d1) + bias1) * s2_16;
-  const f16x2 h2 = (__builtin_bit_cast(f16x2, d2) + bias0) * s2;
-  const f16x2 h3 = (__builtin_bit_cast(f16x2, d3) + bias1) * s2_16;
-  f16x8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-  return r;
-}
-
-MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; }
-
-// LDS bytes of one pipeline stage: activation rows (256 B = 128 fp16 each,
-// 16-byte parts XOR-swizzled by row), each wave's weight fragments (4
-// subtiles x 1 KB of nibbles) and the bf16 group scales of the wave's 64
-// weight rows for the step's 4 groups (512 B).  Scales are stored
-// group-major, so those are 4 (GEMM2) or 8 (GEMM1: gate and up) contiguous
-// runs: 32 lanes x 16 B.  (Per-row scale requests, 64 per wave per step,
-// were measured to cost more time than the weight nibbles themselves.)
-template <int BM>
-struct I4Stage {
-  static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
-  static constexpr int A_BYTES = BM * 256;
-  static constexpr int B_OFF = A_BYTES;
-  static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
-  static constexpr int BYTES = BS_OFF + 4 * 512;
-  // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
-  // a second resident workgroup covers one's item start-up and waits; one at
-  // 32 rows (a deeper ring wins there) and above 64 rows, where the
-  // activation tile fills the LDS.
-  static constexpr int WPC = (BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
-  static constexpr int SMAX = BM <= 32 ? 7 : 5;
-  static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
-  static constexpr int NPER = NA + 4 + 1;             // DMA instructions per wave per stage
-};
 
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
 // 128 gate + 128 up weight rows; GEMM2: 256 output columns).
@@ -174,7 +125,20 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   // Epilogue: results go through LDS (the stage buffers are free once every
   // wave has passed the barrier below) so that global stores are 16 B per lane.
   lds_barrier();
-  if (G1) {
+  if (G1 && p.save_ab) {
+    // backward recompute: the gate and up pre-activations in fp32, each at its W13 row index
+    float* AB = static_cast<float*>(p.out);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+        if (row < tl.nrows) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) AB[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = acc[m][n][i];
+        }
+      }
+  } else if (G1) {
     constexpr int HS = 272;  // staged row stride (bytes) of the 128 fp16 h values
 #pragma unroll
     for (int m = 0; m < MT; ++m)

@@ -38,6 +38,14 @@ struct GemmArgs {
   int chunk;                   // chunk index c
   int chunk_experts;           // C
   int nb_fastest;              // 1: item order (tile, N block) with N blocks fastest
+  // backward (INT4): GEMM1 with save_ab writes the gate/up pre-activations
+  // a, b as fp32 [R][2I] to out instead of h; the dh GEMM reads them (ab),
+  // the routing weights (topk_w, per flat pair) and writes per-row partial
+  // sums <u, h> over its 256 columns to gpart [R][I/256].
+  int save_ab;
+  const float* ab;
+  const float* topk_w;
+  float* gpart;
 };
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
@@ -78,6 +86,23 @@ void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const ui
                           uint16_t* scratch, hipStream_t s);
 void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
+
+// Frozen-base backward (INT4).  Transposed weight copy: W [E][N][K] nibbles ->
+// W^T [E][K][N]; group scales s [E][K/32][N] (forward orientation) -> fp16
+// pairs per 8 consecutive values of the last dimension (see the kernel).
+void launch_repack_int4(const uint8_t* w, const uint16_t* s, int E, int N, int K, uint8_t* wt, uint16_t* st,
+                        hipStream_t stream);
+// One launch: chunk g1.chunk's dh items (SwiGLU backward epilogue) and chunk
+// g2.chunk's dx' items, both reading the transposed copy.
+void launch_gemm_int4_bwd_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                               hipStream_t s);
+void launch_oft_bwd(const uint16_t* x, const uint16_t* R, int64_t r_stride, const float* dxt, int H, int k,
+                    const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
+                    int E, float* dx, float* dR, hipStream_t s);
+void launch_unpermute_sum(const float* src, const int32_t* row_of, int T, int k, int H, uint16_t* out, hipStream_t s);
+void launch_router_grad(const int32_t* ids, const float* w, const int32_t* row_of, const float* gpart, int nparts,
+                        int T, int k, int E, float* dlogits, hipStream_t s);
+void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 
 // Grouped GEMMs; bm = rows per tile (16, 32, 48, 64, 96, 128 or 192).  One
 // launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2 (either may

@@ -559,9 +559,243 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
     launch_combine(y, wts, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(out_bf16), s); }
   return launch_status();
 }
+// ---------------------------------------------------------------------------
+// Frozen-base backward (INT4 weights).
+
+// The transposed weight copy made by moe_prepare_backward_weights.
+struct BwdWeights {
+  size_t w13t, w2t, s13, s2, total;
+};
+
+BwdWeights bwd_weights_layout(const Dims& d) {
+  BwdWeights b{};
+  const size_t H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+  size_t o = 0;
+  b.w13t = o; o = align_up(o + E * H * 2 * I / 2);
+  b.w2t = o;  o = align_up(o + E * I * H / 2);
+  b.s13 = o;  o = align_up(o + E * (H / 32) * 2 * I * 2);
+  b.s2 = o;   o = align_up(o + E * (I / 32) * H * 2);
+  b.total = o;
+  return b;
+}
+
+moe_status check_backward(const moe_layer* L, Dims* d) {
+  moe_status st = check_layer(L, d);
+  if (st != MOE_OK) return st;
+  if (d->fmt != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->oft && L->adapter_expert_stride == 0) return MOE_ERR_UNSUPPORTED;  // one shared R
+  return MOE_OK;
+}
+
+struct BwdLayout {
+  size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
+  size_t act, gact, ab, dab, gpart, dxt, dxr;
+  size_t total;
+};
+
+int bwd_queue_ints(const Dims& d) { return 16 * (d.E + 1); }
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t R = (size_t)d.R, T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+  w.ids = take(R * 4);
+  w.wts = take(R * 4);
+  w.offsets = take((E + 1) * 4);
+  w.sorted_rows = take(R * 4);
+  w.row_of = take(R * 4);
+  w.active = take(E * 4);
+  w.num_active = take(16);
+  w.tile_a = take((E + 1) * 4);
+  w.tile_16 = take((E + 1) * 4);
+  w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
+  w.queue = take((size_t)bwd_queue_ints(d) * 4);
+  w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
+  w.act = take((d.oft ? R : T) * H * 2);
+  w.gact = take(T * H * 2);
+  w.ab = take(R * 2 * I * 4);
+  w.dab = take(R * 2 * I * 2);
+  w.gpart = take(R * (I / 256) * 4);
+  w.dxt = take(R * H * 4);
+  w.dxr = take(d.oft ? R * H * 4 : 0);
+  w.total = o;
+  return w;
+}
 }  // namespace
 
 extern "C" {
+
+size_t moe_backward_weights_bytes(const moe_layer* layer) {
+  Dims d;
+  if (check_backward(layer, &d) != MOE_OK) return 0;
+  return bwd_weights_layout(d).total;
+}
+
+moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweights* qw, const moe_scales* sc,
+                                        void* bwd_weights, size_t bwd_bytes, void* stream) {
+  Dims d;
+  moe_status st = check_backward(layer, &d);
+  if (st != MOE_OK) return st;
+  if (qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {qw->w13, qw->w2, sc->s13, sc->s2, bwd_weights};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  const BwdWeights b = bwd_weights_layout(d);
+  if (bwd_bytes < b.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(bwd_weights);
+  launch_repack_int4(static_cast<const uint8_t*>(qw->w13), static_cast<const uint16_t*>(sc->s13), d.E, 2 * d.I, d.H,
+                     reinterpret_cast<uint8_t*>(base + b.w13t), reinterpret_cast<uint16_t*>(base + b.s13), s);
+  launch_repack_int4(static_cast<const uint8_t*>(qw->w2), static_cast<const uint16_t*>(sc->s2), d.E, d.H, d.I,
+                     reinterpret_cast<uint8_t*>(base + b.w2t), reinterpret_cast<uint16_t*>(base + b.s2), s);
+  return launch_status();
+}
+
+size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
+  Dims d;
+  if (check_backward(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
+  return bwd_layout(d).total;
+}
+
+moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
+                               const moe_qweights* qw, const moe_scales* sc, const void* bwd_weights,
+                               const void* adapter_bf16, const void* d_out_bf16, int32_t chunk_experts,
+                               void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Dims d;
+  moe_status st = check_backward(layer, &d);
+  if (st != MOE_OK) return st;
+  if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if ((adapter_bf16 != nullptr) != d.oft || (d_adapter != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.T == 0) return MOE_OK;
+  const void* ptrs[] = {x_bf16, logits, qw->w13, qw->w2, sc->s13, sc->s2, bwd_weights, d_out_bf16, d_x_bf16,
+                        d_logits, ws};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.oft && (!aligned16(adapter_bf16) || !aligned16(d_adapter) || (layer->adapter_expert_stride % 8) != 0))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const BwdLayout wl = bwd_layout(d);
+  if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const BwdWeights bw = bwd_weights_layout(d);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  int32_t* ids = I32(wl.ids);
+  float* wts = reinterpret_cast<float*>(base + wl.wts);
+  int32_t* offsets = I32(wl.offsets);
+  int32_t* sorted_rows = I32(wl.sorted_rows);
+  int32_t* row_of = I32(wl.row_of);
+  int32_t* active = I32(wl.active);
+  int32_t* num_active = I32(wl.num_active);
+  int32_t* tile_a = I32(wl.tile_a);
+  int32_t* tile_16 = I32(wl.tile_16);
+  int32_t* tiles = I32(wl.tiles);
+  int32_t* queue = I32(wl.queue);
+  int32_t* hist = I32(wl.hist);
+  uint16_t* act = reinterpret_cast<uint16_t*>(base + wl.act);
+  uint16_t* gact = reinterpret_cast<uint16_t*>(base + wl.gact);
+  float* ab = reinterpret_cast<float*>(base + wl.ab);
+  uint16_t* dab = reinterpret_cast<uint16_t*>(base + wl.dab);
+  float* gpart = reinterpret_cast<float*>(base + wl.gpart);
+  float* dxt = reinterpret_cast<float*>(base + wl.dxt);
+  float* dxr = reinterpret_cast<float*>(base + wl.dxr);
+  const char* bwb = static_cast<const char*>(bwd_weights);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const int bm = choose_bm(d);
+
+  launch_route(logits, d.T, d.E, d.k, ids, wts, s);
+  launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
+                 tiles, queue, bwd_queue_ints(d), s);
+  if (d.oft)
+    launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
+                   sorted_rows, active, num_active, tile_16, d.E, act, s);
+  else
+    launch_act_f16(x, d.T, d.H, act, s);
+  launch_act_f16(static_cast<const uint16_t*>(d_out_bf16), d.T, d.H, gact, s);
+  if (d.oft) launch_zero_f32(d_adapter, (int64_t)d.E * layer->adapter_expert_stride, s);
+
+  GemmArgs r1{}, none{}, bh{}, bx{};
+  const int64_t n13 = (int64_t)2 * d.I * d.H, n2 = (int64_t)d.H * d.I;
+  // recompute of GEMM1 (gate/up pre-activations)
+  r1.a = act;
+  r1.a_per_token = d.oft ? 0 : 1;
+  r1.w = static_cast<const uint8_t*>(qw->w13);
+  r1.w_scale = sc->s13;
+  r1.w_expert_bytes = n13 / 2;
+  r1.ws_expert_elems = n13 / 32;
+  r1.N = 2 * d.I;
+  r1.K = d.H;
+  r1.inter = d.I;
+  r1.out = ab;
+  r1.save_ab = 1;
+  // u = dout W2 with the SwiGLU backward in the epilogue
+  bh.a = gact;
+  bh.a_per_token = 1;
+  bh.w = reinterpret_cast<const uint8_t*>(bwb + bw.w2t);
+  bh.w_scale = bwb + bw.s2;
+  bh.w_expert_bytes = n2 / 2;
+  bh.ws_expert_elems = n2 / 32;
+  bh.N = d.I;
+  bh.K = d.H;
+  bh.inter = d.I;
+  bh.out = dab;
+  bh.ab = ab;
+  bh.topk_w = wts;
+  bh.gpart = gpart;
+  // dx' = [da | db] W13
+  bx.a = dab;
+  bx.a_per_token = 0;
+  bx.w = reinterpret_cast<const uint8_t*>(bwb + bw.w13t);
+  bx.w_scale = bwb + bw.s13;
+  bx.w_expert_bytes = n13 / 2;
+  bx.ws_expert_elems = n13 / 32;
+  bx.N = d.H;
+  bx.K = 2 * d.I;
+  bx.inter = d.I;
+  bx.out = dxt;
+  for (GemmArgs* g : {&r1, &none, &bh, &bx}) {
+    g->offsets = offsets;
+    g->sorted_rows = sorted_rows;
+    g->active = active;
+    g->num_active = num_active;
+    g->tile_start = tile_a;
+    g->tiles = tiles;
+    g->top_k = d.k;
+    g->chunk_experts = chunk_experts;
+    g->nb_fastest = 1;
+  }
+  none.chunk = -1;
+  const int gridr = gemm_grid(d, bm, chunk_experts, d.I / 128);
+  const int gh = gemm_grid(d, bm, chunk_experts, d.I / 256), gx = gemm_grid(d, bm, chunk_experts, d.H / 256);
+  const int gridb = gh > gx ? gh : gx;
+  const int nchunks = (d.E + chunk_experts - 1) / chunk_experts;
+  // launch pair c: recompute chunk c, then chunk c's dh items with chunk c-1's dx' items
+  for (int c = 0; c <= nchunks; ++c) {
+    if (c < nchunks) {
+      r1.chunk = c;
+      launch_gemm_int4_pair(r1, none, queue + 16 * c, bm, gridr, s);
+    }
+    bh.chunk = c < nchunks ? c : -1;
+    bx.chunk = c - 1;
+    launch_gemm_int4_bwd_pair(bh, bx, queue + 16 * c + 8, bm, gridb, s);
+  }
+  const float* dx_rows = dxt;
+  if (d.oft) {
+    launch_oft_bwd(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, dxt, d.H, d.k,
+                   offsets, sorted_rows, active, num_active, d.E, dxr, d_adapter, s);
+    dx_rows = dxr;
+  }
+  launch_unpermute_sum(dx_rows, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(d_x_bf16), s);
+  launch_router_grad(ids, wts, row_of, gpart, d.I / 256, d.T, d.k, d.E, d_logits, s);
+  return launch_status();
+}
 
 moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w, const int32_t* row_of,
                        void* out_bf16, void* stream) {
