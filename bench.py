@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialized", action="store_true",
                     help="time the materialized-chunk scheme (per-chunk BF16 weight copy + BF16 GEMMs) instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the frozen-base backward (d_x, d_logits, d_adapter; INT4 layers) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the expert-parallel split "
@@ -102,13 +104,26 @@ def main():
     oft = dev(li.oft, True) if li.oft is not None else None
     layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
                                tile_rows=args.tile_rows)
-    mat = args.materialized
-    ws_bytes = (binding.materialized_workspace_bytes if mat else binding.workspace_bytes)(layer, cfg.chunk)
+    mat, bwd = args.materialized, args.backward
+    if bwd:
+        ws_bytes = binding.backward_workspace_bytes(layer, cfg.chunk)
+        bw = binding.prepare_backward_weights(layer, w13, w2, s13, s2)
+        rng = np.random.default_rng(12345)
+        d_out_bits = synth._to_bf16_bits(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32))
+        d_out = dev(d_out_bits, True)
+        d_x = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        d_lg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+        d_ad = torch.empty(oft.shape, dtype=torch.float32, device="cuda") if oft is not None else None
+    else:
+        ws_bytes = (binding.materialized_workspace_bytes if mat else binding.workspace_bytes)(layer, cfg.chunk)
     ws = binding.alloc_workspace(ws_bytes)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
 
     def step():
-        if mat:
+        if bwd:
+            binding.expert_backward(layer, x, logits, w13, w2, s13, s2, bw, d_out, adapter=oft,
+                                    chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad)
+        elif mat:
             binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
                                                 chunk_experts=cfg.chunk, out=out, ws=ws)
         else:
@@ -133,7 +148,11 @@ def main():
     stage_ms = {s: 0.0 for s in binding.STAGES}
     stage_n = {s: 0 for s in binding.STAGES}
     for _ in range(args.steps):
-        if mat:
+        if bwd:
+            st = binding.expert_backward(layer, x, logits, w13, w2, s13, s2, bw, d_out, adapter=oft,
+                                         chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad,
+                                         timed=True)[3]
+        elif mat:
             _, st = binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
                                                         chunk_experts=cfg.chunk, out=out, ws=ws, timed=True)
         else:
@@ -153,7 +172,28 @@ def main():
     peak = MFMA_PEAK[cfg.fmt]
     fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4", 4: "fp8"}[cfg.fmt]
     bm = binding.tile_rows(layer)
-    if mat:
+    if bwd:
+        # recompute (forward INT4 GEMM1) and the backward GEMM pair: 4 + 6 R H I FLOPs;
+        # the dominant one by event time is reported
+        R = cfg.T * cfg.k
+        w13b = weight_bytes_per_expert(cfg.fmt, 2 * cfg.I, cfg.H)
+        w2b = weight_bytes_per_expert(cfg.fmt, cfg.H, cfg.I)
+        peak = MFMA_PEAK[1]
+        if stage_ms["gemm1"] > stage_ms["gemm2"]:
+            dom, launches = "gemm1", stage_n["gemm1"]
+            f_dom = 4.0 * R * cfg.H * cfg.I
+            b_dom = acc["active"] * w13b + (R if cfg.oft else cfg.T) * cfg.H * 2 + R * 2 * cfg.I * 4
+            kname = f"k_gemm_int4<{bm}>"
+        else:
+            dom, launches = "gemm2", stage_n["gemm2"]
+            f_dom = 6.0 * R * cfg.H * cfg.I
+            # transposed weights, d_out rows, [da|db] written and read, pre-activations read, dx' written
+            b_dom = (acc["active"] * (w13b + w2b) + cfg.T * cfg.H * 2 + 2 * R * 2 * cfg.I * 2 + R * 2 * cfg.I * 4
+                     + R * cfg.H * 4)
+            kname = f"k_gemm_int4_bwd<{bm}>"
+        launch_ms = stage_ms[dom] / max(launches, 1)
+        acc["flops"] = 10.0 * R * cfg.H * cfg.I + (4.0 * R * cfg.H * 32 if cfg.oft else 0.0)
+    elif mat:
         # the BF16 copy: packed weights read and 2 bytes per weight written by the
         # dequant kernel, then read back by the BF16 GEMMs with bf16 activations
         nw = acc["active"] * 3 * cfg.H * cfg.I
@@ -194,7 +234,8 @@ def main():
     # valid only while the kernel source is unchanged
     from precision_moe_expert_amd import profiling
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{fmt_name}_{cfg.name}_traffic.txt"))
-    roof["traffic"] = tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname and not mat else None
+    roof["traffic"] = (tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname and not mat and not bwd
+                       else None)
     roof["launch_ms"] = launch_ms
     roof["algorithmic_bytes_per_launch"] = b_launch
     roof["algorithmic_flops_per_launch"] = f_launch
@@ -210,12 +251,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16_from_" + DTYPE[cfg.fmt] if mat else DTYPE[cfg.fmt],
+        "dtype": "bf16_from_" + DTYPE[cfg.fmt] if mat else ("fp16_backward_" + DTYPE[cfg.fmt] if bwd
+                                                             else DTYPE[cfg.fmt]),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE expert layer", "tokens": cfg.T, "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I, "weight_format": synth.FMT_NAMES[cfg.fmt],
                    "chunk_experts": cfg.chunk, "tile_rows": args.tile_rows or "auto", "oft_adapter": cfg.oft,
-                   "active_experts": acc["active"], "mode": "materialized_bf16_copy" if mat else "fused"},
+                   "active_experts": acc["active"],
+                   "mode": "materialized_bf16_copy" if mat else ("frozen_base_backward" if bwd else "fused")},
         "tflops": acc["flops"] / sec / 1e12,
         "pct_mfma_peak": 100.0 * acc["flops"] / sec / peak,
         "hbm_gbps_algorithmic": acc["bytes"] / sec / 1e9,
@@ -234,8 +277,13 @@ def main():
         toks = np.arange(n, dtype=np.int32)
         # repeat short samples until about 10 s of oracle work has been timed
         passes, c0 = 0, time.perf_counter()
+        if bwd:
+            d_out_f32 = (d_out_bits[toks].astype(np.uint32) << 16).view(np.float32)
         while passes == 0 or (time.perf_counter() - c0 < 10.0 and passes < 8):
-            oracle.forward_inputs(li, tokens=toks, materialized=mat)
+            if bwd:
+                oracle.backward_inputs(li, d_out_f32, tokens=toks)
+            else:
+                oracle.forward_inputs(li, tokens=toks, materialized=mat)
             passes += 1
         csec = time.perf_counter() - c0
         result["cpu_baseline"] = {"value": n * passes / csec, "unit": "tokens/s", "cores": oracle.num_threads(),

@@ -252,12 +252,19 @@ size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_expert
  * to fp16, so their magnitudes must stay below 65504), accumulation fp32.
  * bwd_weights: from moe_prepare_backward_weights for the same weights.
  * Unsupported layers return MOE_ERR_UNSUPPORTED; the rest as moe_expert_forward.
- * Stream-ordered, no host synchronisation, nothing allocated. */
+ * Stream-ordered, no host synchronisation, nothing allocated, unless
+ * stage_ms and stage_launches (HOST arrays of MOE_NUM_STAGES, both or
+ * neither) are given: then per-stage event times are filled as by
+ * moe_expert_forward_timed and the call synchronises the stream.  Stages:
+ * ROUTE, PERMUTE; ACT = GEMM inputs (x or x R_e, d_out as fp16); GEMM1 =
+ * gate/up recompute launches; GEMM2 = backward GEMM launches (chunk c's
+ * u items with chunk c-1's dx' items); COMBINE = adapter backward,
+ * un-permute sum and router gradient. */
 moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
                                const moe_qweights* qweights, const moe_scales* scales, const void* bwd_weights,
                                const void* adapter_bf16, const void* d_out_bf16, int32_t chunk_experts,
                                void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
-                               void* stream);
+                               void* stream, float* stage_ms, int32_t* stage_launches);
 
 /* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
  * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:

@@ -101,7 +101,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales), ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                          ctypes.c_void_p]
+                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_int32)]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -250,8 +251,9 @@ def backward_workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
 
 
 def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d_out, adapter=None,
-                    chunk_experts: int = 1, ws=None, d_x=None, d_logits=None, d_adapter=None):
-    """moe_expert_backward -> (d_x [T][H] bf16, d_logits [T][E] fp32, d_adapter fp32 or None)."""
+                    chunk_experts: int = 1, ws=None, d_x=None, d_logits=None, d_adapter=None, timed: bool = False):
+    """moe_expert_backward -> (d_x [T][H] bf16, d_logits [T][E] fp32, d_adapter fp32 or None)
+    (+ {stage: (ms, launches)} if timed)."""
     T, H, E = layer.num_tokens, layer.hidden, layer.num_experts
     dev = x.device
     if d_x is None:
@@ -264,10 +266,14 @@ def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d
         ws = alloc_workspace(backward_workspace_bytes(layer, chunk_experts), dev)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
     sc = MoeScales(_ptr(s13), _ptr(s2))
+    ms = (ctypes.c_float * len(STAGES))() if timed else None
+    n = (ctypes.c_int32 * len(STAGES))() if timed else None
     _check(lib().moe_expert_backward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
                                      _ptr(bwd_weights), _ptr(adapter), _ptr(d_out), int(chunk_experts), _ptr(d_x),
-                                     _ptr(d_logits), _ptr(d_adapter), _ptr(ws), ws.numel(), _stream()),
+                                     _ptr(d_logits), _ptr(d_adapter), _ptr(ws), ws.numel(), _stream(), ms, n),
            "moe_expert_backward")
+    if timed:
+        return d_x, d_logits, d_adapter, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
     return d_x, d_logits, d_adapter
 
 

@@ -663,11 +663,13 @@ size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_expert
   return bwd_layout(d).total;
 }
 
-moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
-                               const moe_qweights* qw, const moe_scales* sc, const void* bwd_weights,
-                               const void* adapter_bf16, const void* d_out_bf16, int32_t chunk_experts,
-                               void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float* logits, const moe_qweights* qw,
+                         const moe_scales* sc, const void* bwd_weights, const void* adapter_bf16,
+                         const void* d_out_bf16, int32_t chunk_experts, void* d_x_bf16, float* d_logits,
+                         float* d_adapter, void* ws, size_t ws_bytes, void* stream, StageTimer* tm) {
   Dims d;
   moe_status st = check_backward(layer, &d);
   if (st != MOE_OK) return st;
@@ -710,9 +712,12 @@ moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   const int bm = choose_bm(d);
 
-  launch_route(logits, d.T, d.E, d.k, ids, wts, s);
-  launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
-                 tiles, queue, bwd_queue_ints(d), s);
+  { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
+  { Scope sc_(tm, MOE_STAGE_PERMUTE);
+    launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
+                   tiles, queue, bwd_queue_ints(d), s); }
+  {
+  Scope sc_(tm, MOE_STAGE_ACT);
   if (d.oft)
     launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
                    sorted_rows, active, num_active, tile_16, d.E, act, s);
@@ -720,6 +725,7 @@ moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const
     launch_act_f16(x, d.T, d.H, act, s);
   launch_act_f16(static_cast<const uint16_t*>(d_out_bf16), d.T, d.H, gact, s);
   if (d.oft) launch_zero_f32(d_adapter, (int64_t)d.E * layer->adapter_expert_stride, s);
+  }
 
   GemmArgs r1{}, none{}, bh{}, bx{};
   const int64_t n13 = (int64_t)2 * d.I * d.H, n2 = (int64_t)d.H * d.I;
@@ -780,12 +786,16 @@ moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const
   for (int c = 0; c <= nchunks; ++c) {
     if (c < nchunks) {
       r1.chunk = c;
+      Scope sc_(tm, MOE_STAGE_GEMM1);
       launch_gemm_int4_pair(r1, none, queue + 16 * c, bm, gridr, s);
     }
     bh.chunk = c < nchunks ? c : -1;
     bx.chunk = c - 1;
+    Scope sc_(tm, MOE_STAGE_GEMM2);
     launch_gemm_int4_bwd_pair(bh, bx, queue + 16 * c + 8, bm, gridb, s);
   }
+  {
+  Scope sc_(tm, MOE_STAGE_COMBINE);
   const float* dx_rows = dxt;
   if (d.oft) {
     launch_oft_bwd(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, dxt, d.H, d.k,
@@ -794,7 +804,31 @@ moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const
   }
   launch_unpermute_sum(dx_rows, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(d_x_bf16), s);
   launch_router_grad(ids, wts, row_of, gpart, d.I / 256, d.T, d.k, d.E, d_logits, s);
+  }
   return launch_status();
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
+                               const moe_qweights* qw, const moe_scales* sc, const void* bwd_weights,
+                               const void* adapter_bf16, const void* d_out_bf16, int32_t chunk_experts,
+                               void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
+                               void* stream, float* stage_ms, int32_t* stage_launches) {
+  if ((stage_ms == nullptr) != (stage_launches == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage_ms == nullptr)
+    return backward_impl(layer, x_bf16, logits, qw, sc, bwd_weights, adapter_bf16, d_out_bf16, chunk_experts,
+                         d_x_bf16, d_logits, d_adapter, ws, ws_bytes, stream, nullptr);
+  StageTimer* tm = new StageTimer();
+  tm->s = static_cast<hipStream_t>(stream);
+  moe_status st = backward_impl(layer, x_bf16, logits, qw, sc, bwd_weights, adapter_bf16, d_out_bf16,
+                                chunk_experts, d_x_bf16, d_logits, d_adapter, ws, ws_bytes, stream, tm);
+  tm->finish(stage_ms, stage_launches);
+  const bool ok = tm->ok;
+  delete tm;
+  if (st == MOE_OK && !ok) st = MOE_ERR_DEVICE;
+  return st;
 }
 
 moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w, const int32_t* row_of,
