@@ -233,9 +233,9 @@ def main():
     # HBM bytes per launch measured by rocprofv3 counters (copy-calibrated),
     # valid only while the kernel source is unchanged
     from precision_moe_expert_amd import profiling
-    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{fmt_name}_{cfg.name}_traffic.txt"))
-    roof["traffic"] = (tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname and not mat and not bwd
-                       else None)
+    kfam = kname.split("<")[0].replace("k_gemm_", "")
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"gemm_{kfam}_{cfg.name}_traffic.txt"))
+    roof["traffic"] = tr["hbm_bytes_per_dispatch"] if tr and tr["kernel"] == kname and not mat else None
     roof["launch_ms"] = launch_ms
     roof["algorithmic_bytes_per_launch"] = b_launch
     roof["algorithmic_flops_per_launch"] = f_launch
