@@ -55,7 +55,9 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
   const int wc = wave & 3, wr = wave >> 2;
   const int ln = lane & 15, lg = lane >> 4;
   const int mb0 = wr * MTW;                       // first row block of this wave
-  const int nmb = min(MTW, MT - mb0);             // row blocks of this wave (wave-uniform)
+  // row blocks of this wave (wave-uniform); compile-time whenever the tile
+  // splits evenly, so the row-block loop unrolls without branches
+  const int nmb = (MT % 2 == 0) ? MTW : min(MTW, MT - mb0);
   const int K = p.K, KT = K / 128;
   const char* Abase = static_cast<const char*>(p.a);
   const char* ASbase = static_cast<const char*>(p.a_scale);
