@@ -213,11 +213,12 @@ def forward_inputs(li, chunk_experts=None, tokens=None, **kw):
 
 
 def backward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, dout, oft=None, chunk_experts=1, tokens=None,
-             adapter_expert_stride=None):
+             adapter_expert_stride=None, return_g=False):
     """Frozen-base backward of the oracle forward.  dout: [n][H] fp32 gradient of
     the requested tokens' outputs (all tokens if tokens is None).
     Returns (dx [n][H] fp32, dlogits [n][E] fp32, doft or None), doft float64
-    shaped like the adapter, summed over the requested tokens' rows."""
+    shaped like the adapter, summed over the requested tokens' rows; with
+    return_g also g [n][k] float64 (g_tj = <dout_t, y_tj>)."""
     stride = (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride
     layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0, stride, 0)
     tok = None if tokens is None else _c(tokens, np.int32)
@@ -228,22 +229,24 @@ def backward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, dout, oft=None, ch
     doft = None
     if oft is not None:
         doft = np.zeros((E * stride if stride else H * 32,), np.float64)
+    g = np.empty((n, k), np.float64) if return_g else None
     rc = lib().oracle_backward(ctypes.byref(layer), _p(_c(x, np.uint16)), _p(_c(logits, np.float32)),
                                _p(_c(w13, np.uint8)), _p(_c(w2, np.uint8)), _p(np.ascontiguousarray(s13)),
                                _p(np.ascontiguousarray(s2)), _p(None if oft is None else _c(oft, np.uint16)),
-                               _p(dout), int(chunk_experts), _p(tok), int(n), _p(dx), _p(dl), _p(doft))
+                               _p(dout), int(chunk_experts), _p(tok), int(n), _p(dx), _p(dl), _p(doft), _p(g))
     if rc != 0:
         raise ValueError("oracle_backward: invalid arguments")
     if doft is not None:
         doft = doft.reshape((E, H // 32, 32, 32) if stride else (H // 32, 32, 32))
-    return dx, dl, doft
+    return (dx, dl, doft, g) if return_g else (dx, dl, doft)
 
 
-def backward_inputs(li, dout, chunk_experts=None, tokens=None):
+def backward_inputs(li, dout, chunk_experts=None, tokens=None, return_g=False):
     """oracle backward on a synth.LayerInputs bundle."""
     c = li.cfg
     return backward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2, dout,
-                    oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts, tokens=tokens)
+                    oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts, tokens=tokens,
+                    return_g=return_g)
 
 
 def combine(y_perm_bf16: np.ndarray, w: np.ndarray, row_of: np.ndarray) -> np.ndarray:

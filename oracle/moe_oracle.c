@@ -603,11 +603,12 @@ static void expert_row_backward(const oracle_layer* L, const uint16_t* xrow, con
  * Outputs for the requested tokens: dx [n][H] fp32, dlogits [n][E] fp32;
  * doft (optional, with an adapter): fp64, shaped like the adapter (per-expert
  * blocks at adapter_expert_stride, or one shared block set), accumulated over
- * the rows of the requested tokens only (zeroed first). */
+ * the rows of the requested tokens only (zeroed first); g (optional): [n][k]
+ * fp64, g_tj = <dout_t, y_tj> per selected slot. */
 int oracle_backward(const oracle_layer* L, const uint16_t* x, const float* logits, const uint8_t* w13,
                     const uint8_t* w2, const void* s13, const void* s2, const uint16_t* oft, const float* dout,
                     int chunk_experts, const int32_t* tokens, int n_tokens, float* dx_out, float* dlogits_out,
-                    double* doft_out) {
+                    double* doft_out, double* g_out) {
   const int T = L->T, H = L->H, I = L->I, E = L->E, k = L->k, fmt = L->fmt;
   const int64_t R = (int64_t)T * k;
   int32_t *ids, *counts, *offsets, *sorted_rows, *row_of, *active, *slot, num_active = 0;
@@ -693,6 +694,8 @@ int oracle_backward(const oracle_layer* L, const uint16_t* x, const float* logit
     double mean = 0.0;
     for (int j = 0; j < k; ++j) mean += (double)wts[(int64_t)t * k + j] * gbuf[(int64_t)i * k + j];
     for (int e = 0; e < E; ++e) dlogits_out[(int64_t)i * E + e] = 0.0f;
+    if (g_out)
+      for (int j = 0; j < k; ++j) g_out[(int64_t)i * k + j] = gbuf[(int64_t)i * k + j];
     for (int j = 0; j < k; ++j)
       dlogits_out[(int64_t)i * E + ids[(int64_t)t * k + j]] =
           (float)((double)wts[(int64_t)t * k + j] * (gbuf[(int64_t)i * k + j] - mean));

@@ -27,6 +27,16 @@ MOE_DEV uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// E4M3FN byte -> fp32 (exact; the NaN code is not expected in weights).
+MOE_DEV float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0) {  // subnormal: m * 2^-9
+    const float v = (float)m * 0x1p-9f;
+    return s ? -v : v;
+  }
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
 MOE_DEV uint32_t pack_f16x2(float a, float b) {
   _Float16 ha = (_Float16)a, hb = (_Float16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);

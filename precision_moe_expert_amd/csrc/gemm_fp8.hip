@@ -244,6 +244,19 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
   // Epilogue: results go through LDS (the stage buffers are free once every
   // wave has passed the barrier below) so that global stores are 16 B per lane.
   if (G1) {
+    if (p.ab_out != nullptr) {
+      // backward recompute: the gate and up pre-activations in fp32 as well
+#pragma unroll
+      for (int m = 0; m < MTW; ++m)
+        if (m < nmb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = (mb0 + m) * 16 + lg * 4 + i;
+            if (row < tl.nrows)
+#pragma unroll
+              for (int n = 0; n < 4; ++n) p.ab_out[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = acc[m][n][i];
+          }
+    }
     constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
     float hv[MTW][4][2];
 #pragma unroll

@@ -168,6 +168,18 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   // Epilogue: results go through LDS (the stage buffers are free once every
   // wave has passed the barrier below) so that global stores are 16 B per lane.
   if (G1) {
+    if (p.ab_out != nullptr) {
+      // backward recompute: the gate and up pre-activations in fp32 as well
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m * 16 + lg * 4 + i;
+          if (row < tl.nrows)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) p.ab_out[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = acc[m][n][i];
+        }
+    }
     constexpr int HS = 144;  // staged row stride (bytes) of the 128 h codes
     uint8_t* He = static_cast<uint8_t*>(p.out_scale);
     lds_barrier();

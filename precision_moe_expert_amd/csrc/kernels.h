@@ -46,6 +46,13 @@ struct GemmArgs {
   const float* ab;
   const float* topk_w;
   float* gpart;
+  // backward (FP8, MXFP4): GEMM1 also writes the fp32 pre-activations to
+  // ab_out next to its usual h; the dh GEMM reads that quantized h (hq codes,
+  // hsc scales with hsc_stride bytes per row) for the router term <u, Q(h)>.
+  float* ab_out;
+  const uint8_t* hq;
+  const void* hsc;
+  int hsc_stride;
 };
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
@@ -87,15 +94,18 @@ void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const ui
 void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
 
-// Frozen-base backward (INT4).  Transposed weight copy: W [E][N][K] nibbles ->
-// W^T [E][K][N]; group scales s [E][K/32][N] (forward orientation) -> fp16
-// pairs per 8 consecutive values of the last dimension (see the kernel).
-void launch_repack_int4(const uint8_t* w, const uint16_t* s, int E, int N, int K, uint8_t* wt, uint16_t* st,
-                        hipStream_t stream);
+// Frozen-base backward.  Transposed weight copy of W [E][N][K]:
+//   INT4 / MXFP4: nibbles W^T [E][K][N]; group scales [E][K/32][N] (forward
+//     orientation) -> fp16 values regrouped per 8 consecutive entries of the
+//     last dimension (INT4: bf16 scales, odd pairs pre-divided by 16; MXFP4:
+//     E8M0 -> 2^(e-127));
+//   FP8: bytes W^T [E][K][N]; block scales [E][N/128][K/128] -> [E][K/128][N/128].
+void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, int K, uint8_t* wt, void* st,
+                       hipStream_t stream);
 // One launch: chunk g1.chunk's dh items (SwiGLU backward epilogue) and chunk
-// g2.chunk's dx' items, both reading the transposed copy.
-void launch_gemm_int4_bwd_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
-                               hipStream_t s);
+// g2.chunk's dx' items, both reading the transposed copy; fmt = kernel family.
+void launch_gemm_bwd_pair(int fmt, const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                          hipStream_t s);
 void launch_oft_bwd(const uint16_t* x, const uint16_t* R, int64_t r_stride, const float* dxt, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
                     int E, float* dx, float* dR, hipStream_t s);

@@ -20,16 +20,6 @@ namespace moe {
 
 // ------------------------------------------------------------------ dequant
 
-// E4M3FN byte -> fp32 (exact; the NaN code is not expected in weights).
-MOE_DEV float e4m3_to_f32(uint32_t b) {
-  const uint32_t s = (b & 0x80u) << 24, e = (b >> 3) & 15u, m = b & 7u;
-  if (e == 0) {  // subnormal: m * 2^-9
-    const float v = (float)m * 0x1p-9f;
-    return s ? -v : v;
-  }
-  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
-}
-
 // E2M1 nibble -> fp32 (exact): 0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign bit 3.
 MOE_DEV float e2m1_to_f32(uint32_t nib) {
   const uint32_t s = (nib & 8u) << 28, e = (nib >> 1) & 3u, m = nib & 1u;

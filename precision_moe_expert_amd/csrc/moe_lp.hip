@@ -567,14 +567,17 @@ struct BwdWeights {
   size_t w13t, w2t, s13, s2, total;
 };
 
+// INT4 / MXFP4: nibbles + fp16 scales (2 bytes per 32 weights); FP8: bytes +
+// fp32 block scales (the forward sizes).
 BwdWeights bwd_weights_layout(const Dims& d) {
   BwdWeights b{};
   const size_t H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+  const bool fp8 = d.fmt == MOE_W_FP8_E4M3_B128;
   size_t o = 0;
-  b.w13t = o; o = align_up(o + E * H * 2 * I / 2);
-  b.w2t = o;  o = align_up(o + E * I * H / 2);
-  b.s13 = o;  o = align_up(o + E * (H / 32) * 2 * I * 2);
-  b.s2 = o;   o = align_up(o + E * (I / 32) * H * 2);
+  b.w13t = o; o = align_up(o + E * H * 2 * I / (fp8 ? 1 : 2));
+  b.w2t = o;  o = align_up(o + E * I * H / (fp8 ? 1 : 2));
+  b.s13 = o;  o = align_up(o + (fp8 ? E * (H / 128) * (2 * I / 128) * 4 : E * (H / 32) * 2 * I * 2));
+  b.s2 = o;   o = align_up(o + (fp8 ? E * (I / 128) * (H / 128) * 4 : E * (I / 32) * H * 2));
   b.total = o;
   return b;
 }
@@ -582,15 +585,23 @@ BwdWeights bwd_weights_layout(const Dims& d) {
 moe_status check_backward(const moe_layer* L, Dims* d) {
   moe_status st = check_layer(L, d);
   if (st != MOE_OK) return st;
-  if (d->fmt != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
+  if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
   if (d->oft && L->adapter_expert_stride == 0) return MOE_ERR_UNSUPPORTED;  // one shared R
   return MOE_OK;
 }
 
+// The backward's tile height: the forward's, at most 128 rows for FP8 (whose
+// 192-row stage ring does not fit the LDS).
+int bwd_bm(const Dims& d) {
+  const int bm = choose_bm(d);
+  return (d.fmt == MOE_W_FP8_E4M3_B128 && bm > 128) ? 128 : bm;
+}
+
 struct BwdLayout {
   size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
-  size_t act, gact, ab, dab, gpart, dxt, dxr;
+  size_t act, act_scale, h, h_scale, gact, ab, dab, gpart, dxt, dxr;
   size_t total;
 };
 
@@ -617,7 +628,18 @@ BwdLayout bwd_layout(const Dims& d) {
   w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
   w.queue = take((size_t)bwd_queue_ints(d) * 4);
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
-  w.act = take((d.oft ? R : T) * H * 2);
+  if (d.fmt == MOE_W_INT4_G32_BF16) {
+    w.act = take((d.oft ? R : T) * H * 2);
+    w.act_scale = take(0);
+    w.h = take(0);
+    w.h_scale = take(0);
+  } else {
+    // the forward's GEMM1 input and its quantized h, as the recompute writes them
+    w.act = take(T * H);
+    w.act_scale = take(T * scale_row_bytes((int)H));
+    w.h = take(R * I);
+    w.h_scale = take(R * scale_row_bytes((int)I));
+  }
   w.gact = take(T * H * 2);
   w.ab = take(R * 2 * I * 4);
   w.dab = take(R * 2 * I * 2);
@@ -650,10 +672,10 @@ moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweigh
   if (bwd_bytes < b.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(bwd_weights);
-  launch_repack_int4(static_cast<const uint8_t*>(qw->w13), static_cast<const uint16_t*>(sc->s13), d.E, 2 * d.I, d.H,
-                     reinterpret_cast<uint8_t*>(base + b.w13t), reinterpret_cast<uint16_t*>(base + b.s13), s);
-  launch_repack_int4(static_cast<const uint8_t*>(qw->w2), static_cast<const uint16_t*>(sc->s2), d.E, d.H, d.I,
-                     reinterpret_cast<uint8_t*>(base + b.w2t), reinterpret_cast<uint16_t*>(base + b.s2), s);
+  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13, d.E, 2 * d.I, d.H,
+                    reinterpret_cast<uint8_t*>(base + b.w13t), base + b.s13, s);
+  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w2), sc->s2, d.E, d.H, d.I,
+                    reinterpret_cast<uint8_t*>(base + b.w2t), base + b.s2, s);
   return launch_status();
 }
 
@@ -701,7 +723,10 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   int32_t* tiles = I32(wl.tiles);
   int32_t* queue = I32(wl.queue);
   int32_t* hist = I32(wl.hist);
-  uint16_t* act = reinterpret_cast<uint16_t*>(base + wl.act);
+  void* act = base + wl.act;
+  void* act_scale = base + wl.act_scale;
+  uint8_t* hq = reinterpret_cast<uint8_t*>(base + wl.h);
+  void* h_scale = base + wl.h_scale;
   uint16_t* gact = reinterpret_cast<uint16_t*>(base + wl.gact);
   float* ab = reinterpret_cast<float*>(base + wl.ab);
   uint16_t* dab = reinterpret_cast<uint16_t*>(base + wl.dab);
@@ -710,7 +735,7 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   float* dxr = reinterpret_cast<float*>(base + wl.dxr);
   const char* bwb = static_cast<const char*>(bwd_weights);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  const int bm = choose_bm(d);
+  const int bm = bwd_bm(d);
 
   { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
   { Scope sc_(tm, MOE_STAGE_PERMUTE);
@@ -718,36 +743,56 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
                    tiles, queue, bwd_queue_ints(d), s); }
   {
   Scope sc_(tm, MOE_STAGE_ACT);
-  if (d.oft)
+  // the forward's GEMM1 input
+  if (d.fmt == MOE_W_FP8_E4M3_B128)
+    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H),
+                   d.pow2, s);
+  else if (d.fmt == MOE_W_MXFP4)
+    launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), scale_row_bytes(d.H),
+                     s);
+  else if (d.oft)
     launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
-                   sorted_rows, active, num_active, tile_16, d.E, act, s);
+                   sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
   else
-    launch_act_f16(x, d.T, d.H, act, s);
+    launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   launch_act_f16(static_cast<const uint16_t*>(d_out_bf16), d.T, d.H, gact, s);
   if (d.oft) launch_zero_f32(d_adapter, (int64_t)d.E * layer->adapter_expert_stride, s);
   }
 
   GemmArgs r1{}, none{}, bh{}, bx{};
   const int64_t n13 = (int64_t)2 * d.I * d.H, n2 = (int64_t)d.H * d.I;
-  // recompute of GEMM1 (gate/up pre-activations)
+  // recompute of GEMM1 (gate/up pre-activations; FP8 / MXFP4 also the quantized h)
   r1.a = act;
   r1.a_per_token = d.oft ? 0 : 1;
   r1.w = static_cast<const uint8_t*>(qw->w13);
   r1.w_scale = sc->s13;
-  r1.w_expert_bytes = n13 / 2;
-  r1.ws_expert_elems = n13 / 32;
   r1.N = 2 * d.I;
   r1.K = d.H;
   r1.inter = d.I;
-  r1.out = ab;
-  r1.save_ab = 1;
+  if (d.fmt == MOE_W_INT4_G32_BF16) {
+    r1.w_expert_bytes = n13 / 2;
+    r1.ws_expert_elems = n13 / 32;
+    r1.out = ab;
+    r1.save_ab = 1;
+  } else {
+    const bool fp8 = d.fmt == MOE_W_FP8_E4M3_B128;
+    r1.w_expert_bytes = fp8 ? n13 : n13 / 2;
+    r1.ws_expert_elems = fp8 ? n13 / (128 * 128) : n13 / 32;
+    r1.a_scale = act_scale;
+    r1.a_scale_stride = scale_row_bytes(d.H);
+    r1.out = hq;
+    r1.out_scale = h_scale;
+    r1.out_scale_stride = scale_row_bytes(d.I);
+    r1.ab_out = ab;
+  }
   // u = dout W2 with the SwiGLU backward in the epilogue
   bh.a = gact;
   bh.a_per_token = 1;
+  const bool fp8 = d.fmt == MOE_W_FP8_E4M3_B128;
   bh.w = reinterpret_cast<const uint8_t*>(bwb + bw.w2t);
   bh.w_scale = bwb + bw.s2;
-  bh.w_expert_bytes = n2 / 2;
-  bh.ws_expert_elems = n2 / 32;
+  bh.w_expert_bytes = fp8 ? n2 : n2 / 2;
+  bh.ws_expert_elems = fp8 ? n2 / (128 * 128) : n2 / 32;
   bh.N = d.I;
   bh.K = d.H;
   bh.inter = d.I;
@@ -755,13 +800,16 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   bh.ab = ab;
   bh.topk_w = wts;
   bh.gpart = gpart;
+  bh.hq = hq;
+  bh.hsc = h_scale;
+  bh.hsc_stride = scale_row_bytes(d.I);
   // dx' = [da | db] W13
   bx.a = dab;
   bx.a_per_token = 0;
   bx.w = reinterpret_cast<const uint8_t*>(bwb + bw.w13t);
   bx.w_scale = bwb + bw.s13;
-  bx.w_expert_bytes = n13 / 2;
-  bx.ws_expert_elems = n13 / 32;
+  bx.w_expert_bytes = fp8 ? n13 : n13 / 2;
+  bx.ws_expert_elems = fp8 ? n13 / (128 * 128) : n13 / 32;
   bx.N = d.H;
   bx.K = 2 * d.I;
   bx.inter = d.I;
@@ -787,12 +835,14 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
     if (c < nchunks) {
       r1.chunk = c;
       Scope sc_(tm, MOE_STAGE_GEMM1);
-      launch_gemm_int4_pair(r1, none, queue + 16 * c, bm, gridr, s);
+      if (d.fmt == MOE_W_INT4_G32_BF16) launch_gemm_int4_pair(r1, none, queue + 16 * c, bm, gridr, s);
+      else if (fp8) (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)(r1, none, queue + 16 * c, bm, gridr, s);
+      else launch_gemm_mxfp4_pair(r1, none, queue + 16 * c, bm, gridr, s);
     }
     bh.chunk = c < nchunks ? c : -1;
     bx.chunk = c - 1;
     Scope sc_(tm, MOE_STAGE_GEMM2);
-    launch_gemm_int4_bwd_pair(bh, bx, queue + 16 * c + 8, bm, gridb, s);
+    launch_gemm_bwd_pair(d.fmt, bh, bx, queue + 16 * c + 8, bm, gridb, s);
   }
   {
   Scope sc_(tm, MOE_STAGE_COMBINE);
