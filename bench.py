@@ -178,19 +178,27 @@ def main():
         R = cfg.T * cfg.k
         w13b = weight_bytes_per_expert(cfg.fmt, 2 * cfg.I, cfg.H)
         w2b = weight_bytes_per_expert(cfg.fmt, cfg.H, cfg.I)
-        peak = MFMA_PEAK[1]
+        fam = {1: 1, 2: 2, 3: 3, 4: 2}[cfg.fmt]
         if stage_ms["gemm1"] > stage_ms["gemm2"]:
+            # the forward GEMM1 kernel of the format (pre-activation recompute)
+            peak = MFMA_PEAK[cfg.fmt]
             dom, launches = "gemm1", stage_n["gemm1"]
             f_dom = 4.0 * R * cfg.H * cfg.I
-            b_dom = acc["active"] * w13b + (R if cfg.oft else cfg.T) * cfg.H * 2 + R * 2 * cfg.I * 4
-            kname = f"k_gemm_int4<{bm}>"
+            b_dom = (acc["active"] * w13b + act_bytes(cfg.fmt, R if cfg.oft else cfg.T, cfg.H) + R * 2 * cfg.I * 4
+                     + (act_bytes(cfg.fmt, R, cfg.I) if cfg.fmt != 1 else 0))
+            if cfg.fmt in (2, 4):
+                kname = f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>"
+            else:
+                kname = f"k_gemm_{fmt_name}<{bm}>"
         else:
+            # the backward GEMMs run on fp16 MFMA for every weight format
+            peak = MFMA_PEAK[1]
             dom, launches = "gemm2", stage_n["gemm2"]
             f_dom = 6.0 * R * cfg.H * cfg.I
             # transposed weights, d_out rows, [da|db] written and read, pre-activations read, dx' written
             b_dom = (acc["active"] * (w13b + w2b) + cfg.T * cfg.H * 2 + 2 * R * 2 * cfg.I * 2 + R * 2 * cfg.I * 4
                      + R * cfg.H * 4)
-            kname = f"k_gemm_int4_bwd<{bm}>"
+            kname = f"k_gemm_bwd<{fam}, {min(bm, 64)}>"
         launch_ms = stage_ms[dom] / max(launches, 1)
         acc["flops"] = 10.0 * R * cfg.H * cfg.I + (4.0 * R * cfg.H * 32 if cfg.oft else 0.0)
     elif mat:

@@ -592,15 +592,18 @@ moe_status check_backward(const moe_layer* L, Dims* d) {
   return MOE_OK;
 }
 
-// The backward's tile height: the forward's, at most 128 rows for FP8 (whose
-// 192-row stage ring does not fit the LDS).
+// Tile heights of the backward: the recompute of GEMM1 uses the forward's;
+// the backward GEMMs at most 64 rows (measured on MI355X: their fp16 operand
+// tiles are twice the forward's FP8 / MXFP8 bytes, and 64-row tiles keep
+// three stages in flight).
 int bwd_bm(const Dims& d) {
   const int bm = choose_bm(d);
-  return (d.fmt == MOE_W_FP8_E4M3_B128 && bm > 128) ? 128 : bm;
+  return bm > 64 ? 64 : bm;
 }
 
 struct BwdLayout {
   size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
+  size_t tile_a_r, tiles_r;  // tiles of the recompute's height
   size_t act, act_scale, h, h_scale, gact, ab, dab, gpart, dxt, dxr;
   size_t total;
 };
@@ -628,6 +631,8 @@ BwdLayout bwd_layout(const Dims& d) {
   w.tiles = take((size_t)max_row_tiles(d.R, d.E) * 16);
   w.queue = take((size_t)bwd_queue_ints(d) * 4);
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
+  w.tile_a_r = take((E + 1) * 4);
+  w.tiles_r = take((size_t)max_row_tiles(d.R, d.E) * 16);
   if (d.fmt == MOE_W_INT4_G32_BF16) {
     w.act = take((d.oft ? R : T) * H * 2);
     w.act_scale = take(0);
@@ -735,10 +740,16 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   float* dxr = reinterpret_cast<float*>(base + wl.dxr);
   const char* bwb = static_cast<const char*>(bwd_weights);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  const int bm = bwd_bm(d);
+  const int bm = bwd_bm(d), bm_r = choose_bm(d);
+  int32_t* tile_a_r = bm_r == bm ? tile_a : I32(wl.tile_a_r);
+  int32_t* tiles_r = bm_r == bm ? tiles : I32(wl.tiles_r);
 
   { Scope sc_(tm, MOE_STAGE_ROUTE); launch_route(logits, d.T, d.E, d.k, ids, wts, s); }
   { Scope sc_(tm, MOE_STAGE_PERMUTE);
+    // second pass (same permutation) for the recompute's tile list when its height differs
+    if (bm_r != bm)
+      launch_permute(ids, (int)d.R, d.E, bm_r, hist, offsets, sorted_rows, row_of, active, num_active, tile_a_r,
+                     tile_16, tiles_r, queue, bwd_queue_ints(d), s);
     launch_permute(ids, (int)d.R, d.E, bm, hist, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16,
                    tiles, queue, bwd_queue_ints(d), s); }
   {
@@ -826,7 +837,9 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
     g->nb_fastest = 1;
   }
   none.chunk = -1;
-  const int gridr = gemm_grid(d, bm, chunk_experts, d.I / 128);
+  r1.tile_start = tile_a_r;
+  r1.tiles = tiles_r;
+  const int gridr = gemm_grid(d, bm_r, chunk_experts, d.I / 128);
   const int gh = gemm_grid(d, bm, chunk_experts, d.I / 256), gx = gemm_grid(d, bm, chunk_experts, d.H / 256);
   const int gridb = gh > gx ? gh : gx;
   const int nchunks = (d.E + chunk_experts - 1) / chunk_experts;
@@ -835,9 +848,10 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
     if (c < nchunks) {
       r1.chunk = c;
       Scope sc_(tm, MOE_STAGE_GEMM1);
-      if (d.fmt == MOE_W_INT4_G32_BF16) launch_gemm_int4_pair(r1, none, queue + 16 * c, bm, gridr, s);
-      else if (fp8) (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)(r1, none, queue + 16 * c, bm, gridr, s);
-      else launch_gemm_mxfp4_pair(r1, none, queue + 16 * c, bm, gridr, s);
+      if (d.fmt == MOE_W_INT4_G32_BF16) launch_gemm_int4_pair(r1, none, queue + 16 * c, bm_r, gridr, s);
+      else if (fp8)
+        (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)(r1, none, queue + 16 * c, bm_r, gridr, s);
+      else launch_gemm_mxfp4_pair(r1, none, queue + 16 * c, bm_r, gridr, s);
     }
     bh.chunk = c < nchunks ? c : -1;
     bx.chunk = c - 1;
