@@ -212,22 +212,25 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
                                            void* ws, size_t ws_bytes, void* stream, float* stage_ms,
                                            int32_t* stage_launches);
 
-/* ---- Frozen-base backward (INT4 weights) ----------------------------------
+/* ---- Frozen-base backward --------------------------------------------------
  * The GEMM backward that bypasses the base weight gradient (Orbit
  * announcement, 技术细节): gradients for the layer inputs and the adapter only.
  * Its two GEMMs contract over the weights' output dimension, so they read a
  * transposed copy of the frozen weights, made once per base. */
 
-/* Bytes of the transposed copy: W13^T [E][H][2I] and W2^T [E][I][H] INT4
- * nibbles plus the group scales as fp16 (same count as the bf16 scales);
- * 0 if the layer is not supported by the backward (INT4 only, I multiple of
- * 256, per-expert adapter). */
+/* Bytes of the transposed copy: W13^T [E][H][2I] and W2^T [E][I][H] in the
+ * format's codes (INT4 / E2M1 nibbles, E4M3 bytes) plus scales (INT4, MXFP4:
+ * one fp16 per group scale; FP8: the fp32 block scales transposed); 0 if the
+ * layer is not supported by the backward (I multiple of 256; FP8 H and 2I at
+ * most 8192; per-expert adapter). */
 size_t moe_backward_weights_bytes(const moe_layer* layer);
 
 /* Writes the transposed copy of (qweights, scales) into bwd_weights (device,
- * caller-owned, >= moe_backward_weights_bytes).  Values are bit-identical
- * re-layouts; the scales are converted to fp16 (exact for bf16 scales in
- * [2^-10, 4096]) and pre-divided by 16 where the unpack needs it. */
+ * caller-owned, >= moe_backward_weights_bytes).  Codes are bit-identical
+ * re-layouts; INT4 scales are converted to fp16 (exact for bf16 scales in
+ * [2^-10, 4096]) and pre-divided by 16 where the unpack needs it, MXFP4
+ * scales to fp16 2^(e-127) (exact within fp16's range), FP8 block scales
+ * are transposed. */
 moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweights* qweights,
                                         const moe_scales* scales, void* bwd_weights, size_t bwd_bytes,
                                         void* stream);
@@ -247,9 +250,12 @@ size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_expert
  * (routing, gate/up pre-activations); per permuted row (t, j) of expert e:
  * u = d_out_t W2, dh = w_tj u, da = dh b silu'(a), db = dh silu(a),
  * dx' = da Wg + db Wu, dR_e += x_t^T dx' (32x32 diagonal blocks),
- * dx_tj = dx' R_e^T, d_x_t = sum_j dx_tj.  GEMM operands are fp16 (INT4
- * weights times their scales exactly; d_out and the SwiGLU gradients rounded
- * to fp16, so their magnitudes must stay below 65504), accumulation fp32.
+ * dx_tj = dx' R_e^T, d_x_t = sum_j dx_tj.  Activation quantizers of the
+ * FP8 / MXFP4 formats pass gradients straight through; the router term uses
+ * h as the forward quantized it.  GEMM operands are fp16 (INT4 and E2M1
+ * weights times their scales exactly, E4M3 times the block scale rounded
+ * once; d_out and the SwiGLU gradients rounded to fp16, so their magnitudes
+ * must stay below 65504), accumulation fp32.
  * bwd_weights: from moe_prepare_backward_weights for the same weights.
  * Unsupported layers return MOE_ERR_UNSUPPORTED; the rest as moe_expert_forward.
  * Stream-ordered, no host synchronisation, nothing allocated, unless
