@@ -20,15 +20,23 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   __syncthreads();
   for (int c = threadIdx.x; c < H / 8; c += 256) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)rows[j] * H + c * 8);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-      const float wj = wts[j];
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      // up to 8 rows' loads in flight, then the FMAs in ascending j
+      uint4 v[8];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        acc[2 * h] = fmaf(wj, bf16_bits_to_f32(u[h] & 0xFFFFu), acc[2 * h]);
-        acc[2 * h + 1] = fmaf(wj, bf16_bits_to_f32(u[h] >> 16), acc[2 * h + 1]);
-      }
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k) v[i] = *reinterpret_cast<const uint4*>(y + (int64_t)rows[j0 + i] * H + c * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k) {
+          const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          const float wj = wts[j0 + i];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            acc[2 * h] = fmaf(wj, bf16_bits_to_f32(u[h] & 0xFFFFu), acc[2 * h]);
+            acc[2 * h + 1] = fmaf(wj, bf16_bits_to_f32(u[h] >> 16), acc[2 * h + 1]);
+          }
+        }
     }
     uint4 o;
     o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);

@@ -15,21 +15,42 @@ MOE_DEV uint32_t float_key(float f) {
 }
 MOE_DEV float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// One wave per token.  Each lane keeps SLOTS = ceil(E/64) logits (E <= 1024)
-// as 64-bit keys (value key << 32 | (0xFFFF - id)): the wave maximum is the
-// largest logit and, among equal logits, the smallest expert id.
+template <int CTRL>
+MOE_DEV uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over each row of 16 lanes, returned in every lane of the row:
+// quad swaps, then row rotations by 4 and 8 (DPP, register to register).
+MOE_DEV uint64_t row16_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;   // quad_perm [1,0,3,2]
+  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;   // quad_perm [2,3,0,1]
+  o = dpp_u64<0x124>(v); v = o > v ? o : v;   // row_ror:4
+  o = dpp_u64<0x128>(v); v = o > v ? o : v;   // row_ror:8
+  return v;
+}
+
+// One token per row of 16 lanes (4 tokens per wave).  Lane r keeps the
+// logits of experts r, r + 16, ... (SLOTS of them, E <= 16 SLOTS) as 64-bit
+// keys (value key << 32 | (0xFFFF - id)), so the row maximum is the largest
+// logit and, among equal logits, the smallest expert id.  Each of the k
+// rounds takes the row maximum and clears it.  Rows past the last token
+// still run the rounds (on zero keys) so that every DPP source lane is live.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                     int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
+  const int r = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = t < T;
+  const float* row = logits + (int64_t)(live ? t : 0) * E;
   uint64_t key[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)float_key(row[e]) << 32) | (uint64_t)(0xFFFFu - e)) : 0ull;
+    const int e = r + 16 * i;
+    key[i] = (live && e < E) ? (((uint64_t)float_key(row[e]) << 32) | (uint64_t)(0xFFFFu - e)) : 0ull;
   }
   float sel_val[MAX_TOPK];
   int sel_id[MAX_TOPK];
@@ -39,12 +60,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < SLOTS; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)best, m, 64), hi = __shfl_xor((uint32_t)(best >> 32), m, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-      }
+      best = row16_max_u64(best);
       sel_id[j] = 0xFFFF - (int)(best & 0xFFFFu);
       sel_val[j] = key_float((uint32_t)(best >> 32));
 #pragma unroll
@@ -52,6 +68,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
         if (key[i] == best) key[i] = 0;  // keys are unique (distinct ids), so only the winner clears
     }
   }
+  if (!live) return;
   // softmax over the selected logits, relative to the largest (slot 0)
   float z = 0.0f;
 #pragma unroll
@@ -59,7 +76,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     if (j < k) z += expf(sel_val[j] - sel_val[0]);
 #pragma unroll
   for (int j = 0; j < MAX_TOPK; ++j)
-    if (j < k && lane == j) {
+    if (j < k && r == j) {
       ids[(int64_t)t * k + j] = sel_id[j];
       w[(int64_t)t * k + j] = expf(sel_val[j] - sel_val[0]) / z;
     }
@@ -106,10 +123,13 @@ MOE_DEV i32x4 block_excl_scan4_1024(i32x4 v, i32x4* sh, i32x4* total) {
   return before + incl - v;
 }
 
-// One workgroup of 1024 threads (thread = expert).  Turns the per-block
-// histograms into per-(block, expert) scatter bases, writes the expert
-// offsets, the ascending active-expert list, and the per-active-expert tile
-// prefixes for tiles of bm_a rows and of 16 rows.
+// One workgroup of 1024 threads.  Turns the per-block histograms into
+// per-(block, expert) scatter bases, writes the expert offsets, the ascending
+// active-expert list, and the per-active-expert tile prefixes for tiles of
+// bm_a rows and of 16 rows.  The blocks are split into G = 1024 / E
+// contiguous ranges: thread (g, e) sums range g of expert e's column (all
+// loads of a range in flight together), the experts' totals are scanned with
+// thread = expert, and each thread then writes the bases of its range.
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int bm_a,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
@@ -117,19 +137,27 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
                                                int32_t* __restrict__ queue, int nqueue) {
   __shared__ i32x4 sh4[16];
   __shared__ int s_tstart[MAX_EXPERTS + 1], s_exp[MAX_EXPERTS], s_off[MAX_EXPERTS], s_cnt[MAX_EXPERTS];
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E)
-    for (int b0 = 0; b0 < nblk; b0 += 16) {  // running per-expert prefix over blocks
+  __shared__ int s_part[1024], s_base[MAX_EXPERTS];
+  const int G = 1024 / E;
+  const int tid = threadIdx.x;
+  const int g = tid / E, ce = tid - g * E;  // this thread's range and column (g < G)
+  const int b0 = (int)((int64_t)nblk * g / G), b1 = (int)((int64_t)nblk * (g + 1) / G);
+  if (g < G) {
+    int sum = 0;
+    for (int b = b0; b < b1; b += 16) {
       int h[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) h[i] = (b0 + i < nblk) ? hist[(int64_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) h[i] = (b + i < b1) ? hist[(int64_t)(b + i) * E + ce] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (b0 + i < nblk) hist[(int64_t)(b0 + i) * E + e] = cnt;
-        cnt += h[i];
-      }
+      for (int i = 0; i < 16; ++i) sum += h[i];
     }
+    s_part[tid] = sum;
+  }
+  __syncthreads();
+  const int e = tid;
+  int cnt = 0;
+  if (e < E)
+    for (int q = 0; q < G; ++q) cnt += s_part[q * E + e];
   // one scan for: row offsets, active positions, bm_a-row tiles, 16-row tiles
   const int act = (e < E && cnt > 0) ? 1 : 0;
   const i32x4 v = {e < E ? cnt : 0, act, act ? (cnt + bm_a - 1) / bm_a : 0, act ? (cnt + 15) / 16 : 0};
@@ -139,7 +167,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   const int na = tot[1], nta = tot[2], nt16 = tot[3];
   if (e < E) {
     offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;  // independent updates, pipelined
+    s_base[e] = off;
   }
   if (e == 0) offsets[E] = tot[0];
   if (act) {
@@ -159,6 +187,23 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   }
   for (int i = threadIdx.x; i < nqueue; i += blockDim.x) queue[i] = 0;  // GEMM work-queue counters
   __syncthreads();
+  // scatter bases of this thread's range: the expert's offset, the ranges
+  // before it, then the blocks before it within the range
+  if (g < G) {
+    int base = s_base[ce];
+    for (int q = 0; q < g; ++q) base += s_part[q * E + ce];
+    for (int b = b0; b < b1; b += 16) {
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = (b + i < b1) ? hist[(int64_t)(b + i) * E + ce] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (b + i < b1) {
+          hist[(int64_t)(b + i) * E + ce] = base;
+          base += h[i];
+        }
+    }
+  }
   // One descriptor per bm_a-row tile, in (active expert, tile) order:
   // {expert, first permuted row, valid rows, active index}.
   for (int t = threadIdx.x; t < nta; t += blockDim.x) {
@@ -213,12 +258,13 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return;
-  const dim3 g((T + 3) / 4), b(256);
-  if (E <= 64) hipLaunchKernelGGL(k_route_topk<1>, g, b, 0, s, logits, T, E, k, ids, w);
-  else if (E <= 128) hipLaunchKernelGGL(k_route_topk<2>, g, b, 0, s, logits, T, E, k, ids, w);
-  else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, T, E, k, ids, w);
-  else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, T, E, k, ids, w);
-  else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, s, logits, T, E, k, ids, w);
+  const dim3 g((T + 15) / 16), b(256);
+  if (E <= 64) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 128) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 256) hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 384) hipLaunchKernelGGL(k_route_topk<24>, g, b, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 512) hipLaunchKernelGGL(k_route_topk<32>, g, b, 0, s, logits, T, E, k, ids, w);
+  else hipLaunchKernelGGL(k_route_topk<64>, g, b, 0, s, logits, T, E, k, ids, w);
 }
 
 void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, int32_t* offsets,

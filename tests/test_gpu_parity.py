@@ -43,7 +43,8 @@ def test_route_bitexact_configs(name):
     check_route(synth.gen_logits(cfg), cfg.k, cfg.E)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (5, 4, 4), (300, 130, 16), (2049, 1024, 8), (4099, 64, 1)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (5, 4, 4), (300, 130, 16), (2049, 1024, 8), (4099, 64, 1),
+                                   (20000, 8, 2), (9000, 384, 8)])
 def test_route_bitexact_edge(T, E, k):
     r = np.random.default_rng(T * 7 + E)
     lg = r.standard_normal((T, E)).astype(np.float32)
