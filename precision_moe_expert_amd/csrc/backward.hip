@@ -131,12 +131,20 @@ __global__ __launch_bounds__(256) void k_unpermute_sum(const float* __restrict__
   const int t = blockIdx.x;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)row_of[(int64_t)t * k + j] * H + c);
-      s[0] += v.x;
-      s[1] += v.y;
-      s[2] += v.z;
-      s[3] += v.w;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      // up to 8 rows' loads in flight, then the sums in ascending j
+      float4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k) v[i] = *reinterpret_cast<const float4*>(src + (int64_t)row_of[(int64_t)t * k + j0 + i] * H + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k) {
+          s[0] += v[i].x;
+          s[1] += v[i].y;
+          s[2] += v[i].z;
+          s[3] += v[i].w;
+        }
     }
     *reinterpret_cast<uint2*>(out + (int64_t)t * H + c) =
         make_uint2(f32_to_bf16_bits(s[0]) | (f32_to_bf16_bits(s[1]) << 16),

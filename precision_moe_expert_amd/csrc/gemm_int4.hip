@@ -105,20 +105,27 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
       const int r = m * 16 + ln;
       return *reinterpret_cast<const f16x8*>(st + r * 256 + (((4 * lg + s) ^ (r & 15)) << 4));
     };
+    // The activation fragments of sub-step s + 1 are read while sub-step s
+    // unpacks its weights and runs its MFMAs (the scheduling barriers keep
+    // the compiler from sinking the reads to their first use).
+    f16x8 af[2][MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) af[0][m] = read_a(m, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) af[(s + 1) & 1][m] = read_a(m, s + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f16x8 bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bq[i], s), s2[i], s2_16[i]);
-      f16x8 afc = read_a(0, s);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        f16x8 afn = afc;
-        if (m + 1 < MT) afn = read_a(m + 1, s);  // next row block's operand in flight
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(afc, bf[i], acc[m][i]);
-        afc = afn;
-      }
+        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[i], acc[m][i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 

@@ -148,20 +148,20 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
       af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sa = (int)asb[((kt >> 2) & 1) * ST::AS_BLOCK + r * 16 + (kt & 3) * 4 + lg];
     };
-    i32x8 afc;
-    int sac;
-    read_a(0, afc, sac);
+    // Row block m + 1's operands are read before block m's MFMAs issue (the
+    // scheduling barriers keep the compiler from sinking the reads to their
+    // first use).
+    i32x8 af[2];
+    int sa[2];
+    read_a(0, af[0], sa[0]);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      i32x8 afn;
-      int san = 0;
-      if (m + 1 < MT) read_a(m + 1, afn, san);  // next row block's operands in flight
+      if (m + 1 < MT) read_a(m + 1, af[(m + 1) & 1], sa[(m + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(afc, bf[i], sac, sb[i], acc[m][i]);
-      if (m + 1 < MT) {
-        afc = afn;
-        sac = san;
-      }
+      for (int i = 0; i < 4; ++i)
+        acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(af[m & 1], bf[i], sa[m & 1], sb[i], acc[m][i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
