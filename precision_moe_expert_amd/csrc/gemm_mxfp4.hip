@@ -74,18 +74,22 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   // per-lane global sources of this item's DMA pieces (K offset added per step)
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
   const char* wsexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems;
-  const char* bsrc[4];
+  // the four subtiles' weight rows are col[i] + ln: one per-lane pointer plus
+  // wave-uniform row offsets (fewer live registers than four pointers)
+  const char* bsrc0 = wexp + (int64_t)(col[0] + ln) * (K / 2) + lg * 16;
+  int64_t boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  for (int i = 0; i < 4; ++i) boff[i] = (int64_t)(col[i] - col[0]) * (K / 2);
   // E8M0 weight scales (group-major): lane l < 16 takes 16 consecutive
   // weight rows of group l/4, i.e. one subtile
-  const char* bssrc;
+  uint32_t bsoff;  // from wsexp
   {
     const int g = (lane >> 2) & 3, pc = lane & 3;
     const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
-    bssrc = wsexp + (int64_t)g * p.N + c;
+    bsoff = (uint32_t)(g * p.N + c);
   }
-  const char* asrc[ST::NA];
+  // activation pieces as 16-byte unit offsets from Abase (32 bits each)
+  uint32_t aoff[ST::NA];
 #pragma unroll
   for (int j = 0; j < ST::NA; ++j) {
     const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/8, slot c%8
@@ -94,25 +98,26 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
     const int sr = p.sorted_rows[rr];
     const int src = p.a_per_token ? sr / p.top_k : rr;
-    asrc[j] = Abase + (int64_t)src * K + part * 16;
+    aoff[j] = (uint32_t)src * (uint32_t)(K / 16) + (uint32_t)part;
   }
-  const char* ssrc;
+  uint32_t soff;  // from ASbase
   {
     const int row = wave * 64 + lane;
     const int rr = tl.rbase + min(min(row, BM - 1), tl.nrows - 1);
     const int sr = p.sorted_rows[rr];
     const int src = p.a_per_token ? sr / p.top_k : rr;
-    ssrc = ASbase + (int64_t)src * p.a_scale_stride;
+    soff = (uint32_t)src * (uint32_t)p.a_scale_stride;
   }
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * ST::BYTES;
 #pragma unroll
-    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 128, sb + (wave * ST::NA + j) * 1024);
+    for (int j = 0; j < ST::NA; ++j)
+      dma_b128(Abase + (uint64_t)aoff[j] * 16 + kt * 128, sb + (wave * ST::NA + j) * 1024);
     if (wave < ST::NASW && (kt & 3) == 0)
-      dma_b128(ssrc + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
+      dma_b128(ASbase + (uint64_t)soff + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-    if (lane < 16) dma_b128(bssrc + (int64_t)kt * 4 * p.N, sb + ST::BS_OFF + wave * 256);
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc0 + boff[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
+    if (lane < 16) dma_b128(wsexp + (uint64_t)bsoff + (int64_t)kt * 4 * p.N, sb + ST::BS_OFF + wave * 256);
   };
   f32x4 acc[MT][4];
 #pragma unroll
