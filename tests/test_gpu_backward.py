@@ -121,6 +121,15 @@ def test_backward_small_vs_oracle(fmt, oft):
     check(li, dout, Bwd(li).run(dout))
 
 
+@pytest.mark.parametrize("fmt,oft", [(1, True), (2, False), (3, False)])
+def test_backward_max_experts_and_top_k(fmt, oft):
+    """E = 1024 with top-16 routing (most experts one or two rows, a few hot)."""
+    li = synth.make_inputs(small(T=64, H=256, I=256, E=1024, k=16, zipf=0.4, chunk=64, oft=oft,
+                                 cfg_id=280 + fmt, fmt=fmt))
+    dout = d_out_of(li.cfg, 12)
+    check(li, dout, Bwd(li).run(dout))
+
+
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
 def test_backward_every_tile_height(fmt, tile_rows):

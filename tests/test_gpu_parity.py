@@ -92,6 +92,20 @@ def test_forward_c1_vs_oracle():
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+def test_forward_max_experts_and_top_k(fmt):
+    """E = 1024 (the library's maximum) with top-16 routing: about 500 active
+    experts, most with one or two rows, a few (Zipf bias) with up to ~50;
+    16 chunks of 64."""
+    cfg = small(fmt, T=96, H=256, I=128, E=1024, k=16, zipf=0.4, chunk=64, cfg_id=90 + fmt)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    err = gu.row_rel_err(out, oracle.forward_inputs(li))
+    print(f"fmt {fmt} E=1024 k=16: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
 def test_chunk_size_bitwise_invariance(fmt):
     cfg = small(fmt, E=9, k=3, zipf=1.2)
     d = gu.DevInputs(synth.make_inputs(cfg))
