@@ -273,6 +273,14 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         if (m < nmb && ln == 0) red[wc][(mb0 + m) * 16 + lg * 4 + i] = am;
       }
     lds_barrier();
+    // the four column waves' maxima of this lane's 4 rows per row block, all
+    // read before the first is used (one 16-byte read per wave and block)
+    f32x4 rmax[MTW][4];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+      if (m < nmb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rmax[m][c] = *reinterpret_cast<const f32x4*>(&red[c][(mb0 + m) * 16 + lg * 4]);
     float* Hs = static_cast<float*>(p.out_scale);
 #pragma unroll
     for (int m = 0; m < MTW; ++m)
@@ -280,7 +288,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = (mb0 + m) * 16 + lg * 4 + i;
-          const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+          const float amax = fmaxf(fmaxf(rmax[m][0][i], rmax[m][1][i]), fmaxf(rmax[m][2][i], rmax[m][3][i]));
           // the row's [1,128] block scale: amax/448 (codes h/s with the hardware
           // reciprocal), or the power of two at or above it (exact scaling)
           float sc, inv;
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(FP8_THREADS, 1) void k_gemm_fp8(GemmArgs p1, GemmAr
   __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
   static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
   __shared__ __align__(16) uint8_t asb[2 * ST::AS_BLOCK];
-  __shared__ float red[4][BM];
+  __shared__ __align__(16) float red[4][BM];
   __shared__ int s_item;
   ChunkWork c1, c2;
   const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
