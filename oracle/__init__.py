@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
+FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2, FMT_NVFP4 = 1, 2, 3, 4, 5
 
 
 def build(force: bool = False) -> str:
@@ -39,7 +39,7 @@ class _Layer(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("fmt", ctypes.c_int32),
                 ("oft_block", ctypes.c_int32), ("adapter_expert_stride", ctypes.c_int64),
-                ("materialized", ctypes.c_int32)]
+                ("materialized", ctypes.c_int32), ("g13", ctypes.c_void_p), ("g2", ctypes.c_void_p)]
 
 
 def lib():
@@ -144,10 +144,10 @@ def quant_mxfp8(v: np.ndarray):
     return q, e
 
 
-def dequant(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """One expert's packed [N][K] weights -> fp32 [N][K]."""
+def dequant(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray, g: float = 1.0) -> np.ndarray:
+    """One expert's packed [N][K] weights -> fp32 [N][K] (g: NVFP4 second-level scale)."""
     out = np.empty((N, K), np.float32)
-    lib().oracle_dequant(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), _p(out))
+    lib().oracle_dequant(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), ctypes.c_double(g), _p(out))
     return out
 
 
@@ -159,26 +159,37 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_bf16(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray) -> np.ndarray:
+def dequant_bf16(fmt: int, N: int, K: int, q: np.ndarray, s: np.ndarray, g: float = 1.0) -> np.ndarray:
     """One expert's packed [N][K] weights -> the BF16 temporary copy's values (fp32)."""
     out = np.empty((N, K), np.float32)
-    lib().oracle_dequant_bf16(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), _p(out))
+    lib().oracle_dequant_bf16(fmt, N, K, _p(_c(q, np.uint8)), _p(np.ascontiguousarray(s)), ctypes.c_double(g),
+                              _p(out))
     return out
+
+
+def _layer(T, H, I, E, k, fmt, oft, stride, materialized, g13, g2):
+    """oracle_layer plus the arrays its pointers reference (kept alive by the caller)."""
+    g13 = None if g13 is None else _c(g13, np.float32)
+    g2 = None if g2 is None else _c(g2, np.float32)
+    layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0, stride, 1 if materialized else 0,
+                   _p(g13), _p(g2))
+    return layer, (g13, g2)
 
 
 def forward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, chunk_experts=1,
             tokens=None, adapter_expert_stride=None, return_y=False, return_routing=False,
-            materialized=False):
+            materialized=False, g13=None, g2=None):
     """Oracle MoE expert forward.  x: [T][H] bf16 bits (uint16); logits [T][E] fp32;
     weights/scales in the packed storage layouts; oft [E][H/32][32][32] bf16 bits
     (or [H/32][32][32] with adapter_expert_stride=0) or None.
     tokens: optional int array of token indices to compute (default: all).
     materialized: BF16 temporary weights and bf16 GEMM inputs instead of the
     format's activation quantizers (the chunk dequantized to a BF16 copy).
+    g13, g2: NVFP4 per-expert second-level scales of W13 and W2 (fp32 [E]).
     Returns out [n][H] fp32 (+ y [n][k][H], + (ids, w) when requested)."""
-    layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0,
-                   (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride,
-                   1 if materialized else 0)
+    layer, keep = _layer(T, H, I, E, k, fmt, oft,
+                         (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride,
+                         materialized, g13, g2)
     x = _c(x, np.uint16)
     logits = _c(logits, np.float32)
     w13 = _c(w13, np.uint8)
@@ -209,18 +220,18 @@ def forward_inputs(li, chunk_experts=None, tokens=None, **kw):
     c = li.cfg
     return forward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2,
                    oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts,
-                   tokens=tokens, **kw)
+                   tokens=tokens, g13=getattr(li, "g13", None), g2=getattr(li, "g2", None), **kw)
 
 
 def backward(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, dout, oft=None, chunk_experts=1, tokens=None,
-             adapter_expert_stride=None, return_g=False):
+             adapter_expert_stride=None, return_g=False, g13=None, g2=None):
     """Frozen-base backward of the oracle forward.  dout: [n][H] fp32 gradient of
     the requested tokens' outputs (all tokens if tokens is None).
     Returns (dx [n][H] fp32, dlogits [n][E] fp32, doft or None), doft float64
     shaped like the adapter, summed over the requested tokens' rows; with
     return_g also g [n][k] float64 (g_tj = <dout_t, y_tj>)."""
     stride = (32 * 32 * (H // 32)) if adapter_expert_stride is None else adapter_expert_stride
-    layer = _Layer(T, H, I, E, k, fmt, 32 if oft is not None else 0, stride, 0)
+    layer, keep = _layer(T, H, I, E, k, fmt, oft, stride, False, g13, g2)
     tok = None if tokens is None else _c(tokens, np.int32)
     n = T if tok is None else len(tok)
     dout = _c(dout, np.float32).reshape(n, H)
@@ -246,7 +257,7 @@ def backward_inputs(li, dout, chunk_experts=None, tokens=None, return_g=False):
     c = li.cfg
     return backward(c.T, c.H, c.I, c.E, c.k, c.fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2, dout,
                     oft=li.oft, chunk_experts=c.chunk if chunk_experts is None else chunk_experts, tokens=tokens,
-                    return_g=return_g)
+                    return_g=return_g, g13=getattr(li, "g13", None), g2=getattr(li, "g2", None))
 
 
 def combine(y_perm_bf16: np.ndarray, w: np.ndarray, row_of: np.ndarray) -> np.ndarray:

@@ -47,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_INT4 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_FP8_POW2 = 4 };
+enum { OR_INT4 = 1, OR_FP8 = 2, OR_MXFP4 = 3, OR_FP8_POW2 = 4, OR_NVFP4 = 5 };
 
 /* ------------------------------------------------------------------ codecs */
 
@@ -279,8 +279,13 @@ int oracle_permute(int T, int E, int k, const int32_t* ids, int32_t* counts, int
  *   INT4 : q two's-complement nibble, s bf16 per (n, 32 along K), stored
  *          group-major: s[(k/32) * N + n]
  *   FP8  : q E4M3FN, s fp32 per [128,128] block (n/128, k/128)
- *   MXFP4: q E2M1 nibble, s E8M0 per (n, 32 along K), group-major as INT4 */
-static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* s, int to_bf16, float* out) {
+ *   MXFP4: q E2M1 nibble, s E8M0 per (n, 32 along K), group-major as INT4
+ *   NVFP4: q E2M1 nibble, s E4M3 per (n, 16 along K), group-major
+ *          s[(k/16) * N + n], times g, the matrix's fp32 second-level scale
+ *          (the format's public definition; the pages only name it)
+ * g is 1 for the other formats. */
+static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* s, double g, int to_bf16,
+                           float* out) {
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < N; ++n) {
     for (int kk = 0; kk < K; ++kk) {
@@ -291,6 +296,9 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
       } else if (fmt == OR_FP8 || fmt == OR_FP8_POW2) {
         v = e4m3_value(q[(int64_t)n * K + kk]) *
             (double)((const float*)s)[(int64_t)(n / 128) * (K / 128) + kk / 128];
+      } else if (fmt == OR_NVFP4) {
+        v = e2m1_value(nibble_at(q, (int64_t)n * K + kk)) *
+            e4m3_value(((const uint8_t*)s)[(int64_t)(kk / 16) * N + n]) * g;
       } else {
         v = e2m1_value(nibble_at(q, (int64_t)n * K + kk)) *
             e8m0_value(((const uint8_t*)s)[(int64_t)(kk / 32) * N + n]);
@@ -301,8 +309,8 @@ static void dequant_matrix(int fmt, int N, int K, const uint8_t* q, const void* 
 }
 
 /* Activation quantizer of a weight format applied to one fp32 row: returns
- * the dequantized values (exact in double).  INT4 weights take the activations
- * as they are. */
+ * the dequantized values (exact in double).  INT4 and NVFP4 weights take the
+ * activations as they are. */
 static void act_quant_row(int fmt, int K, const float* v, double* out, uint8_t* qtmp, float* stmp,
                           uint8_t* etmp) {
   if (fmt == OR_FP8 || fmt == OR_FP8_POW2) {
@@ -324,7 +332,11 @@ typedef struct {
   int32_t oft_block;             /* 0: no adapter; 32: block-diagonal 32x32 R */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = shared */
   int32_t materialized;          /* 1: BF16 temporary weights (see the header) */
+  const float* g13;              /* NVFP4: per-expert second-level scales of W13 and W2 */
+  const float* g2;
 } oracle_layer;
+
+static double gscale(const float* g, int e) { return g != NULL ? (double)g[e] : 1.0; }
 
 /* One expert FFN row: x (bf16 token row) -> y (fp32, length H).
  * W13 = [2I][H] fp32 dequantized (gate rows then up rows), W2 = [H][I]. */
@@ -382,6 +394,7 @@ static void expert_row(const oracle_layer* L, const uint16_t* xrow, const uint16
 static int64_t packed_bytes(int fmt, int64_t n) { return (fmt == OR_FP8 || fmt == OR_FP8_POW2) ? n : n / 2; }
 static int64_t scale_bytes(int fmt, int N, int K) {
   if (fmt == OR_INT4) return (int64_t)N * (K / 32) * 2;
+  if (fmt == OR_NVFP4) return (int64_t)N * (K / 16);
   if (fmt == OR_FP8 || fmt == OR_FP8_POW2) return (int64_t)(N / 128) * (K / 128) * 4;
   return (int64_t)N * (K / 32);
 }
@@ -445,9 +458,11 @@ int oracle_forward(const oracle_layer* L, const uint16_t* x, const float* logits
       W13c[a] = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
       W2c[a] = (float*)malloc(sizeof(float) * (size_t)H * I);
       dequant_matrix(fmt, 2 * I, H, w13 + packed_bytes(fmt, (int64_t)e * 2 * I * H),
-                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), L->materialized, W13c[a]);
+                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), gscale(L->g13, e),
+                     L->materialized, W13c[a]);
       dequant_matrix(fmt, H, I, w2 + packed_bytes(fmt, (int64_t)e * H * I),
-                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), L->materialized, W2c[a]);
+                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), gscale(L->g2, e),
+                     L->materialized, W2c[a]);
     }
     /* the chunk's grouped GEMM, row by row */
     rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(offsets[active[c0 + nc - 1] + 1] - offsets[active[c0]] + 1));
@@ -652,9 +667,9 @@ int oracle_backward(const oracle_layer* L, const uint16_t* x, const float* logit
       float* W13 = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
       float* W2 = (float*)malloc(sizeof(float) * (size_t)H * I);
       dequant_matrix(fmt, 2 * I, H, w13 + packed_bytes(fmt, (int64_t)e * 2 * I * H),
-                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), 0, W13);
+                     (const uint8_t*)s13 + (int64_t)e * scale_bytes(fmt, 2 * I, H), gscale(L->g13, e), 0, W13);
       dequant_matrix(fmt, H, I, w2 + packed_bytes(fmt, (int64_t)e * H * I),
-                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), 0, W2);
+                     (const uint8_t*)s2 + (int64_t)e * scale_bytes(fmt, H, I), gscale(L->g2, e), 0, W2);
       const uint16_t* R_e = oft ? oft + (int64_t)e * L->adapter_expert_stride : NULL;
       double* dR_e = (oft && doft_out) ? doft_out + (int64_t)e * L->adapter_expert_stride : NULL;
       const int32_t r0 = offsets[e], r1 = offsets[e + 1];
@@ -783,13 +798,13 @@ void oracle_quant_mxfp8(int R, int K, const float* v, uint8_t* q, uint8_t* e8) {
 }
 
 /* One expert's N x K weights dequantized to fp32 (format codes as above). */
-void oracle_dequant(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
-  dequant_matrix(fmt, N, K, q, s, 0, out);
+void oracle_dequant(int fmt, int N, int K, const uint8_t* q, const void* s, double g, float* out) {
+  dequant_matrix(fmt, N, K, q, s, g, 0, out);
 }
 
 /* One expert's weights as the BF16 temporary copy holds them. */
-void oracle_dequant_bf16(int fmt, int N, int K, const uint8_t* q, const void* s, float* out) {
-  dequant_matrix(fmt, N, K, q, s, 1, out);
+void oracle_dequant_bf16(int fmt, int N, int K, const uint8_t* q, const void* s, double g, float* out) {
+  dequant_matrix(fmt, N, K, q, s, g, 1, out);
 }
 
 void oracle_round_bf16(int64_t n, const double* v, double* out) {

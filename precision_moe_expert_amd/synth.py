@@ -16,6 +16,8 @@ Weight storage (all K-contiguous, Y = X @ W^T):
            bf16 scales [E][N][K/32]
   fp8    : OCP E4M3FN codes, one byte each; fp32 scales [E][N/128][K/128]
   mxfp4  : E2M1 nibbles (low nibble first); E8M0 scale bytes [E][N][K/32]
+  nvfp4  : E2M1 nibbles (low nibble first); E4M3 scale bytes per 16 along K,
+           group-major [E][K/16][N]; fp32 second-level scales g13[E], g2[E]
 OFT adapter: R[E][H/32][32][32] bf16, x' = x @ blockdiag(R_e).
 """
 from __future__ import annotations
@@ -27,12 +29,12 @@ import numpy as np
 import torch
 
 SEED_ROOT = 20261202
-FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
+FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2, FMT_NVFP4 = 1, 2, 3, 4, 5
 FMT_NAMES = {FMT_INT4: "int4_g32_bf16", FMT_FP8: "fp8_e4m3_b128", FMT_MXFP4: "mxfp4",
-             FMT_FP8_POW2: "fp8_e4m3_b128_pow2"}
+             FMT_FP8_POW2: "fp8_e4m3_b128_pow2", FMT_NVFP4: "nvfp4"}
 
 # tensor ids inside one seed sequence
-_T_X, _T_LOGITS, _T_ZIPF, _T_W13, _T_W2, _T_S13, _T_S2, _T_OFT, _T_WLM, _T_TGT = range(10)
+_T_X, _T_LOGITS, _T_ZIPF, _T_W13, _T_W2, _T_S13, _T_S2, _T_OFT, _T_WLM, _T_TGT, _T_G = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -72,6 +74,10 @@ CONFIGS = {
     # the Qwen3-30B-A3B shape with the power-of-two scale variant of the FP8 recipe
     "c2p": LayerConfig("qwen3_30b_a3b_fp8_pow2", 6, T=4096, H=2048, E=128, k=8, I=768,
                        fmt=FMT_FP8_POW2, chunk=16),
+    # the DeepSeek-V3 shape and routing with NVFP4 weights (the format the
+    # B200/B300 samplers serve) and 16-bit activations
+    "c4n": LayerConfig("deepseek_v3_nvfp4_zipf", 7, T=16384, H=7168, E=256, k=8, I=2048,
+                       fmt=FMT_NVFP4, chunk=32, zipf_alpha=1.2),
 }
 
 
@@ -174,10 +180,34 @@ def _gen_mxfp4(cfg, N, K, tensor, stensor):
     return q, s
 
 
+def _gen_nvfp4(cfg, N, K, tensor, stensor):
+    """E2M1 codes as for MXFP4; E4M3 block scales log-uniform in [16, 448]
+    (the range a per-16 amax / 6 maps to under a second-level scale)."""
+    E = cfg.E
+    q, _ = _gen_mxfp4(cfg, N, K, tensor, stensor)
+    s = np.empty((E, K // 16, N), np.uint8)  # group-major: s[e][g][n] scales row n, k in [16g, 16g+16)
+    for e in range(E):
+        v = np.exp2(_rng(cfg.cfg_id, stensor, 1000 + e).uniform(4.0, np.log2(448.0), (K // 16, N)))
+        s[e] = _to_e4m3_codes(v.astype(np.float32))
+    return q, s
+
+
+def gen_gscales(cfg: LayerConfig):
+    """NVFP4 second-level scales (fp32, one per expert and matrix) such that
+    weights are ~0.02 in magnitude; (None, None) for the other formats."""
+    if cfg.fmt != FMT_NVFP4:
+        return None, None
+    r = _rng(cfg.cfg_id, _T_G)
+    g13 = (r.uniform(0.8, 1.2, cfg.E) * 2.0e-4).astype(np.float32)
+    g2 = (r.uniform(0.8, 1.2, cfg.E) * 2.0e-4).astype(np.float32)
+    return g13, g2
+
+
 def gen_weights(cfg: LayerConfig):
     """Returns (w13, w2, s13, s2) as numpy arrays in the storage layouts above."""
     H, I = cfg.H, cfg.I
-    gen = {FMT_INT4: _gen_int4, FMT_FP8: _gen_fp8, FMT_MXFP4: _gen_mxfp4, FMT_FP8_POW2: _gen_fp8_pow2}[cfg.fmt]
+    gen = {FMT_INT4: _gen_int4, FMT_FP8: _gen_fp8, FMT_MXFP4: _gen_mxfp4, FMT_FP8_POW2: _gen_fp8_pow2,
+           FMT_NVFP4: _gen_nvfp4}[cfg.fmt]
     w13, s13 = gen(cfg, 2 * I, H, _T_W13, _T_S13)
     w2, s2 = gen(cfg, H, I, _T_W2, _T_S2)
     return w13, w2, s13, s2
@@ -227,10 +257,12 @@ class LayerInputs:
     oft: np.ndarray | None
     w_lm: np.ndarray | None = None
     targets: np.ndarray | None = None
+    g13: np.ndarray | None = None  # NVFP4 second-level scales
+    g2: np.ndarray | None = None
 
     def digest(self) -> dict:
         out = {}
-        for name in ("x", "logits", "w13", "w2", "s13", "s2", "oft", "w_lm", "targets"):
+        for name in ("x", "logits", "w13", "w2", "s13", "s2", "oft", "w_lm", "targets", "g13", "g2"):
             a = getattr(self, name)
             if a is not None:
                 out[name] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
@@ -241,6 +273,7 @@ def make_inputs(cfg: LayerConfig, with_lm: bool | None = None) -> LayerInputs:
     oft = gen_oft(cfg) if cfg.oft else None
     w13, w2, s13, s2 = gen_weights(cfg)
     li = LayerInputs(cfg, gen_x(cfg), gen_logits(cfg), w13, w2, s13, s2, oft)
+    li.g13, li.g2 = gen_gscales(cfg)
     if (cfg.lm_vocab > 0) if with_lm is None else with_lm:
         li.w_lm, li.targets = gen_lm_head(cfg)
     return li

@@ -41,7 +41,12 @@ def int4_values(nibbles):
     return ((np.asarray(nibbles, np.uint8) << 4).astype(np.int8) >> 4).astype(np.float64)
 
 
-def dequant(fmt, q, s, N, K):
+def dequant(fmt, q, s, N, K, g=1.0):
+    if fmt == 5:
+        # NVFP4: E2M1 values times the E4M3 scale of (n, 16 along K), group-major, times g
+        v = E2M1_TABLE[unpack_nibbles(q)].reshape(N, K)
+        sc = np.repeat(e4m3_to_f64(s).reshape(K // 16, N).T, 16, axis=1)
+        return v * sc * np.float64(g)
     if fmt == 1:
         v = int4_values(unpack_nibbles(q)).reshape(N, K)
         sc = np.repeat(bf16_to_f32(s).astype(np.float64).reshape(K // 32, N).T, 32, axis=1)  # group-major
@@ -111,7 +116,7 @@ def quant_mxfp8_rows(v):
 
 def act_values(fmt, v32):
     """Activation format applied to fp32 rows -> float64 values."""
-    if fmt == 1:
+    if fmt in (1, 5):
         return np.asarray(v32, np.float64)
     if fmt == 2:
         q, s = quant_fp8_rows(v32)
@@ -138,7 +143,7 @@ def route_bruteforce(logits, k):
 
 
 def dense_moe(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, adapter_stride_zero=False,
-              materialized=False):
+              materialized=False, g13=None, g2=None):
     """Dense MoE in float64: every expert runs on every token; the routing mask
     (softmax over the top-k, zero elsewhere) weights the sum.  materialized:
     weights rounded to bf16, bf16 GEMM inputs, h rounded to bf16, no
@@ -151,12 +156,14 @@ def dense_moe(T, H, I, E, k, fmt, x, logits, w13, w2, s13, s2, oft=None, adapter
             mask[t, ids[t, j]] = np.float32(w[t, j])
     out = np.zeros((T, H))
     for e in range(E):
+        ga = 1.0 if g13 is None else g13[e]
+        gb = 1.0 if g2 is None else g2[e]
         if materialized:
-            W13 = bf16_round_rto(dequant(fmt, w13[e], s13[e], 2 * I, H))
-            W2 = bf16_round_rto(dequant(fmt, w2[e], s2[e], H, I))
+            W13 = bf16_round_rto(dequant(fmt, w13[e], s13[e], 2 * I, H, ga))
+            W2 = bf16_round_rto(dequant(fmt, w2[e], s2[e], H, I, gb))
         else:
-            W13 = dequant(fmt, w13[e], s13[e], 2 * I, H).astype(np.float32).astype(np.float64)
-            W2 = dequant(fmt, w2[e], s2[e], H, I).astype(np.float32).astype(np.float64)
+            W13 = dequant(fmt, w13[e], s13[e], 2 * I, H, ga).astype(np.float32).astype(np.float64)
+            W2 = dequant(fmt, w2[e], s2[e], H, I, gb).astype(np.float32).astype(np.float64)
         xin = xf.astype(np.float64)
         if oft is not None:
             R = bf16_to_f32(oft if adapter_stride_zero else oft[e]).astype(np.float64).reshape(H // 32, 32, 32)

@@ -156,7 +156,7 @@ def test_mxfp8_act_quant_bitexact_vs_numpy(seed):
     assert np.all((mags[nz] >> 3) == 15)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_dequant_matches_reference(fmt):
     r = np.random.default_rng(fmt)
     N, K = 256, 384
@@ -168,12 +168,46 @@ def test_dequant_matches_reference(fmt):
         s = r.uniform(1e-4, 1e-3, (N // 128, K // 128)).astype(np.float32)
         if fmt == 4:
             s = np.ldexp(np.float32(1.0), np.floor(np.log2(s)).astype(np.int32)).astype(np.float32)
+    elif fmt == 5:
+        q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s = r.integers(0x01, 0x7F, (K // 16, N), dtype=np.uint8)   # every positive E4M3 code
     else:
         q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
         s = r.integers(110, 130, (N, K // 32), dtype=np.uint8)
-    got = oracle.dequant(fmt, N, K, q, s)
-    ref = refimpl.dequant(fmt, q, s, N, K)
+    g = 3.0517578125e-05 * 1.375 if fmt == 5 else 1.0
+    got = oracle.dequant(fmt, N, K, q, s, g)
+    ref = refimpl.dequant(fmt, q, s, N, K, g)
     assert np.array_equal(got.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+
+
+def test_nvfp4_layout_one_hot():
+    """Element 2i sits in the low nibble of byte i; scale byte [g][n] covers
+    row n, k in [16g, 16g+16); the second-level scale multiplies everything."""
+    N, K = 2, 64
+    q = np.zeros((N, K // 2), np.uint8)
+    q[0, 0] = 0x2 | (0xF << 4)    # k=0 -> +1.0, k=1 -> -6.0
+    q[1, 12] = 0x07               # k=24 -> +6.0
+    q[1, 8] = 0x10                # k=17 -> +0.5
+    s = np.full((K // 16, N), 0x38, np.uint8)  # E4M3 1.0
+    s[1, 1] = 0x40                # 2.0 for row 1, k in [16, 32)
+    w = oracle.dequant(5, N, K, q, s, 0.25)
+    expect = np.zeros((N, K), np.float32)
+    expect[0, 0], expect[0, 1], expect[1, 24], expect[1, 17] = 0.25, -1.5, 3.0, 0.25
+    assert np.array_equal(w, expect)
+
+
+def test_nvfp4_power_of_two_scales_reduce_to_mxfp4():
+    """With E4M3 block scales that are powers of two 2^e (the same for both
+    16-halves of a 32-group) and g = 1, NVFP4 decodes to exactly the MXFP4
+    value of the same codes with E8M0 scale 127 + e."""
+    r = np.random.default_rng(11)
+    N, K = 64, 256
+    q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    e = r.integers(-6, 9, (K // 32, N))
+    e8m0 = (127 + e).astype(np.uint8)                       # [K/32][N]
+    e4m3 = ((e + 7) << 3).astype(np.uint8)                   # 2^e, mantissa 0 (e >= -6 is normal)
+    s16 = np.repeat(e4m3, 2, axis=0)                         # [K/16][N]
+    assert np.array_equal(oracle.dequant(5, N, K, q, s16, 1.0), oracle.dequant(3, N, K, q, e8m0))
 
 
 def test_int4_layout_one_hot():
