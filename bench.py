@@ -26,14 +26,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE expert-layer tokens/s + TFLOP/s (% MFMA peak) / HBM GB/s per weight format"
 HBM_PEAK = 8.0e12
-# fp16 MFMA (INT4 path), fp8, fp8 x fp4 (issued at the fp8 rate), fp8 with E8M0 block scales
-MFMA_PEAK = {1: 2.5e15, 2: 5.0e15, 3: 5.0e15, 4: 5.0e15}
-DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a", 4: "fp8_e4m3_pow2"}
+# fp16 MFMA (INT4 path), fp8, fp8 x fp4 (issued at the fp8 rate), fp8 with E8M0 block scales,
+# fp16 MFMA (NVFP4 path)
+MFMA_PEAK = {1: 2.5e15, 2: 5.0e15, 3: 5.0e15, 4: 5.0e15, 5: 2.5e15}
+DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a", 4: "fp8_e4m3_pow2", 5: "nvfp4_w_fp16_mfma"}
 
 
 def weight_bytes_per_expert(fmt: int, N: int, K: int) -> float:
     if fmt == 1:
         return N * K / 2 + N * (K // 32) * 2
+    if fmt == 5:
+        return N * K / 2 + N * (K // 16) + 4
     if fmt in (2, 4):
         return N * K + (N // 128) * (K // 128) * 4
     return N * K / 2 + N * (K // 32)
@@ -41,7 +44,7 @@ def weight_bytes_per_expert(fmt: int, N: int, K: int) -> float:
 
 def act_bytes(fmt: int, rows: int, K: int) -> float:
     """Bytes of one activation matrix in the GEMM input format."""
-    if fmt == 1:
+    if fmt in (1, 5):
         return rows * K * 2
     if fmt in (2, 4):
         return rows * K + rows * (K // 128) * 4
@@ -70,7 +73,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", help="c1..c5 (default c2: the Qwen3-30B-A3B-shaped FP8 layer)")
+    ap.add_argument("--config", default="c2", help="c1..c5, c2p, c4n (default c2: the Qwen3-30B-A3B-shaped FP8 layer)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk_experts (default: the workload's)")
     ap.add_argument("--tile-rows", type=int, default=0, help="grouped-GEMM tile rows (0: automatic)")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle token sample (default: sized per workload)")
@@ -101,6 +104,8 @@ def main():
 
     x, logits = dev(li.x, True), dev(li.logits)
     w13, w2, s13, s2 = dev(li.w13), dev(li.w2), dev(li.s13), dev(li.s2)
+    g13 = dev(li.g13) if li.g13 is not None else None   # NVFP4 second-level scales
+    g2 = dev(li.g2) if li.g2 is not None else None
     oft = dev(li.oft, True) if li.oft is not None else None
     layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
                                tile_rows=args.tile_rows)
@@ -125,10 +130,10 @@ def main():
                                     chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad)
         elif mat:
             binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
-                                                chunk_experts=cfg.chunk, out=out, ws=ws)
+                                                chunk_experts=cfg.chunk, out=out, ws=ws, g13=g13, g2=g2)
         else:
             binding.expert_forward(layer, x, logits, w13, w2, s13, s2, adapter=oft, chunk_experts=cfg.chunk,
-                                   out=out, ws=ws)
+                                   out=out, ws=ws, g13=g13, g2=g2)
 
     for _ in range(args.warmup):
         step()
@@ -154,10 +159,11 @@ def main():
                                          timed=True)[3]
         elif mat:
             _, st = binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
-                                                        chunk_experts=cfg.chunk, out=out, ws=ws, timed=True)
+                                                        chunk_experts=cfg.chunk, out=out, ws=ws, timed=True,
+                                                        g13=g13, g2=g2)
         else:
             _, st = binding.expert_forward_timed(layer, x, logits, w13, w2, s13, s2, adapter=oft,
-                                                 chunk_experts=cfg.chunk, out=out, ws=ws)
+                                                 chunk_experts=cfg.chunk, out=out, ws=ws, g13=g13, g2=g2)
         for s, (ms, n) in st.items():
             stage_ms[s] += ms
             stage_n[s] += n
@@ -170,7 +176,7 @@ def main():
 
     sec = ms_per_step / 1e3
     peak = MFMA_PEAK[cfg.fmt]
-    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4", 4: "fp8"}[cfg.fmt]
+    fmt_name = {1: "int4", 2: "fp8", 3: "mxfp4", 4: "fp8", 5: "nvfp4"}[cfg.fmt]
     bm = binding.tile_rows(layer)
     if bwd:
         # recompute (forward INT4 GEMM1) and the backward GEMM pair: 4 + 6 R H I FLOPs;

@@ -7,8 +7,9 @@
  * frozen low-precision weights are dequantized temporarily for a grouped
  * GEMM and released afterwards.  Weight formats: INT4 (Kimi INT4 base, same
  * page), FP8 E4M3 with [128,128] fp32 block scales and [1,128] activation
- * scales (NeMo RL FP8 post, Table 1), MXFP4 (named as a serving format in
- * the mixed-precision sampler post).  The optional BF16 adapter is an OFT
+ * scales (NeMo RL FP8 post, Table 1), MXFP4 and NVFP4 (named as serving
+ * formats in the mixed-precision sampler post, which defines neither; both
+ * follow their public definitions).  The optional BF16 adapter is an OFT
  * orthogonal rotation of the expert input (Orbit analysis page, section on
  * why OFT matters); passing no adapter gives the frozen base, i.e. the
  * reference policy of that page.
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_LP_ABI_VERSION 3
+#define MOE_LP_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -65,7 +66,15 @@ typedef enum {
    * scales must be exact powers of two (fp32, only their exponent is used);
    * activation scales are the smallest power of two >= fl32(amax/448).  The
    * GEMMs then apply both scales inside the block-scaled MFMA. */
-  MOE_W_FP8_E4M3_B128_POW2 = 4
+  MOE_W_FP8_E4M3_B128_POW2 = 4,
+  /* NVFP4 (named as a serving format in the mixed-precision sampler post;
+   * this is the format's public definition): E2M1 codes (low nibble
+   * first), an E4M3 scale byte per (n, 16 consecutive k), and one fp32
+   * second-level scale per expert matrix (moe_scales.g13 / g2):
+   * w = e2m1(q) * e4m3(s) * g.  Activations into the GEMMs: 16-bit floats,
+   * as for INT4.  Forward only (no adapter, no materialized mode, no
+   * backward: those entry points return MOE_ERR_UNSUPPORTED). */
+  MOE_W_NVFP4 = 5
 } moe_wformat;
 
 /* Layer description (host memory). */
@@ -90,14 +99,19 @@ typedef struct {
 } moe_qweights;
 
 /* Scales, layouts per format.  Group scales (one per output row n and 32
- * consecutive k) are stored group-major, [K/32][N] per expert, so that the
- * scales of one K step for a block of output rows are contiguous:
+ * or 16 consecutive k) are stored group-major, [K/32][N] per expert, so that
+ * the scales of one K step for a block of output rows are contiguous:
  *   INT4 : s13 bf16 [E][H/32][2I],   s2 bf16 [E][I/32][H]
  *   FP8, FP8_POW2: s13 fp32 [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]
- *   MXFP4: s13 u8   [E][H/32][2I],   s2 u8   [E][I/32][H]  (E8M0) */
+ *   MXFP4: s13 u8   [E][H/32][2I],   s2 u8   [E][I/32][H]  (E8M0)
+ *   NVFP4: s13 u8   [E][H/16][2I],   s2 u8   [E][I/16][H]  (E4M3, positive),
+ *          g13, g2 fp32 [E] (device; 4-byte aligned).  g13 / g2 are read
+ *          only for NVFP4 and may be NULL otherwise. */
 typedef struct {
   const void* s13;
   const void* s2;
+  const float* g13;
+  const float* g2;
 } moe_scales;
 
 /* Routing result (all device arrays, caller-owned).  R = T*k.

@@ -15,7 +15,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_lp.
 _lib = None
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2 = 1, 2, 3, 4
+FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2, FMT_NVFP4 = 1, 2, 3, 4, 5
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_rows",
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
@@ -37,7 +37,7 @@ class MoeQWeights(ctypes.Structure):
 
 
 class MoeScales(ctypes.Structure):
-    _fields_ = [("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+    _fields_ = [("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("g13", ctypes.c_void_p), ("g2", ctypes.c_void_p)]
 
 
 class MoeRouteOut(ctypes.Structure):
@@ -171,14 +171,15 @@ def route_permute(logits: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None
 
 
 def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, w2, s13, s2, adapter=None,
-                   chunk_experts: int = 1, out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+                   chunk_experts: int = 1, out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                   g13=None, g2=None):
     """moe_expert_forward: x [T][H] bf16, logits [T][E] fp32 -> out [T][H] bf16."""
     if out is None:
         out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     _check(lib().moe_expert_forward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
                                     _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws), ws.numel(), _stream()),
            "moe_expert_forward")
@@ -186,7 +187,7 @@ def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, 
 
 
 def expert_forward_timed(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=None, chunk_experts: int = 1,
-                         out=None, ws=None):
+                         out=None, ws=None, g13=None, g2=None):
     """moe_expert_forward_timed: same result, plus per-stage event times.
     Returns (out, {stage: (ms, launches)})."""
     if out is None:
@@ -194,7 +195,7 @@ def expert_forward_timed(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=N
     if ws is None:
         ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     ms = (ctypes.c_float * len(STAGES))()
     n = (ctypes.c_int32 * len(STAGES))()
     _check(lib().moe_expert_forward_timed(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
@@ -208,7 +209,7 @@ def materialized_workspace_bytes(layer: MoeLayer, chunk_experts: int) -> int:
 
 
 def expert_forward_materialized(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=None, chunk_experts: int = 1,
-                                out=None, ws=None, timed: bool = False):
+                                out=None, ws=None, timed: bool = False, g13=None, g2=None):
     """moe_expert_forward_materialized: per chunk, the experts' BF16 copy in ws,
     then BF16 GEMMs.  Returns out, or (out, {stage: (ms, launches)}) if timed."""
     if out is None:
@@ -216,7 +217,7 @@ def expert_forward_materialized(layer: MoeLayer, x, logits, w13, w2, s13, s2, ad
     if ws is None:
         ws = alloc_workspace(materialized_workspace_bytes(layer, chunk_experts), x.device)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     ms = (ctypes.c_float * len(STAGES))() if timed else None
     n = (ctypes.c_int32 * len(STAGES))() if timed else None
     _check(lib().moe_expert_forward_materialized(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
@@ -240,7 +241,7 @@ def prepare_backward_weights(layer: MoeLayer, w13, w2, s13, s2, out: torch.Tenso
     if out is None:
         out = torch.empty(n, dtype=torch.uint8, device=w13.device)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), None, None)
     _check(lib().moe_prepare_backward_weights(ctypes.byref(layer), ctypes.byref(qw), ctypes.byref(sc), _ptr(out),
                                               out.numel(), _stream()), "moe_prepare_backward_weights")
     return out
@@ -265,7 +266,7 @@ def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d
     if ws is None:
         ws = alloc_workspace(backward_workspace_bytes(layer, chunk_experts), dev)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), None, None)
     ms = (ctypes.c_float * len(STAGES))() if timed else None
     n = (ctypes.c_int32 * len(STAGES))() if timed else None
     _check(lib().moe_expert_backward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),

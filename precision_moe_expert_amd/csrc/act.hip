@@ -5,8 +5,10 @@
 
 namespace moe {
 
-// x bf16 [T][H] -> fp16 in the INT4-path layout (groups of 8 stored in the
-// order 0,4,1,5,2,6,3,7).  bf16 -> fp16 is exact for |x| in [2^-14, 65504].
+// x bf16 [T][H] -> fp16, in the INT4-path layout (I4ORDER: groups of 8 stored
+// in the order 0,4,1,5,2,6,3,7) or in natural order (the NVFP4 path).
+// bf16 -> fp16 is exact for |x| in [2^-14, 65504].
+template <bool I4ORDER>
 __global__ __launch_bounds__(256) void k_act_f16(const uint16_t* __restrict__ x, int64_t n8,
                                                  uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -20,10 +22,17 @@ __global__ __launch_bounds__(256) void k_act_f16(const uint16_t* __restrict__ x,
     f[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
   }
   uint4 o;
-  o.x = pack_f16x2(f[0], f[4]);
-  o.y = pack_f16x2(f[1], f[5]);
-  o.z = pack_f16x2(f[2], f[6]);
-  o.w = pack_f16x2(f[3], f[7]);
+  if (I4ORDER) {
+    o.x = pack_f16x2(f[0], f[4]);
+    o.y = pack_f16x2(f[1], f[5]);
+    o.z = pack_f16x2(f[2], f[6]);
+    o.w = pack_f16x2(f[3], f[7]);
+  } else {
+    o.x = pack_f16x2(f[0], f[1]);
+    o.y = pack_f16x2(f[2], f[3]);
+    o.z = pack_f16x2(f[4], f[5]);
+    o.w = pack_f16x2(f[6], f[7]);
+  }
   reinterpret_cast<uint4*>(out)[i] = o;
 }
 
@@ -207,7 +216,12 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
 void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s) {
   const int64_t n8 = (int64_t)T * H / 8;
   if (n8 == 0) return;
-  hipLaunchKernelGGL(k_act_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
+  hipLaunchKernelGGL(k_act_f16<true>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
+}
+void launch_act_f16_natural(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s) {
+  const int64_t n8 = (int64_t)T * H / 8;
+  if (n8 == 0) return;
+  hipLaunchKernelGGL(k_act_f16<false>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, out);
 }
 void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, bool pow2,
                     hipStream_t s) {

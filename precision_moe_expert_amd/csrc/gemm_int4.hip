@@ -1,4 +1,6 @@
-// Grouped expert GEMMs for INT4 group-32 weights on gfx950.
+// Grouped expert GEMMs for 4-bit weights with 16-bit activations on gfx950:
+// INT4 group-32 (bf16 scales) and NVFP4 (E2M1 values, an E4M3 scale per 16
+// along K, an fp32 second-level scale per expert matrix).
 //
 // Dequantization (Orbit announcement, 技术细节: the active experts' weights
 // are dequantized temporarily for the grouped GEMM) happens in registers:
@@ -20,9 +22,24 @@
 
 namespace moe {
 
+// NVFP4: 8 E2M1 codes (element i in bits 4i..4i+3) times the block scale s
+// -> 8 fp16 in natural order.  The hardware conversion decodes each byte's
+// two codes exactly (its scale operand takes only a power of two, so 1.0);
+// q * s is exact in fp16 (at most 2 + 4 significant bits).
+MOE_DEV f16x8 e2m1x8_to_f16(uint32_t w, f16x2 s2) {
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  f16x8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+  return r;
+}
+
 // One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
-// 128 gate + 128 up weight rows; GEMM2: 256 output columns).
-template <int BM, bool G1>
+// 128 gate + 128 up weight rows; GEMM2: 256 output columns).  NV: NVFP4
+// weights (activations and h in natural order, results times the expert's
+// second-level scale); else INT4 (activations and h in the unpack order).
+template <int BM, bool G1, bool NV>
 __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
   constexpr int MT = BM / 16;
   using ST = I4Stage<BM>;
@@ -44,13 +61,19 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   }
   // per-lane global sources of this item's DMA pieces (K offset added per step)
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
-  const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * 2;
+  const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * (NV ? 1 : 2);
   const char* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
-  // group scales: lane l < 32 takes 8 consecutive weight rows of group l/8
+  // group scales: INT4 lane l < 32 takes 8 consecutive weight rows (bf16)
+  // of 32-group l/8; NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
+  // bytes) of 16-group l/4.  Either way 16 bytes, 512 per wave and step.
   const char* bssrc;
-  {
+  if constexpr (NV) {
+    const int g = (lane >> 2) & 7, pc = lane & 3;
+    const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
+    bssrc = sexp + (int64_t)g * p.N + c;
+  } else {
     const int g = (lane >> 3) & 3, pc = lane & 7;
     const int c = G1 ? (pc < 4 ? col[0] + pc * 8 : col[2] + (pc - 4) * 8) : col[0] + pc * 8;
     bssrc = sexp + ((int64_t)g * p.N + c) * 2;
@@ -72,7 +95,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-    if (lane < 32) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * 512);
+    if (lane < 32) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * 512);  // 8 N per step either way
   };
   f32x4 acc[MT][4];
 #pragma unroll
@@ -89,16 +112,24 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
     u32x4 bq[4];
-    f16x2 s2[4], s2_16[4];
+    f16x2 s2[4], s2_16[4];  // NVFP4: the scales of 16-groups 2 lg and 2 lg + 1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
-      const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * 512 + lg * 128 +
-                                                             (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
-      const float sf = bf16_bits_to_f32(sw);
-      const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
-      s2[i] = (f16x2){sh, sh};
-      s2_16[i] = (f16x2){sh16, sh16};
+      if constexpr (NV) {
+        const uint8_t* sr = st + ST::BS_OFF + wave * 512 + i * 16 + ln;
+        const uint32_t codes = (uint32_t)sr[(2 * lg) * 64] | ((uint32_t)sr[(2 * lg + 1) * 64] << 8);
+        const f16x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
+        s2[i] = (f16x2){sv[0], sv[0]};
+        s2_16[i] = (f16x2){sv[1], sv[1]};
+      } else {
+        const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * 512 + lg * 128 +
+                                                               (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
+        const float sf = bf16_bits_to_f32(sw);
+        const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
+        s2[i] = (f16x2){sh, sh};
+        s2_16[i] = (f16x2){sh16, sh16};
+      }
     }
     // activation fragment of row block m, 32-K sub-step s: logical part 4*lg + s
     auto read_a = [&](int m, int s) {
@@ -120,7 +151,9 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
       __builtin_amdgcn_sched_barrier(0);
       f16x8 bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bf[i] = int4x8_to_f16(dword_of(bq[i], s), s2[i], s2_16[i]);
+      for (int i = 0; i < 4; ++i)
+        bf[i] = NV ? e2m1x8_to_f16(dword_of(bq[i], s), s < 2 ? s2[i] : s2_16[i])
+                   : int4x8_to_f16(dword_of(bq[i], s), s2[i], s2_16[i]);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -131,6 +164,14 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 
   // Epilogue: results go through LDS (the stage buffers are free once every
   // wave has passed the barrier below) so that global stores are 16 B per lane.
+  // NVFP4 results take the expert matrix's second-level scale here.
+  if constexpr (NV) {
+    const float gs = ld_uniform_f32(p.gscale + tl.e);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[m][i] *= gs;
+  }
   lds_barrier();
   if (G1 && p.save_ab) {
     // backward recompute: the gate and up pre-activations in fp32, each at its W13 row index
@@ -157,7 +198,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
           const float hv = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
           const _Float16 hh = (_Float16)hv;
           // h is stored in the activation order that GEMM2's unpack expects
-          *reinterpret_cast<uint16_t*>(smem + row * HS + i4act_pos(wave * 32 + n * 16 + ln) * 2) =
+          const int c = wave * 32 + n * 16 + ln;
+          *reinterpret_cast<uint16_t*>(smem + row * HS + (NV ? c : i4act_pos(c)) * 2) =
               __builtin_bit_cast(uint16_t, hh);
         }
       }
@@ -195,8 +237,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 // Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
 // items of chunk p2.chunk (either may be empty), dealt through per-XCD
 // atomic work counters exactly as for the FP8 weights.
-template <int BM>
-__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+template <int BM, bool NV>
+__device__ __forceinline__ void w4_pair(const GemmArgs& p1, const GemmArgs& p2, int32_t* queue) {
   using ST = I4Stage<BM>;
   constexpr int S = ST::S;
   static_assert(S >= 2 && S <= 7, "LDS stages");
@@ -219,11 +261,34 @@ __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) i4_item<BM, true>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
-    else i4_item<BM, false>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (cur < len1) i4_item<BM, true, NV>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else i4_item<BM, false, NV>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;
+  }
+}
+
+template <int BM>
+__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  w4_pair<BM, false>(p1, p2, queue);
+}
+
+template <int BM>
+__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
+  w4_pair<BM, true>(p1, p2, queue);
+}
+
+void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                            hipStream_t s) {
+  switch (bm) {
+    case 16: launch_persistent2<k_gemm_nvfp4<16>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_nvfp4<32>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_nvfp4<64>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_nvfp4<48>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_nvfp4<96>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_nvfp4<128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_nvfp4<192>>(g1, g2, queue, grid, s); break;
   }
 }
 

@@ -53,6 +53,8 @@ struct GemmArgs {
   const uint8_t* hq;
   const void* hsc;
   int hsc_stride;
+  // NVFP4: per-expert fp32 second-level scale of this GEMM's weight matrix
+  const float* gscale;
 };
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
@@ -64,6 +66,8 @@ inline int64_t max_row_tiles(int64_t R, int E) { return R / 16 + E; }
 
 // Activation preparation (per token rows, no adapter).
 void launch_act_f16(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
+// bf16 -> fp16 in natural element order (the NVFP4 GEMMs' input)
+void launch_act_f16_natural(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
 // Activation scale rows (FP8: fp32 per 128, MXFP8: E8M0 per 32, i.e. 4 bytes
 // per 128-wide K step either way) are padded to a multiple of 16 bytes, so a
 // GEMM can fetch the scales of 4 consecutive K steps of a row as one
@@ -117,6 +121,8 @@ void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // Grouped GEMMs; bm = rows per tile (16, 32, 48, 64, 96, 128 or 192).  One
 // launch runs chunk g1.chunk's GEMM1 and chunk g2.chunk's GEMM2 (either may
 // be empty); queue: 8 zeroed per-XCD item counters for this launch.
+void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
+                            hipStream_t s);
 void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

@@ -32,6 +32,7 @@ struct Dims {
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Validates the descriptor (pointer checks are done by each entry point).
 moe_status check_layer(const moe_layer* L, Dims* d) {
@@ -40,7 +41,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
     return MOE_ERR_INVALID_ARGUMENT;
   if (L->top_k > L->num_experts) return MOE_ERR_INVALID_ARGUMENT;
   if (L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_FP8_E4M3_B128 && L->wformat != MOE_W_MXFP4 &&
-      L->wformat != MOE_W_FP8_E4M3_B128_POW2)
+      L->wformat != MOE_W_FP8_E4M3_B128_POW2 && L->wformat != MOE_W_NVFP4)
     return MOE_ERR_INVALID_ARGUMENT;
   if (L->oft_block != 0 && L->oft_block != 32) return MOE_ERR_UNSUPPORTED;
   if (L->adapter_expert_stride < 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -95,7 +96,7 @@ WsLayout layout(const Dims& d) {
   w.queue = take((size_t)queue_ints(d) * 4);
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
   const size_t arows = d.oft ? R : T;
-  if (d.fmt == MOE_W_INT4_G32_BF16) {
+  if (d.fmt == MOE_W_INT4_G32_BF16 || d.fmt == MOE_W_NVFP4) {
     w.act = take(arows * H * 2);
     w.act_scale = take(0);
     w.h = take(R * I * 2);
@@ -124,7 +125,7 @@ int choose_bm(const Dims& d) {
   const int64_t mean = d.R / d.E;
   if (mean <= 16) return 16;
   if (mean <= 32) return 32;
-  if (d.fmt == MOE_W_INT4_G32_BF16) return 64;
+  if (d.fmt == MOE_W_INT4_G32_BF16 || d.fmt == MOE_W_NVFP4) return 64;
   if (mean <= 96) return 64;
   return 128;
 }
@@ -282,6 +283,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   const void* ptrs[] = {x_bf16, logits, qw->w13, qw->w2, sc->s13, sc->s2, out_bf16, ws};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.fmt == MOE_W_NVFP4 && (sc->g13 == nullptr || sc->g2 == nullptr || !aligned4(sc->g13) || !aligned4(sc->g2)))
+    return MOE_ERR_INVALID_ARGUMENT;
   if (d.oft && !aligned16(adapter_bf16)) return MOE_ERR_INVALID_ARGUMENT;
   if (d.oft && (layer->adapter_expert_stride % 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
   const WsLayout wl = layout(d);
@@ -325,6 +328,8 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
                      sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
     else
       launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
+  } else if (d.fmt == MOE_W_NVFP4) {
+    launch_act_f16_natural(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
     launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H),
                    d.pow2, s);
@@ -364,6 +369,11 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   if (d.fmt == MOE_W_INT4_G32_BF16) {
     g1.w_expert_bytes = n13 / 2; g1.ws_expert_elems = n13 / 32;
     g2.w_expert_bytes = n2 / 2;  g2.ws_expert_elems = n2 / 32;
+  } else if (d.fmt == MOE_W_NVFP4) {
+    g1.w_expert_bytes = n13 / 2; g1.ws_expert_elems = n13 / 16;
+    g2.w_expert_bytes = n2 / 2;  g2.ws_expert_elems = n2 / 16;
+    g1.gscale = sc->g13;
+    g2.gscale = sc->g2;
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
     g1.w_expert_bytes = n13; g1.ws_expert_elems = n13 / (128 * 128);
     g2.w_expert_bytes = n2;  g2.ws_expert_elems = n2 / (128 * 128);
@@ -391,6 +401,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   // launch c runs chunk c's GEMM1 together with chunk c-1's GEMM2
   const int grid = grid1 > grid2 ? grid1 : grid2;
   auto pair = d.fmt == MOE_W_INT4_G32_BF16 ? launch_gemm_int4_pair
+            : d.fmt == MOE_W_NVFP4         ? launch_gemm_nvfp4_pair
             : d.fmt == MOE_W_FP8_E4M3_B128 ? (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)
                                            : launch_gemm_mxfp4_pair;
   for (int c = 0; c <= nchunks; ++c) {
@@ -468,6 +479,7 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
+  if (d.fmt == MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
   if (d.T == 0) return MOE_OK;
@@ -585,6 +597,7 @@ BwdWeights bwd_weights_layout(const Dims& d) {
 moe_status check_backward(const moe_layer* L, Dims* d) {
   moe_status st = check_layer(L, d);
   if (st != MOE_OK) return st;
+  if (d->fmt == MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
   if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
@@ -933,7 +946,7 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
 
 size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   Dims d;
-  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1 || d.fmt == MOE_W_NVFP4) return 0;
   return mat_layout(d, chunk_experts < d.E ? chunk_experts : d.E).total;
 }
 

@@ -31,19 +31,22 @@ class DevInputs:
         self.s13 = dev(li.s13)
         self.s2 = dev(li.s2)
         self.oft = dev(li.oft, "bf16") if li.oft is not None else None
+        self.g13 = dev(li.g13) if li.g13 is not None else None
+        self.g2 = dev(li.g2) if li.g2 is not None else None
         self.layer = binding.make_layer(c.T, c.H, c.I, c.E, c.k, c.fmt, oft=li.oft is not None)
 
     def forward(self, chunk=None, out=None, ws=None):
         c = self.li.cfg
         return binding.expert_forward(self.layer, self.x, self.logits, self.w13, self.w2, self.s13, self.s2,
                                       adapter=self.oft, chunk_experts=c.chunk if chunk is None else chunk,
-                                      out=out, ws=ws)
+                                      out=out, ws=ws, g13=self.g13, g2=self.g2)
 
     def forward_materialized(self, chunk=None, out=None, ws=None):
         c = self.li.cfg
         return binding.expert_forward_materialized(self.layer, self.x, self.logits, self.w13, self.w2, self.s13,
                                                    self.s2, adapter=self.oft,
-                                                   chunk_experts=c.chunk if chunk is None else chunk, out=out, ws=ws)
+                                                   chunk_experts=c.chunk if chunk is None else chunk, out=out, ws=ws,
+                                                   g13=self.g13, g2=self.g2)
 
 
 def bf16_to_np(t: torch.Tensor) -> np.ndarray:

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = binding.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -63,7 +63,7 @@ FAKE = 1 << 20  # aligned non-null address; never dereferenced because validatio
 
 def _fwd(layer, x=FAKE, lg=FAKE, w=FAKE, adapter=None, chunk=1, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
     qw = binding.MoeQWeights(w, w)
-    sc = binding.MoeScales(w, w)
+    sc = binding.MoeScales(w, w, None, None)
     return binding.lib().moe_expert_forward(ctypes.byref(layer), x, lg, ctypes.byref(qw), ctypes.byref(sc), adapter,
                                             chunk, out, ws, ws_bytes, None)
 
@@ -88,6 +88,31 @@ def test_forward_rejects_bad_layer(case, expect):
         assert _fwd(L, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
     else:
         assert _fwd(L) == expect
+
+
+def test_nvfp4_host_checks():
+    """NVFP4: forward workspace as for INT4 (16-bit activations); the
+    second-level scale pointers are required; the adapter, the materialized
+    mode and the backward are not supported for this format."""
+    Ln = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4)
+    Li = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
+    assert binding.workspace_bytes(Ln, 4) == binding.workspace_bytes(Li, 4) > 0
+    lib = binding.lib()
+
+    def fwd(g13, g2, ws_bytes=0):
+        qw = binding.MoeQWeights(FAKE, FAKE)
+        sc = binding.MoeScales(FAKE, FAKE, g13, g2)
+        return lib.moe_expert_forward(ctypes.byref(Ln), FAKE, FAKE, ctypes.byref(qw), ctypes.byref(sc), None, 1,
+                                      FAKE, FAKE, ws_bytes, None)
+    assert fwd(None, FAKE) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert fwd(FAKE, FAKE + 2) == binding.MOE_ERR_INVALID_ARGUMENT           # misaligned fp32
+    assert fwd(FAKE, FAKE + 4) == binding.MOE_ERR_WORKSPACE_TOO_SMALL        # valid; the workspace fails
+    Lo = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4, oft=True)
+    assert _fwd(Lo, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.materialized_workspace_bytes(Ln, 4) == 0
+    assert _mat(Ln) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.backward_weights_bytes(Ln) == 0
+    assert binding.backward_workspace_bytes(Ln, 4) == 0
 
 
 def test_forward_rejects_bad_pointers_and_workspace():
@@ -123,7 +148,7 @@ def test_other_entry_points_reject_bad_args():
 
 def _mat(layer, chunk=1, ws_bytes=1 << 40, ms=None, n=None, x=FAKE):
     qw = binding.MoeQWeights(FAKE, FAKE)
-    sc = binding.MoeScales(FAKE, FAKE)
+    sc = binding.MoeScales(FAKE, FAKE, None, None)
     return binding.lib().moe_expert_forward_materialized(ctypes.byref(layer), x, FAKE, ctypes.byref(qw),
                                                          ctypes.byref(sc), None, chunk, FAKE, FAKE, ws_bytes, None,
                                                          ms, n)

@@ -51,6 +51,10 @@ def test_kimi_k2_int4_oft_full():
     run_full("c3", 16)
 
 
+def test_deepseek_v3_nvfp4_zipf_full():
+    run_full("c4n", 16)
+
+
 def test_deepseek_v3_mxfp4_zipf_full_and_chunk_sweep():
     d, out = run_full("c4", 16, chunk=32)
     ref = out.clone()

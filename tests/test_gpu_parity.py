@@ -58,7 +58,7 @@ def test_route_bitexact_edge(T, E, k):
     check_route(lg, k, E)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_forward_small_vs_oracle(fmt):
     cfg = small(fmt)
     li = synth.make_inputs(cfg)
@@ -91,7 +91,7 @@ def test_forward_c1_vs_oracle():
     assert err.max() <= gu.ROW_TOL
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_forward_max_experts_and_top_k(fmt):
     """E = 1024 (the library's maximum) with top-16 routing: about 500 active
     experts, most with one or two rows, a few (Zipf bias) with up to ~50;
@@ -105,7 +105,7 @@ def test_forward_max_experts_and_top_k(fmt):
     assert err.max() <= gu.ROW_TOL
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_chunk_size_bitwise_invariance(fmt):
     cfg = small(fmt, E=9, k=3, zipf=1.2)
     d = gu.DevInputs(synth.make_inputs(cfg))
@@ -115,7 +115,7 @@ def test_chunk_size_bitwise_invariance(fmt):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_run_twice_bitwise(fmt):
     d = gu.DevInputs(synth.make_inputs(small(fmt)))
     a = d.forward().clone()
@@ -174,7 +174,7 @@ def test_t0_is_noop():
     assert out.shape == (0, 256)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
 def test_forward_every_tile_height(fmt, tile_rows):
     """Each grouped-GEMM tile height against the oracle: ~250 rows per expert,
