@@ -220,7 +220,7 @@ def main():
         if stage_ms["dequant"] > g_ms:
             dom, launches, f_dom, b_dom = "dequant", stage_n["dequant"], 0.0, deq_b
             launch_ms = stage_ms["dequant"] / max(launches, 1)
-            kname = f"k_dequant_chunk<{ {1: 1, 2: 2, 3: 3, 4: 2}[cfg.fmt] }>"
+            kname = f"k_dequant_chunk<{ {1: 1, 2: 2, 3: 3, 4: 2, 5: 5}[cfg.fmt] }>"
         else:
             dom, launches = "gemm", stage_n["gemm1"] + stage_n["gemm2"]
             launch_ms = g_ms / max(launches, 1)

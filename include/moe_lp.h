@@ -72,8 +72,8 @@ typedef enum {
    * first), an E4M3 scale byte per (n, 16 consecutive k), and one fp32
    * second-level scale per expert matrix (moe_scales.g13 / g2):
    * w = e2m1(q) * e4m3(s) * g.  Activations into the GEMMs: 16-bit floats,
-   * as for INT4.  Forward only (no adapter, no materialized mode, no
-   * backward: those entry points return MOE_ERR_UNSUPPORTED). */
+   * as for INT4.  Forward and materialized forward; no adapter and no
+   * backward (those return MOE_ERR_UNSUPPORTED). */
   MOE_W_NVFP4 = 5
 } moe_wformat;
 

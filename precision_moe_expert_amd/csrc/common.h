@@ -16,7 +16,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #define MOE_DEV __device__ __forceinline__
 
 // Format ids (same values as moe_wformat).
-enum { FMT_INT4 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3 };
+enum { FMT_INT4 = 1, FMT_FP8 = 2, FMT_MXFP4 = 3, FMT_NVFP4 = 5 };
 
 MOE_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

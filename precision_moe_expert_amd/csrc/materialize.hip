@@ -47,8 +47,8 @@ MOE_DEV uint32_t bf16_of_product(float a, float s) {
 // wave's loads and stores are contiguous.  Each thread loads four units
 // before converting any, to keep four loads in flight per wave.
 struct Raw8 {
-  uint2 q;       // FP8: 8 codes; INT4 / MXFP4: 8 nibbles in q.x
-  uint32_t s;    // scale bits (fp32, bf16 or E8M0)
+  uint2 q;       // FP8: 8 codes; INT4 / MXFP4 / NVFP4: 8 nibbles in q.x
+  uint32_t s;    // scale bits (fp32, bf16, E8M0 or E4M3)
 };
 
 template <int FMT>
@@ -60,17 +60,27 @@ MOE_DEV Raw8 load8(const uint8_t* __restrict__ w, const void* __restrict__ sc, i
   } else {
     r.q.x = *reinterpret_cast<const uint32_t*>(w + ((int64_t)n * K + k0) / 2);
     r.q.y = 0;
-    const int si = (k0 / 32) * N + n;  // group-major [K/32][N]
+    const int si = (k0 / (FMT == FMT_NVFP4 ? 16 : 32)) * N + n;  // group-major [K/32][N] ([K/16][N])
     r.s = FMT == FMT_INT4 ? (uint32_t) static_cast<const uint16_t*>(sc)[si]
                           : (uint32_t) static_cast<const uint8_t*>(sc)[si];
   }
   return r;
 }
 
+// g: the matrix's NVFP4 second-level scale (unused by the other formats).
 template <int FMT>
-MOE_DEV uint4 cvt8(const Raw8& r) {
+MOE_DEV uint4 cvt8(const Raw8& r, float g) {
   uint32_t o[4];
-  if (FMT == FMT_FP8) {
+  if (FMT == FMT_NVFP4) {
+    const float s = e4m3_to_f32(r.s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = r.q.x >> (i * 8);
+      // E2M1 times an E4M3 scale is exact in fp32; the product with g is
+      // rounded once to bf16
+      o[i] = bf16_of_product(e2m1_to_f32(b & 15u) * s, g) | (bf16_of_product(e2m1_to_f32((b >> 4) & 15u) * s, g) << 16);
+    }
+  } else if (FMT == FMT_FP8) {
     const float s = __uint_as_float(r.s);
     const uint32_t qs[2] = {r.q.x, r.q.y};
 #pragma unroll
@@ -106,7 +116,8 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
                                                        const uint8_t* __restrict__ w2, const void* __restrict__ s2,
                                                        const int32_t* __restrict__ active,
                                                        const int32_t* __restrict__ num_active, int chunk, int C,
-                                                       int H, int I, uint16_t* __restrict__ scratch) {
+                                                       int H, int I, const float* __restrict__ g13,
+                                                       const float* __restrict__ g2, uint16_t* __restrict__ scratch) {
   const int na = *num_active;
   const int slot = blockIdx.y;
   const int a = chunk * C + slot;
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
   const int e = active[a];
   const int64_t n13 = (int64_t)2 * I * H, n2 = (int64_t)H * I;
   constexpr int64_t WB = FMT == FMT_FP8 ? 1 : 2;                 // weights per byte
-  constexpr int64_t SB = FMT == FMT_FP8 ? 128 * 128 : 32;        // weights per scale
+  constexpr int64_t SB = FMT == FMT_FP8 ? 128 * 128 : FMT == FMT_NVFP4 ? 16 : 32;  // weights per scale
   constexpr int64_t SZ = FMT == FMT_FP8 ? 4 : FMT == FMT_INT4 ? 2 : 1;  // scale bytes
   const int u13 = (int)(n13 / 8), total = (int)((n13 + n2) / 8);
   const int KU1 = H / 8, KU2 = I / 8;
@@ -123,6 +134,7 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
   const char* s13e = static_cast<const char*>(s13) + (int64_t)e * (n13 / SB) * SZ;
   const char* s2e = static_cast<const char*>(s2) + (int64_t)e * (n2 / SB) * SZ;
   uint16_t* dst = scratch + (int64_t)slot * (n13 + n2);
+  const float ga = FMT == FMT_NVFP4 ? g13[e] : 1.0f, gb = FMT == FMT_NVFP4 ? g2[e] : 1.0f;
   const int stride = gridDim.x * 256;
   constexpr int U = 4;
   for (int u0 = blockIdx.x * 256 + threadIdx.x; u0 < total; u0 += U * stride) {
@@ -141,26 +153,29 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int u = u0 + j * stride;
-      if (u < total) *reinterpret_cast<uint4*>(dst + (int64_t)u * 8) = cvt8<FMT>(r[j]);
+      if (u < total) *reinterpret_cast<uint4*>(dst + (int64_t)u * 8) = cvt8<FMT>(r[j], u < u13 ? ga : gb);
     }
   }
 }
 
 void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
                           const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
-                          uint16_t* scratch, hipStream_t s) {
+                          const float* g13, const float* g2, uint16_t* scratch, hipStream_t s) {
   // about 4096 workgroups over the chunk's slots, at least 16 per slot
   const int gx = C >= 256 ? 16 : 4096 / C;
   const dim3 grid(gx, C), block(256);
   if (fmt == FMT_INT4)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_INT4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
-                       H, I, scratch);
+                       H, I, g13, g2, scratch);
   else if (fmt == FMT_FP8)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_FP8>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
-                       H, I, scratch);
+                       H, I, g13, g2, scratch);
+  else if (fmt == FMT_NVFP4)
+    hipLaunchKernelGGL(k_dequant_chunk<FMT_NVFP4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk,
+                       C, H, I, g13, g2, scratch);
   else
     hipLaunchKernelGGL(k_dequant_chunk<FMT_MXFP4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk,
-                       C, H, I, scratch);
+                       C, H, I, g13, g2, scratch);
 }
 
 // ------------------------------------------------------------- BF16 GEMM

@@ -479,13 +479,14 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
-  if (d.fmt == MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
   if (d.T == 0) return MOE_OK;
   const void* ptrs[] = {x_bf16, logits, qw->w13, qw->w2, sc->s13, sc->s2, out_bf16, ws};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.fmt == MOE_W_NVFP4 && (sc->g13 == nullptr || sc->g2 == nullptr || !aligned4(sc->g13) || !aligned4(sc->g2)))
+    return MOE_ERR_INVALID_ARGUMENT;
   if (d.oft && !aligned16(adapter_bf16)) return MOE_ERR_INVALID_ARGUMENT;
   if (d.oft && (layer->adapter_expert_stride % 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
   const int C = chunk_experts < d.E ? chunk_experts : d.E;  // a chunk never holds more than E experts
@@ -559,7 +560,8 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   for (int c = 0; c < nchunks; ++c) {
     { Scope sc_(tm, MOE_STAGE_DEQUANT);
       launch_dequant_chunk(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13,
-                           static_cast<const uint8_t*>(qw->w2), sc->s2, active, num_active, c, C, d.H, d.I, copy, s); }
+                           static_cast<const uint8_t*>(qw->w2), sc->s2, active, num_active, c, C, d.H, d.I, sc->g13,
+                           sc->g2, copy, s); }
     g1.chunk = c;
     g2.chunk = -1;
     { Scope sc_(tm, MOE_STAGE_GEMM1); launch_gemm_bf16_pair(g1, g2, queue + 16 * c, bm, grid1, s); }
@@ -946,7 +948,7 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
 
 size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   Dims d;
-  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1 || d.fmt == MOE_W_NVFP4) return 0;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
   return mat_layout(d, chunk_experts < d.E ? chunk_experts : d.E).total;
 }
 

@@ -92,8 +92,8 @@ def test_forward_rejects_bad_layer(case, expect):
 
 def test_nvfp4_host_checks():
     """NVFP4: forward workspace as for INT4 (16-bit activations); the
-    second-level scale pointers are required; the adapter, the materialized
-    mode and the backward are not supported for this format."""
+    second-level scale pointers are required; the adapter and the backward
+    are not supported for this format."""
     Ln = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4)
     Li = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
     assert binding.workspace_bytes(Ln, 4) == binding.workspace_bytes(Li, 4) > 0
@@ -109,8 +109,8 @@ def test_nvfp4_host_checks():
     assert fwd(FAKE, FAKE + 4) == binding.MOE_ERR_WORKSPACE_TOO_SMALL        # valid; the workspace fails
     Lo = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4, oft=True)
     assert _fwd(Lo, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED
-    assert binding.materialized_workspace_bytes(Ln, 4) == 0
-    assert _mat(Ln) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.materialized_workspace_bytes(Ln, 4) == binding.materialized_workspace_bytes(Li, 4) > 0
+    assert _mat(Ln) == binding.MOE_ERR_INVALID_ARGUMENT                     # no second-level scales
     assert binding.backward_weights_bytes(Ln) == 0
     assert binding.backward_workspace_bytes(Ln, 4) == 0
 

@@ -33,7 +33,7 @@ def check(li, chunk=None, tile_rows=0):
     return d
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
 def test_materialized_small_vs_oracle(fmt):
     check(synth.make_inputs(small(fmt)))
 
@@ -42,7 +42,7 @@ def test_materialized_int4_oft_vs_oracle():
     check(synth.make_inputs(small(1, T=53, H=512, I=256, E=9, k=4, oft=True, chunk=2)))
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 5])
 @pytest.mark.parametrize("tile_rows", [16, 32, 64, 128])
 def test_materialized_every_tile_height(fmt, tile_rows):
     """~250 rows per expert: tall tiles run full and ragged; I = 768 gives six
