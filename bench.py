@@ -127,7 +127,8 @@ def main():
     def step():
         if bwd:
             binding.expert_backward(layer, x, logits, w13, w2, s13, s2, bw, d_out, adapter=oft,
-                                    chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad)
+                                    chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad,
+                                    g13=g13, g2=g2)
         elif mat:
             binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
                                                 chunk_experts=cfg.chunk, out=out, ws=ws, g13=g13, g2=g2)
@@ -156,7 +157,7 @@ def main():
         if bwd:
             st = binding.expert_backward(layer, x, logits, w13, w2, s13, s2, bw, d_out, adapter=oft,
                                          chunk_experts=cfg.chunk, ws=ws, d_x=d_x, d_logits=d_lg, d_adapter=d_ad,
-                                         timed=True)[3]
+                                         timed=True, g13=g13, g2=g2)[3]
         elif mat:
             _, st = binding.expert_forward_materialized(layer, x, logits, w13, w2, s13, s2, adapter=oft,
                                                         chunk_experts=cfg.chunk, out=out, ws=ws, timed=True,
@@ -184,14 +185,14 @@ def main():
         R = cfg.T * cfg.k
         w13b = weight_bytes_per_expert(cfg.fmt, 2 * cfg.I, cfg.H)
         w2b = weight_bytes_per_expert(cfg.fmt, cfg.H, cfg.I)
-        fam = {1: 1, 2: 2, 3: 3, 4: 2}[cfg.fmt]
+        fam = {1: 1, 2: 2, 3: 3, 4: 2, 5: 5}[cfg.fmt]
         if stage_ms["gemm1"] > stage_ms["gemm2"]:
             # the forward GEMM1 kernel of the format (pre-activation recompute)
             peak = MFMA_PEAK[cfg.fmt]
             dom, launches = "gemm1", stage_n["gemm1"]
             f_dom = 4.0 * R * cfg.H * cfg.I
             b_dom = (acc["active"] * w13b + act_bytes(cfg.fmt, R if cfg.oft else cfg.T, cfg.H) + R * 2 * cfg.I * 4
-                     + (act_bytes(cfg.fmt, R, cfg.I) if cfg.fmt != 1 else 0))
+                     + (act_bytes(cfg.fmt, R, cfg.I) if cfg.fmt not in (1, 5) else 0))
             if cfg.fmt in (2, 4):
                 kname = f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>"
             else:
@@ -286,7 +287,7 @@ def main():
 
     if not args.no_cpu_baseline:
         import oracle
-        n = args.cpu_tokens or {1: 64, 2: 4096, 3: 64, 4: 64, 5: 64, 6: 4096}[cfg.cfg_id]
+        n = args.cpu_tokens or {1: 64, 2: 4096, 3: 64, 4: 64, 5: 64, 6: 4096, 7: 64}[cfg.cfg_id]
         n = min(n, cfg.T)
         toks = np.arange(n, dtype=np.int32)
         # repeat short samples until about 10 s of oracle work has been timed

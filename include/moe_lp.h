@@ -72,8 +72,8 @@ typedef enum {
    * first), an E4M3 scale byte per (n, 16 consecutive k), and one fp32
    * second-level scale per expert matrix (moe_scales.g13 / g2):
    * w = e2m1(q) * e4m3(s) * g.  Activations into the GEMMs: 16-bit floats,
-   * as for INT4.  Forward and materialized forward; no adapter and no
-   * backward (those return MOE_ERR_UNSUPPORTED). */
+   * as for INT4.  Forward, materialized forward and frozen-base backward;
+   * no adapter (MOE_ERR_UNSUPPORTED). */
   MOE_W_NVFP4 = 5
 } moe_wformat;
 
@@ -233,8 +233,8 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
  * transposed copy of the frozen weights, made once per base. */
 
 /* Bytes of the transposed copy: W13^T [E][H][2I] and W2^T [E][I][H] in the
- * format's codes (INT4 / E2M1 nibbles, E4M3 bytes) plus scales (INT4, MXFP4:
- * one fp16 per group scale; FP8: the fp32 block scales transposed); 0 if the
+ * format's codes (INT4 / E2M1 nibbles, E4M3 bytes) plus scales (INT4, MXFP4,
+ * NVFP4: one fp16 per group scale; FP8: the fp32 block scales transposed); 0 if the
  * layer is not supported by the backward (I multiple of 256; FP8 H and 2I at
  * most 8192; per-expert adapter). */
 size_t moe_backward_weights_bytes(const moe_layer* layer);
@@ -243,8 +243,10 @@ size_t moe_backward_weights_bytes(const moe_layer* layer);
  * caller-owned, >= moe_backward_weights_bytes).  Codes are bit-identical
  * re-layouts; INT4 scales are converted to fp16 (exact for bf16 scales in
  * [2^-10, 4096]) and pre-divided by 16 where the unpack needs it, MXFP4
- * scales to fp16 2^(e-127) (exact within fp16's range), FP8 block scales
- * are transposed. */
+ * scales to fp16 2^(e-127) (exact within fp16's range), NVFP4 E4M3 scales
+ * to fp16 (exact), FP8 block scales are transposed.  NVFP4's fp32
+ * second-level scales are not copied: moe_expert_backward reads them from
+ * its moe_scales (g13 / g2 required there, 4-byte aligned). */
 moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweights* qweights,
                                         const moe_scales* scales, void* bwd_weights, size_t bwd_bytes,
                                         void* stream);
@@ -267,8 +269,8 @@ size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_expert
  * dx_tj = dx' R_e^T, d_x_t = sum_j dx_tj.  Activation quantizers of the
  * FP8 / MXFP4 formats pass gradients straight through; the router term uses
  * h as the forward quantized it.  GEMM operands are fp16 (INT4 and E2M1
- * weights times their scales exactly, E4M3 times the block scale rounded
- * once; d_out and the SwiGLU gradients rounded to fp16, so their magnitudes
+ * weights times their scales exactly, NVFP4's second-level scale applied to
+ * the fp32 accumulators, E4M3 times the block scale rounded once; d_out and the SwiGLU gradients rounded to fp16, so their magnitudes
  * must stay below 65504), accumulation fp32.
  * bwd_weights: from moe_prepare_backward_weights for the same weights.
  * Unsupported layers return MOE_ERR_UNSUPPORTED; the rest as moe_expert_forward.

@@ -252,7 +252,8 @@ def backward_workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
 
 
 def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d_out, adapter=None,
-                    chunk_experts: int = 1, ws=None, d_x=None, d_logits=None, d_adapter=None, timed: bool = False):
+                    chunk_experts: int = 1, ws=None, d_x=None, d_logits=None, d_adapter=None, timed: bool = False,
+                    g13=None, g2=None):
     """moe_expert_backward -> (d_x [T][H] bf16, d_logits [T][E] fp32, d_adapter fp32 or None)
     (+ {stage: (ms, launches)} if timed)."""
     T, H, E = layer.num_tokens, layer.hidden, layer.num_experts
@@ -266,7 +267,7 @@ def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d
     if ws is None:
         ws = alloc_workspace(backward_workspace_bytes(layer, chunk_experts), dev)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
-    sc = MoeScales(_ptr(s13), _ptr(s2), None, None)
+    sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     ms = (ctypes.c_float * len(STAGES))() if timed else None
     n = (ctypes.c_int32 * len(STAGES))() if timed else None
     _check(lib().moe_expert_backward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),

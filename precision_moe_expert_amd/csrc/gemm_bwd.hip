@@ -7,8 +7,10 @@
 // K-contiguous rows for the backward GEMMs.  A group scale of INT4 or MXFP4
 // belongs to (weight row group, K) in the forward orientation, so in the
 // transposed copy it varies along K: every element gets its own scale, kept
-// as fp16 in the pair order the unpack multiplies.  FP8 block scales cover
-// 128 x 128 squares and stay per (row block, K block).
+// as fp16 in the pair order the unpack multiplies.  NVFP4 groups 16 forward
+// K values per E4M3 scale (16-row groups of the transposed copy) and applies
+// its per-matrix fp32 scale to the accumulators, as the forward does.  FP8
+// block scales cover 128 x 128 squares and stay per (row block, K block).
 //
 // k_gemm_bwd<FMT, BM>: the forward INT4 kernel's DMA ring, LDS layout and
 // fp16 16x16x32 MFMA (weights become fp16: INT4 codes and E2M1 values times
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__
 // Group scales [E][G][L] (G groups of the transposed copy's rows, L along its
 // K) -> per 8 consecutive K values four fp16 pairs {s0, s4}, {s1, s5},
 // {s2, s6}, {s3, s7}; INT4 (bf16 scales) divides the odd pairs by 16 for its
-// unpack, MXFP4 turns E8M0 bytes into 2^(e-127).
+// unpack, MXFP4 turns E8M0 bytes into 2^(e-127), NVFP4 E4M3 bytes into their
+// values (exact in fp16: at most 448, at least 2^-9).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_repack_scales_f16(const void* __restrict__ s, int64_t n8,
                                                            u32x4* __restrict__ out) {
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void k_repack_scales_f16(const void* __restric
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t e = (w[j >> 2] >> ((j & 3) * 8)) & 0xFFu;
-        f[j] = __uint_as_float(e ? e << 23 : 0x00400000u);
+        f[j] = FMT == FMT_NVFP4 ? e4m3_to_f32(e) : __uint_as_float(e ? e << 23 : 0x00400000u);
       }
     }
     const float d = FMT == FMT_INT4 ? 0.0625f : 1.0f;
@@ -141,8 +144,11 @@ void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, i
     return;
   }
   hipLaunchKernelGGL(k_repack_int4_t, dim3(tg), dim3(256), 0, stream, w, E, N, K, wt);
-  const int64_t n8 = (int64_t)E * N * K / 32 / 8;
-  if (fmt == FMT_INT4)
+  const int64_t n8 = (int64_t)E * N * K / (fmt == FMT_NVFP4 ? 16 : 32) / 8;
+  if (fmt == FMT_NVFP4)
+    hipLaunchKernelGGL(k_repack_scales_f16<FMT_NVFP4>, dim3(grid_of(n8, 4096)), dim3(256), 0, stream, s, n8,
+                       reinterpret_cast<u32x4*>(st));
+  else if (fmt == FMT_INT4)
     hipLaunchKernelGGL(k_repack_scales_f16<FMT_INT4>, dim3(grid_of(n8, 4096)), dim3(256), 0, stream, s, n8,
                        reinterpret_cast<u32x4*>(st));
   else
@@ -192,7 +198,8 @@ MOE_DEV f16x8 e4m3x8_to_f16(uint32_t lo, uint32_t hi, float p2, f16x2 m2) {
 // LDS of one stage: activation rows (fp16, 256 B each, 16-byte parts
 // XOR-swizzled by row), each wave's weight fragments (4 subtiles x 16 rows x
 // 64 B of nibbles or 128 B of E4M3 codes) and, for INT4 / MXFP4, the fp16
-// scales of the wave's 64 weight rows for the step (2 row groups x 128 K).
+// scales of the wave's 64 weight rows for the step (2 row groups x 128 K;
+// NVFP4 4 row groups of 16).
 template <int FMT, int BM>
 struct BwStage {
   static constexpr int NA = BM / 16;                      // activation DMAs per wave
@@ -200,7 +207,7 @@ struct BwStage {
   static constexpr int B_OFF = A_BYTES;
   static constexpr int NB = FMT == FMT_FP8 ? 8 : 4;       // weight DMAs per wave
   static constexpr int BS_OFF = B_OFF + 4 * NB * 1024;
-  static constexpr int BS = FMT == FMT_FP8 ? 0 : 4 * 512;
+  static constexpr int BS = FMT == FMT_FP8 ? 0 : FMT == FMT_NVFP4 ? 4 * 1024 : 4 * 512;
   static constexpr int BYTES = BS_OFF + BS;
   static constexpr int WPC = (FMT != FMT_FP8 && (BM == 16 || BM == 48 || BM == 64)) ? 2 : 1;
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
@@ -211,7 +218,7 @@ struct BwStage {
 // The row's h value at column col as the forward fed it to GEMM2.
 template <int FMT>
 MOE_DEV float fwd_h(const GemmArgs& p, int r, int col, float a, float b, float sg) {
-  if (FMT == FMT_INT4) return a * sg * b;
+  if (FMT == FMT_INT4 || FMT == FMT_NVFP4) return a * sg * b;
   const float q = e4m3_to_f32(p.hq[(int64_t)r * p.inter + col]);
   const char* sr = static_cast<const char*>(p.hsc) + (int64_t)r * p.hsc_stride;
   if (FMT == FMT_FP8) return q * reinterpret_cast<const float*>(sr)[col / 128];
@@ -240,7 +247,11 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
   for (int i = 0; i < 4; ++i)
     bsrc[i] = wexp + (int64_t)(c0 + 16 * i + ln) * (FMT == FMT_FP8 ? K : K / 2) + lg * (BROW / 4);
   const char* bssrc = nullptr;
-  if (FMT != FMT_FP8) {
+  if (FMT == FMT_NVFP4) {
+    // fp16 scales of the wave's four 16-row groups: 4 runs of 128 K values per step
+    const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * 2;
+    bssrc = sexp + ((int64_t)(c0 / 16 + (lane >> 4)) * K + (lane & 15) * 8) * 2;
+  } else if (FMT != FMT_FP8) {
     // fp16 scales of the wave's two row groups: 2 runs of 128 K values per step
     const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * 2;
     bssrc = sexp + ((int64_t)(c0 / 32 + ((lane >> 4) & 1)) * K + (lane & 15) * 8) * 2;
@@ -269,7 +280,8 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
 #pragma unroll
       for (int h = 0; h < ST::NB / 4; ++h)
         dma_b128(bsrc[i] + kt * BROW + h * 16, sb + ST::B_OFF + ((wave * 4 + i) * (ST::NB / 4) + h) * 1024);
-    if (FMT != FMT_FP8)
+    if (FMT == FMT_NVFP4) dma_b128(bssrc + (int64_t)kt * 256, sb + ST::BS_OFF + wave * 1024);
+    else if (FMT != FMT_FP8)
       if (lane < 32) dma_b128(bssrc + (int64_t)kt * 256, sb + ST::BS_OFF + wave * 512);
   };
   f32x4 acc[MT][4];
@@ -328,9 +340,9 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
           const uint32_t lo = (s & 1) ? q.z : q.x, hi = (s & 1) ? q.w : q.y;
           bf[i] = e4m3x8_to_f16(lo, hi, p2, m2);
         } else {
-          // K values 32 lg + 8 s .. +7 of weight row c0 + 16 i + ln: row group i / 2, octet 4 lg + s
-          const u32x4 sc = *reinterpret_cast<const u32x4*>(st + ST::BS_OFF + wave * 512 + (i >> 1) * 256 +
-                                                           (4 * lg + s) * 16);
+          // K values 32 lg + 8 s .. +7 of weight row c0 + 16 i + ln: row group i / 2 (NVFP4: i), octet 4 lg + s
+          const int soff = FMT == FMT_NVFP4 ? wave * 1024 + i * 256 : wave * 512 + (i >> 1) * 256;
+          const u32x4 sc = *reinterpret_cast<const u32x4*>(st + ST::BS_OFF + soff + (4 * lg + s) * 16);
           bf[i] = FMT == FMT_INT4 ? int4x8_to_f16_se(dword_of(bq[i][0], s), sc)
                                   : e2m1x8_to_f16_se(dword_of(bq[i][0], s), sc);
         }
@@ -341,6 +353,13 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
         for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[i], acc[m][i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if constexpr (FMT == FMT_NVFP4) {
+    const float gs = ld_uniform_f32(p.gscale + tl.e);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[m][i] *= gs;
   }
 
   if (DH) {
@@ -453,6 +472,7 @@ void launch_gemm_bwd_pair(int fmt, const GemmArgs& g1, const GemmArgs& g2, int32
                           hipStream_t s) {
   if (fmt == FMT_INT4) launch_bwd<FMT_INT4>(g1, g2, queue, bm, grid, s);
   else if (fmt == FMT_FP8) launch_bwd<FMT_FP8>(g1, g2, queue, bm, grid, s);
+  else if (fmt == FMT_NVFP4) launch_bwd<FMT_NVFP4>(g1, g2, queue, bm, grid, s);
   else launch_bwd<FMT_MXFP4>(g1, g2, queue, bm, grid, s);
 }
 

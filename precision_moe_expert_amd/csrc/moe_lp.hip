@@ -574,24 +574,25 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   return launch_status();
 }
 // ---------------------------------------------------------------------------
-// Frozen-base backward (INT4 weights).
+// Frozen-base backward (every weight format).
 
 // The transposed weight copy made by moe_prepare_backward_weights.
 struct BwdWeights {
   size_t w13t, w2t, s13, s2, total;
 };
 
-// INT4 / MXFP4: nibbles + fp16 scales (2 bytes per 32 weights); FP8: bytes +
-// fp32 block scales (the forward sizes).
+// INT4 / MXFP4: nibbles + fp16 scales (2 bytes per 32 weights; NVFP4 per 16);
+// FP8: bytes + fp32 block scales (the forward sizes).
 BwdWeights bwd_weights_layout(const Dims& d) {
   BwdWeights b{};
   const size_t H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
   const bool fp8 = d.fmt == MOE_W_FP8_E4M3_B128;
+  const size_t gk = d.fmt == MOE_W_NVFP4 ? 16 : 32;
   size_t o = 0;
   b.w13t = o; o = align_up(o + E * H * 2 * I / (fp8 ? 1 : 2));
   b.w2t = o;  o = align_up(o + E * I * H / (fp8 ? 1 : 2));
-  b.s13 = o;  o = align_up(o + (fp8 ? E * (H / 128) * (2 * I / 128) * 4 : E * (H / 32) * 2 * I * 2));
-  b.s2 = o;   o = align_up(o + (fp8 ? E * (I / 128) * (H / 128) * 4 : E * (I / 32) * H * 2));
+  b.s13 = o;  o = align_up(o + (fp8 ? E * (H / 128) * (2 * I / 128) * 4 : E * (H / gk) * 2 * I * 2));
+  b.s2 = o;   o = align_up(o + (fp8 ? E * (I / 128) * (H / 128) * 4 : E * (I / gk) * H * 2));
   b.total = o;
   return b;
 }
@@ -599,7 +600,6 @@ BwdWeights bwd_weights_layout(const Dims& d) {
 moe_status check_backward(const moe_layer* L, Dims* d) {
   moe_status st = check_layer(L, d);
   if (st != MOE_OK) return st;
-  if (d->fmt == MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
   if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
@@ -648,7 +648,7 @@ BwdLayout bwd_layout(const Dims& d) {
   w.hist = take((size_t)(d.nblk > 0 ? d.nblk : 1) * E * 4);
   w.tile_a_r = take((E + 1) * 4);
   w.tiles_r = take((size_t)max_row_tiles(d.R, d.E) * 16);
-  if (d.fmt == MOE_W_INT4_G32_BF16) {
+  if (d.fmt == MOE_W_INT4_G32_BF16 || d.fmt == MOE_W_NVFP4) {
     w.act = take((d.oft ? R : T) * H * 2);
     w.act_scale = take(0);
     w.h = take(0);
@@ -724,6 +724,8 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   if (d.oft && (!aligned16(adapter_bf16) || !aligned16(d_adapter) || (layer->adapter_expert_stride % 8) != 0))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (d.fmt == MOE_W_NVFP4 && (sc->g13 == nullptr || sc->g2 == nullptr || !aligned4(sc->g13) || !aligned4(sc->g2)))
+    return MOE_ERR_INVALID_ARGUMENT;
   const BwdLayout wl = bwd_layout(d);
   if (ws_bytes < wl.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const BwdWeights bw = bwd_weights_layout(d);
@@ -776,6 +778,8 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   else if (d.fmt == MOE_W_MXFP4)
     launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<uint8_t*>(act_scale), scale_row_bytes(d.H),
                      s);
+  else if (d.fmt == MOE_W_NVFP4)
+    launch_act_f16_natural(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   else if (d.oft)
     launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
                    sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
@@ -795,9 +799,11 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   r1.N = 2 * d.I;
   r1.K = d.H;
   r1.inter = d.I;
-  if (d.fmt == MOE_W_INT4_G32_BF16) {
+  if (d.fmt == MOE_W_INT4_G32_BF16 || d.fmt == MOE_W_NVFP4) {
+    const bool nv = d.fmt == MOE_W_NVFP4;
     r1.w_expert_bytes = n13 / 2;
-    r1.ws_expert_elems = n13 / 32;
+    r1.ws_expert_elems = n13 / (nv ? 16 : 32);
+    r1.gscale = nv ? sc->g13 : nullptr;
     r1.out = ab;
     r1.save_ab = 1;
   } else {
@@ -815,10 +821,12 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   bh.a = gact;
   bh.a_per_token = 1;
   const bool fp8 = d.fmt == MOE_W_FP8_E4M3_B128;
+  const int64_t gk = d.fmt == MOE_W_NVFP4 ? 16 : 32;  // weights per fp16 scale of the transposed copy
   bh.w = reinterpret_cast<const uint8_t*>(bwb + bw.w2t);
   bh.w_scale = bwb + bw.s2;
+  bh.gscale = sc->g2;
   bh.w_expert_bytes = fp8 ? n2 : n2 / 2;
-  bh.ws_expert_elems = fp8 ? n2 / (128 * 128) : n2 / 32;
+  bh.ws_expert_elems = fp8 ? n2 / (128 * 128) : n2 / gk;
   bh.N = d.I;
   bh.K = d.H;
   bh.inter = d.I;
@@ -834,8 +842,9 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   bx.a_per_token = 0;
   bx.w = reinterpret_cast<const uint8_t*>(bwb + bw.w13t);
   bx.w_scale = bwb + bw.s13;
+  bx.gscale = sc->g13;
   bx.w_expert_bytes = fp8 ? n13 : n13 / 2;
-  bx.ws_expert_elems = fp8 ? n13 / (128 * 128) : n13 / 32;
+  bx.ws_expert_elems = fp8 ? n13 / (128 * 128) : n13 / gk;
   bx.N = d.H;
   bx.K = 2 * d.I;
   bx.inter = d.I;
@@ -864,6 +873,7 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
       r1.chunk = c;
       Scope sc_(tm, MOE_STAGE_GEMM1);
       if (d.fmt == MOE_W_INT4_G32_BF16) launch_gemm_int4_pair(r1, none, queue + 16 * c, bm_r, gridr, s);
+      else if (d.fmt == MOE_W_NVFP4) launch_gemm_nvfp4_pair(r1, none, queue + 16 * c, bm_r, gridr, s);
       else if (fp8)
         (d.pow2 ? launch_gemm_fp8_pow2_pair : launch_gemm_fp8_pair)(r1, none, queue + 16 * c, bm_r, gridr, s);
       else launch_gemm_mxfp4_pair(r1, none, queue + 16 * c, bm_r, gridr, s);

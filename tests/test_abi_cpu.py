@@ -92,8 +92,9 @@ def test_forward_rejects_bad_layer(case, expect):
 
 def test_nvfp4_host_checks():
     """NVFP4: forward workspace as for INT4 (16-bit activations); the
-    second-level scale pointers are required; the adapter and the backward
-    are not supported for this format."""
+    second-level scale pointers are required; the adapter is not supported
+    for this format.  Backward: the transposed copy holds one fp16 per E4M3
+    scale (16 weights); its workspace is INT4's."""
     Ln = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4)
     Li = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
     assert binding.workspace_bytes(Ln, 4) == binding.workspace_bytes(Li, 4) > 0
@@ -111,8 +112,17 @@ def test_nvfp4_host_checks():
     assert _fwd(Lo, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED
     assert binding.materialized_workspace_bytes(Ln, 4) == binding.materialized_workspace_bytes(Li, 4) > 0
     assert _mat(Ln) == binding.MOE_ERR_INVALID_ARGUMENT                     # no second-level scales
-    assert binding.backward_weights_bytes(Ln) == 0
-    assert binding.backward_workspace_bytes(Ln, 4) == 0
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    E, H, I = 8, 256, 512
+    assert binding.backward_weights_bytes(Ln) == (al(E * H * I) + al(E * I * H // 2) + al(E * (H // 16) * 2 * I * 2)
+                                                  + al(E * (I // 16) * H * 2))
+    assert binding.backward_workspace_bytes(Ln, 4) == binding.backward_workspace_bytes(Li, 4) > 0
+    qw = binding.MoeQWeights(FAKE, FAKE)
+    for g13, g2 in ((None, FAKE), (FAKE, FAKE + 2)):
+        sc = binding.MoeScales(FAKE, FAKE, g13, g2)
+        assert lib.moe_expert_backward(ctypes.byref(Ln), FAKE, FAKE, ctypes.byref(qw), ctypes.byref(sc), FAKE, None,
+                                       FAKE, 1, FAKE, FAKE, None, FAKE, 1 << 40, None, None,
+                                       None) == binding.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_forward_rejects_bad_pointers_and_workspace():

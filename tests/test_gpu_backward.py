@@ -1,5 +1,5 @@
 """GPU parity of the frozen-base backward (moe_expert_backward; INT4, FP8
-(fp32 and power-of-two block scales) and MXFP4 weights) against the oracle's
+(fp32 and power-of-two block scales), MXFP4 and NVFP4 weights) against the oracle's
 fp64 backward, through the C ABI.
 
 Transposed weight copy: bit-exact against numpy.  Gradients: d_x per token
@@ -45,7 +45,7 @@ class Bwd:
         c = d.li.cfg
         return binding.expert_backward(d.layer, d.x, d.logits, d.w13, d.w2, d.s13, d.s2, self.bw,
                                        gu.dev(dout_bits, "bf16"), adapter=d.oft,
-                                       chunk_experts=c.chunk if chunk is None else chunk)
+                                       chunk_experts=c.chunk if chunk is None else chunk, g13=d.g13, g2=d.g2)
 
 
 def check(li, dout_bits, got, tokens=None, check_adapter=True):
@@ -114,14 +114,14 @@ def test_backward_weight_copy_bitexact():
         assert np.array_equal(raw[os2 + e * n2: os2 + (e + 1) * n2], f16_pairs(li.s2[e], I // 32, H))
 
 
-@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False)])
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False), (5, False)])
 def test_backward_small_vs_oracle(fmt, oft):
     li = synth.make_inputs(small(oft=oft, fmt=fmt))
     dout = d_out_of(li.cfg)
     check(li, dout, Bwd(li).run(dout))
 
 
-@pytest.mark.parametrize("fmt,oft", [(1, True), (2, False), (3, False)])
+@pytest.mark.parametrize("fmt,oft", [(1, True), (2, False), (3, False), (5, False)])
 def test_backward_max_experts_and_top_k(fmt, oft):
     """E = 1024 with top-16 routing (most experts one or two rows, a few hot)."""
     li = synth.make_inputs(small(T=64, H=256, I=256, E=1024, k=16, zipf=0.4, chunk=64, oft=oft,
@@ -130,7 +130,7 @@ def test_backward_max_experts_and_top_k(fmt, oft):
     check(li, dout, Bwd(li).run(dout))
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 5])
 @pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
 def test_backward_every_tile_height(fmt, tile_rows):
     li = synth.make_inputs(small(T=300, H=512, I=512, E=5, k=4, chunk=2, oft=fmt == 1, cfg_id=250 + fmt, fmt=fmt))
@@ -138,7 +138,7 @@ def test_backward_every_tile_height(fmt, tile_rows):
     check(li, dout, Bwd(li, tile_rows).run(dout))
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 5])
 def test_backward_chunk_size_bitwise_invariance(fmt):
     li = synth.make_inputs(small(E=9, k=3, zipf=1.2, oft=fmt == 1, fmt=fmt))
     dout = d_out_of(li.cfg, 7)
@@ -188,6 +188,30 @@ def test_backward_weight_copy_bitexact_fp8_mxfp4():
                 ref = np.ldexp(1.0, li.s13[e].reshape(H // 32, 2 * I // 8, 8).astype(np.int64) - 127)
                 order = [0, 4, 1, 5, 2, 6, 3, 7]
                 assert np.array_equal(got.astype(np.float64), ref[:, :, order])
+
+
+def test_backward_weight_copy_bitexact_nvfp4():
+    """NVFP4: nibbles transposed, E4M3 scales [K/16][N] as their fp16 values
+    in pairs; the second-level scales are not part of the copy."""
+    from tests import refimpl
+    H, I, E = 256, 512, 3
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    cfg = small(T=8, H=H, I=I, E=E, k=1, fmt=5, cfg_id=275)
+    li = synth.make_inputs(cfg)
+    raw = Bwd(li).bw.cpu().numpy()
+    o2 = al(E * H * 2 * I // 2)
+    os13 = o2 + al(E * I * H // 2)
+    os2 = os13 + al(E * (H // 16) * 2 * I * 2)
+    order = [0, 4, 1, 5, 2, 6, 3, 7]
+    for e in range(E):
+        w13t = raw[e * H * I:(e + 1) * H * I]
+        v = refimpl.unpack_nibbles(li.w13[e]).reshape(2 * I, H).T.copy()
+        assert np.array_equal(w13t, (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8).reshape(-1))
+        for off, s, G, L in ((os13, li.s13[e], H // 16, 2 * I), (os2, li.s2[e], I // 16, H)):
+            n = G * L
+            got = raw[off + e * n * 2:off + (e + 1) * n * 2].view(np.float16).reshape(G, L // 8, 8)
+            val = torch.from_numpy(np.ascontiguousarray(s).reshape(-1)).view(torch.float8_e4m3fn).double().numpy()
+            assert np.array_equal(got.astype(np.float64), val.reshape(G, L // 8, 8)[:, :, order])
 
 
 @pytest.mark.slow
