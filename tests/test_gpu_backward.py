@@ -235,6 +235,16 @@ def test_backward_deepseek_mxfp4_fullsize_sampled():
 
 
 @pytest.mark.slow
+def test_backward_deepseek_nvfp4_fullsize_sampled():
+    li = synth.make_inputs(synth.CONFIGS["c4n"], with_lm=False)
+    dout = d_out_of(li.cfg, 13)
+    got = Bwd(li).run(dout)
+    torch.cuda.synchronize()
+    toks = np.sort(np.random.default_rng(6).choice(li.cfg.T, size=8, replace=False)).astype(np.int32)
+    check(li, dout, got, tokens=toks)
+
+
+@pytest.mark.slow
 def test_backward_decode_fullsize():
     """Decode shape (64 tokens, 384 experts, H 7168, I 2048, OFT): every token,
     every expert's adapter gradient."""
