@@ -150,11 +150,22 @@ __global__ __launch_bounds__(256) void k_act_mxfp8(const uint16_t* __restrict__ 
   }
 }
 
+// LDS written by some lanes of a wave is visible to the wave's other lanes.
+__device__ __forceinline__ void oft_wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // OFT rotation x' = x R_e (R_e block-diagonal, 32x32 bf16 blocks; row i of a
 // block indexes the input dim) for every permuted row, on bf16 MFMA with fp32
 // accumulation, written as fp16 in the INT4-path layout (BF16OUT: bf16 in
 // natural order, the BF16 GEMMs' input).  Work item = 16 rows of one expert
-// (the 16-row tile list); the 4 waves split the H/32 blocks.
+// (the 16-row tile list) times 32 consecutive diagonal blocks, 8 per wave:
+// a wave loads its 8 blocks of R_e (16 KB) and x values at once, stages the
+// blocks in its own LDS slice and runs 16 MFMAs, so each item costs one
+// memory round trip.  The active experts' tile starts are kept in LDS for
+// the item -> expert search.
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
                                                  int64_t r_stride, int H, int k, const int32_t* __restrict__ offsets,
@@ -162,54 +173,82 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
                                                  const int32_t* __restrict__ active,
                                                  const int32_t* __restrict__ num_active,
                                                  const int32_t* __restrict__ tile16, uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint16_t rs[4][32 * 32];
+  constexpr int BPW = 4;  // diagonal blocks per wave and item
+  __shared__ __align__(16) uint16_t rs[4][BPW][32 * 32];
+  __shared__ int32_t s_t16[MAX_EXPERTS + 1];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int ln = lane & 15, lg = lane >> 4;
   const int na = *num_active;
-  const int ngroups = tile16[na];
+  for (int i = threadIdx.x; i <= na; i += 256) s_t16[i] = tile16[i];
+  __syncthreads();
+  const int ngroups = s_t16[na];
   const int nb = H / 32;
-  for (int gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
+  const int nbc = (nb + 4 * BPW - 1) / (4 * BPW);
+  const int64_t nitems = (int64_t)ngroups * nbc;
+  for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {
+    const int gi = (int)(it / nbc), bc = (int)(it - (int64_t)gi * nbc);
     int lo = 0, hi = na - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tile16[mid] <= gi) lo = mid; else hi = mid - 1;
+      if (s_t16[mid] <= gi) lo = mid; else hi = mid - 1;
     }
+    const int b0 = (bc * 4 + wave) * BPW;
+    const int nbw = min(BPW, nb - b0);  // <= 0: no blocks for this wave
+    if (nbw <= 0) continue;
     const int e = active[lo];
-    const int r0 = offsets[e] + (gi - tile16[lo]) * 16;
+    const int r0 = offsets[e] + (gi - s_t16[lo]) * 16;
     const int nrows = min(16, offsets[e + 1] - r0);
     const int tok = sorted_rows[r0 + min(ln, nrows - 1)] / k;
     const uint16_t* xrow = x + (int64_t)tok * H;
-    const uint16_t* Re = R + (int64_t)e * r_stride;
-    for (int b = wave; b < nb; b += 4) {
-      // stage R_e[b] (2 KB) in this wave's LDS slice
-      const uint4* src = reinterpret_cast<const uint4*>(Re + (int64_t)b * 1024);
-      uint4* dst = reinterpret_cast<uint4*>(rs[wave]);
-      dst[lane * 2] = src[lane * 2];
-      dst[lane * 2 + 1] = src[lane * 2 + 1];
-      __syncthreads();
-      const uint4 av = *reinterpret_cast<const uint4*>(xrow + b * 32 + lg * 8);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+    const uint4* src = reinterpret_cast<const uint4*>(R + (int64_t)e * r_stride + (int64_t)b0 * 1024);
+    // (a wave with fewer than BPW blocks loads its last block again)
+    uint4 rv[BPW][2], xv[BPW];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint16_t bv[8];
+    for (int j = 0; j < BPW; ++j) {
+      const int jj = min(j, nbw - 1);
+      rv[j][0] = src[jj * 128 + lane * 2];
+      rv[j][1] = src[jj * 128 + lane * 2 + 1];
+      xv[j] = *reinterpret_cast<const uint4*>(xrow + (b0 + jj) * 32 + lg * 8);
+    }
+    // a wave's LDS accesses run in order, so the previous item's reads of
+    // this slice are done before these writes
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bv[i] = rs[wave][(lg * 8 + i) * 32 + half * 16 + ln];
-        const bf16x8 bb = __builtin_bit_cast(bf16x8, bv);
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma_bf16_16x16x32(a, bb, acc);
-        const int col = BF16OUT ? b * 32 + half * 16 + ln : i4act_pos(b * 32 + half * 16 + ln);
+    for (int j = 0; j < BPW; ++j)
+      if (j < nbw) {
+        uint4* dst = reinterpret_cast<uint4*>(rs[wave][j]);
+        dst[lane * 2] = rv[j][0];
+        dst[lane * 2 + 1] = rv[j][1];
+      }
+    oft_wave_lds_sync();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = lg * 4 + i;
-          if (m < nrows) {
-            const _Float16 hv = (_Float16)acc[i];
-            out[(int64_t)(r0 + m) * H + col] =
-                BF16OUT ? (uint16_t)f32_to_bf16_bits(acc[i]) : __builtin_bit_cast(uint16_t, hv);
+    for (int j = 0; j < BPW; ++j)
+      if (j < nbw) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, xv[j]);
+        const int b = b0 + j;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint16_t* rc = rs[wave][j] + lg * 8 * 32 + half * 16 + ln;
+          u32x4 bw;
+          bw.x = (uint32_t)rc[0] | ((uint32_t)rc[32] << 16);
+          bw.y = (uint32_t)rc[64] | ((uint32_t)rc[96] << 16);
+          bw.z = (uint32_t)rc[128] | ((uint32_t)rc[160] << 16);
+          bw.w = (uint32_t)rc[192] | ((uint32_t)rc[224] << 16);
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, bw);
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc = mfma_bf16_16x16x32(a, bb, acc);
+          const int col = BF16OUT ? b * 32 + half * 16 + ln : i4act_pos(b * 32 + half * 16 + ln);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = lg * 4 + i;
+            if (m < nrows) {
+              const _Float16 hv = (_Float16)acc[i];
+              out[(int64_t)(r0 + m) * H + col] =
+                  BF16OUT ? (uint16_t)f32_to_bf16_bits(acc[i]) : __builtin_bit_cast(uint16_t, hv);
+            }
           }
         }
       }
-      __syncthreads();
-    }
+    oft_wave_lds_sync();  // this item's LDS reads are issued before the next item's writes
   }
 }
 

@@ -82,6 +82,18 @@ def test_forward_int4_oft_small(oft):
     assert err.max() <= gu.ROW_TOL
 
 
+def test_forward_int4_oft_partial_block_chunk():
+    """H = 1280: 40 diagonal blocks, so the rotation's second 32-block item
+    has blocks for one wave only (8), and 16-row groups are ragged."""
+    cfg = small(1, T=45, H=1280, I=256, E=6, k=2, oft=True, chunk=3, cfg_id=68)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    err = gu.row_rel_err(out, oracle.forward_inputs(li))
+    print(f"oft H=1280: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
 def test_forward_c1_vs_oracle():
     li = synth.make_inputs(synth.CONFIGS["c1"])
     d = gu.DevInputs(li)
