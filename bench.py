@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--tile-rows", type=int, default=0, help="grouped-GEMM tile rows (0: automatic)")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle token sample (default: sized per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-layout", choices=("auto", "rows", "kblocked"), default="auto",
+                    help="INT4 / NVFP4 code order for the fused forward: rows [N][K] or 16 x 128 tiles "
+                         "(auto: tiles where the format and mode allow)")
     ap.add_argument("--materialized", action="store_true",
                     help="time the materialized-chunk scheme (per-chunk BF16 weight copy + BF16 GEMMs) instead")
     ap.add_argument("--backward", action="store_true",
@@ -107,9 +110,17 @@ def main():
     g13 = dev(li.g13) if li.g13 is not None else None   # NVFP4 second-level scales
     g2 = dev(li.g2) if li.g2 is not None else None
     oft = dev(li.oft, True) if li.oft is not None else None
-    layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
-                               tile_rows=args.tile_rows)
     mat, bwd = args.materialized, args.backward
+    tiled_ok = cfg.fmt in (1, 5) and not mat and not bwd
+    if args.weight_layout == "kblocked" and not tiled_ok:
+        sys.exit("--weight-layout kblocked: INT4 / NVFP4 fused forward only")
+    wl = binding.WL_KBLOCKED if tiled_ok and args.weight_layout != "rows" else binding.WL_ROWS
+    layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
+                               tile_rows=args.tile_rows, weight_layout=wl)
+    if wl == binding.WL_KBLOCKED:
+        # the frozen codes re-laid once, outside the timed region, as a server stores them
+        w13, w2 = binding.pack_weights_kblocked(layer, w13, w2)
+        torch.cuda.synchronize()
     if bwd:
         ws_bytes = binding.backward_workspace_bytes(layer, cfg.chunk)
         bw = binding.prepare_backward_weights(layer, w13, w2, s13, s2)
@@ -272,6 +283,7 @@ def main():
         "config": {"workload": f"{cfg.name} MoE expert layer", "tokens": cfg.T, "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I, "weight_format": synth.FMT_NAMES[cfg.fmt],
                    "chunk_experts": cfg.chunk, "tile_rows": args.tile_rows or "auto", "oft_adapter": cfg.oft,
+                   "weight_layout": "kblocked_16x128" if wl == binding.WL_KBLOCKED else "rows",
                    "active_experts": acc["active"],
                    "mode": "materialized_bf16_copy" if mat else ("frozen_base_backward" if bwd else "fused")},
         "tflops": acc["flops"] / sec / 1e12,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_LP_ABI_VERSION 4
+#define MOE_LP_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -77,6 +77,19 @@ typedef enum {
   MOE_W_NVFP4 = 5
 } moe_wformat;
 
+/* Storage order of the packed INT4 / NVFP4 codes in w13 and w2. */
+typedef enum {
+  MOE_WL_ROWS = 0,   /* [E][N][K]: each output row's K codes contiguous */
+  /* [E][N/16][K/128][16][64 bytes]: tiles of 16 rows x 128 codes, a row's
+   * 128 codes (64 bytes, usual nibble order) contiguous within its tile,
+   * tiles K-fastest.  A GEMM step then streams 1 KB runs instead of 64-byte
+   * pieces of rows K/2 bytes apart.  INT4 and NVFP4, fused forward only
+   * (other formats: MOE_ERR_UNSUPPORTED; the materialized forward and the
+   * backward: MOE_ERR_UNSUPPORTED, workspace and copy sizes 0); written by
+   * moe_pack_weights_kblocked.  Scales keep their layout. */
+  MOE_WL_KBLOCKED = 1
+} moe_wlayout;
+
 /* Layer description (host memory). */
 typedef struct {
   int32_t num_tokens;  /* T >= 0 (T = 0 is a no-op) */
@@ -88,6 +101,7 @@ typedef struct {
   int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation  */
   int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128 or 192 */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
+  int32_t weight_layout;         /* a moe_wlayout value; other values: MOE_ERR_INVALID_ARGUMENT */
 } moe_layer;
 
 /* Packed expert weights.
@@ -136,6 +150,16 @@ typedef struct {
  * chunk_experts, which is accepted for symmetry; any value >= 1 gives the
  * same size).  Returns 0 for an invalid descriptor. */
 size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
+
+/* Re-lays INT4 / NVFP4 codes from MOE_WL_ROWS (qweights, as described by
+ * layer's dimensions and format; layer->weight_layout must be a valid value
+ * but does not change what is read or written) into
+ * MOE_WL_KBLOCKED: w13_out and w2_out (device, caller-owned, 16-byte
+ * aligned, the same sizes as w13 and w2).  Bit-identical codes; a forward
+ * with weight_layout = MOE_WL_KBLOCKED on the copy gives bit-identical
+ * outputs.  Stream-ordered; other formats return MOE_ERR_UNSUPPORTED. */
+moe_status moe_pack_weights_kblocked(const moe_layer* layer, const moe_qweights* qweights, void* w13_out,
+                                     void* w2_out, void* stream);
 
 /* Workspace bytes moe_route_permute needs (scan scratch only). */
 size_t moe_route_workspace_bytes(const moe_layer* layer);

@@ -16,12 +16,13 @@ _lib = None
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
 FMT_INT4, FMT_FP8, FMT_MXFP4, FMT_FP8_POW2, FMT_NVFP4 = 1, 2, 3, 4, 5
+WL_ROWS, WL_KBLOCKED = 0, 1
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_tile_rows",
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
             "moe_lm_head_workspace_bytes", "moe_lm_head_logprob", "moe_materialized_workspace_bytes",
             "moe_expert_forward_materialized", "moe_backward_weights_bytes", "moe_prepare_backward_weights",
-            "moe_backward_workspace_bytes", "moe_expert_backward")
+            "moe_backward_workspace_bytes", "moe_expert_backward", "moe_pack_weights_kblocked")
 STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine", "dequant")
 
 
@@ -29,7 +30,7 @@ class MoeLayer(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wformat", ctypes.c_int32),
                 ("oft_block", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
-                ("adapter_expert_stride", ctypes.c_int64)]
+                ("adapter_expert_stride", ctypes.c_int64), ("weight_layout", ctypes.c_int32)]
 
 
 class MoeQWeights(ctypes.Structure):
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_forward_materialized.argtypes = L.moe_expert_forward_timed.argtypes
         L.moe_backward_weights_bytes.restype = ctypes.c_size_t
         L.moe_backward_weights_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
+        L.moe_pack_weights_kblocked.restype = ctypes.c_int
+        L.moe_pack_weights_kblocked.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoeQWeights),
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.moe_prepare_backward_weights.restype = ctypes.c_int
         L.moe_prepare_backward_weights.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoeQWeights),
                                                    ctypes.POINTER(MoeScales), ctypes.c_void_p, ctypes.c_size_t,
@@ -135,9 +139,10 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None, tile_rows=0) -> MoeLayer:
+def make_layer(T, H, I, E, k, fmt, oft=False, adapter_expert_stride=None, tile_rows=0,
+               weight_layout=0) -> MoeLayer:
     stride = (H // 32) * 1024 if adapter_expert_stride is None else adapter_expert_stride
-    return MoeLayer(T, H, I, E, k, fmt, 32 if oft else 0, tile_rows, stride if oft else 0)
+    return MoeLayer(T, H, I, E, k, fmt, 32 if oft else 0, tile_rows, stride if oft else 0, weight_layout)
 
 
 def workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:
@@ -245,6 +250,15 @@ def prepare_backward_weights(layer: MoeLayer, w13, w2, s13, s2, out: torch.Tenso
     _check(lib().moe_prepare_backward_weights(ctypes.byref(layer), ctypes.byref(qw), ctypes.byref(sc), _ptr(out),
                                               out.numel(), _stream()), "moe_prepare_backward_weights")
     return out
+
+
+def pack_weights_kblocked(layer: MoeLayer, w13, w2):
+    """moe_pack_weights_kblocked -> (w13, w2) in 16-row x 128-K tiles (same sizes)."""
+    o13, o2 = torch.empty_like(w13), torch.empty_like(w2)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    _check(lib().moe_pack_weights_kblocked(ctypes.byref(layer), ctypes.byref(qw), _ptr(o13), _ptr(o2), _stream()),
+           "moe_pack_weights_kblocked")
+    return o13, o2
 
 
 def backward_workspace_bytes(layer: MoeLayer, chunk_experts: int = 1) -> int:

@@ -64,7 +64,10 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * (NV ? 1 : 2);
   const char* bsrc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bsrc[i] = wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  for (int i = 0; i < 4; ++i)
+    bsrc[i] = p.w_kblocked ? wexp + (int64_t)(col[i] / 16) * (K / 128) * 1024 + ln * 64 + lg * 16
+                           : wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
+  const int bstep = p.w_kblocked ? 1024 : 64;  // bytes between K steps of one lane's piece
   // group scales: INT4 lane l < 32 takes 8 consecutive weight rows (bf16)
   // of 32-group l/8; NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
   // bytes) of 16-group l/4.  Either way 16 bytes, 512 per wave and step.
@@ -94,7 +97,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * bstep, sb + ST::B_OFF + (wave * 4 + i) * 1024);
     if (lane < 32) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * 512);  // 8 N per step either way
   };
   f32x4 acc[MT][4];
@@ -277,6 +280,29 @@ __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1
 template <int BM>
 __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
   w4_pair<BM, true>(p1, p2, queue);
+}
+
+// One thread per 16-byte piece of the tiled copy: piece (e, n/16, k/128, row,
+// part) takes bytes part*16 .. +15 of row n's 64 bytes for K block k/128.
+__global__ __launch_bounds__(256) void k_pack_kblocked(const u32x4* __restrict__ w, int64_t npieces, int N, int K,
+                                                       u32x4* __restrict__ out) {
+  const int kb = K / 128;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npieces; i += (int64_t)gridDim.x * 256) {
+    const int part = (int)(i & 3), row = (int)((i >> 2) & 15);
+    const int64_t tile = i >> 6;                       // (e, n/16, k/128)
+    const int k128 = (int)(tile % kb);
+    const int64_t g = tile / kb;                        // e * N/16 + n/16
+    const int64_t n = g * 16 + row;                     // row index across experts ([E*N][K] rows)
+    out[i] = w[(n * (K / 2) + (int64_t)k128 * 64 + part * 16) / 16];
+  }
+}
+
+void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, uint8_t* out, hipStream_t s) {
+  const int64_t npieces = (int64_t)E * N * (K / 2) / 16;
+  if (npieces == 0) return;
+  const int64_t blocks = (npieces + 255) / 256;
+  hipLaunchKernelGGL(k_pack_kblocked, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(w), npieces, N, K, reinterpret_cast<u32x4*>(out));
 }
 
 void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

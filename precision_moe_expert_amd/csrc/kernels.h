@@ -43,6 +43,9 @@ struct GemmArgs {
   // the routing weights (topk_w, per flat pair) and writes per-row partial
   // sums <u, h> over its 256 columns to gpart [R][I/256].
   int save_ab;
+  // INT4 / NVFP4 weights in 16-row x 128-K tiles of 1 KB, K-fastest
+  // ([N/16][K/128][16][64 B] per expert) instead of K-contiguous rows
+  int w_kblocked;
   const float* ab;
   const float* topk_w;
   float* gpart;
@@ -123,6 +126,8 @@ void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // be empty); queue: 8 zeroed per-XCD item counters for this launch.
 void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                             hipStream_t s);
+// [E][N][K] nibble rows -> [E][N/16][K/128][16][64 B] tiles (N % 16 == 0, K % 128 == 0)
+void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, uint8_t* out, hipStream_t s);
 void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

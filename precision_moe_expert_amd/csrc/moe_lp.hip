@@ -26,6 +26,7 @@ struct Dims {
   int T, H, I, E, k, fmt;  // fmt: the kernel family (the pow2 FP8 variant runs the FP8 kernels)
   bool pow2;               // FP8 with power-of-two scales
   bool oft;
+  bool kblocked;           // weights in 16 x 128 tiles (MOE_WL_KBLOCKED)
   int64_t R;
   int nblk;
   int tile_rows;
@@ -49,6 +50,9 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if (L->num_experts > MAX_EXPERTS || L->top_k > MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
+  if (L->weight_layout != MOE_WL_ROWS && L->weight_layout != MOE_WL_KBLOCKED) return MOE_ERR_INVALID_ARGUMENT;
+  if (L->weight_layout == MOE_WL_KBLOCKED && L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_NVFP4)
+    return MOE_ERR_UNSUPPORTED;
   if (L->tile_rows != 0 && L->tile_rows != 16 && L->tile_rows != 32 && L->tile_rows != 48 && L->tile_rows != 64 &&
       L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 192)
     return MOE_ERR_UNSUPPORTED;
@@ -67,6 +71,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   d->R = (int64_t)d->T * d->k;
   d->nblk = (int)((d->R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK);
   d->tile_rows = L->tile_rows;
+  d->kblocked = L->weight_layout == MOE_WL_KBLOCKED;
   return MOE_OK;
 }
 
@@ -199,6 +204,22 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_DEVICE: return "device launch error";
   }
   return "unknown status";
+}
+
+moe_status moe_pack_weights_kblocked(const moe_layer* layer, const moe_qweights* qw, void* w13_out, void* w2_out,
+                                     void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (d.fmt != MOE_W_INT4_G32_BF16 && d.fmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
+  if (qw == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {qw->w13, qw->w2, w13_out, w2_out};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w13), d.E, 2 * d.I, d.H, static_cast<uint8_t*>(w13_out), s);
+  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w2), d.E, d.H, d.I, static_cast<uint8_t*>(w2_out), s);
+  return launch_status();
 }
 
 size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
@@ -390,6 +411,7 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
     g->tiles = tiles;
     g->top_k = d.k;
     g->chunk_experts = chunk_experts;
+    g->w_kblocked = d.kblocked ? 1 : 0;
   }
   // expert-major item order (N blocks fastest, an expert's tiles adjacent):
   // an XCD then works on all items of one or two experts at once, so both
@@ -479,6 +501,7 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
+  if (d.kblocked) return MOE_ERR_UNSUPPORTED;  // the dequant kernel reads K-contiguous rows
   if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
   if (d.T == 0) return MOE_OK;
@@ -600,6 +623,7 @@ BwdWeights bwd_weights_layout(const Dims& d) {
 moe_status check_backward(const moe_layer* L, Dims* d) {
   moe_status st = check_layer(L, d);
   if (st != MOE_OK) return st;
+  if (d->kblocked) return MOE_ERR_UNSUPPORTED;  // the recompute and the transposed copy read rows
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
   if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
@@ -958,7 +982,7 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
 
 size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   Dims d;
-  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1 || d.kblocked) return 0;
   return mat_layout(d, chunk_experts < d.E ? chunk_experts : d.E).total;
 }
 

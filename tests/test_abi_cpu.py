@@ -23,7 +23,7 @@ def test_header_declares_expected_entry_points():
     fns = declared_functions()
     for name in ("moe_route_permute", "moe_expert_forward", "moe_combine", "moe_workspace_bytes",
                  "moe_lm_head_logprob", "moe_status_str", "moe_abi_version", "moe_expert_forward_materialized",
-                 "moe_materialized_workspace_bytes"):
+                 "moe_materialized_workspace_bytes", "moe_pack_weights_kblocked"):
         assert name in fns
 
 
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = binding.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 def test_status_strings():
@@ -185,3 +185,32 @@ def test_materialized_rejects_bad_args():
     assert _mat(L, ws_bytes=binding.materialized_workspace_bytes(L, 2) - 1, chunk=2) == \
         binding.MOE_ERR_WORKSPACE_TOO_SMALL
     assert _mat(L, ws_bytes=0, ms=ms, n=n) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_kblocked_layout_host_checks():
+    """The 16 x 128 tiled code layout: INT4 and NVFP4 fused forward only; an
+    unknown layout value is invalid; the other paths report unsupported or a
+    zero size; the pack entry rejects other formats and bad pointers."""
+    lib = binding.lib()
+    Lk = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4, weight_layout=binding.WL_KBLOCKED)
+    Lr = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
+    assert binding.workspace_bytes(Lk, 4) == binding.workspace_bytes(Lr, 4) > 0
+    assert _fwd(Lk, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL      # accepted up to the workspace check
+    bad = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4, weight_layout=2)
+    assert binding.workspace_bytes(bad, 4) == 0
+    assert _fwd(bad) == binding.MOE_ERR_INVALID_ARGUMENT
+    for fmt in (binding.FMT_FP8, binding.FMT_FP8_POW2, binding.FMT_MXFP4):
+        Lf = binding.make_layer(64, 256, 512, 8, 2, fmt, weight_layout=binding.WL_KBLOCKED)
+        assert _fwd(Lf) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.materialized_workspace_bytes(Lk, 4) == 0
+    assert _mat(Lk) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.backward_weights_bytes(Lk) == 0
+    assert binding.backward_workspace_bytes(Lk, 4) == 0
+    qw = binding.MoeQWeights(FAKE, FAKE)
+    pack = lambda L, o13=FAKE, o2=FAKE: lib.moe_pack_weights_kblocked(ctypes.byref(L), ctypes.byref(qw), o13, o2,
+                                                                       None)  # noqa: E731
+    assert pack(binding.make_layer(64, 256, 512, 8, 2, binding.FMT_FP8)) == binding.MOE_ERR_UNSUPPORTED
+    assert pack(binding.make_layer(64, 256, 512, 8, 2, binding.FMT_MXFP4)) == binding.MOE_ERR_UNSUPPORTED
+    assert pack(Lr, o13=None) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert pack(Lr, o2=FAKE + 8) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert pack(bad) == binding.MOE_ERR_INVALID_ARGUMENT

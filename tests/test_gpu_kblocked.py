@@ -1,0 +1,72 @@
+"""GPU tests of the 16-row x 128-K tiled code layout (MOE_WL_KBLOCKED) of
+INT4 and NVFP4 weights, through the C ABI.
+
+The tiled copy (moe_pack_weights_kblocked) is checked byte for byte against
+a numpy re-layout of the row-major codes.  Only the addresses the GEMMs read
+change, so the fused forward on the tiled copy must equal the forward on the
+row-major codes bit for bit; it is also checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_moe_expert_amd import binding, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def tiled_np(codes, N, K):
+    """[N][K/2] bytes -> [N/16][K/128][16][64] bytes."""
+    return np.ascontiguousarray(codes.reshape(N // 16, 16, K // 128, 64).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def run(d, layout, w13, w2, tile_rows=0, chunk=None):
+    c = d.li.cfg
+    layer = binding.make_layer(c.T, c.H, c.I, c.E, c.k, c.fmt, oft=d.oft is not None, tile_rows=tile_rows,
+                               weight_layout=layout)
+    return binding.expert_forward(layer, d.x, d.logits, w13, w2, d.s13, d.s2, adapter=d.oft,
+                                  chunk_experts=c.chunk if chunk is None else chunk, g13=d.g13, g2=d.g2)
+
+
+@pytest.mark.parametrize("fmt", [1, 5])
+def test_pack_bitexact(fmt):
+    cfg = synth.LayerConfig("kblk_pack", 290 + fmt, T=8, H=512, E=3, k=1, I=384, fmt=fmt, chunk=1)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    o13, o2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
+    torch.cuda.synchronize()
+    g13, g2 = o13.cpu().numpy().reshape(cfg.E, -1), o2.cpu().numpy().reshape(cfg.E, -1)
+    for e in range(cfg.E):
+        assert np.array_equal(g13[e], tiled_np(li.w13[e].reshape(2 * cfg.I, cfg.H // 2), 2 * cfg.I, cfg.H))
+        assert np.array_equal(g2[e], tiled_np(li.w2[e].reshape(cfg.H, cfg.I // 2), cfg.H, cfg.I))
+
+
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (5, False)])
+@pytest.mark.parametrize("tile_rows", [16, 32, 64, 128, 192])
+def test_forward_kblocked_equals_rows(fmt, oft, tile_rows):
+    cfg = synth.LayerConfig("kblk_fwd", 292 + fmt + (3 if oft else 0), T=150, H=512, E=7, k=3, I=384, fmt=fmt,
+                            chunk=3, oft=oft, zipf_alpha=0.8)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    o13, o2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
+    ref = run(d, binding.WL_ROWS, d.w13, d.w2, tile_rows).clone()
+    got = run(d, binding.WL_KBLOCKED, o13, o2, tile_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    err = gu.row_rel_err(gu.bf16_to_np(got), oracle.forward_inputs(li))
+    print(f"fmt {fmt} oft {oft} tile {tile_rows}: max row rel err {err.max():.3e}")
+    assert err.max() <= gu.ROW_TOL
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["c5", "c3"])
+def test_fullsize_kblocked_equals_rows(name):
+    """Decode and Kimi-K2 shapes (INT4 + OFT): bit-identical outputs."""
+    li = synth.make_inputs(synth.CONFIGS[name], with_lm=False)
+    d = gu.DevInputs(li)
+    o13, o2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
+    ref = run(d, binding.WL_ROWS, d.w13, d.w2).clone()
+    got = run(d, binding.WL_KBLOCKED, o13, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
