@@ -79,8 +79,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle token sample (default: sized per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-layout", choices=("auto", "rows", "kblocked"), default="auto",
-                    help="INT4 / NVFP4 code order for the fused forward: rows [N][K] or 16 x 128 tiles "
-                         "(auto: tiles where the format and mode allow)")
+                    help="weight code order for the fused forward: rows [N][K] or 16 x 128 tiles "
+                         "(auto: tiles for the fused forward, rows for the other modes)")
     ap.add_argument("--materialized", action="store_true",
                     help="time the materialized-chunk scheme (per-chunk BF16 weight copy + BF16 GEMMs) instead")
     ap.add_argument("--backward", action="store_true",
@@ -111,9 +111,9 @@ def main():
     g2 = dev(li.g2) if li.g2 is not None else None
     oft = dev(li.oft, True) if li.oft is not None else None
     mat, bwd = args.materialized, args.backward
-    tiled_ok = cfg.fmt in (1, 5) and not mat and not bwd
+    tiled_ok = not mat and not bwd
     if args.weight_layout == "kblocked" and not tiled_ok:
-        sys.exit("--weight-layout kblocked: INT4 / NVFP4 fused forward only")
+        sys.exit("--weight-layout kblocked: fused forward only")
     wl = binding.WL_KBLOCKED if tiled_ok and args.weight_layout != "rows" else binding.WL_ROWS
     layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
                                tile_rows=args.tile_rows, weight_layout=wl)

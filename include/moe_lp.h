@@ -77,16 +77,16 @@ typedef enum {
   MOE_W_NVFP4 = 5
 } moe_wformat;
 
-/* Storage order of the packed INT4 / NVFP4 codes in w13 and w2. */
+/* Storage order of the packed codes in w13 and w2 (every format). */
 typedef enum {
   MOE_WL_ROWS = 0,   /* [E][N][K]: each output row's K codes contiguous */
-  /* [E][N/16][K/128][16][64 bytes]: tiles of 16 rows x 128 codes, a row's
-   * 128 codes (64 bytes, usual nibble order) contiguous within its tile,
-   * tiles K-fastest.  A GEMM step then streams 1 KB runs instead of 64-byte
-   * pieces of rows K/2 bytes apart.  INT4 and NVFP4, fused forward only
-   * (other formats: MOE_ERR_UNSUPPORTED; the materialized forward and the
-   * backward: MOE_ERR_UNSUPPORTED, workspace and copy sizes 0); written by
-   * moe_pack_weights_kblocked.  Scales keep their layout. */
+  /* [E][N/16][K/128][16][B]: tiles of 16 rows x 128 codes, a row's 128
+   * codes (B = 64 bytes of 4-bit codes in the usual nibble order, 128 bytes
+   * of E4M3) contiguous within its tile, tiles K-fastest.  A GEMM step then
+   * streams 1-2 KB runs instead of 64- or 128-byte pieces of rows K/2 or K
+   * bytes apart.  Fused forward only (the materialized forward and the
+   * backward return MOE_ERR_UNSUPPORTED, their workspace and copy sizes are
+   * 0); written by moe_pack_weights_kblocked.  Scales keep their layout. */
   MOE_WL_KBLOCKED = 1
 } moe_wlayout;
 
@@ -151,13 +151,13 @@ typedef struct {
  * same size).  Returns 0 for an invalid descriptor. */
 size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
 
-/* Re-lays INT4 / NVFP4 codes from MOE_WL_ROWS (qweights, as described by
+/* Re-lays the codes from MOE_WL_ROWS (qweights, as described by
  * layer's dimensions and format; layer->weight_layout must be a valid value
  * but does not change what is read or written) into
  * MOE_WL_KBLOCKED: w13_out and w2_out (device, caller-owned, 16-byte
  * aligned, the same sizes as w13 and w2).  Bit-identical codes; a forward
  * with weight_layout = MOE_WL_KBLOCKED on the copy gives bit-identical
- * outputs.  Stream-ordered; other formats return MOE_ERR_UNSUPPORTED. */
+ * outputs.  Stream-ordered. */
 moe_status moe_pack_weights_kblocked(const moe_layer* layer, const moe_qweights* qweights, void* w13_out,
                                      void* w2_out, void* stream);
 

@@ -87,8 +87,10 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     const int c = (wr * 4 + j) * 64 + lane;
     const int r = c >> 3, part = (c & 7) ^ (r & 7);
     const int n = G1 ? (r < 32 ? col[0] + r : col[2] + r - 32) : col[0] + r;
-    bsrc[j] = wexp + (int64_t)n * K + part * 16;
+    bsrc[j] = p.w_kblocked ? wexp + (int64_t)(n / 16) * (K / 128) * 2048 + (n % 16) * 128 + part * 16
+                           : wexp + (int64_t)n * K + part * 16;
   }
+  const int bstep = p.w_kblocked ? 2048 : 128;  // bytes between K steps of one lane's piece
   const char* asrc[ST::NA];
 #pragma unroll
   for (int j = 0; j < ST::NA; ++j) {
@@ -115,7 +117,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
     if (wave < ST::NASW && (kt & 3) == 0)
       dma_b128(ssrc + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma_b128(bsrc[j] + kt * 128, sb + ST::B_OFF + (wc * 8 + wr * 4 + j) * 1024);
+    for (int j = 0; j < 4; ++j) dma_b128(bsrc[j] + kt * bstep, sb + ST::B_OFF + (wc * 8 + wr * 4 + j) * 1024);
   };
   f32x4 acc[MTW][4];
 #pragma unroll

@@ -283,26 +283,34 @@ __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p
 }
 
 // One thread per 16-byte piece of the tiled copy: piece (e, n/16, k/128, row,
-// part) takes bytes part*16 .. +15 of row n's 64 bytes for K block k/128.
-__global__ __launch_bounds__(256) void k_pack_kblocked(const u32x4* __restrict__ w, int64_t npieces, int N, int K,
+// part) takes bytes part*16 .. +15 of row n's KB bytes for K block k/128
+// (KB = 64 for 4-bit codes, 128 for bytes; PP = KB / 16 pieces per row).
+template <int PP>
+__global__ __launch_bounds__(256) void k_pack_kblocked(const u32x4* __restrict__ w, int64_t npieces, int K,
                                                        u32x4* __restrict__ out) {
   const int kb = K / 128;
+  const int64_t row_pieces = (int64_t)kb * PP;      // 16-byte pieces per row
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npieces; i += (int64_t)gridDim.x * 256) {
-    const int part = (int)(i & 3), row = (int)((i >> 2) & 15);
-    const int64_t tile = i >> 6;                       // (e, n/16, k/128)
+    const int part = (int)(i % PP), row = (int)((i / PP) & 15);
+    const int64_t tile = i / (16 * PP);                // (e, n/16, k/128)
     const int k128 = (int)(tile % kb);
     const int64_t g = tile / kb;                        // e * N/16 + n/16
-    const int64_t n = g * 16 + row;                     // row index across experts ([E*N][K] rows)
-    out[i] = w[(n * (K / 2) + (int64_t)k128 * 64 + part * 16) / 16];
+    const int64_t n = g * 16 + row;                     // row index across experts ([E*N] rows)
+    out[i] = w[n * row_pieces + (int64_t)k128 * PP + part];
   }
 }
 
-void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, uint8_t* out, hipStream_t s) {
-  const int64_t npieces = (int64_t)E * N * (K / 2) / 16;
+void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, bool bytes, uint8_t* out, hipStream_t s) {
+  const int64_t npieces = (int64_t)E * N * (bytes ? K : K / 2) / 16;
   if (npieces == 0) return;
-  const int64_t blocks = (npieces + 255) / 256;
-  hipLaunchKernelGGL(k_pack_kblocked, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4*>(w), npieces, N, K, reinterpret_cast<u32x4*>(out));
+  const int64_t b = (npieces + 255) / 256;
+  const dim3 grid((unsigned)(b < 8192 ? b : 8192));
+  if (bytes)
+    hipLaunchKernelGGL(k_pack_kblocked<8>, grid, dim3(256), 0, s, reinterpret_cast<const u32x4*>(w), npieces, K,
+                       reinterpret_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL(k_pack_kblocked<4>, grid, dim3(256), 0, s, reinterpret_cast<const u32x4*>(w), npieces, K,
+                       reinterpret_cast<u32x4*>(out));
 }
 
 void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

@@ -76,10 +76,13 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
   const char* wsexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems;
   // the four subtiles' weight rows are col[i] + ln: one per-lane pointer plus
   // wave-uniform row offsets (fewer live registers than four pointers)
-  const char* bsrc0 = wexp + (int64_t)(col[0] + ln) * (K / 2) + lg * 16;
+  const char* bsrc0 = p.w_kblocked ? wexp + (int64_t)(col[0] / 16) * (K / 128) * 1024 + ln * 64 + lg * 16
+                                   : wexp + (int64_t)(col[0] + ln) * (K / 2) + lg * 16;
+  const int bstep = p.w_kblocked ? 1024 : 64;  // bytes between K steps of one lane's piece
   int64_t boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) boff[i] = (int64_t)(col[i] - col[0]) * (K / 2);
+  for (int i = 0; i < 4; ++i)
+    boff[i] = p.w_kblocked ? (int64_t)((col[i] - col[0]) / 16) * (K / 128) * 1024 : (int64_t)(col[i] - col[0]) * (K / 2);
   // E8M0 weight scales (group-major): lane l < 16 takes 16 consecutive
   // weight rows of group l/4, i.e. one subtile
   uint32_t bsoff;  // from wsexp
@@ -116,7 +119,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     if (wave < ST::NASW && (kt & 3) == 0)
       dma_b128(ASbase + (uint64_t)soff + (kt >> 2) * 16, asb0 + ((kt >> 2) & 1) * ST::AS_BLOCK + wave * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b128(bsrc0 + boff[i] + kt * 64, sb + ST::B_OFF + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma_b128(bsrc0 + boff[i] + kt * bstep, sb + ST::B_OFF + (wave * 4 + i) * 1024);
     if (lane < 16) dma_b128(wsexp + (uint64_t)bsoff + (int64_t)kt * 4 * p.N, sb + ST::BS_OFF + wave * 256);
   };
   f32x4 acc[MT][4];

@@ -43,8 +43,8 @@ struct GemmArgs {
   // the routing weights (topk_w, per flat pair) and writes per-row partial
   // sums <u, h> over its 256 columns to gpart [R][I/256].
   int save_ab;
-  // INT4 / NVFP4 weights in 16-row x 128-K tiles of 1 KB, K-fastest
-  // ([N/16][K/128][16][64 B] per expert) instead of K-contiguous rows
+  // weights in 16-row x 128-K tiles, K-fastest ([N/16][K/128][16][KB] per
+  // expert, KB = 64 bytes of 4-bit codes or 128 of E4M3) instead of rows
   int w_kblocked;
   const float* ab;
   const float* topk_w;
@@ -126,8 +126,9 @@ void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // be empty); queue: 8 zeroed per-XCD item counters for this launch.
 void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                             hipStream_t s);
-// [E][N][K] nibble rows -> [E][N/16][K/128][16][64 B] tiles (N % 16 == 0, K % 128 == 0)
-void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, uint8_t* out, hipStream_t s);
+// [E][N][K] code rows -> [E][N/16][K/128][16][KB] tiles (N % 16 == 0, K % 128 == 0;
+// KB = 128 bytes for byte codes, else 64 for 4-bit codes)
+void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, bool bytes, uint8_t* out, hipStream_t s);
 void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
 void launch_gemm_fp8_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

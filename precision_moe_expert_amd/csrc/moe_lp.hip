@@ -51,8 +51,6 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
   if (L->weight_layout != MOE_WL_ROWS && L->weight_layout != MOE_WL_KBLOCKED) return MOE_ERR_INVALID_ARGUMENT;
-  if (L->weight_layout == MOE_WL_KBLOCKED && L->wformat != MOE_W_INT4_G32_BF16 && L->wformat != MOE_W_NVFP4)
-    return MOE_ERR_UNSUPPORTED;
   if (L->tile_rows != 0 && L->tile_rows != 16 && L->tile_rows != 32 && L->tile_rows != 48 && L->tile_rows != 64 &&
       L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 192)
     return MOE_ERR_UNSUPPORTED;
@@ -211,14 +209,15 @@ moe_status moe_pack_weights_kblocked(const moe_layer* layer, const moe_qweights*
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
-  if (d.fmt != MOE_W_INT4_G32_BF16 && d.fmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
   if (qw == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {qw->w13, qw->w2, w13_out, w2_out};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w13), d.E, 2 * d.I, d.H, static_cast<uint8_t*>(w13_out), s);
-  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w2), d.E, d.H, d.I, static_cast<uint8_t*>(w2_out), s);
+  const bool bytes = d.fmt == MOE_W_FP8_E4M3_B128;
+  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w13), d.E, 2 * d.I, d.H, bytes,
+                       static_cast<uint8_t*>(w13_out), s);
+  launch_pack_kblocked(static_cast<const uint8_t*>(qw->w2), d.E, d.H, d.I, bytes, static_cast<uint8_t*>(w2_out), s);
   return launch_status();
 }
 

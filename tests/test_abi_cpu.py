@@ -188,9 +188,9 @@ def test_materialized_rejects_bad_args():
 
 
 def test_kblocked_layout_host_checks():
-    """The 16 x 128 tiled code layout: INT4 and NVFP4 fused forward only; an
-    unknown layout value is invalid; the other paths report unsupported or a
-    zero size; the pack entry rejects other formats and bad pointers."""
+    """The 16 x 128 tiled code layout: fused forward only; an unknown layout
+    value is invalid; the other paths report unsupported or a zero size; the
+    pack entry rejects bad pointers."""
     lib = binding.lib()
     Lk = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4, weight_layout=binding.WL_KBLOCKED)
     Lr = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
@@ -201,7 +201,8 @@ def test_kblocked_layout_host_checks():
     assert _fwd(bad) == binding.MOE_ERR_INVALID_ARGUMENT
     for fmt in (binding.FMT_FP8, binding.FMT_FP8_POW2, binding.FMT_MXFP4):
         Lf = binding.make_layer(64, 256, 512, 8, 2, fmt, weight_layout=binding.WL_KBLOCKED)
-        assert _fwd(Lf) == binding.MOE_ERR_UNSUPPORTED
+        assert _fwd(Lf, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+        assert binding.materialized_workspace_bytes(Lf, 4) == binding.backward_weights_bytes(Lf) == 0
     assert binding.materialized_workspace_bytes(Lk, 4) == 0
     assert _mat(Lk) == binding.MOE_ERR_UNSUPPORTED
     assert binding.backward_weights_bytes(Lk) == 0
@@ -209,8 +210,6 @@ def test_kblocked_layout_host_checks():
     qw = binding.MoeQWeights(FAKE, FAKE)
     pack = lambda L, o13=FAKE, o2=FAKE: lib.moe_pack_weights_kblocked(ctypes.byref(L), ctypes.byref(qw), o13, o2,
                                                                        None)  # noqa: E731
-    assert pack(binding.make_layer(64, 256, 512, 8, 2, binding.FMT_FP8)) == binding.MOE_ERR_UNSUPPORTED
-    assert pack(binding.make_layer(64, 256, 512, 8, 2, binding.FMT_MXFP4)) == binding.MOE_ERR_UNSUPPORTED
     assert pack(Lr, o13=None) == binding.MOE_ERR_INVALID_ARGUMENT
     assert pack(Lr, o2=FAKE + 8) == binding.MOE_ERR_INVALID_ARGUMENT
     assert pack(bad) == binding.MOE_ERR_INVALID_ARGUMENT

@@ -1,5 +1,5 @@
 """GPU tests of the 16-row x 128-K tiled code layout (MOE_WL_KBLOCKED) of
-INT4 and NVFP4 weights, through the C ABI.
+the weights of every format, through the C ABI.
 
 The tiled copy (moe_pack_weights_kblocked) is checked byte for byte against
 a numpy re-layout of the row-major codes.  Only the addresses the GEMMs read
@@ -16,9 +16,9 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def tiled_np(codes, N, K):
-    """[N][K/2] bytes -> [N/16][K/128][16][64] bytes."""
-    return np.ascontiguousarray(codes.reshape(N // 16, 16, K // 128, 64).transpose(0, 2, 1, 3)).reshape(-1)
+def tiled_np(codes, N, K, kb):
+    """[N][K*kb/128] bytes -> [N/16][K/128][16][kb] bytes."""
+    return np.ascontiguousarray(codes.reshape(N // 16, 16, K // 128, kb).transpose(0, 2, 1, 3)).reshape(-1)
 
 
 def run(d, layout, w13, w2, tile_rows=0, chunk=None):
@@ -29,7 +29,7 @@ def run(d, layout, w13, w2, tile_rows=0, chunk=None):
                                   chunk_experts=c.chunk if chunk is None else chunk, g13=d.g13, g2=d.g2)
 
 
-@pytest.mark.parametrize("fmt", [1, 5])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 5])
 def test_pack_bitexact(fmt):
     cfg = synth.LayerConfig("kblk_pack", 290 + fmt, T=8, H=512, E=3, k=1, I=384, fmt=fmt, chunk=1)
     li = synth.make_inputs(cfg)
@@ -37,15 +37,18 @@ def test_pack_bitexact(fmt):
     o13, o2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
     torch.cuda.synchronize()
     g13, g2 = o13.cpu().numpy().reshape(cfg.E, -1), o2.cpu().numpy().reshape(cfg.E, -1)
+    kb = 128 if fmt == 2 else 64
     for e in range(cfg.E):
-        assert np.array_equal(g13[e], tiled_np(li.w13[e].reshape(2 * cfg.I, cfg.H // 2), 2 * cfg.I, cfg.H))
-        assert np.array_equal(g2[e], tiled_np(li.w2[e].reshape(cfg.H, cfg.I // 2), cfg.H, cfg.I))
+        w13 = np.asarray(li.w13[e]).reshape(2 * cfg.I, -1)
+        w2 = np.asarray(li.w2[e]).reshape(cfg.H, -1)
+        assert np.array_equal(g13[e], tiled_np(w13, 2 * cfg.I, cfg.H, kb))
+        assert np.array_equal(g2[e], tiled_np(w2, cfg.H, cfg.I, kb))
 
 
-@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (5, False)])
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False), (5, False)])
 @pytest.mark.parametrize("tile_rows", [16, 32, 64, 128, 192])
 def test_forward_kblocked_equals_rows(fmt, oft, tile_rows):
-    cfg = synth.LayerConfig("kblk_fwd", 292 + fmt + (3 if oft else 0), T=150, H=512, E=7, k=3, I=384, fmt=fmt,
+    cfg = synth.LayerConfig("kblk_fwd", 300 + fmt + (5 if oft else 0), T=150, H=512, E=7, k=3, I=384, fmt=fmt,
                             chunk=3, oft=oft, zipf_alpha=0.8)
     li = synth.make_inputs(cfg)
     d = gu.DevInputs(li)
@@ -60,9 +63,10 @@ def test_forward_kblocked_equals_rows(fmt, oft, tile_rows):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["c5", "c3"])
+@pytest.mark.parametrize("name", ["c5", "c3", "c2", "c2p", "c4"])
 def test_fullsize_kblocked_equals_rows(name):
-    """Decode and Kimi-K2 shapes (INT4 + OFT): bit-identical outputs."""
+    """Decode and Kimi-K2 shapes (INT4 + OFT), Qwen3 shape (FP8, both scale
+    kinds), DeepSeek-V3 shape (MXFP4): bit-identical outputs."""
     li = synth.make_inputs(synth.CONFIGS[name], with_lm=False)
     d = gu.DevInputs(li)
     o13, o2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
