@@ -257,7 +257,8 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
  * transposed copy of the frozen weights, made once per base. */
 
 /* Bytes of the transposed copy: W13^T [E][H][2I] and W2^T [E][I][H] in the
- * format's codes (INT4 / E2M1 nibbles, E4M3 bytes) plus scales (INT4, MXFP4,
+ * format's codes (INT4 / E2M1 nibbles, E4M3 bytes), stored in tiles of 16
+ * rows x 128 codes as MOE_WL_KBLOCKED describes, plus scales (INT4, MXFP4,
  * NVFP4: one fp16 per group scale; FP8: the fp32 block scales transposed); 0 if the
  * layer is not supported by the backward (I multiple of 256; FP8 H and 2I at
  * most 8192; per-expert adapter). */

@@ -31,9 +31,11 @@ namespace moe {
 
 // ------------------------------------------------------------- repacking
 
-// W [E][N][K] nibbles (element 2m in the low nibble of byte m) -> W^T
-// [E][K][N] in the same convention.  One 64 x 64 nibble tile per iteration,
-// transposed through LDS (one byte per nibble).
+// W [E][N][K] nibbles (element 2m in the low nibble of byte m) -> W^T with
+// K rows of N nibbles in the same convention, stored in 16-row x 128-column
+// tiles of 1 KB, columns fastest: [E][K/16][N/128][16][64 B], so that a
+// backward GEMM step reads one contiguous run per 16 rows.  One 64 x 64
+// nibble tile per iteration, transposed through LDS (one byte per nibble).
 __global__ __launch_bounds__(256) void k_repack_int4_t(const uint8_t* __restrict__ w, int E, int N, int K,
                                                        uint8_t* __restrict__ wt) {
   __shared__ uint8_t tile[64][65];
@@ -55,12 +57,16 @@ __global__ __launch_bounds__(256) void k_repack_int4_t(const uint8_t* __restrict
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[q >> 3] |= (uint32_t)tile[part * 16 + q][row] << ((q & 7) * 4);
     uint8_t* dst = wt + (int64_t)e * N * K / 2;
-    *reinterpret_cast<uint2*>(dst + ((int64_t)(k0 + row) * N + n0) / 2 + part * 8) = make_uint2(o[0], o[1]);
+    const int r = k0 + row, n = n0 + part * 16;
+    *reinterpret_cast<uint2*>(dst + ((int64_t)(r / 16) * (N / 128) + n / 128) * 1024 + (r % 16) * 64 + (n % 128) / 2) =
+        make_uint2(o[0], o[1]);
     __syncthreads();
   }
 }
 
-// W [E][N][K] bytes -> W^T [E][K][N], 64 x 64 byte tiles through LDS.
+// W [E][N][K] bytes -> W^T with K rows of N bytes in 16-row x 128-column
+// tiles of 2 KB, columns fastest ([E][K/16][N/128][16][128 B]); 64 x 64
+// byte tiles through LDS.
 __global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__ w, int E, int N, int K,
                                                      uint8_t* __restrict__ wt) {
   __shared__ uint8_t tile[64][68];
@@ -79,8 +85,9 @@ __global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__
     uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[q >> 2] |= (uint32_t)tile[part * 16 + q][row] << ((q & 3) * 8);
-    *reinterpret_cast<u32x4*>(wt + (int64_t)e * N * K + (int64_t)(k0 + row) * N + n0 + part * 16) =
-        (u32x4){o[0], o[1], o[2], o[3]};
+    const int r = k0 + row, n = n0 + part * 16;
+    *reinterpret_cast<u32x4*>(wt + (int64_t)e * N * K + ((int64_t)(r / 16) * (N / 128) + n / 128) * 2048 +
+                              (r % 16) * 128 + n % 128) = (u32x4){o[0], o[1], o[2], o[3]};
     __syncthreads();
   }
 }
@@ -242,10 +249,11 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
   const int c0 = tl.nb * 256 + wave * 64;
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
   // weight fragments: lane holds 32 consecutive K values of row c0 + 16 i + ln
+  // (the copy is tiled 16 rows x 128 K, BROW bytes per row and tile)
   const char* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    bsrc[i] = wexp + (int64_t)(c0 + 16 * i + ln) * (FMT == FMT_FP8 ? K : K / 2) + lg * (BROW / 4);
+    bsrc[i] = wexp + (int64_t)((c0 + 16 * i) / 16) * KT * (16 * BROW) + ln * BROW + lg * (BROW / 4);
   const char* bssrc = nullptr;
   if (FMT == FMT_NVFP4) {
     // fp16 scales of the wave's four 16-row groups: 4 runs of 128 K values per step
@@ -279,7 +287,7 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < ST::NB / 4; ++h)
-        dma_b128(bsrc[i] + kt * BROW + h * 16, sb + ST::B_OFF + ((wave * 4 + i) * (ST::NB / 4) + h) * 1024);
+        dma_b128(bsrc[i] + kt * (16 * BROW) + h * 16, sb + ST::B_OFF + ((wave * 4 + i) * (ST::NB / 4) + h) * 1024);
     if (FMT == FMT_NVFP4) dma_b128(bssrc + (int64_t)kt * 256, sb + ST::BS_OFF + wave * 1024);
     else if (FMT != FMT_FP8)
       if (lane < 32) dma_b128(bssrc + (int64_t)kt * 256, sb + ST::BS_OFF + wave * 512);

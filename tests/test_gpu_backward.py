@@ -48,6 +48,13 @@ class Bwd:
                                        chunk_experts=c.chunk if chunk is None else chunk, g13=d.g13, g2=d.g2)
 
 
+def tiles(a, tb):
+    """Row-major transposed copy [R][C] bytes -> the library's 16-row tiles
+    [R/16][C/tb][16][tb] (tb = 64 bytes of nibbles or 128 of E4M3)."""
+    R, C = a.shape
+    return np.ascontiguousarray(a.reshape(R // 16, 16, C // tb, tb).transpose(0, 2, 1, 3)).reshape(-1)
+
+
 def check(li, dout_bits, got, tokens=None, check_adapter=True):
     from tests import refimpl
     dout = refimpl.bf16_to_f32(dout_bits).reshape(li.cfg.T, li.cfg.H)
@@ -105,9 +112,9 @@ def test_backward_weight_copy_bitexact():
 
     for e in range(E):
         w13t = raw[o13 + e * H * I: o13 + (e + 1) * H * I]
-        assert np.array_equal(w13t, nib_t(li.w13[e], 2 * I, H).reshape(-1))
+        assert np.array_equal(w13t, tiles(nib_t(li.w13[e], 2 * I, H), 64))
         w2t = raw[o2 + e * H * I // 2: o2 + (e + 1) * H * I // 2]
-        assert np.array_equal(w2t, nib_t(li.w2[e], H, I).reshape(-1))
+        assert np.array_equal(w2t, tiles(nib_t(li.w2[e], H, I), 64))
         n13 = (H // 32) * 2 * I * 2
         assert np.array_equal(raw[os13 + e * n13: os13 + (e + 1) * n13], f16_pairs(li.s13[e], H // 32, 2 * I))
         n2 = (I // 32) * H * 2
@@ -172,17 +179,17 @@ def test_backward_weight_copy_bitexact_fp8_mxfp4():
         os13 = o2 + al(E * I * H // per)
         for e in range(E):
             if fmt == 2:
-                w13t = raw[e * H * 2 * I:(e + 1) * H * 2 * I].reshape(H, 2 * I)
-                assert np.array_equal(w13t, li.w13[e].reshape(2 * I, H).T)
-                w2t = raw[o2 + e * H * I:o2 + (e + 1) * H * I].reshape(I, H)
-                assert np.array_equal(w2t, li.w2[e].reshape(H, I).T)
+                w13t = raw[e * H * 2 * I:(e + 1) * H * 2 * I]
+                assert np.array_equal(w13t, tiles(li.w13[e].reshape(2 * I, H).T, 128))
+                w2t = raw[o2 + e * H * I:o2 + (e + 1) * H * I]
+                assert np.array_equal(w2t, tiles(li.w2[e].reshape(H, I).T, 128))
                 n13 = (2 * I // 128) * (H // 128)
                 s13t = raw[os13:].view(np.float32)[e * n13:(e + 1) * n13].reshape(H // 128, 2 * I // 128)
                 assert np.array_equal(s13t, li.s13[e].reshape(2 * I // 128, H // 128).T)
             else:
                 w2t = raw[o2 + e * H * I // 2:o2 + (e + 1) * H * I // 2]
                 v = refimpl.unpack_nibbles(li.w2[e]).reshape(H, I).T.copy()
-                assert np.array_equal(w2t, (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8).reshape(-1))
+                assert np.array_equal(w2t, tiles((v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8), 64))
                 n13 = (H // 32) * 2 * I
                 got = raw[os13 + e * n13 * 2:os13 + (e + 1) * n13 * 2].view(np.float16).reshape(H // 32, 2 * I // 8, 8)
                 ref = np.ldexp(1.0, li.s13[e].reshape(H // 32, 2 * I // 8, 8).astype(np.int64) - 127)
@@ -206,7 +213,7 @@ def test_backward_weight_copy_bitexact_nvfp4():
     for e in range(E):
         w13t = raw[e * H * I:(e + 1) * H * I]
         v = refimpl.unpack_nibbles(li.w13[e]).reshape(2 * I, H).T.copy()
-        assert np.array_equal(w13t, (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8).reshape(-1))
+        assert np.array_equal(w13t, tiles((v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8), 64))
         for off, s, G, L in ((os13, li.s13[e], H // 16, 2 * I), (os2, li.s2[e], I // 16, H)):
             n = G * L
             got = raw[off + e * n * 2:off + (e + 1) * n * 2].view(np.float16).reshape(G, L // 8, 8)
