@@ -80,7 +80,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-layout", choices=("auto", "rows", "kblocked"), default="auto",
                     help="weight code order for the fused forward: rows [N][K] or 16 x 128 tiles "
-                         "(auto: tiles for the fused forward, rows for the other modes)")
+                         "(auto: tiles, except for the materialized mode)")
     ap.add_argument("--materialized", action="store_true",
                     help="time the materialized-chunk scheme (per-chunk BF16 weight copy + BF16 GEMMs) instead")
     ap.add_argument("--backward", action="store_true",
@@ -111,9 +111,9 @@ def main():
     g2 = dev(li.g2) if li.g2 is not None else None
     oft = dev(li.oft, True) if li.oft is not None else None
     mat, bwd = args.materialized, args.backward
-    tiled_ok = not mat and not bwd
+    tiled_ok = not mat
     if args.weight_layout == "kblocked" and not tiled_ok:
-        sys.exit("--weight-layout kblocked: fused forward only")
+        sys.exit("--weight-layout kblocked: not with --materialized")
     wl = binding.WL_KBLOCKED if tiled_ok and args.weight_layout != "rows" else binding.WL_ROWS
     layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft is not None,
                                tile_rows=args.tile_rows, weight_layout=wl)

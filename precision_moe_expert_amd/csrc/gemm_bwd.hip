@@ -36,8 +36,9 @@ namespace moe {
 // tiles of 1 KB, columns fastest: [E][K/16][N/128][16][64 B], so that a
 // backward GEMM step reads one contiguous run per 16 rows.  One 64 x 64
 // nibble tile per iteration, transposed through LDS (one byte per nibble).
+// (tiled = 1: the source codes are in the forward's 16-row x 128-K tiles.)
 __global__ __launch_bounds__(256) void k_repack_int4_t(const uint8_t* __restrict__ w, int E, int N, int K,
-                                                       uint8_t* __restrict__ wt) {
+                                                       int tiled, uint8_t* __restrict__ wt) {
   __shared__ uint8_t tile[64][65];
   const int tn = N / 64, tk = K / 64;
   const int64_t ntiles = (int64_t)E * tn * tk;
@@ -47,7 +48,10 @@ __global__ __launch_bounds__(256) void k_repack_int4_t(const uint8_t* __restrict
     const int rem = (int)(ti - (int64_t)e * tn * tk);
     const int n0 = (rem / tk) * 64, k0 = (rem % tk) * 64;
     const uint8_t* src = w + (int64_t)e * N * K / 2;
-    const uint2 v = *reinterpret_cast<const uint2*>(src + ((int64_t)(n0 + row) * K + k0) / 2 + part * 8);
+    const int sn = n0 + row, sk = k0 + part * 16;  // source row and first K value
+    const uint2 v = *reinterpret_cast<const uint2*>(
+        src + (tiled ? ((int64_t)(sn / 16) * (K / 128) + sk / 128) * 1024 + (sn % 16) * 64 + (sk % 128) / 2
+                     : ((int64_t)sn * K + sk) / 2));
     const uint32_t vs[2] = {v.x, v.y};
 #pragma unroll
     for (int q = 0; q < 16; ++q) tile[row][part * 16 + q] = (uint8_t)((vs[q >> 3] >> ((q & 7) * 4)) & 15u);
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void k_repack_int4_t(const uint8_t* __restrict
 // W [E][N][K] bytes -> W^T with K rows of N bytes in 16-row x 128-column
 // tiles of 2 KB, columns fastest ([E][K/16][N/128][16][128 B]); 64 x 64
 // byte tiles through LDS.
-__global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__ w, int E, int N, int K,
+__global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__ w, int E, int N, int K, int tiled,
                                                      uint8_t* __restrict__ wt) {
   __shared__ uint8_t tile[64][68];
   const int tn = N / 64, tk = K / 64;
@@ -77,7 +81,11 @@ __global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__
     const int e = (int)(ti / ((int64_t)tn * tk));
     const int rem = (int)(ti - (int64_t)e * tn * tk);
     const int n0 = (rem / tk) * 64, k0 = (rem % tk) * 64;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(w + (int64_t)e * N * K + (int64_t)(n0 + row) * K + k0 + part * 16);
+    const int sn = n0 + row, sk = k0 + part * 16;  // source row and first K value
+    const u32x4 v = *reinterpret_cast<const u32x4*>(
+        w + (int64_t)e * N * K +
+        (tiled ? ((int64_t)(sn / 16) * (K / 128) + sk / 128) * 2048 + (sn % 16) * 128 + sk % 128
+               : (int64_t)sn * K + sk));
     const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 16; ++q) tile[row][part * 16 + q] = (uint8_t)(vs[q >> 2] >> ((q & 3) * 8));
@@ -139,18 +147,18 @@ __global__ __launch_bounds__(256) void k_repack_scales_t(const float* __restrict
 
 static unsigned grid_of(int64_t n, int64_t cap) { return (unsigned)((n + 255) / 256 < cap ? (n + 255) / 256 : cap); }
 
-void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, int K, uint8_t* wt, void* st,
-                       hipStream_t stream) {
+void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, int K, bool tiled, uint8_t* wt,
+                       void* st, hipStream_t stream) {
   const int64_t tiles = (int64_t)E * (N / 64) * (K / 64);
   const unsigned tg = (unsigned)(tiles < 8192 ? tiles : 8192);
   if (fmt == FMT_FP8) {
-    hipLaunchKernelGGL(k_repack_u8_t, dim3(tg), dim3(256), 0, stream, w, E, N, K, wt);
+    hipLaunchKernelGGL(k_repack_u8_t, dim3(tg), dim3(256), 0, stream, w, E, N, K, tiled ? 1 : 0, wt);
     const int64_t n = (int64_t)E * (N / 128) * (K / 128);
     hipLaunchKernelGGL(k_repack_scales_t, dim3(grid_of(n, 4096)), dim3(256), 0, stream, static_cast<const float*>(s),
                        E, N / 128, K / 128, static_cast<float*>(st));
     return;
   }
-  hipLaunchKernelGGL(k_repack_int4_t, dim3(tg), dim3(256), 0, stream, w, E, N, K, wt);
+  hipLaunchKernelGGL(k_repack_int4_t, dim3(tg), dim3(256), 0, stream, w, E, N, K, tiled ? 1 : 0, wt);
   const int64_t n8 = (int64_t)E * N * K / (fmt == FMT_NVFP4 ? 16 : 32) / 8;
   if (fmt == FMT_NVFP4)
     hipLaunchKernelGGL(k_repack_scales_f16<FMT_NVFP4>, dim3(grid_of(n8, 4096)), dim3(256), 0, stream, s, n8,

@@ -107,8 +107,8 @@ void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queu
 //     last dimension (INT4: bf16 scales, odd pairs pre-divided by 16; MXFP4:
 //     E8M0 -> 2^(e-127));
 //   FP8: bytes W^T [E][K][N]; block scales [E][N/128][K/128] -> [E][K/128][N/128].
-void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, int K, uint8_t* wt, void* st,
-                       hipStream_t stream);
+void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, int K, bool tiled, uint8_t* wt,
+                       void* st, hipStream_t stream);
 // One launch: chunk g1.chunk's dh items (SwiGLU backward epilogue) and chunk
 // g2.chunk's dx' items, both reading the transposed copy; fmt = kernel family.
 void launch_gemm_bwd_pair(int fmt, const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,

@@ -622,7 +622,6 @@ BwdWeights bwd_weights_layout(const Dims& d) {
 moe_status check_backward(const moe_layer* L, Dims* d) {
   moe_status st = check_layer(L, d);
   if (st != MOE_OK) return st;
-  if (d->kblocked) return MOE_ERR_UNSUPPORTED;  // the recompute and the transposed copy read rows
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
   if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
@@ -715,9 +714,9 @@ moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweigh
   if (bwd_bytes < b.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(bwd_weights);
-  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13, d.E, 2 * d.I, d.H,
+  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13, d.E, 2 * d.I, d.H, d.kblocked,
                     reinterpret_cast<uint8_t*>(base + b.w13t), base + b.s13, s);
-  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w2), sc->s2, d.E, d.H, d.I,
+  launch_repack_bwd(d.fmt, static_cast<const uint8_t*>(qw->w2), sc->s2, d.E, d.H, d.I, d.kblocked,
                     reinterpret_cast<uint8_t*>(base + b.w2t), base + b.s2, s);
   return launch_status();
 }
@@ -884,6 +883,7 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
     g->nb_fastest = 1;
   }
   none.chunk = -1;
+  r1.w_kblocked = d.kblocked ? 1 : 0;  // the recompute reads the forward's codes as given
   r1.tile_start = tile_a_r;
   r1.tiles = tiles_r;
   const int gridr = gemm_grid(d, bm_r, chunk_experts, d.I / 128);

@@ -74,3 +74,33 @@ def test_fullsize_kblocked_equals_rows(name):
     got = run(d, binding.WL_KBLOCKED, o13, o2)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt,oft", [(1, True), (2, False), (3, False), (4, False), (5, False)])
+def test_backward_kblocked_equals_rows(fmt, oft):
+    """The backward on tiled codes: the transposed copy made from the tiles
+    equals the one made from rows byte for byte, and d_x, d_logits and
+    d_adapter are bit-identical."""
+    cfg = synth.LayerConfig("kblk_bwd", 310 + fmt + (5 if oft else 0), T=90, H=512, E=6, k=3, I=512, fmt=fmt,
+                            chunk=2, oft=oft, zipf_alpha=0.5)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    r = np.random.default_rng(3)
+    dout = gu.dev(synth._to_bf16_bits(r.standard_normal((cfg.T, cfg.H)).astype(np.float32)), "bf16")
+    outs, copies = [], []
+    for wl in (binding.WL_ROWS, binding.WL_KBLOCKED):
+        layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=oft, weight_layout=wl)
+        w13, w2 = (d.w13, d.w2) if wl == binding.WL_ROWS else binding.pack_weights_kblocked(layer, d.w13, d.w2)
+        # zero-filled so that the alignment padding between sections compares equal
+        bw = torch.zeros(binding.backward_weights_bytes(layer), dtype=torch.uint8, device="cuda")
+        binding.prepare_backward_weights(layer, w13, w2, d.s13, d.s2, out=bw)
+        got = binding.expert_backward(layer, d.x, d.logits, w13, w2, d.s13, d.s2, bw, dout, adapter=d.oft,
+                                      chunk_experts=cfg.chunk, g13=d.g13, g2=d.g2)
+        torch.cuda.synchronize()
+        copies.append(bw.clone())
+        outs.append([None if t is None else t.clone() for t in got])
+    assert torch.equal(copies[0], copies[1])
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    if oft:
+        assert torch.equal(outs[0][2], outs[1][2])
