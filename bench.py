@@ -87,8 +87,8 @@ def main():
                     help="time the frozen-base backward (d_x, d_logits, d_adapter; INT4 layers) instead")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the expert-parallel split "
-              "across GPUs is a design, not part of this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs one "
+              "GPU's share of the layer; the expert-parallel split across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
