@@ -161,9 +161,9 @@ __device__ __forceinline__ void oft_wave_lds_sync() {
 // block indexes the input dim) for every permuted row, on bf16 MFMA with fp32
 // accumulation, written as fp16 in the INT4-path layout (BF16OUT: bf16 in
 // natural order, the BF16 GEMMs' input).  Work item = 16 rows of one expert
-// (the 16-row tile list) times 32 consecutive diagonal blocks, 8 per wave:
-// a wave loads its 8 blocks of R_e (16 KB) and x values at once, stages the
-// blocks in its own LDS slice and runs 16 MFMAs, so each item costs one
+// (the 16-row tile list) times 16 consecutive diagonal blocks, 4 per wave:
+// a wave loads its 4 blocks of R_e (8 KB) and x values at once, stages the
+// blocks in its own LDS slice and runs 8 MFMAs, so each item costs one
 // memory round trip.  The active experts' tile starts are kept in LDS for
 // the item -> expert search.
 template <bool BF16OUT>
