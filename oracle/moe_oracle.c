@@ -156,7 +156,9 @@ static void quant_fp8_row(int K, const float* v, uint8_t* q, float* s) {
 /* FP8 [1,128] with power-of-two scales (NeMo RL FP8 post, recipe switches
  * for power-of-two weight and activation scaling factors): as above, but
  * the scale is the smallest power of two >= fl32(amax / 448), so no element
- * saturates and v / s is exact scaling.  s = 1 when amax = 0. */
+ * saturates and v / s is exact scaling.  s = 1 when amax = 0.  The scale is
+ * kept within the E8M0 range: at least 2^-127 (an amax below 448 * 2^-127,
+ * i.e. a block of bf16 subnormals, takes 2^-127). */
 static float pow2_at_least(float x) {
   int e;
   const float m = frexpf(x, &e); /* x = m * 2^e, m in [0.5, 1) */
@@ -170,6 +172,7 @@ static void quant_fp8_row_pow2(int K, const float* v, uint8_t* q, float* s) {
       if (a > amax) amax = a;
     }
     sc = (amax == 0.0f) ? 1.0f : pow2_at_least(amax / 448.0f);
+    if (sc < ldexpf(1.0f, -127)) sc = ldexpf(1.0f, -127);
     s[b] = sc;
     for (int i = 0; i < 128; ++i) {
       volatile float r = v[b * 128 + i] / sc; /* exact: sc is a power of two */

@@ -210,15 +210,99 @@ def test_nvfp4_power_of_two_scales_reduce_to_mxfp4():
     assert np.array_equal(oracle.dequant(5, N, K, q, s16, 1.0), oracle.dequant(3, N, K, q, e8m0))
 
 
+def _flat_swap_would_differ(G, N, g, n):
+    """True when scale [g][n] of a [G][N] group-major array lands on another
+    (row, group) under the transposed [N][G] reading."""
+    flat = g * N + n
+    return (flat // G, flat % G) != (n, g)
+
+
 def test_int4_layout_one_hot():
-    """Element 2i sits in the low nibble of byte i; scale g covers k in [32g, 32g+32)."""
-    N, K = 2, 64
+    """Element 2i sits in the low nibble of byte i; the bf16 scale stored at
+    [g][n] of the group-major [K/32][N] array covers row n, k in [32g, 32g+32).
+    N = 3 rows and K/32 = 4 groups make the scale array non-square, and the
+    scale changed is off the diagonal, so a row-major [N][K/32] reading or a
+    swapped (n, g) index moves the 2.0 onto another (row, group)."""
+    N, K = 3, 128
+    G = K // 32
     q = np.zeros((N, K // 2), np.uint8)
-    q[0, 0] = 0x0F | (0x3 << 4)   # k=0 -> -1, k=1 -> 3
-    q[1, 20] = 0x08               # k=40 -> -8
-    s = np.full((N, K // 32), 0x3F80, np.uint16)  # 1.0
-    s[1, 1] = 0x4000              # 2.0 for k in [32, 64) of row 1
+    q[0, 0] = 0x0F | (0x3 << 4)   # row 0: k=0 -> -1, k=1 -> 3
+    q[1, 40] = 0x08               # row 1: k=80 (group 2) -> -8
+    q[1, 50] = 0x50               # row 1: k=101 (group 3) -> 5
+    q[2, 10] = 0x07               # row 2: k=20 (group 0) -> 7
+    s = np.full((G, N), 0x3F80, np.uint16)  # 1.0
+    s[2, 1] = 0x4000              # 2.0: row 1, k in [64, 96)
+    s[0, 2] = 0x3F00              # 0.5: row 2, k in [0, 32)
+    assert _flat_swap_would_differ(G, N, 2, 1) and _flat_swap_would_differ(G, N, 0, 2)
     w = oracle.dequant(1, N, K, q, s)
     expect = np.zeros((N, K), np.float32)
-    expect[0, 0], expect[0, 1], expect[1, 40] = -1.0, 3.0, -16.0
+    expect[0, 0], expect[0, 1] = -1.0, 3.0
+    expect[1, 80], expect[1, 101] = -16.0, 5.0
+    expect[2, 20] = 3.5
     assert np.array_equal(w, expect)
+
+
+def test_mxfp4_layout_one_hot():
+    """E2M1 element 2i in the low nibble of byte i; the E8M0 byte at [g][n] of
+    the group-major [K/32][N] array scales row n, k in [32g, 32g+32).  Non-square
+    (N = 3, K/32 = 4) with off-diagonal scales, so a transposed reading fails."""
+    N, K = 3, 128
+    G = K // 32
+    q = np.zeros((N, K // 2), np.uint8)
+    q[0, 17] = 0x2 << 4           # row 0: k=35 (group 1) -> +1.0
+    q[1, 48] = 0xF                # row 1: k=96 (group 3) -> -6.0
+    q[1, 0] = 0x3                 # row 1: k=0 (group 0) -> +1.5
+    q[2, 33] = 0x1                # row 2: k=66 (group 2) -> +0.5
+    s = np.full((G, N), 127, np.uint8)   # 2^0
+    s[1, 0] = 130                 # row 0, group 1: 2^3
+    s[3, 1] = 125                 # row 1, group 3: 2^-2
+    s[2, 2] = 121                 # row 2, group 2: 2^-6
+    for g, n in ((1, 0), (3, 1), (2, 2)):
+        if g != n:
+            assert _flat_swap_would_differ(G, N, g, n)
+    w = oracle.dequant(3, N, K, q, s)
+    expect = np.zeros((N, K), np.float32)
+    expect[0, 35] = 8.0
+    expect[1, 96], expect[1, 0] = -1.5, 1.5
+    expect[2, 66] = 0.5 / 64
+    assert np.array_equal(w, expect)
+
+
+def test_nvfp4_layout_one_hot_nonsquare():
+    """NVFP4 scales [K/16][N] group-major: the E4M3 byte at [g][n] scales row n,
+    k in [16g, 16g+16).  N = 3, K/16 = 8, off-diagonal scales."""
+    N, K = 3, 128
+    G = K // 16
+    q = np.zeros((N, K // 2), np.uint8)
+    q[0, 56] = 0x4                # row 0: k=112 (group 7) -> 2.0
+    q[1, 8] = 0x6 << 4            # row 1: k=17 (group 1) -> 4.0
+    q[2, 20] = 0xA                # row 2: k=40 (group 2) -> -1.0
+    s = np.full((G, N), 0x38, np.uint8)  # E4M3 1.0
+    s[7, 0] = 0x30                # 0.5
+    s[1, 1] = 0x48                # 4.0 (diagonal on purpose: a swapped index reads s[?] = 1.0 elsewhere)
+    s[2, 2] = 0x44                # 3.0
+    assert _flat_swap_would_differ(G, N, 7, 0) and _flat_swap_would_differ(G, N, 1, 1)
+    w = oracle.dequant(5, N, K, q, s, 0.5)
+    expect = np.zeros((N, K), np.float32)
+    expect[0, 112] = 0.5
+    expect[1, 17] = 8.0
+    expect[2, 40] = -1.5
+    assert np.array_equal(w, expect)
+
+
+def test_fp8_pow2_scale_floor_is_e8m0_min():
+    """Power-of-two activation scales stay within E8M0's range: a block whose
+    amax/448 lies below 2^-127 (bf16 subnormal inputs) takes s = 2^-127, one
+    just above 2^-127 takes 2^-126, and the codes are E4M3 of v / s."""
+    v = np.zeros((3, 128), np.float32)
+    v[0, 0] = np.float32(2.0 ** -130)                  # amax/448 ~ 2^-138.8
+    v[0, 1] = -np.float32(2.0 ** -133)
+    v[1, 5] = np.float32(448.0 * 1.5 * 2.0 ** -127)    # amax/448 = 1.5 * 2^-127
+    v[2, 9] = np.float32(448.0 * 2.0 ** -127)          # amax/448 = 2^-127 exactly
+    q, s = oracle.quant_fp8_pow2(v)
+    assert s[0, 0] == np.float32(2.0 ** -127) and s[1, 0] == np.float32(2.0 ** -126)
+    assert s[2, 0] == np.float32(2.0 ** -127)
+    assert q[0, 0] == 0x20                              # 2^-3: exponent field 4, mantissa 0
+    assert q[0, 1] == 0x88                              # -2^-6: sign, exponent field 1
+    assert q[1, 5] == 0x7A                              # 336, midway between 320 and 352: even code 320
+    assert q[2, 9] == 0x7E                              # 448

@@ -232,3 +232,64 @@ def test_logprob_normalised_and_bruteforce():
     m = lg.max(1, keepdims=True)
     ref = lg[np.arange(T), tg] - (m[:, 0] + np.log(np.exp(lg - m).sum(1)))
     assert np.max(np.abs(lp - ref)) <= 1e-5
+
+
+def _bf16_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("T,k,H,seed", [(1, 1, 8, 0), (13, 4, 32, 1), (40, 16, 24, 2), (7, 8, 64, 3)])
+def test_combine_matches_gather_sum(T, k, H, seed):
+    """oracle.combine against a brute-force gather: out[t] = sum_j w[t, j] *
+    y_perm[row_of[t*k + j]], summed in fp64 in ascending j, with row_of a
+    random permutation of the T*k permuted rows and y_perm bf16."""
+    r = np.random.default_rng(seed)
+    R = T * k
+    row_of = r.permutation(R).astype(np.int32)
+    y = synth._to_bf16_bits((r.standard_normal((R, H)) * 4).astype(np.float32))
+    w = r.random((T, k)).astype(np.float32)
+    got = oracle.combine(y, w, row_of)
+    yv = _bf16_f64(y)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            acc = acc + np.float64(w[t, j]) * yv[row_of[t * k + j]]
+        ref[t] = acc
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_combine_one_hot_reveals_pair_indexing():
+    """With y_perm row r = 2^-r at column r (one-hot) and weights 1, output
+    row t holds 2^-row_of[t*k+j] exactly at columns row_of[t*k+j] for its k
+    slots and zeros elsewhere: a transposed (j*T + t) or inverse
+    (sorted_rows) index lands on other columns."""
+    T, k = 5, 3
+    R = T * k
+    row_of = np.random.default_rng(9).permutation(R).astype(np.int32)
+    vals = np.float32(2.0) ** -np.arange(R, dtype=np.float32)
+    y = np.zeros((R, R), np.float32)
+    y[np.arange(R), np.arange(R)] = vals
+    out = oracle.combine(synth._to_bf16_bits(y), np.ones((T, k), np.float32), row_of)
+    expect = np.zeros((T, R), np.float32)
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t * k + j]
+            expect[t, r] = vals[r]
+    assert np.array_equal(out, expect)
+
+
+def test_combine_weights_weight_slots_in_order():
+    """Distinct power-of-two weights per slot on identical y rows of ones:
+    out[t] = sum_j w[t, j], and swapping two slots' weights changes nothing
+    only when their rows are equal, so slot j must read w[t, j]."""
+    T, k, H = 3, 4, 8
+    row_of = np.arange(T * k, dtype=np.int32)
+    y = np.zeros((T * k, H), np.float32)
+    for r in range(T * k):
+        y[r] = r + 1                      # row r holds the value r + 1
+    w = np.array([[2.0 ** -(j + 1) for j in range(k)]] * T, np.float32)
+    out = oracle.combine(synth._to_bf16_bits(y), w, row_of)
+    for t in range(T):
+        expect = sum((t * k + j + 1) * 2.0 ** -(j + 1) for j in range(k))
+        assert np.all(out[t] == np.float32(expect))
