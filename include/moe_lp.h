@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_LP_ABI_VERSION 5
+#define MOE_LP_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -51,7 +51,12 @@ typedef enum {
 typedef enum {
   /* Two's-complement 4-bit codes, element 2i in the low nibble of byte i;
    * bf16 scale per (output row n, 32 consecutive k).  w = q * s.
-   * Activations into the GEMMs: 16-bit floats (no activation quantization). */
+   * Activations into the GEMMs: 16-bit floats (no activation quantization).
+   * The GEMMs run on fp16 operands: w = q*s is exact in fp16 for bf16 scales
+   * in [2^-17, 8188]; x (or x R_e with an adapter) and h = silu(gate)*up are
+   * converted to fp16, exact in magnitude range [2^-14, 65504) for bf16 x.
+   * Preconditions (not checked on the device): scales in that range and
+   * |x|, |x R_e|, |h| < 65504 (larger values become infinite). */
   MOE_W_INT4_G32_BF16 = 1,
   /* OCP E4M3FN codes, one byte each; fp32 scale per [128,128] block
    * [n/128][k/128].  Activations (x and the SwiGLU output) are quantized to
@@ -72,8 +77,9 @@ typedef enum {
    * first), an E4M3 scale byte per (n, 16 consecutive k), and one fp32
    * second-level scale per expert matrix (moe_scales.g13 / g2):
    * w = e2m1(q) * e4m3(s) * g.  Activations into the GEMMs: 16-bit floats,
-   * as for INT4.  Forward, materialized forward and frozen-base backward;
-   * no adapter (MOE_ERR_UNSUPPORTED). */
+   * as for INT4 (same range preconditions on x, x R_e and h; e2m1 * e4m3 is
+   * exact in fp16 for every code, g multiplies the fp32 accumulators).
+   * Forward, materialized forward and frozen-base backward. */
   MOE_W_NVFP4 = 5
 } moe_wformat;
 
@@ -93,13 +99,16 @@ typedef enum {
 
 /* Layer description (host memory). */
 typedef struct {
-  int32_t num_tokens;  /* T >= 0 (T = 0 is a no-op) */
+  /* T >= 0 (T = 0 is a no-op).  T*k*max(H, I)*2 must stay below 2^32 (the
+   * grouped GEMMs address gathered activation rows with 32-bit byte offsets;
+   * e.g. T <= 37449 at k = 8, H = 7168); larger: MOE_ERR_UNSUPPORTED. */
+  int32_t num_tokens;
   int32_t hidden;      /* H: multiple of 256                                */
   int32_t inter;       /* I: multiple of 128 (expert intermediate size)     */
   int32_t num_experts; /* E: 1..1024                                        */
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */
-  int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation  */
+  int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation (INT4 only for now; other formats: MOE_ERR_UNSUPPORTED) */
   int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128 or 192 */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
   int32_t weight_layout;         /* a moe_wlayout value; other values: MOE_ERR_INVALID_ARGUMENT */
@@ -268,7 +277,7 @@ size_t moe_backward_weights_bytes(const moe_layer* layer);
 /* Writes the transposed copy of (qweights, scales) into bwd_weights (device,
  * caller-owned, >= moe_backward_weights_bytes).  Codes are bit-identical
  * re-layouts; INT4 scales are converted to fp16 (exact for bf16 scales in
- * [2^-10, 4096]) and pre-divided by 16 where the unpack needs it, MXFP4
+ * [2^-17, 8188]), MXFP4
  * scales to fp16 2^(e-127) (exact within fp16's range), NVFP4 E4M3 scales
  * to fp16 (exact), FP8 block scales are transposed.  NVFP4's fp32
  * second-level scales are not copied: moe_expert_backward reads them from
@@ -314,13 +323,31 @@ moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const
                                void* d_x_bf16, float* d_logits, float* d_adapter, void* ws, size_t ws_bytes,
                                void* stream, float* stage_ms, int32_t* stage_launches);
 
+/* The GEMM1 input quantizer of the layer's weight format applied to x, one
+ * row per token (what moe_expert_forward feeds its first grouped GEMM when no
+ * adapter is given), written to caller buffers:
+ *   FP8 (NeMo RL FP8 post, Table 1, input activations): codes [T][H] E4M3FN,
+ *     scales fp32 [T][H/128]: s = amax/448 (1 for an all-zero block),
+ *     q = RNE-saturate(v/s), both quotients correctly rounded in fp32;
+ *   FP8_POW2: as FP8 with s the smallest power of two >= amax/448;
+ *   MXFP4: codes [T][H] E4M3FN, scales [T][H/32] E8M0 bytes: shared exponent
+ *     X = floor(log2 amax) - 8 (0 for an all-zero block, clamped to
+ *     [-127, 127]), q = RNE-saturate(v * 2^-X).
+ * INT4 and NVFP4 layers take 16-bit activations and have no quantizer:
+ * MOE_ERR_UNSUPPORTED.  x, codes: 16-byte aligned; scales: 4-byte aligned.
+ * Stream-ordered, no host synchronisation. */
+moe_status moe_quantize_activations(const moe_layer* layer, const void* x_bf16, void* codes, void* scales,
+                                    void* stream);
+
 /* Weighted combine on its own: out[t] = sum_{j<k} topk_w[t][j] *
  * y_perm[row_of[t*k+j]], fp32 sum in ascending j, RNE to bf16.  y_perm:
  * [T*k][H] bf16.  Atomic-free and deterministic. */
 moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w,
                        const int32_t* row_of, void* out_bf16, void* stream);
 
-/* Workspace bytes moe_lm_head_logprob needs: T*V fp32 logits + 256 B. */
+/* Workspace bytes moe_lm_head_logprob needs: 2*T*V fp32 partial logits (two
+ * K slices), T fp32 inverse RMS values and T*ceil(V/4096)*3 fp32 per-chunk
+ * log-softmax statistics, each 256-byte aligned. */
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V);
 
 /* Log-prob of target tokens under an LM head (the rollout log-probs whose

@@ -22,7 +22,8 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rou
             "moe_route_permute", "moe_expert_forward", "moe_expert_forward_timed", "moe_combine",
             "moe_lm_head_workspace_bytes", "moe_lm_head_logprob", "moe_materialized_workspace_bytes",
             "moe_expert_forward_materialized", "moe_backward_weights_bytes", "moe_prepare_backward_weights",
-            "moe_backward_workspace_bytes", "moe_expert_backward", "moe_pack_weights_kblocked")
+            "moe_backward_workspace_bytes", "moe_expert_backward", "moe_pack_weights_kblocked",
+            "moe_quantize_activations")
 STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine", "dequant")
 
 
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_int32)]
+        L.moe_quantize_activations.restype = ctypes.c_int
+        L.moe_quantize_activations.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -291,6 +295,20 @@ def expert_backward(layer: MoeLayer, x, logits, w13, w2, s13, s2, bwd_weights, d
     if timed:
         return d_x, d_logits, d_adapter, {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}
     return d_x, d_logits, d_adapter
+
+
+def quantize_activations(layer: MoeLayer, x: torch.Tensor):
+    """moe_quantize_activations -> (codes [T][H] uint8, scales): fp32 [T][H/128]
+    for FP8 layers, E8M0 bytes [T][H/32] for MXFP4 layers."""
+    T, H = layer.num_tokens, layer.hidden
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    if layer.wformat in (FMT_FP8, FMT_FP8_POW2):
+        scales = torch.empty((T, H // 128), dtype=torch.float32, device=x.device)
+    else:
+        scales = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quantize_activations(ctypes.byref(layer), _ptr(x), _ptr(codes), _ptr(scales), _stream()),
+           "moe_quantize_activations")
+    return codes, scales
 
 
 def combine(layer: MoeLayer, y_perm: torch.Tensor, topk_w: torch.Tensor, row_of: torch.Tensor,

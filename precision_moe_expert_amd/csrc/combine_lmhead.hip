@@ -67,58 +67,126 @@ __global__ __launch_bounds__(64) void k_inv_rms(const uint16_t* __restrict__ h, 
   if (lane == 0) inv_rms[t] = 1.0f / sqrtf(ss / (float)H + 1e-6f);
 }
 
-// logits[t][v] = inv_rms[t] * sum_k h[t][k] W[v][k], bf16 MFMA with fp32
-// accumulation.  A wave owns 16 vocabulary rows and 64 tokens; the weight
-// rows stream from HBM once, the token rows are re-read from L2.
-__global__ __launch_bounds__(256) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                 const float* __restrict__ inv_rms, int T, int H, int V,
-                                                 float* __restrict__ logits) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Partial logits part[ks][t][v] = sum over the ks-th K slice of h[t][k] W[v][k]
+// (bf16 MFMA, fp32 accumulation).  The head is a skinny GEMM (<= 64 tokens
+// against V x H weights) bound by streaming W once from HBM, so the kernel
+// is built around that stream: a workgroup owns 128 vocabulary rows (32 per
+// wave) and one K slice (KS = 2 slices give enough workgroups to fill the
+// chip), and moves 128-K steps of its W rows (256 B of each row, 32 KB) and
+// of the token rows (16 KB, shared by the 4 waves) into an LDS ring of
+// LM_S stages by global_load_lds DMA.  Inside a stage each 256-byte row is
+// kept as 16 parts of 16 B with part p at slot p ^ (row & 15), so the
+// 16 lanes that read one MFMA fragment hit 16 different slots.
+constexpr int LM_S = 3;            // stages in flight
+constexpr int LM_VB = 128;         // vocabulary rows per workgroup
+constexpr int LM_STAGE = (LM_VB + 64) * 256;
+constexpr int LM_NPER = 8 + 4;     // DMA instructions per wave per stage (W: 32 rows, h: 16 rows)
+
+__global__ __launch_bounds__(256, 1) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                    int T, int H, int V, int ks_len, float* __restrict__ part) {
+  __shared__ __align__(16) uint8_t smem[LM_S * LM_STAGE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
-  const int v0 = (blockIdx.x * 4 + wave) * 16;
-  const int t0 = blockIdx.y * 64;
-  if (v0 >= V) return;
-  const int vr = min(v0 + ln, V - 1);
-  const uint16_t* wrow = W + (int64_t)vr * H + lg * 8;
-  const uint16_t* hrow[4];
+  const int vb = blockIdx.x, ks = blockIdx.y, t0 = blockIdx.z * 64;
+  const int k0 = ks * ks_len, KT = ks_len / 128;
+  const uint32_t smem0 = lds_u32(smem);
+  // DMA sources: lane l of instruction j writes LDS slot l%16 of row 4j + l/16
+  // of the wave's rows; that slot holds part (l%16) ^ (row & 15).
+  const char* wsrc[8];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) hrow[m] = h + (int64_t)min(t0 + m * 16 + ln, T - 1) * H + lg * 8;
-  f32x4 acc[4];
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 32 + j * 4 + lg;                      // row within the W block
+    const int v = min(vb * LM_VB + r, V - 1);
+    wsrc[j] = reinterpret_cast<const char*>(W) + ((int64_t)v * H + k0 + ((ln ^ (r & 15)) * 8)) * 2;
+  }
+  const char* hsrc[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kk = 0; kk < H; kk += 128) {
-    uint4 bw[4], ah[4][4];
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 16 + j * 4 + lg;                      // token row within the block
+    const int t = min(t0 + r, T - 1);
+    hsrc[j] = reinterpret_cast<const char*>(h) + ((int64_t)t * H + k0 + ((ln ^ (r & 15)) * 8)) * 2;
+  }
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sb = smem0 + slot * LM_STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bw[s] = *reinterpret_cast<const uint4*>(wrow + kk + s * 32);
+    for (int j = 0; j < 8; ++j) dma_b128(wsrc[j] + kt * 256, sb + (wave * 32 + j * 4) * 256);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int j = 0; j < 4; ++j) dma_b128(hsrc[j] + kt * 256, sb + LM_VB * 256 + (wave * 16 + j * 4) * 256);
+  };
+  f32x4 acc[4][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ah[m][s] = *reinterpret_cast<const uint4*>(hrow[m] + kk + s * 32);
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int c = 0; c < 2; ++c) acc[m][c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s + 1 < LM_S; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<LM_NPER>(min(LM_S - 2, KT - 1 - kt));  // this wave's pieces of stage kt have landed
+    lds_barrier();                                      // ... and every other wave's
+    if (kt + LM_S - 1 < KT) issue(kt + LM_S - 1, (kt + LM_S - 1) % LM_S);
+    const uint8_t* st = smem + (kt % LM_S) * LM_STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int part_ = s * 4 + lg;
+      bf16x8 bw[2], ah[4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int r = wave * 32 + c * 16 + ln;
+        bw[c] = *reinterpret_cast<const bf16x8*>(st + r * 256 + ((part_ ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = m * 16 + ln;
+        ah[m] = *reinterpret_cast<const bf16x8*>(st + LM_VB * 256 + r * 256 + ((part_ ^ (r & 15)) << 4));
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        acc[m] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, ah[m][s]), __builtin_bit_cast(bf16x8, bw[s]), acc[m]);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[m][c] = mfma_bf16_16x16x32(ah[m], bw[c], acc[m][c]);
+    }
   }
-  const int v = v0 + ln;
-  if (v < V)
+  float* out = part + (int64_t)ks * T * V;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+  for (int c = 0; c < 2; ++c) {
+    const int v = vb * LM_VB + wave * 32 + c * 16 + ln;
+    if (v < V)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + m * 16 + lg * 4 + i;
-        if (t < T) logits[(int64_t)t * V + v] = acc[m][i] * inv_rms[t];
-      }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + m * 16 + lg * 4 + i;
+          if (t < T) out[(int64_t)t * V + v] = acc[m][c][i];
+        }
+  }
 }
 
-// logprob[t] = logits[t][y_t] - (max + log(sum exp(logits - max))).
-__global__ __launch_bounds__(256) void k_logsoftmax_gather(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
-                                                           int V, float* __restrict__ lp) {
-  const int t = blockIdx.x;
-  const float* row = logits + (int64_t)t * V;
+// Per token and vocabulary chunk of LM_VC entries: logits = inv_rms[t] *
+// (part[0] + part[1]) (slices summed in order), the chunk's maximum m, its
+// sum of exp(logit - m), and the target's logit if it falls in the chunk.
+constexpr int LM_VC = 4096;
+__global__ __launch_bounds__(256) void k_lm_softmax_part(const float* __restrict__ part, int ks_n,
+                                                         const float* __restrict__ inv_rms,
+                                                         const int32_t* __restrict__ tgt, int T, int V,
+                                                         float* __restrict__ stats) {
+  const int t = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
+  const int v0 = ch * LM_VC, v1 = min(V, v0 + LM_VC);
+  const float ir = inv_rms[t];
   __shared__ float red[4];
+  float lv[LM_VC / 256];
   float mx = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += 256) mx = fmaxf(mx, row[v]);
+#pragma unroll
+  for (int i = 0; i < LM_VC / 256; ++i) {
+    const int v = v0 + i * 256 + threadIdx.x;
+    float z = -INFINITY;
+    if (v < v1) {
+      float sum = part[(int64_t)t * V + v];
+      for (int q = 1; q < ks_n; ++q) sum += part[((int64_t)q * T + t) * V + v];
+      z = sum * ir;
+    }
+    lv[i] = z;
+    mx = fmaxf(mx, z);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor(mx, m));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -126,15 +194,39 @@ __global__ __launch_bounds__(256) void k_logsoftmax_gather(const float* __restri
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float se = 0.0f;
-  for (int v = threadIdx.x; v < V; v += 256) se += expf(row[v] - mx);
+#pragma unroll
+  for (int i = 0; i < LM_VC / 256; ++i)
+    if (v0 + i * 256 + (int)threadIdx.x < v1) se += expf(lv[i] - mx);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) se += shfl_xor(se, m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = se;
   __syncthreads();
+  float* st = stats + ((int64_t)t * nch + ch) * 3;
   if (threadIdx.x == 0) {
-    const int y = tgt[t];  // out-of-range targets give NaN instead of a stray read
-    lp[t] = (y >= 0 && y < V) ? row[y] - (mx + logf((red[0] + red[1]) + (red[2] + red[3]))) : __builtin_nanf("");
+    st[0] = mx;
+    st[1] = (red[0] + red[1]) + (red[2] + red[3]);
   }
+  const int y = tgt[t];
+  if (y >= v0 && y < v1 && ((y - v0) & 255) == (int)threadIdx.x) {
+#pragma unroll
+    for (int i = 0; i < LM_VC / 256; ++i)
+      if (i == (y - v0) / 256) st[2] = lv[i];
+  }
+}
+
+// logprob[t] = logit[t][y_t] - (M + log sum_c s_c exp(m_c - M)), chunks in order.
+__global__ __launch_bounds__(64) void k_lm_softmax_final(const float* __restrict__ stats, int nch,
+                                                         const int32_t* __restrict__ tgt, int T, int V,
+                                                         float* __restrict__ lp) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= T) return;
+  const float* st = stats + (int64_t)t * nch * 3;
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c * 3]);
+  float S = 0.0f;
+  for (int c = 0; c < nch; ++c) S += st[c * 3 + 1] * expf(st[c * 3] - M);
+  const int y = tgt[t];  // out-of-range targets give NaN instead of a stray read
+  lp[t] = (y >= 0 && y < V) ? st[(y / LM_VC) * 3 + 2] - (M + logf(S)) : __builtin_nanf("");
 }
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
@@ -143,13 +235,19 @@ void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, in
   hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, y, w, row_of, k, H, out);
 }
 
+int lm_head_slices(int H) { return (H / 128) % 2 == 0 ? 2 : 1; }
+int lm_head_chunks(int V) { return (V + LM_VC - 1) / LM_VC; }
+
 void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,
-                    float* logits_ws, float* inv_rms_ws, float* logprob, hipStream_t s) {
+                    float* part_ws, float* inv_rms_ws, float* stats_ws, float* logprob, hipStream_t s) {
   if (T == 0) return;
+  const int ks = lm_head_slices(H), nch = lm_head_chunks(V);
   hipLaunchKernelGGL(k_inv_rms, dim3(T), dim3(64), 0, s, h, H, inv_rms_ws);
-  hipLaunchKernelGGL(k_lm_gemm, dim3((V + 63) / 64, (T + 63) / 64), dim3(256), 0, s, h, wlm, inv_rms_ws, T, H, V,
-                     logits_ws);
-  hipLaunchKernelGGL(k_logsoftmax_gather, dim3(T), dim3(256), 0, s, logits_ws, targets, V, logprob);
+  hipLaunchKernelGGL(k_lm_gemm, dim3((V + LM_VB - 1) / LM_VB, ks, (T + 63) / 64), dim3(256), 0, s, h, wlm, T, H, V,
+                     H / ks, part_ws);
+  hipLaunchKernelGGL(k_lm_softmax_part, dim3(T, nch), dim3(256), 0, s, part_ws, ks, inv_rms_ws, targets, T, V,
+                     stats_ws);
+  hipLaunchKernelGGL(k_lm_softmax_final, dim3((T + 63) / 64), dim3(64), 0, s, stats_ws, nch, targets, T, V, logprob);
 }
 
 }  // namespace moe

@@ -62,10 +62,13 @@ MOE_DEV uint32_t cvt_e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)r;
 }
 
-// Smallest power of two >= x for a positive normal float x (x itself when it
-// is one), and the exact reciprocal of a power of two.
+// Smallest power of two >= x for a positive float x (x itself when it is
+// one), at least 2^-127, and the exact reciprocal of such a power of two.
 MOE_DEV float pow2_at_least(float x) {
   const uint32_t b = __float_as_uint(x);
+  // fp32 subnormals: 2^-126 above 2^-127, else 2^-127, the smallest power of
+  // two an E8M0 scale holds (so every scale this returns is an E8M0 value)
+  if ((b >> 23) == 0) return __uint_as_float(b > 0x00400000u ? 0x00800000u : 0x00400000u);
   return (b & 0x7FFFFFu) ? __uint_as_float(((b >> 23) + 1) << 23) : x;
 }
 MOE_DEV float pow2_reciprocal(float p) { return __uint_as_float((254u - (__float_as_uint(p) >> 23)) << 23); }

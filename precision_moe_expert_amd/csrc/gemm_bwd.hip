@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void k_repack_u8_t(const uint8_t* __restrict__
 
 // Group scales [E][G][L] (G groups of the transposed copy's rows, L along its
 // K) -> per 8 consecutive K values four fp16 pairs {s0, s4}, {s1, s5},
-// {s2, s6}, {s3, s7}; INT4 (bf16 scales) divides the odd pairs by 16 for its
-// unpack, MXFP4 turns E8M0 bytes into 2^(e-127), NVFP4 E4M3 bytes into their
+// {s2, s6}, {s3, s7}; INT4 bf16 scales are converted as they are, MXFP4
+// turns E8M0 bytes into 2^(e-127), NVFP4 E4M3 bytes into their
 // values (exact in fp16: at most 448, at least 2^-9).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_repack_scales_f16(const void* __restrict__ s, int64_t n8,
@@ -124,12 +124,11 @@ __global__ __launch_bounds__(256) void k_repack_scales_f16(const void* __restric
         f[j] = FMT == FMT_NVFP4 ? e4m3_to_f32(e) : __uint_as_float(e ? e << 23 : 0x00400000u);
       }
     }
-    const float d = FMT == FMT_INT4 ? 0.0625f : 1.0f;
     u32x4 o;
     o.x = pack_f16x2(f[0], f[4]);
-    o.y = pack_f16x2(f[1] * d, f[5] * d);
+    o.y = pack_f16x2(f[1], f[5]);
     o.z = pack_f16x2(f[2], f[6]);
-    o.w = pack_f16x2(f[3] * d, f[7] * d);
+    o.w = pack_f16x2(f[3], f[7]);
     out[i] = o;
   }
 }

@@ -291,17 +291,19 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         for (int i = 0; i < 4; ++i) {
           const int row = (mb0 + m) * 16 + lg * 4 + i;
           const float amax = fmaxf(fmaxf(rmax[m][0][i], rmax[m][1][i]), fmaxf(rmax[m][2][i], rmax[m][3][i]));
-          // the row's [1,128] block scale: amax/448 (codes h/s with the hardware
-          // reciprocal), or the power of two at or above it (exact scaling)
-          float sc, inv;
+          // the row's [1,128] block scale: s = amax/448 with codes RNE(h/s), both
+          // quotients correctly rounded (the activation quantizer's definition),
+          // or the power of two at or above amax/448 (exact scaling)
+          float sc;
+          uint32_t c2;
           if constexpr (P2) {
             sc = amax == 0.0f ? 1.0f : pow2_at_least(amax / 448.0f);
-            inv = pow2_reciprocal(sc);
+            const float inv = pow2_reciprocal(sc);
+            c2 = cvt_e4m3x2(hv[m][i][0] * inv, hv[m][i][1] * inv);
           } else {
-            sc = amax == 0.0f ? 1.0f : amax * (1.0f / 448.0f);
-            inv = __builtin_amdgcn_rcpf(sc);
+            sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+            c2 = cvt_e4m3x2(hv[m][i][0] / sc, hv[m][i][1] / sc);
           }
-          const uint32_t c2 = cvt_e4m3x2(hv[m][i][0] * inv, hv[m][i][1] * inv);
           smem[row * HS + wc * 32 + ln] = (uint8_t)(c2 & 0xFF);
           smem[row * HS + wc * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
           if (wc == 0 && ln == 0 && row < tl.nrows)

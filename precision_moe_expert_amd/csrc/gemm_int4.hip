@@ -5,8 +5,9 @@
 // Dequantization (Orbit announcement, 技术细节: the active experts' weights
 // are dequantized temporarily for the grouped GEMM) happens in registers:
 // each lane unpacks its own 32 nibbles per 128-K step and multiplies by the
-// group's scale in fp16.  Every INT4 code times a bf16 group scale is exact
-// in fp16 (at most 3 + 8 significant bits), so the MFMA sees w = q*s exactly;
+// group's scale in fp16.  Every INT4 code times a bf16 group scale in
+// [2^-17, 8188] is exact in fp16 (at most 3 + 8 significant bits), so the
+// MFMA sees w = q*s exactly;
 // nothing is written back to memory and no dequantized copy exists.
 //
 // Tile: BM rows x 256 output columns per workgroup (4 waves x 4 subtiles of
@@ -128,10 +129,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
       } else {
         const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * 512 + lg * 128 +
                                                                (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
-        const float sf = bf16_bits_to_f32(sw);
-        const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f);
+        const _Float16 sh = (_Float16)bf16_bits_to_f32(sw);
         s2[i] = (f16x2){sh, sh};
-        s2_16[i] = (f16x2){sh16, sh16};
       }
     }
     // activation fragment of row block m, 32-K sub-step s: logical part 4*lg + s
@@ -156,7 +155,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bf[i] = NV ? e2m1x8_to_f16(dword_of(bq[i], s), s < 2 ? s2[i] : s2_16[i])
-                   : int4x8_to_f16(dword_of(bq[i], s), s2[i], s2_16[i]);
+                   : int4x8_to_f16(dword_of(bq[i], s), s2[i]);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll

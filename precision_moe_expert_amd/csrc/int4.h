@@ -6,25 +6,34 @@
 namespace moe {
 
 // 8 INT4 codes (one dword, element i in bits 4i..4i+3, two's complement) times
-// scale s -> 8 fp16 values ordered (0,4),(1,5),(2,6),(3,7).  Each pair comes
-// from one bitop3 that keeps the two code fields, flips their sign bit (q + 8)
-// and sets the exponent of 1024, i.e. fp16 1024 + (q + 8) for codes in bits
-// 0-3 / 16-19, or 1024 + 16 (q + 8) for codes in bits 4-7 / 20-23 (still
-// inside the 10-bit mantissa, so no shift is needed).  Subtracting the bias
-// gives q or 16 q exactly; multiplying by s or s/16 gives q s, exact in fp16.
+// scale s -> 8 fp16 values ordered (0,4),(1,5),(2,6),(3,7).  This is the
+// "magic number" conversion of Kim et al., "Who Says Elephants Can't Run"
+// (2022): each pair comes from one bitop3 that keeps the two code fields,
+// flips their sign bit (q + 8) and sets the exponent of 1024, i.e. fp16
+// 1024 + (q + 8) for codes in bits 0-3 / 16-19, or 1024 + 16 (q + 8) for
+// codes in bits 4-7 / 20-23 (still inside the 10-bit mantissa, so no shift is
+// needed).  Subtracting 1032 gives q; for the second form one fused
+// multiply-add v/16 - 72 gives q (every intermediate is an integer below
+// 2048, exact in fp16).  Multiplying by s then gives q s, exact in fp16
+// whenever it is representable: s in [2^-17, 8188] for bf16 scales (at most
+// 3 + 8 significant bits, lowest bit at or above fp16's 2^-24, |q s| < 65504).
 // bitop3 truth table 0x6A: b ? (c ? ~a : a) : c.
-MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2, f16x2 s2_16) {
+MOE_DEV f16x2 int4_pair_hi(uint32_t d) {
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 bias = {(_Float16)-72.0f, (_Float16)-72.0f};
+  return __builtin_elementwise_fma(__builtin_bit_cast(f16x2, d), sixteenth, bias);
+}
+MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2) {
   const f16x2 bias0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 bias1 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   const uint32_t v = w >> 8;
   const uint32_t d0 = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, 0x6A);
   const uint32_t d1 = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, 0x6A);
   const uint32_t d2 = __builtin_amdgcn_bitop3_b32(v, 0x000F000Fu, 0x64086408u, 0x6A);
   const uint32_t d3 = __builtin_amdgcn_bitop3_b32(v, 0x00F000F0u, 0x64806480u, 0x6A);
   const f16x2 h0 = (__builtin_bit_cast(f16x2, d0) + bias0) * s2;
-  const f16x2 h1 = (__builtin_bit_cast(f16x2, d1) + bias1) * s2_16;
+  const f16x2 h1 = int4_pair_hi(d1) * s2;
   const f16x2 h2 = (__builtin_bit_cast(f16x2, d2) + bias0) * s2;
-  const f16x2 h3 = (__builtin_bit_cast(f16x2, d3) + bias1) * s2_16;
+  const f16x2 h3 = int4_pair_hi(d3) * s2;
   f16x8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
   return r;
 }
@@ -56,11 +65,10 @@ struct I4Stage {
 };
 
 // The same 8 codes with one scale per element: sc holds the fp16 pairs
-// {s0, s4}, {s1/16, s5/16}, {s2, s6}, {s3/16, s7/16} for elements 0..7 (the
-// layout the backward weight copy stores), output order as above.
+// {s0, s4}, {s1, s5}, {s2, s6}, {s3, s7} for elements 0..7 (the layout the
+// backward weight copy stores), output order as above.
 MOE_DEV f16x8 int4x8_to_f16_se(uint32_t w, const u32x4& sc) {
   const f16x2 bias0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 bias1 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   const uint32_t v = w >> 8;
   const uint32_t d0 = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, 0x6A);
   const uint32_t d1 = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, 0x6A);
@@ -70,9 +78,9 @@ MOE_DEV f16x8 int4x8_to_f16_se(uint32_t w, const u32x4& sc) {
   // reads from the start of the vector, i.e. sc.x
   const uint32_t s0 = sc.x, s1 = sc.y, s2 = sc.z, s3 = sc.w;
   const f16x2 h0 = (__builtin_bit_cast(f16x2, d0) + bias0) * __builtin_bit_cast(f16x2, s0);
-  const f16x2 h1 = (__builtin_bit_cast(f16x2, d1) + bias1) * __builtin_bit_cast(f16x2, s1);
+  const f16x2 h1 = int4_pair_hi(d1) * __builtin_bit_cast(f16x2, s1);
   const f16x2 h2 = (__builtin_bit_cast(f16x2, d2) + bias0) * __builtin_bit_cast(f16x2, s2);
-  const f16x2 h3 = (__builtin_bit_cast(f16x2, d3) + bias1) * __builtin_bit_cast(f16x2, s3);
+  const f16x2 h3 = int4_pair_hi(d3) * __builtin_bit_cast(f16x2, s3);
   f16x8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
   return r;
 }

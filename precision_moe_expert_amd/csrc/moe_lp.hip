@@ -221,6 +221,26 @@ moe_status moe_pack_weights_kblocked(const moe_layer* layer, const moe_qweights*
   return launch_status();
 }
 
+moe_status moe_quantize_activations(const moe_layer* layer, const void* x_bf16, void* codes, void* scales,
+                                    void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (d.fmt != MOE_W_FP8_E4M3_B128 && d.fmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (d.T == 0) return MOE_OK;
+  if (x_bf16 == nullptr || codes == nullptr || scales == nullptr || !aligned16(x_bf16) || !aligned16(codes) ||
+      !aligned4(scales))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  if (d.fmt == MOE_W_FP8_E4M3_B128)
+    launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(codes), static_cast<float*>(scales), (d.H / 128) * 4, d.pow2,
+                   s);
+  else
+    launch_act_mxfp8(x, d.T, d.H, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales), d.H / 32, s);
+  return launch_status();
+}
+
 size_t moe_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   Dims d;
   if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
@@ -959,7 +979,9 @@ moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const fl
 
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V) {
   if (T < 0 || V <= 0) return 0;
-  return align_up((size_t)T * (size_t)V * 4) + align_up((size_t)T * 4);
+  // room for two K slices of partial logits (the most lm_head_slices returns)
+  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * 4) +
+         align_up((size_t)T * lm_head_chunks(V) * 3 * 4);
 }
 
 moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf16, const void* w_lm_bf16,
@@ -972,10 +994,11 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < moe_lm_head_workspace_bytes(T, V)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   char* base = static_cast<char*>(ws);
-  float* logits = reinterpret_cast<float*>(base);
-  float* inv_rms = reinterpret_cast<float*>(base + align_up((size_t)T * (size_t)V * 4));
+  float* part = reinterpret_cast<float*>(base);
+  float* inv_rms = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4));
+  float* stats = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * 4));
   launch_lm_head(static_cast<const uint16_t*>(h_bf16), static_cast<const uint16_t*>(w_lm_bf16), targets, T, H, V,
-                 logits, inv_rms, logprob, static_cast<hipStream_t>(stream));
+                 part, inv_rms, stats, logprob, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -13,17 +13,19 @@ Kimi-K2-shaped INT4 + OFT layer followed by an LM head).
 Weight storage (all K-contiguous, Y = X @ W^T):
   W13[E][2I][H]  gate rows 0..I-1 then up rows I..2I-1;  W2[E][H][I]
   int4   : two's-complement nibbles, element 2i in the low nibble of byte i;
-           bf16 scales [E][N][K/32]
+           bf16 scales, group-major [E][K/32][N]
   fp8    : OCP E4M3FN codes, one byte each; fp32 scales [E][N/128][K/128]
-  mxfp4  : E2M1 nibbles (low nibble first); E8M0 scale bytes [E][N][K/32]
+  mxfp4  : E2M1 nibbles (low nibble first); E8M0 scale bytes, group-major [E][K/32][N]
   nvfp4  : E2M1 nibbles (low nibble first); E4M3 scale bytes per 16 along K,
            group-major [E][K/16][N]; fp32 second-level scales g13[E], g2[E]
 OFT adapter: R[E][H/32][32][32] bf16, x' = x @ blockdiag(R_e).
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import hashlib
+import os
 
 import numpy as np
 import torch
@@ -85,6 +87,20 @@ def _rng(cfg_id: int, tensor: int, extra: int = 0) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([SEED_ROOT, cfg_id, tensor, extra]))
 
 
+def _per_expert(fn, E: int) -> None:
+    """Runs fn(e) for every expert on a thread pool.  Each expert draws from its
+    own seed and writes its own slice, so the result does not depend on the
+    thread count (numpy's generators and torch's casts release the GIL)."""
+    workers = max(1, min(16, os.cpu_count() or 1, E))
+    if workers == 1:
+        for e in range(E):
+            fn(e)
+        return
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for _ in ex.map(fn, range(E)):
+            pass
+
+
 def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 array -> bf16 bit patterns (uint16) via torch's RNE cast."""
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
@@ -134,10 +150,11 @@ def _gen_int4(cfg, N, K, tensor, stensor):
     E = cfg.E
     q = np.empty((E, N, K // 2), np.uint8)
     s = np.empty((E, K // 32, N), np.uint16)  # group-major: s[e][g][n] scales row n, k in [32g, 32g+32)
-    for e in range(E):
+    def one(e):
         # uniform bytes = two independent uniform nibbles over all 16 codes
         q[e] = _rng(cfg.cfg_id, tensor, e).integers(0, 256, (N, K // 2), dtype=np.uint8)
         s[e] = _to_bf16_bits(_rng(cfg.cfg_id, stensor, e).uniform(0.005, 0.02, (N, K // 32)).astype(np.float32)).T
+    _per_expert(one, E)
     return q, s
 
 
@@ -146,11 +163,12 @@ def _gen_fp8(cfg, N, K, tensor, stensor):
     q = np.empty((E, N, K), np.uint8)
     s = np.empty((E, N // 128, K // 128), np.float32)
     sig = 448.0 / 4.5  # code-space spread: block maxima land near the top codes
-    for e in range(E):
+    def one(e):
         v = _rng(cfg.cfg_id, tensor, e).standard_normal((N, K), dtype=np.float32) * sig
         q[e] = _to_e4m3_codes(np.clip(v, -448.0, 448.0))
         # block scales so that weights are ~N(0, 0.02^2)
         s[e] = (_rng(cfg.cfg_id, stensor, e).uniform(0.5, 1.5, (N // 128, K // 128)) * (0.02 / sig)).astype(np.float32)
+    _per_expert(one, E)
     return q, s
 
 
@@ -170,13 +188,14 @@ def _gen_mxfp4(cfg, N, K, tensor, stensor):
     lut16[256:] = mag | 8
     q = np.empty((E, N, K // 2), np.uint8)
     s = np.empty((E, K // 32, N), np.uint8)  # group-major, as for INT4
-    for e in range(E):
+    def one(e):
         r = _rng(cfg.cfg_id, tensor, e)
         lo = lut16[r.integers(0, 512, (N, K // 2), dtype=np.uint16)]
         hi = lut16[r.integers(0, 512, (N, K // 2), dtype=np.uint16)]
         q[e] = lo | (hi << 4)
         # E8M0 scale bytes 2^-8 .. 2^-6 -> weights of magnitude ~0.02
         s[e] = _rng(cfg.cfg_id, stensor, e).integers(119, 122, (N, K // 32), dtype=np.uint8).T
+    _per_expert(one, E)
     return q, s
 
 
@@ -186,9 +205,10 @@ def _gen_nvfp4(cfg, N, K, tensor, stensor):
     E = cfg.E
     q, _ = _gen_mxfp4(cfg, N, K, tensor, stensor)
     s = np.empty((E, K // 16, N), np.uint8)  # group-major: s[e][g][n] scales row n, k in [16g, 16g+16)
-    for e in range(E):
+    def one(e):
         v = np.exp2(_rng(cfg.cfg_id, stensor, 1000 + e).uniform(4.0, np.log2(448.0), (K // 16, N)))
         s[e] = _to_e4m3_codes(v.astype(np.float32))
+    _per_expert(one, E)
     return q, s
 
 
@@ -222,13 +242,14 @@ def gen_oft(cfg: LayerConfig, sigma: float | None = None) -> np.ndarray:
     out = np.empty((cfg.E, nb, 32, 32), np.uint16)
     eye = np.eye(32)
     iu = np.triu_indices(32, 1)
-    for e in range(cfg.E):
+    def one(e):
         u = np.zeros((nb, 32, 32))
         u[:, iu[0], iu[1]] = _rng(cfg.cfg_id, _T_OFT, e).standard_normal((nb, len(iu[0]))) * sig
         s = u - np.transpose(u, (0, 2, 1))
         # (I - S)(I + S)^-1 == solve((I + S)^T, (I - S)^T)^T; both factors commute
         r = np.linalg.solve(eye + s, eye - s)
         out[e] = _to_bf16_bits(r.astype(np.float32))
+    _per_expert(one, cfg.E)
     return out
 
 
@@ -237,10 +258,13 @@ def gen_lm_head(cfg: LayerConfig):
     V = cfg.lm_vocab
     w = np.empty((V, cfg.H), np.uint16)
     step = 4096
-    for i in range(0, V, step):
+
+    def one(b):
+        i = b * step
         r = _rng(cfg.cfg_id, _T_WLM, i)
         n = min(step, V - i)
         w[i:i + n] = _to_bf16_bits(r.standard_normal((n, cfg.H), dtype=np.float32) / np.float32(np.sqrt(cfg.H)))
+    _per_expert(one, (V + step - 1) // step)
     tgt = _rng(cfg.cfg_id, _T_TGT).integers(0, V, cfg.T, dtype=np.int64).astype(np.int32)
     return w, tgt
 

@@ -5,7 +5,25 @@ import torch
 
 from precision_moe_expert_amd import binding, synth
 
-ROW_TOL = 2e-2  # max relative L2 error per output row (bf16 output)
+ROW_TOL = 2e-2  # the stated bound: max relative L2 error per output row (bf16 output)
+# Measured GPU-vs-oracle row errors (relative L2, every layer shape): the bf16
+# rounding of y_perm and out gives ~2.3e-3 on every row.  Formats with 16-bit
+# activations (INT4, NVFP4) stay below 2.8e-3 on every row.  Formats that
+# quantize the activations (FP8, FP8 pow2, MXFP4) add outlier rows: where h
+# sits within the two sides' fp32 rounding difference (~1e-6 relative) of an
+# E4M3 rounding boundary they pick neighbouring codes and that element of h
+# moves by one E4M3 step (6-12% of it).  About 1e-4 of the h elements do, so
+# ~1% of the rows exceed 5e-3 (1.0% Qwen3 shape, 1.3% with pow2 scales, whose
+# codes use half the E4M3 range); the largest measured is 1.8e-2.
+QUANTIZED_ACTS = {2, 3, 4}
+ROW_TOL_16BIT = 4e-3      # max row error, 16-bit-activation formats
+MEAN_TOL = 3.2e-3         # mean row error, every format
+OUTLIER_ROW = 5e-3        # rows above this count as code-flip outliers (quantized formats) ...
+OUTLIER_FRAC = 0.02       # ... at most this fraction of the rows (at least 2 rows; measured 1.0% FP8, 1.3% pow2)
+# max over elements of |y_gpu - y_ref| / RMS(y_ref row) on rows that are not
+# outliers: the bf16 rounding of y_perm and out alone reaches ~2e-2 on
+# 4-sigma elements
+ELEM_TOL = 5e-2
 
 
 def dev(a: np.ndarray, dtype=None):
@@ -57,3 +75,29 @@ def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     return np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+
+
+def check_rows(got: np.ndarray, ref: np.ndarray, fmt: int, label: str):
+    """Asserts the per-row relative L2 errors (max, mean, outlier count) and the
+    per-element error over the row RMS; prints the statistics."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = row_rel_err(got, ref)
+    rms = np.maximum(np.sqrt(np.mean(ref * ref, axis=1)), 1e-30)
+    elem = np.abs(got - ref).max(axis=1) / rms
+    quant = fmt in QUANTIZED_ACTS
+    out = rel > OUTLIER_ROW
+    n_out = int(out.sum())
+    elem_in = elem[~out] if (~out).any() else np.zeros(1)
+    print(f"{label}: {len(rel)} rows, row rel err max {rel.max():.3e} mean {rel.mean():.3e} "
+          f"p99 {np.percentile(rel, 99):.3e}, rows > {OUTLIER_ROW:.0e}: {n_out}; "
+          f"max elem err / row RMS {elem_in.max():.3e} (all rows {elem.max():.3e})")
+    assert np.isfinite(got).all(), label
+    assert rel.mean() <= MEAN_TOL, (label, rel.mean())
+    assert elem_in.max() <= ELEM_TOL, (label, elem_in.max())
+    if quant:
+        assert rel.max() <= ROW_TOL, (label, int(rel.argmax()), rel.max())
+        assert n_out <= max(2, int(OUTLIER_FRAC * len(rel))), (label, n_out)
+    else:
+        assert rel.max() <= ROW_TOL_16BIT, (label, int(rel.argmax()), rel.max())
+    return rel, elem

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = binding.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 def test_status_strings():

@@ -105,9 +105,9 @@ def test_backward_weight_copy_bitexact():
         from tests import refimpl
         f = refimpl.bf16_to_f32(s_bits).reshape(G, L // 8, 8)
         out = np.empty((G, L // 8, 8), np.float16)
-        for w, (a, b_, d) in enumerate(((0, 4, 1.0), (1, 5, 1 / 16), (2, 6, 1.0), (3, 7, 1 / 16))):
-            out[:, :, 2 * w] = (f[:, :, a] * d).astype(np.float16)
-            out[:, :, 2 * w + 1] = (f[:, :, b_] * d).astype(np.float16)
+        for w, (a, b_) in enumerate(((0, 4), (1, 5), (2, 6), (3, 7))):
+            out[:, :, 2 * w] = f[:, :, a].astype(np.float16)
+            out[:, :, 2 * w + 1] = f[:, :, b_].astype(np.float16)
         return out.view(np.uint8).reshape(-1)
 
     for e in range(E):
