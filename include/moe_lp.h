@@ -361,6 +361,27 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
                                const int32_t* targets, float* logprob, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ---- Allocation-free forward -------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same computation, arguments (minus ws / ws_bytes) and result
+ * as moe_expert_forward; the workspace is instead a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, reserved when
+ * the library is loaded on that GPU and held until the process ends.  Layers
+ * whose moe_workspace_bytes() exceeds it (e.g. more than a few thousand
+ * tokens at hidden 7168) return MOE_ERR_WORKSPACE_TOO_SMALL with nothing
+ * enqueued.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the first call on a device looks up that device's array
+ * address once.  The stream must belong to the current device.  Every call on
+ * one GPU uses the same array, whose contents persist between calls and are
+ * overwritten by each call: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_expert_forward_noalloc(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                      const moe_qweights* qweights, const moe_scales* scales,
+                                      const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                                      void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* moe_status_str(moe_status status);
 

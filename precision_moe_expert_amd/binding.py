@@ -23,7 +23,8 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rou
             "moe_lm_head_workspace_bytes", "moe_lm_head_logprob", "moe_materialized_workspace_bytes",
             "moe_expert_forward_materialized", "moe_backward_weights_bytes", "moe_prepare_backward_weights",
             "moe_backward_workspace_bytes", "moe_expert_backward", "moe_pack_weights_kblocked",
-            "moe_quantize_activations")
+            "moe_quantize_activations", "moe_expert_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("route", "permute", "act", "gemm1", "gemm2", "combine", "dequant")
 
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales), ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]
+        L.moe_expert_forward_noalloc.restype = ctypes.c_int
+        L.moe_expert_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayer), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.POINTER(MoeQWeights), ctypes.POINTER(MoeScales),
+                                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.moe_expert_forward_timed.restype = ctypes.c_int
         L.moe_expert_forward_timed.argtypes = L.moe_expert_forward.argtypes + [ctypes.POINTER(ctypes.c_float),
                                                                                 ctypes.POINTER(ctypes.c_int32)]
@@ -192,6 +197,20 @@ def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, 
     _check(lib().moe_expert_forward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
                                     _ptr(adapter), int(chunk_experts), _ptr(out), _ptr(ws), ws.numel(), _stream()),
            "moe_expert_forward")
+    return out
+
+
+def expert_forward_noalloc(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=None, chunk_experts: int = 1,
+                           out: torch.Tensor | None = None, g13=None, g2=None):
+    """moe_expert_forward_noalloc: as expert_forward, with the library's static
+    per-GPU scratch in place of a workspace (layers whose workspace fits it)."""
+    if out is None:
+        out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
+    qw = MoeQWeights(_ptr(w13), _ptr(w2))
+    sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
+    _check(lib().moe_expert_forward_noalloc(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
+                                            ctypes.byref(sc), _ptr(adapter), int(chunk_experts), _ptr(out),
+                                            _stream()), "moe_expert_forward_noalloc")
     return out
 
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -1028,3 +1029,48 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a file-scope device array, one
+// copy per GPU the library runs on, alive until the process ends.
+
+namespace {
+// In host code `scratch` names a host-side stand-in, not a device address:
+// its device address is taken once per device with hipGetSymbolAddress and
+// kept in g_scratch; only that pointer is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this device's scratch (set-up on the first call per device).
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_DEVICE;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_expert_forward_noalloc(const moe_layer* layer, const void* x_bf16, const float* logits,
+                                                 const moe_qweights* qweights, const moe_scales* scales,
+                                                 const void* adapter_bf16, int32_t chunk_experts, void* out_bf16,
+                                                 void* stream) {
+  Dims d;
+  moe_status st = check_layer(layer, &d);
+  if (st != MOE_OK) return st;
+  if (chunk_experts < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (layout(d).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(layer, x_bf16, logits, qweights, scales, adapter_bf16, chunk_experts, out_bf16, ws,
+                      (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
