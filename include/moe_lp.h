@@ -108,7 +108,7 @@ typedef struct {
   int32_t num_experts; /* E: 1..1024                                        */
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */
-  int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation (INT4 only for now; other formats: MOE_ERR_UNSUPPORTED) */
+  int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation (every weight format) */
   int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128 or 192 */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
   int32_t weight_layout;         /* a moe_wlayout value; other values: MOE_ERR_INVALID_ARGUMENT */
@@ -193,8 +193,9 @@ moe_status moe_route_permute(const moe_layer* layer, const float* logits, const 
  * (down), and finally the weighted combine
  *   out[t] = sum_j topk_w[t][j] * y[t][j]   (fp32 sum in ascending j, bf16 out).
  * x: [T][H] bf16; logits: [T][E] fp32; adapter: NULL or bf16
- * R[E or 1][H/32][32][32] (x' = x R_e, rows of R index the input dim);
- * out: [T][H] bf16.  The launch count is fixed by (E, chunk_experts); the
+ * R[E or 1][H/32][32][32] (x' = x R_e, rows of R index the input dim,
+ * rotated per permuted row in fp32 and then given to the weight format's
+ * GEMM1 input quantizer, as x is without an adapter); out: [T][H] bf16.  The launch count is fixed by (E, chunk_experts); the
  * result does not depend on chunk_experts.  ws: >= moe_workspace_bytes(). */
 moe_status moe_expert_forward(const moe_layer* layer, const void* x_bf16, const float* logits,
                               const moe_qweights* qweights, const moe_scales* scales,
@@ -271,7 +272,7 @@ moe_status moe_expert_forward_materialized(const moe_layer* layer, const void* x
  * rows x 128 codes as MOE_WL_KBLOCKED describes, plus scales (INT4, MXFP4,
  * NVFP4: one fp16 per group scale; FP8: the fp32 block scales transposed); 0 if the
  * layer is not supported by the backward (I multiple of 256; FP8 H and 2I at
- * most 8192; per-expert adapter). */
+ * most 8192). */
 size_t moe_backward_weights_bytes(const moe_layer* layer);
 
 /* Writes the transposed copy of (qweights, scales) into bwd_weights (device,
@@ -288,15 +289,17 @@ moe_status moe_prepare_backward_weights(const moe_layer* layer, const moe_qweigh
 
 /* Workspace bytes of moe_expert_backward (routing, recomputed gate/up
  * pre-activations fp32 [R][2I], their gradients fp16 [R][2I], dx' fp32
- * [R][H] (twice with an adapter), the fp16 copy of d_out). */
+ * [R][H] (twice with an adapter), the fp16 copy of d_out, and for a shared
+ * adapter the per-expert gradient partials fp32 [E][H/32][32][32]). */
 size_t moe_backward_workspace_bytes(const moe_layer* layer, int32_t chunk_experts);
 
 /* Backward of moe_expert_forward for given d_out = dL/dout [T][H] bf16:
  *   d_x      [T][H] bf16    dL/dx
  *   d_logits [T][E] fp32    dL/dlogits: w_tj (g_tj - sum_i w_ti g_ti) for the
  *                           selected experts, g_tj = <d_out_t, y_tj>; 0 elsewhere
- *   d_adapter fp32, shaped like the adapter (per-expert R only), dL/dR; NULL
- *                           exactly when adapter is NULL
+ *   d_adapter fp32, shaped like the adapter, dL/dR (a shared R, stride 0,
+ *                           gets the sum over all experts, added in ascending
+ *                           active-expert order); NULL exactly when adapter is NULL
  * No gradient is formed for W13 or W2.  The forward is recomputed per chunk
  * (routing, gate/up pre-activations); per permuted row (t, j) of expert e:
  * u = d_out_t W2, dh = w_tj u, da = dh b silu'(a), db = dh silu(a),

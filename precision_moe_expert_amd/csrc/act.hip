@@ -157,24 +157,39 @@ __device__ __forceinline__ void oft_wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Output formats of the OFT rotation: the GEMM1 input of each weight format.
+enum { OFT_F16_I4 = 0,  // fp16 in the INT4-path layout (groups of 8 as 0,4,1,5,2,6,3,7)
+       OFT_BF16 = 1,    // bf16, natural order (the BF16 GEMMs of the materialized scheme)
+       OFT_F16 = 2,     // fp16, natural order (NVFP4 weights)
+       OFT_FP8 = 3,     // E4M3 codes + fp32 scale per [1,128]: s = amax/448, RNE(v/s)
+       OFT_FP8_POW2 = 4,// E4M3 codes + power-of-two fp32 scale per [1,128]
+       OFT_MXFP8 = 5 }; // E4M3 codes + E8M0 scale per 32 (MXFP4 weights)
+
 // OFT rotation x' = x R_e (R_e block-diagonal, 32x32 bf16 blocks; row i of a
 // block indexes the input dim) for every permuted row, on bf16 MFMA with fp32
-// accumulation, written as fp16 in the INT4-path layout (BF16OUT: bf16 in
-// natural order, the BF16 GEMMs' input).  Work item = 16 rows of one expert
-// (the 16-row tile list) times 16 consecutive diagonal blocks, 4 per wave:
-// a wave loads its 4 blocks of R_e (8 KB) and x values at once, stages the
-// blocks in its own LDS slice and runs 8 MFMAs, so each item costs one
-// memory round trip.  The active experts' tile starts are kept in LDS for
+// accumulation, written in the GEMM1 input format OUT of the weight format.
+// Work item = 16 rows of one expert (the 16-row tile list) times 16
+// consecutive diagonal blocks, 4 per wave: a wave loads its 4 blocks of R_e
+// (8 KB) and x values at once, stages the blocks in its own LDS slice and
+// runs 8 MFMAs, so each item costs one memory round trip.  A wave's 4 blocks
+// are 128 columns, i.e. exactly one FP8 [1,128] block per row (H is a
+// multiple of 256), and each diagonal block is one MXFP8 32-block, so the
+// quantized formats take their block maxima from the wave's own registers
+// (16-lane row reductions), stage the codes in the wave's LDS slice and
+// write 16-byte pieces.  The active experts' tile starts are kept in LDS for
 // the item -> expert search.
-template <bool BF16OUT>
+template <int OUT>
 __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
-                                                 int64_t r_stride, int H, int k, const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ sorted_rows,
-                                                 const int32_t* __restrict__ active,
-                                                 const int32_t* __restrict__ num_active,
-                                                 const int32_t* __restrict__ tile16, uint16_t* __restrict__ out) {
+                                             int64_t r_stride, int H, int k, const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ sorted_rows,
+                                             const int32_t* __restrict__ active,
+                                             const int32_t* __restrict__ num_active,
+                                             const int32_t* __restrict__ tile16, void* __restrict__ out,
+                                             void* __restrict__ out_scale, int scale_stride) {
   constexpr int BPW = 4;  // diagonal blocks per wave and item
+  constexpr bool QUANT = OUT == OFT_FP8 || OUT == OFT_FP8_POW2 || OUT == OFT_MXFP8;
   __shared__ __align__(16) uint16_t rs[4][BPW][32 * 32];
+  __shared__ __align__(16) uint8_t qs[QUANT ? 4 : 1][16 * 128];  // a wave's 16 rows x 128 codes
   __shared__ int32_t s_t16[MAX_EXPERTS + 1];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int ln = lane & 15, lg = lane >> 4;
@@ -220,34 +235,107 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
         dst[lane * 2 + 1] = rv[j][1];
       }
     oft_wave_lds_sync();
+    // acc[j][half][i]: row lg*4 + i, column (b0 + j)*32 + half*16 + ln
+    f32x4 acc[BPW][2];
 #pragma unroll
     for (int j = 0; j < BPW; ++j)
-      if (j < nbw) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xv[j]);
-        const int b = b0 + j;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < 2; ++half) {
+        acc[j][half] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        if (j < nbw) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, xv[j]);
           const uint16_t* rc = rs[wave][j] + lg * 8 * 32 + half * 16 + ln;
           u32x4 bw;
           bw.x = (uint32_t)rc[0] | ((uint32_t)rc[32] << 16);
           bw.y = (uint32_t)rc[64] | ((uint32_t)rc[96] << 16);
           bw.z = (uint32_t)rc[128] | ((uint32_t)rc[160] << 16);
           bw.w = (uint32_t)rc[192] | ((uint32_t)rc[224] << 16);
-          const bf16x8 bb = __builtin_bit_cast(bf16x8, bw);
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-          acc = mfma_bf16_16x16x32(a, bb, acc);
-          const int col = BF16OUT ? b * 32 + half * 16 + ln : i4act_pos(b * 32 + half * 16 + ln);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = lg * 4 + i;
-            if (m < nrows) {
-              const _Float16 hv = (_Float16)acc[i];
-              out[(int64_t)(r0 + m) * H + col] =
-                  BF16OUT ? (uint16_t)f32_to_bf16_bits(acc[i]) : __builtin_bit_cast(uint16_t, hv);
-            }
-          }
+          acc[j][half] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, bw), acc[j][half]);
         }
       }
+    if constexpr (!QUANT) {
+      uint16_t* o = static_cast<uint16_t*>(out);
+#pragma unroll
+      for (int j = 0; j < BPW; ++j)
+        if (j < nbw)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int c = (b0 + j) * 32 + half * 16 + ln;
+            const int col = OUT == OFT_F16_I4 ? i4act_pos(c) : c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = lg * 4 + i;
+              if (m < nrows) {
+                const _Float16 hv = (_Float16)acc[j][half][i];
+                o[(int64_t)(r0 + m) * H + col] =
+                    OUT == OFT_BF16 ? (uint16_t)f32_to_bf16_bits(acc[j][half][i]) : __builtin_bit_cast(uint16_t, hv);
+              }
+            }
+          }
+    } else {
+      // block maxima per row (the row's 16 lanes share lg), codes into the
+      // wave's staging slice qs[wave][row][col - 128 * (b0 / 4)]
+      uint8_t* q = qs[wave];
+      if constexpr (OUT == OFT_MXFP8) {
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float am = row16_max_nonneg(fmaxf(fabsf(acc[j][0][i]), fabsf(acc[j][1][i])));
+            int X = 0;
+            if (am > 0.0f) {
+              X = floor_log2_pos(am) - 8;
+              X = X < -127 ? -127 : (X > 127 ? 127 : X);
+            }
+            const float mul = exp2_int(-X);
+            const uint32_t c2 = cvt_e4m3x2(acc[j][0][i] * mul, acc[j][1][i] * mul);
+            const int m = lg * 4 + i;
+            q[m * 128 + j * 32 + ln] = (uint8_t)(c2 & 0xFF);
+            q[m * 128 + j * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+            if (ln == 0 && m < nrows)
+              static_cast<uint8_t*>(out_scale)[(int64_t)(r0 + m) * scale_stride + b0 + j] = (uint8_t)(X + 127);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float am = 0.0f;
+#pragma unroll
+          for (int j = 0; j < BPW; ++j) am = fmaxf(am, fmaxf(fabsf(acc[j][0][i]), fabsf(acc[j][1][i])));
+          am = row16_max_nonneg(am);
+          const int m = lg * 4 + i;
+          float sc;
+          if constexpr (OUT == OFT_FP8_POW2) {
+            sc = am == 0.0f ? 1.0f : pow2_at_least(am / 448.0f);
+            const float inv = pow2_reciprocal(sc);
+#pragma unroll
+            for (int j = 0; j < BPW; ++j) {
+              const uint32_t c2 = cvt_e4m3x2(acc[j][0][i] * inv, acc[j][1][i] * inv);
+              q[m * 128 + j * 32 + ln] = (uint8_t)(c2 & 0xFF);
+              q[m * 128 + j * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+            }
+          } else {
+            sc = am == 0.0f ? 1.0f : am / 448.0f;
+#pragma unroll
+            for (int j = 0; j < BPW; ++j) {
+              const uint32_t c2 = cvt_e4m3x2(acc[j][0][i] / sc, acc[j][1][i] / sc);
+              q[m * 128 + j * 32 + ln] = (uint8_t)(c2 & 0xFF);
+              q[m * 128 + j * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
+            }
+          }
+          if (ln == 0 && m < nrows)
+            static_cast<float*>(out_scale)[(int64_t)(r0 + m) * (scale_stride / 4) + b0 / 4] = sc;
+        }
+      }
+      oft_wave_lds_sync();
+      // 16 rows x 128 codes: lane l writes 32 bytes of row l/4
+      const int m = lane >> 2, part = lane & 3;
+      if (m < nrows) {
+        const u32x4* sp = reinterpret_cast<const u32x4*>(q + m * 128 + part * 32);
+        u32x4* dp = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(out) + (int64_t)(r0 + m) * H + b0 * 32 + part * 32);
+        dp[0] = sp[0];
+        dp[1] = sp[1];
+      }
+    }
     oft_wave_lds_sync();  // this item's LDS reads are issued before the next item's writes
   }
 }
@@ -270,19 +358,39 @@ void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int 
 void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s) {
   hipLaunchKernelGGL(k_act_mxfp8, dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, q, e8, e8_stride);
 }
+void launch_oft(int out_fmt, const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
+                const int32_t* tile16, void* out, void* out_scale, int scale_stride, hipStream_t s) {
+  switch (out_fmt) {
+#define MOE_OFT_CASE(F)                                                                                              \
+    case F:                                                                                                          \
+      hipLaunchKernelGGL(k_oft<F>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows, \
+                         active, num_active, tile16, out, out_scale, scale_stride);                                  \
+      break;
+    MOE_OFT_CASE(OFT_F16_I4)
+    MOE_OFT_CASE(OFT_BF16)
+    MOE_OFT_CASE(OFT_F16)
+    MOE_OFT_CASE(OFT_FP8)
+    MOE_OFT_CASE(OFT_FP8_POW2)
+    MOE_OFT_CASE(OFT_MXFP8)
+#undef MOE_OFT_CASE
+    default: break;
+  }
+}
+
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                     const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s) {
   (void)E;
-  hipLaunchKernelGGL(k_oft<false>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows,
-                     active, num_active, tile16, out);
+  launch_oft(OFT_F16_I4, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, out, nullptr,
+             0, s);
 }
 
 void launch_oft_bf16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                      const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                      const int32_t* num_active, const int32_t* tile16, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_oft<true>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows,
-                     active, num_active, tile16, out);
+  launch_oft(OFT_BF16, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, out, nullptr, 0,
+             s);
 }
 
 }  // namespace moe

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void k_oft_bwd(const uint16_t* __restrict__ x,
                                                  const int32_t* __restrict__ sorted_rows,
                                                  const int32_t* __restrict__ active,
                                                  const int32_t* __restrict__ num_active, float* __restrict__ dx,
-                                                 float* __restrict__ dR) {
+                                                 float* __restrict__ dR, int64_t dr_stride, int dr_by_active) {
   __shared__ float sd[4][16][33], sx[4][16][33];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int ln = lane & 15, lg = lane >> 4;
@@ -116,7 +116,9 @@ __global__ __launch_bounds__(256) void k_oft_bwd(const uint16_t* __restrict__ x,
       acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
   }
-  float* dRb = dR + (int64_t)e * r_stride + (int64_t)b * 1024;
+  // per expert (its own R_e), or per active index into partials that
+  // k_sum_active adds up when all experts share one R
+  float* dRb = dR + (int64_t)(dr_by_active ? a : e) * dr_stride + (int64_t)b * 1024;
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
@@ -185,11 +187,29 @@ void launch_zero_f32(float* p, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p, n);
 }
 
+// out[i] = sum over a = 0 .. num_active-1 of part[a][i], in ascending a
+// (the shared adapter's gradient from the per-expert partials).
+__global__ __launch_bounds__(256) void k_sum_active(const float* __restrict__ part, const int32_t* __restrict__ num_active,
+                                                    int64_t n, float* __restrict__ out) {
+  const int na = *num_active;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float acc = 0.0f;
+    for (int a = 0; a < na; ++a) acc += part[(int64_t)a * n + i];
+    out[i] = acc;
+  }
+}
+
 void launch_oft_bwd(const uint16_t* x, const uint16_t* R, int64_t r_stride, const float* dxt, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
-                    int E, float* dx, float* dR, hipStream_t s) {
+                    int E, float* dx, float* dR, float* dR_part, hipStream_t s) {
+  const bool shared = r_stride == 0;
   hipLaunchKernelGGL(k_oft_bwd, dim3((H / 32 + 3) / 4, E), dim3(256), 0, s, x, R, r_stride, dxt, H, k, offsets,
-                     sorted_rows, active, num_active, dx, dR);
+                     sorted_rows, active, num_active, dx, shared ? dR_part : dR,
+                     shared ? (int64_t)H * 32 : r_stride, shared ? 1 : 0);
+  if (shared) {
+    const int64_t n = (int64_t)H * 32;
+    hipLaunchKernelGGL(k_sum_active, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dR_part, num_active, n, dR);
+  }
 }
 
 void launch_unpermute_sum(const float* src, const int32_t* row_of, int T, int k, int H, uint16_t* out,

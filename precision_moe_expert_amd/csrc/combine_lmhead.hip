@@ -70,48 +70,55 @@ __global__ __launch_bounds__(64) void k_inv_rms(const uint16_t* __restrict__ h, 
 // Partial logits part[ks][t][v] = sum over the ks-th K slice of h[t][k] W[v][k]
 // (bf16 MFMA, fp32 accumulation).  The head is a skinny GEMM (<= 64 tokens
 // against V x H weights) bound by streaming W once from HBM, so the kernel
-// is built around that stream: a workgroup owns 128 vocabulary rows (32 per
-// wave) and one K slice (KS = 2 slices give enough workgroups to fill the
-// chip), and moves 128-K steps of its W rows (256 B of each row, 32 KB) and
-// of the token rows (16 KB, shared by the 4 waves) into an LDS ring of
-// LM_S stages by global_load_lds DMA.  Inside a stage each 256-byte row is
-// kept as 16 parts of 16 B with part p at slot p ^ (row & 15), so the
-// 16 lanes that read one MFMA fragment hit 16 different slots.
+// is built around keeping that stream deep: a workgroup owns 128 vocabulary
+// rows (32 per wave) and one K slice (KS = 2 slices), and moves 64-K steps of
+// its W rows (128 B of each row, 16 KB) and of the token rows (8 KB, shared
+// by the 4 waves) into an LDS ring of LM_S stages by global_load_lds DMA;
+// 72 KB of LDS per workgroup lets two workgroups share a CU, so every
+// workgroup of the grid is resident at once.  Inside a stage each 128-byte
+// row is kept as 8 parts of 16 B with part p at slot p ^ ((row >> 1) & 7):
+// the 16 lanes reading one MFMA fragment then cover 16 distinct 16-byte
+// bank groups.
 constexpr int LM_S = 3;            // stages in flight
 constexpr int LM_VB = 128;         // vocabulary rows per workgroup
-constexpr int LM_STAGE = (LM_VB + 64) * 256;
-constexpr int LM_NPER = 8 + 4;     // DMA instructions per wave per stage (W: 32 rows, h: 16 rows)
+constexpr int LM_KS = 64;          // K per stage
+constexpr int LM_RB = LM_KS * 2;   // bytes of a row per stage
+constexpr int LM_STAGE = (LM_VB + 64) * LM_RB;
+constexpr int LM_NPER = 4 + 2;     // DMA instructions per wave per stage (W: 32 rows, h: 16 rows)
 
-__global__ __launch_bounds__(256, 1) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+MOE_DEV int lm_slot(int row, int part) { return part ^ ((row >> 1) & 7); }
+
+__global__ __launch_bounds__(256, 2) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                     int T, int H, int V, int ks_len, float* __restrict__ part) {
   __shared__ __align__(16) uint8_t smem[LM_S * LM_STAGE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int vb = blockIdx.x, ks = blockIdx.y, t0 = blockIdx.z * 64;
-  const int k0 = ks * ks_len, KT = ks_len / 128;
+  const int k0 = ks * ks_len, KT = ks_len / LM_KS;
   const uint32_t smem0 = lds_u32(smem);
-  // DMA sources: lane l of instruction j writes LDS slot l%16 of row 4j + l/16
-  // of the wave's rows; that slot holds part (l%16) ^ (row & 15).
-  const char* wsrc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 32 + j * 4 + lg;                      // row within the W block
-    const int v = min(vb * LM_VB + r, V - 1);
-    wsrc[j] = reinterpret_cast<const char*>(W) + ((int64_t)v * H + k0 + ((ln ^ (r & 15)) * 8)) * 2;
-  }
-  const char* hsrc[4];
+  // DMA sources: lane l of instruction j writes LDS slot l%8 of row 8j + l/8
+  // of the wave's rows; that slot holds the part whose slot is l%8.
+  const int rj = lane >> 3, sl = lane & 7;
+  const char* wsrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = wave * 16 + j * 4 + lg;                      // token row within the block
+    const int r = wave * 32 + j * 8 + rj;                      // row within the W block
+    const int v = min(vb * LM_VB + r, V - 1);
+    wsrc[j] = reinterpret_cast<const char*>(W) + ((int64_t)v * H + k0 + lm_slot(r, sl) * 8) * 2;
+  }
+  const char* hsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * 16 + j * 8 + rj;                      // token row within the block
     const int t = min(t0 + r, T - 1);
-    hsrc[j] = reinterpret_cast<const char*>(h) + ((int64_t)t * H + k0 + ((ln ^ (r & 15)) * 8)) * 2;
+    hsrc[j] = reinterpret_cast<const char*>(h) + ((int64_t)t * H + k0 + lm_slot(r, sl) * 8) * 2;
   }
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * LM_STAGE;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma_b128(wsrc[j] + kt * 256, sb + (wave * 32 + j * 4) * 256);
+    for (int j = 0; j < 4; ++j) dma_b128(wsrc[j] + kt * LM_RB, sb + (wave * 32 + j * 8) * LM_RB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma_b128(hsrc[j] + kt * 256, sb + LM_VB * 256 + (wave * 16 + j * 4) * 256);
+    for (int j = 0; j < 2; ++j) dma_b128(hsrc[j] + kt * LM_RB, sb + (LM_VB + wave * 16 + j * 8) * LM_RB);
   };
   f32x4 acc[4][2];
 #pragma unroll
@@ -127,18 +134,18 @@ __global__ __launch_bounds__(256, 1) void k_lm_gemm(const uint16_t* __restrict__
     if (kt + LM_S - 1 < KT) issue(kt + LM_S - 1, (kt + LM_S - 1) % LM_S);
     const uint8_t* st = smem + (kt % LM_S) * LM_STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < LM_KS / 32; ++s) {
       const int part_ = s * 4 + lg;
       bf16x8 bw[2], ah[4];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int r = wave * 32 + c * 16 + ln;
-        bw[c] = *reinterpret_cast<const bf16x8*>(st + r * 256 + ((part_ ^ (r & 15)) << 4));
+        bw[c] = *reinterpret_cast<const bf16x8*>(st + r * LM_RB + (lm_slot(r, part_) << 4));
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = m * 16 + ln;
-        ah[m] = *reinterpret_cast<const bf16x8*>(st + LM_VB * 256 + r * 256 + ((part_ ^ (r & 15)) << 4));
+        ah[m] = *reinterpret_cast<const bf16x8*>(st + (LM_VB + r) * LM_RB + (lm_slot(r, part_) << 4));
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -235,7 +242,7 @@ void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, in
   hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, y, w, row_of, k, H, out);
 }
 
-int lm_head_slices(int H) { return (H / 128) % 2 == 0 ? 2 : 1; }
+int lm_head_slices(int H) { return H % 128 == 0 ? 2 : 1; }
 int lm_head_chunks(int V) { return (V + LM_VC - 1) / LM_VC; }
 
 void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,

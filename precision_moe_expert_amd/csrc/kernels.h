@@ -80,6 +80,13 @@ inline int scale_row_bytes(int K) { return ((K / 128) * 4 + 15) / 16 * 16; }
 void launch_act_fp8(const uint16_t* x, int T, int H, uint8_t* q, float* sc, int sc_stride, bool pow2,
                     hipStream_t s);
 void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, int e8_stride, hipStream_t s);
+// OFT rotation of every permuted row into a GEMM1 input format: out_fmt 0 fp16
+// in the INT4-path layout, 1 bf16, 2 fp16 (NVFP4), 3 FP8 [1,128] (fp32 scales),
+// 4 FP8 [1,128] with power-of-two scales, 5 MXFP8 (E8M0 bytes); out [R][H],
+// out_scale rows of scale_stride bytes (quantized formats).
+void launch_oft(int out_fmt, const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
+                const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
+                const int32_t* tile16, void* out, void* out_scale, int scale_stride, hipStream_t s);
 // OFT rotation of every permuted row into the INT4-path activation layout.
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
@@ -113,9 +120,11 @@ void launch_repack_bwd(int fmt, const uint8_t* w, const void* s, int E, int N, i
 // g2.chunk's dx' items, both reading the transposed copy; fmt = kernel family.
 void launch_gemm_bwd_pair(int fmt, const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                           hipStream_t s);
+// r_stride = 0 (one R shared by all experts): per-active-expert partials go to
+// dR_part [E][H/32][32][32] and are summed into dR in ascending active order.
 void launch_oft_bwd(const uint16_t* x, const uint16_t* R, int64_t r_stride, const float* dxt, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
-                    int E, float* dx, float* dR, hipStream_t s);
+                    int E, float* dx, float* dR, float* dR_part, hipStream_t s);
 void launch_unpermute_sum(const float* src, const int32_t* row_of, int T, int k, int H, uint16_t* out, hipStream_t s);
 void launch_router_grad(const int32_t* ids, const float* w, const int32_t* row_of, const float* gpart, int nparts,
                         int T, int k, int E, float* dlogits, hipStream_t s);

@@ -27,6 +27,7 @@ struct Dims {
   int T, H, I, E, k, fmt;  // fmt: the kernel family (the pow2 FP8 variant runs the FP8 kernels)
   bool pow2;               // FP8 with power-of-two scales
   bool oft;
+  bool oft_shared;         // one R for all experts (adapter_expert_stride = 0)
   bool kblocked;           // weights in 16 x 128 tiles (MOE_WL_KBLOCKED)
   int64_t R;
   int nblk;
@@ -50,7 +51,6 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if (L->hidden % 256 != 0 || L->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (L->num_experts > MAX_EXPERTS || L->top_k > MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
-  if (L->oft_block != 0 && L->wformat != MOE_W_INT4_G32_BF16) return MOE_ERR_UNSUPPORTED;
   if (L->weight_layout != MOE_WL_ROWS && L->weight_layout != MOE_WL_KBLOCKED) return MOE_ERR_INVALID_ARGUMENT;
   if (L->tile_rows != 0 && L->tile_rows != 16 && L->tile_rows != 32 && L->tile_rows != 48 && L->tile_rows != 64 &&
       L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 192)
@@ -67,6 +67,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   d->pow2 = L->wformat == MOE_W_FP8_E4M3_B128_POW2;
   if (d->pow2) d->fmt = MOE_W_FP8_E4M3_B128;  // same layouts and kernels, power-of-two scale path
   d->oft = L->oft_block != 0;
+  d->oft_shared = d->oft && L->adapter_expert_stride == 0;
   d->R = (int64_t)d->T * d->k;
   d->nblk = (int)((d->R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK);
   d->tile_rows = L->tile_rows;
@@ -77,6 +78,14 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
 // Per-XCD work-queue counters of the grouped-GEMM pair launches: 8 per launch, at most
 // num_experts + 1 launches (chunk_experts >= 1).
 int queue_ints(const Dims& d) { return 8 * (d.E + 1); }
+
+// The OFT rotation's output format for the layer's GEMM1 input (launch_oft).
+int oft_out_format(const Dims& d) {
+  if (d.fmt == MOE_W_INT4_G32_BF16) return 0;
+  if (d.fmt == MOE_W_NVFP4) return 2;
+  if (d.fmt == MOE_W_FP8_E4M3_B128) return d.pow2 ? 4 : 3;
+  return 5;
+}
 
 WsLayout layout(const Dims& d) {
   WsLayout w{};
@@ -363,12 +372,11 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   // 3. the GEMM1 input: per token, or per permuted row when the adapter rotates it
   {
   Scope sc_(tm, MOE_STAGE_ACT);
-  if (d.fmt == MOE_W_INT4_G32_BF16) {
-    if (d.oft)
-      launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
-                     sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
-    else
-      launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
+  if (d.oft) {
+    launch_oft(oft_out_format(d), x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H,
+               d.k, offsets, sorted_rows, active, num_active, tile_16, act, act_scale, scale_row_bytes(d.H), s);
+  } else if (d.fmt == MOE_W_INT4_G32_BF16) {
+    launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_NVFP4) {
     launch_act_f16_natural(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_FP8_E4M3_B128) {
@@ -646,7 +654,6 @@ moe_status check_backward(const moe_layer* L, Dims* d) {
   if (d->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // FP8 backward keeps one K run of block scales per item (at most 64 K blocks)
   if (d->fmt == MOE_W_FP8_E4M3_B128 && (d->H > 64 * 128 || 2 * d->I > 64 * 128)) return MOE_ERR_UNSUPPORTED;
-  if (d->oft && L->adapter_expert_stride == 0) return MOE_ERR_UNSUPPORTED;  // one shared R
   return MOE_OK;
 }
 
@@ -662,7 +669,7 @@ int bwd_bm(const Dims& d) {
 struct BwdLayout {
   size_t ids, wts, offsets, sorted_rows, row_of, active, num_active, tile_a, tile_16, tiles, queue, hist;
   size_t tile_a_r, tiles_r;  // tiles of the recompute's height
-  size_t act, act_scale, h, h_scale, gact, ab, dab, gpart, dxt, dxr;
+  size_t act, act_scale, h, h_scale, gact, ab, dab, gpart, dxt, dxr, drp;
   size_t total;
 };
 
@@ -697,9 +704,10 @@ BwdLayout bwd_layout(const Dims& d) {
     w.h = take(0);
     w.h_scale = take(0);
   } else {
-    // the forward's GEMM1 input and its quantized h, as the recompute writes them
-    w.act = take(T * H);
-    w.act_scale = take(T * scale_row_bytes((int)H));
+    // the forward's GEMM1 input (per token, or per permuted row with an
+    // adapter) and its quantized h, as the recompute writes them
+    w.act = take((d.oft ? R : T) * H);
+    w.act_scale = take((d.oft ? R : T) * scale_row_bytes((int)H));
     w.h = take(R * I);
     w.h_scale = take(R * scale_row_bytes((int)I));
   }
@@ -709,6 +717,8 @@ BwdLayout bwd_layout(const Dims& d) {
   w.gpart = take(R * (I / 256) * 4);
   w.dxt = take(R * H * 4);
   w.dxr = take(d.oft ? R * H * 4 : 0);
+  // one shared R: the adapter gradient's per-active-expert partials
+  w.drp = take(d.oft && d.oft_shared ? E * H * 32 * 4 : 0);
   w.total = o;
   return w;
 }
@@ -815,7 +825,10 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   {
   Scope sc_(tm, MOE_STAGE_ACT);
   // the forward's GEMM1 input
-  if (d.fmt == MOE_W_FP8_E4M3_B128)
+  if (d.oft)
+    launch_oft(oft_out_format(d), x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H,
+               d.k, offsets, sorted_rows, active, num_active, tile_16, act, act_scale, scale_row_bytes(d.H), s);
+  else if (d.fmt == MOE_W_FP8_E4M3_B128)
     launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H),
                    d.pow2, s);
   else if (d.fmt == MOE_W_MXFP4)
@@ -823,9 +836,6 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
                      s);
   else if (d.fmt == MOE_W_NVFP4)
     launch_act_f16_natural(x, d.T, d.H, static_cast<uint16_t*>(act), s);
-  else if (d.oft)
-    launch_oft_f16(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H, d.k, offsets,
-                   sorted_rows, active, num_active, tile_16, d.E, static_cast<uint16_t*>(act), s);
   else
     launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   launch_act_f16(static_cast<const uint16_t*>(d_out_bf16), d.T, d.H, gact, s);
@@ -932,7 +942,8 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   const float* dx_rows = dxt;
   if (d.oft) {
     launch_oft_bwd(x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, dxt, d.H, d.k,
-                   offsets, sorted_rows, active, num_active, d.E, dxr, d_adapter, s);
+                   offsets, sorted_rows, active, num_active, d.E, dxr, d_adapter,
+                   reinterpret_cast<float*>(base + wl.drp), s);
     dx_rows = dxr;
   }
   launch_unpermute_sum(dx_rows, row_of, d.T, d.k, d.H, static_cast<uint16_t*>(d_x_bf16), s);

@@ -92,8 +92,7 @@ def test_forward_rejects_bad_layer(case, expect):
 
 def test_nvfp4_host_checks():
     """NVFP4: forward workspace as for INT4 (16-bit activations); the
-    second-level scale pointers are required; the adapter is not supported
-    for this format.  Backward: the transposed copy holds one fp16 per E4M3
+    second-level scale pointers are required, with or without an adapter.  Backward: the transposed copy holds one fp16 per E4M3
     scale (16 weights); its workspace is INT4's."""
     Ln = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4)
     Li = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
@@ -109,7 +108,7 @@ def test_nvfp4_host_checks():
     assert fwd(FAKE, FAKE + 2) == binding.MOE_ERR_INVALID_ARGUMENT           # misaligned fp32
     assert fwd(FAKE, FAKE + 4) == binding.MOE_ERR_WORKSPACE_TOO_SMALL        # valid; the workspace fails
     Lo = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_NVFP4, oft=True)
-    assert _fwd(Lo, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED
+    assert _fwd(Lo, adapter=FAKE) == binding.MOE_ERR_INVALID_ARGUMENT     # adapter accepted; no g13 / g2
     assert binding.materialized_workspace_bytes(Ln, 4) == binding.materialized_workspace_bytes(Li, 4) > 0
     assert _mat(Ln) == binding.MOE_ERR_INVALID_ARGUMENT                     # no second-level scales
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
@@ -135,7 +134,8 @@ def test_forward_rejects_bad_pointers_and_workspace():
     Lo = binding.make_layer(64, 256, 512, 8, 2, 1, oft=True)
     assert _fwd(Lo) == binding.MOE_ERR_INVALID_ARGUMENT                    # oft_block without adapter
     Lf = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_FP8, oft=True)
-    assert _fwd(Lf, adapter=FAKE) == binding.MOE_ERR_UNSUPPORTED           # OFT only on the INT4 path
+    assert _fwd(Lf, adapter=FAKE + 2) == binding.MOE_ERR_INVALID_ARGUMENT  # misaligned adapter
+    assert _fwd(Lf, adapter=FAKE, ws_bytes=1000) == binding.MOE_ERR_WORKSPACE_TOO_SMALL  # OFT on FP8 accepted
     L0 = binding.make_layer(0, 256, 512, 8, 2, 1)
     assert _fwd(L0, x=None, lg=None, w=None, out=None, ws=None) == binding.MOE_OK  # T = 0: no-op
 

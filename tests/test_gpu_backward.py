@@ -121,7 +121,8 @@ def test_backward_weight_copy_bitexact():
         assert np.array_equal(raw[os2 + e * n2: os2 + (e + 1) * n2], f16_pairs(li.s2[e], I // 32, H))
 
 
-@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False), (5, False)])
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (2, True), (3, False), (3, True),
+                                     (4, False), (4, True), (5, False), (5, True)])
 def test_backward_small_vs_oracle(fmt, oft):
     li = synth.make_inputs(small(oft=oft, fmt=fmt))
     dout = d_out_of(li.cfg)
@@ -269,3 +270,30 @@ def test_backward_kimi_fullsize_sampled():
     torch.cuda.synchronize()
     toks = np.sort(np.random.default_rng(3).choice(li.cfg.T, size=12, replace=False)).astype(np.int32)
     check(li, dout, got, tokens=toks, check_adapter=False)
+
+
+@pytest.mark.parametrize("fmt", [1, 3, 5])
+def test_backward_shared_adapter(fmt):
+    """One R shared by all experts: dL/dR sums every expert's x^T dx' blocks
+    (per-expert partials added in ascending active order on the GPU)."""
+    from tests import refimpl
+    cfg = small(T=53, H=256, I=256, E=7, k=3, oft=True, fmt=fmt, cfg_id=300 + fmt)
+    li = synth.make_inputs(cfg)
+    shared = np.ascontiguousarray(li.oft[1])
+    d = gu.DevInputs(li)
+    d.layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, fmt, oft=True, adapter_expert_stride=0)
+    d.oft = gu.dev(shared, "bf16")
+    bw = binding.prepare_backward_weights(d.layer, d.w13, d.w2, d.s13, d.s2)
+    dout_bits = d_out_of(cfg, 9)
+    got = binding.expert_backward(d.layer, d.x, d.logits, d.w13, d.w2, d.s13, d.s2, bw, gu.dev(dout_bits, "bf16"),
+                                  adapter=d.oft, chunk_experts=cfg.chunk, g13=d.g13, g2=d.g2)
+    dout = refimpl.bf16_to_f32(dout_bits).reshape(cfg.T, cfg.H)
+    rdx, rdl, rdR = oracle.backward(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, fmt, li.x, li.logits, li.w13, li.w2, li.s13,
+                                    li.s2, dout, oft=shared, chunk_experts=cfg.chunk, adapter_expert_stride=0,
+                                    g13=li.g13, g2=li.g2)
+    ex = gu.row_rel_err(gu.bf16_to_np(got[0]), rdx)
+    dR = got[2].cpu().numpy().astype(np.float64).reshape(rdR.shape)
+    eR = np.linalg.norm(dR - rdR) / np.linalg.norm(rdR)
+    print(f"shared adapter fmt {fmt}: d_x max row rel err {ex.max():.3e}; d_adapter rel err {eR:.3e}")
+    assert ex.max() <= gu.ROW_TOL
+    assert eR <= gu.ROW_TOL

@@ -237,3 +237,31 @@ def test_nvfp4_full_e4m3_scale_range():
     out = gu.bf16_to_np(d.forward())
     ref = oracle.forward_inputs(li)
     gu.check_rows(out, ref, 5, "nvfp4 all E4M3 scale codes")
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
+def test_forward_oft_every_format(fmt):
+    """The BF16 OFT adapter (per-expert R) on every frozen base: the rotated
+    rows x R_e go through each format's GEMM1 input quantizer (Orbit analysis
+    page, 核心判断: the base frozen at INT4, FP4 or FP8, the trainable
+    freedom in a BF16 adapter)."""
+    cfg = small(fmt, T=61, H=512, I=256, E=9, k=3, oft=True, chunk=2, cfg_id=150 + fmt)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    gu.check_rows(out, oracle.forward_inputs(li), fmt, f"fmt {fmt} oft")
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
+def test_forward_oft_shared_every_format(fmt):
+    """One R shared by all experts (adapter_expert_stride = 0)."""
+    cfg = small(fmt, T=61, H=512, I=256, E=9, k=3, oft=True, chunk=4, cfg_id=160 + fmt)
+    li = synth.make_inputs(cfg)
+    shared = np.ascontiguousarray(li.oft[3])
+    d = gu.DevInputs(li)
+    d.layer = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, fmt, oft=True, adapter_expert_stride=0)
+    d.oft = gu.dev(shared, "bf16")
+    out = gu.bf16_to_np(d.forward())
+    ref = oracle.forward(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2,
+                         oft=shared, chunk_experts=cfg.chunk, adapter_expert_stride=0, g13=li.g13, g2=li.g2)
+    gu.check_rows(out, ref, fmt, f"fmt {fmt} shared oft")
