@@ -335,6 +335,8 @@ def measure_layer(name, args, flush, chunk=None, mode="fused", with_roofline=Tru
     if lb is not None and mode == "fused":
         res["temp_dequant_bytes"]["this_run_lds_per_workgroup"] = lb
         res["temp_dequant_bytes"]["this_run_lds_all_cus"] = lb * wpc * 256
+    if cfg.lm_vocab > 0 and mode == "fused":
+        res["lm_head"] = lm_head_measure(w, args, flush)
     if with_roofline:
         reps = max(3, min(args.steps, 10))
         sm, sn = stage_times(w, cfg.chunk, reps, flush)
@@ -403,6 +405,8 @@ def main():
         "workspace_bytes": head["workspace_bytes"],
         "roofline": head.get("roofline"),
     }
+    if "lm_head" in head:
+        result["lm_head"] = head["lm_head"]
 
     if not args.no_cpu_baseline:
         import oracle
@@ -447,8 +451,6 @@ def main():
             if name == args.config:
                 continue
             r, wx = measure_layer(name, args, flush)
-            if name == "c5":
-                r["lm_head"] = lm_head_measure(wx, args, flush)
             extras[name] = r
             del wx
             torch.cuda.empty_cache()

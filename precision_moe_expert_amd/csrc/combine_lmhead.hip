@@ -47,48 +47,29 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   }
 }
 
-// inv_rms[t] = 1 / sqrt(mean(h[t]^2) + 1e-6): the final parameter-free RMSNorm,
-// applied to the logits instead of the input (logits = inv_rms * (h W^T)).
-__global__ __launch_bounds__(64) void k_inv_rms(const uint16_t* __restrict__ h, int H, float* __restrict__ inv_rms) {
-  const int t = blockIdx.x, lane = lane_id();
-  float ss = 0.0f;
-  for (int c = lane * 8; c < H; c += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(h + (int64_t)t * H + c);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = bf16_bits_to_f32(u[q] & 0xFFFFu), b = bf16_bits_to_f32(u[q] >> 16);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
-  if (lane == 0) inv_rms[t] = 1.0f / sqrtf(ss / (float)H + 1e-6f);
-}
-
 // Partial logits part[ks][t][v] = sum over the ks-th K slice of h[t][k] W[v][k]
 // (bf16 MFMA, fp32 accumulation).  The head is a skinny GEMM (<= 64 tokens
 // against V x H weights) bound by streaming W once from HBM, so the kernel
-// is built around keeping that stream deep: a workgroup owns 128 vocabulary
-// rows (32 per wave) and one K slice (KS = 2 slices), and moves 64-K steps of
-// its W rows (128 B of each row, 16 KB) and of the token rows (8 KB, shared
-// by the 4 waves) into an LDS ring of LM_S stages by global_load_lds DMA;
-// 72 KB of LDS per workgroup lets two workgroups share a CU, so every
-// workgroup of the grid is resident at once.  Inside a stage each 128-byte
-// row is kept as 8 parts of 16 B with part p at slot p ^ ((row >> 1) & 7):
-// the 16 lanes reading one MFMA fragment then cover 16 distinct 16-byte
-// bank groups.
-constexpr int LM_S = 3;            // stages in flight
-constexpr int LM_VB = 128;         // vocabulary rows per workgroup
+// is built around keeping as much of that stream in flight as the LDS holds:
+// a workgroup of 8 waves owns 256 vocabulary rows (32 per wave) and one K
+// slice (KS = 2 slices: 250 workgroups for a 32000-row head, one per CU), and
+// moves 64-K steps of its W rows (128 B of each row, 32 KB) and of the token
+// rows (8 KB, shared by all waves) into an LDS ring of LM_S = 4 stages by
+// global_load_lds DMA (all 160 KB of the CU's LDS, 96 KB of W in flight).
+// Inside a stage each 128-byte row is kept as 8 parts of 16 B with part p at
+// slot p ^ ((row >> 1) & 7): the 16 lanes reading one MFMA fragment then
+// cover 16 distinct 16-byte bank groups.
+constexpr int LM_S = 4;            // stages in flight
+constexpr int LM_VB = 256;         // vocabulary rows per workgroup
+constexpr int LM_WAVES = 8;
 constexpr int LM_KS = 64;          // K per stage
 constexpr int LM_RB = LM_KS * 2;   // bytes of a row per stage
 constexpr int LM_STAGE = (LM_VB + 64) * LM_RB;
-constexpr int LM_NPER = 4 + 2;     // DMA instructions per wave per stage (W: 32 rows, h: 16 rows)
+constexpr int LM_NPER = 4 + 1;     // DMA instructions per wave per stage (W: 32 rows, h: 8 rows)
 
 MOE_DEV int lm_slot(int row, int part) { return part ^ ((row >> 1) & 7); }
 
-__global__ __launch_bounds__(256, 2) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(LM_WAVES * 64, 1) void k_lm_gemm(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                     int T, int H, int V, int ks_len, float* __restrict__ part) {
   __shared__ __align__(16) uint8_t smem[LM_S * LM_STAGE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -106,19 +87,17 @@ __global__ __launch_bounds__(256, 2) void k_lm_gemm(const uint16_t* __restrict__
     const int v = min(vb * LM_VB + r, V - 1);
     wsrc[j] = reinterpret_cast<const char*>(W) + ((int64_t)v * H + k0 + lm_slot(r, sl) * 8) * 2;
   }
-  const char* hsrc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wave * 16 + j * 8 + rj;                      // token row within the block
+  const char* hsrc;
+  {
+    const int r = wave * 8 + rj;                               // token row within the block
     const int t = min(t0 + r, T - 1);
-    hsrc[j] = reinterpret_cast<const char*>(h) + ((int64_t)t * H + k0 + lm_slot(r, sl) * 8) * 2;
+    hsrc = reinterpret_cast<const char*>(h) + ((int64_t)t * H + k0 + lm_slot(r, sl) * 8) * 2;
   }
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * LM_STAGE;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma_b128(wsrc[j] + kt * LM_RB, sb + (wave * 32 + j * 8) * LM_RB);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma_b128(hsrc[j] + kt * LM_RB, sb + (LM_VB + wave * 16 + j * 8) * LM_RB);
+    dma_b128(hsrc + kt * LM_RB, sb + (LM_VB + wave * 8) * LM_RB);
   };
   f32x4 acc[4][2];
 #pragma unroll
@@ -173,13 +152,32 @@ __global__ __launch_bounds__(256, 2) void k_lm_gemm(const uint16_t* __restrict__
 // sum of exp(logit - m), and the target's logit if it falls in the chunk.
 constexpr int LM_VC = 4096;
 __global__ __launch_bounds__(256) void k_lm_softmax_part(const float* __restrict__ part, int ks_n,
-                                                         const float* __restrict__ inv_rms,
+                                                         const uint16_t* __restrict__ h, int H,
                                                          const int32_t* __restrict__ tgt, int T, int V,
                                                          float* __restrict__ stats) {
   const int t = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
   const int v0 = ch * LM_VC, v1 = min(V, v0 + LM_VC);
-  const float ir = inv_rms[t];
   __shared__ float red[4];
+  // inv_rms = 1 / sqrt(mean(h[t]^2) + 1e-6): the final parameter-free
+  // RMSNorm, applied to the logits instead of the input; every chunk's
+  // workgroup recomputes it (one 14 KB row from L2) in the same order
+  float ss = 0.0f;
+  for (int c = threadIdx.x * 8; c < H; c += 2048) {
+    const uint4 u = *reinterpret_cast<const uint4*>(h + (int64_t)t * H + c);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_bits_to_f32(w4[q] & 0xFFFFu), b = bf16_bits_to_f32(w4[q] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float ir = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + 1e-6f);
+  __syncthreads();
   float lv[LM_VC / 256];
   float mx = -INFINITY;
 #pragma unroll
@@ -242,18 +240,16 @@ void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, in
   hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, y, w, row_of, k, H, out);
 }
 
-int lm_head_slices(int H) { return H % 128 == 0 ? 2 : 1; }
+int lm_head_slices(int H) { (void)H; return 2; }
 int lm_head_chunks(int V) { return (V + LM_VC - 1) / LM_VC; }
 
 void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,
-                    float* part_ws, float* inv_rms_ws, float* stats_ws, float* logprob, hipStream_t s) {
+                    float* part_ws, float* stats_ws, float* logprob, hipStream_t s) {
   if (T == 0) return;
   const int ks = lm_head_slices(H), nch = lm_head_chunks(V);
-  hipLaunchKernelGGL(k_inv_rms, dim3(T), dim3(64), 0, s, h, H, inv_rms_ws);
-  hipLaunchKernelGGL(k_lm_gemm, dim3((V + LM_VB - 1) / LM_VB, ks, (T + 63) / 64), dim3(256), 0, s, h, wlm, T, H, V,
+  hipLaunchKernelGGL(k_lm_gemm, dim3((V + LM_VB - 1) / LM_VB, ks, (T + 63) / 64), dim3(LM_WAVES * 64), 0, s, h, wlm, T, H, V,
                      H / ks, part_ws);
-  hipLaunchKernelGGL(k_lm_softmax_part, dim3(T, nch), dim3(256), 0, s, part_ws, ks, inv_rms_ws, targets, T, V,
-                     stats_ws);
+  hipLaunchKernelGGL(k_lm_softmax_part, dim3(T, nch), dim3(256), 0, s, part_ws, ks, h, H, targets, T, V, stats_ws);
   hipLaunchKernelGGL(k_lm_softmax_final, dim3((T + 63) / 64), dim3(64), 0, s, stats_ws, nch, targets, T, V, logprob);
 }
 

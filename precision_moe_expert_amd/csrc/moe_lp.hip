@@ -953,6 +953,7 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
 }
 }  // namespace
 
+
 extern "C" {
 
 moe_status moe_expert_backward(const moe_layer* layer, const void* x_bf16, const float* logits,
@@ -992,9 +993,9 @@ moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const fl
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V) {
   if (T < 0 || V <= 0) return 0;
   // room for two K slices of partial logits (the most lm_head_slices returns)
-  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * 4) +
-         align_up((size_t)T * lm_head_chunks(V) * 3 * 4);
+  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * lm_head_chunks(V) * 3 * 4);
 }
+
 
 moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf16, const void* w_lm_bf16,
                                const int32_t* targets, float* logprob, void* ws, size_t ws_bytes, void* stream) {
@@ -1007,10 +1008,9 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
   if (ws_bytes < moe_lm_head_workspace_bytes(T, V)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   char* base = static_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(base);
-  float* inv_rms = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4));
-  float* stats = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * 4));
+  float* stats = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4));
   launch_lm_head(static_cast<const uint16_t*>(h_bf16), static_cast<const uint16_t*>(w_lm_bf16), targets, T, H, V,
-                 part, inv_rms, stats, logprob, static_cast<hipStream_t>(stream));
+                 part, stats, logprob, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
