@@ -144,6 +144,56 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _need(t, name: str, nbytes: int, elem: int | None = None):
+    """A device tensor, contiguous, of at least nbytes (and elem-byte elements
+    when given): the library reads and writes exactly the sizes the layer
+    implies, so a smaller or strided tensor would be accessed out of bounds."""
+    if t is None:
+        raise ValueError(f"{name}: tensor required")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous device tensor expected")
+    if elem is not None and t.element_size() != elem:
+        raise ValueError(f"{name}: {elem}-byte elements expected, got {t.dtype}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, the layer needs {nbytes}")
+
+
+def _weight_bytes(fmt: int, N: int, K: int, E: int):
+    """(packed code bytes, scale bytes) of E expert matrices [N][K]."""
+    codes = E * N * K if fmt in (FMT_FP8, FMT_FP8_POW2) else E * N * K // 2
+    if fmt == FMT_INT4:
+        sc = E * (K // 32) * N * 2
+    elif fmt in (FMT_FP8, FMT_FP8_POW2):
+        sc = E * (N // 128) * (K // 128) * 4
+    elif fmt == FMT_NVFP4:
+        sc = E * (K // 16) * N
+    else:
+        sc = E * (K // 32) * N
+    return codes, sc
+
+
+def _check_forward_args(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter, out, g13, g2):
+    T, H, I, E = layer.num_tokens, layer.hidden, layer.inter, layer.num_experts
+    if T == 0:
+        return
+    fmt = layer.wformat
+    _need(x, "x", T * H * 2, 2)
+    _need(logits, "logits", T * E * 4, 4)
+    _need(out, "out", T * H * 2, 2)
+    c13, sc13 = _weight_bytes(fmt, 2 * I, H, E)
+    c2, sc2 = _weight_bytes(fmt, H, I, E)
+    _need(w13, "w13", c13)
+    _need(w2, "w2", c2)
+    _need(s13, "s13", sc13)
+    _need(s2, "s2", sc2)
+    if fmt == FMT_NVFP4:
+        _need(g13, "g13", E * 4, 4)
+        _need(g2, "g2", E * 4, 4)
+    if layer.oft_block:
+        stride = layer.adapter_expert_stride
+        _need(adapter, "adapter", ((E - 1) * stride + H * 32) * 2 if stride else H * 32 * 2, 2)
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -192,6 +242,7 @@ def expert_forward(layer: MoeLayer, x: torch.Tensor, logits: torch.Tensor, w13, 
         out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
+    _check_forward_args(layer, x, logits, w13, w2, s13, s2, adapter, out, g13, g2)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
     sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     _check(lib().moe_expert_forward(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw), ctypes.byref(sc),
@@ -206,6 +257,8 @@ def expert_forward_noalloc(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter
     per-GPU scratch in place of a workspace (layers whose workspace fits it)."""
     if out is None:
         out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
+    if workspace_bytes(layer, chunk_experts) <= NOALLOC_SCRATCH_BYTES:  # else the library refuses first
+        _check_forward_args(layer, x, logits, w13, w2, s13, s2, adapter, out, g13, g2)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
     sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     _check(lib().moe_expert_forward_noalloc(ctypes.byref(layer), _ptr(x), _ptr(logits), ctypes.byref(qw),
@@ -222,6 +275,7 @@ def expert_forward_timed(layer: MoeLayer, x, logits, w13, w2, s13, s2, adapter=N
         out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = alloc_workspace(workspace_bytes(layer, chunk_experts), x.device)
+    _check_forward_args(layer, x, logits, w13, w2, s13, s2, adapter, out, g13, g2)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
     sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     ms = (ctypes.c_float * len(STAGES))()
@@ -244,6 +298,7 @@ def expert_forward_materialized(layer: MoeLayer, x, logits, w13, w2, s13, s2, ad
         out = torch.empty((layer.num_tokens, layer.hidden), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = alloc_workspace(materialized_workspace_bytes(layer, chunk_experts), x.device)
+    _check_forward_args(layer, x, logits, w13, w2, s13, s2, adapter, out, g13, g2)
     qw = MoeQWeights(_ptr(w13), _ptr(w2))
     sc = MoeScales(_ptr(s13), _ptr(s2), _ptr(g13), _ptr(g2))
     ms = (ctypes.c_float * len(STAGES))() if timed else None

@@ -265,3 +265,24 @@ def test_forward_oft_shared_every_format(fmt):
     ref = oracle.forward(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, fmt, li.x, li.logits, li.w13, li.w2, li.s13, li.s2,
                          oft=shared, chunk_experts=cfg.chunk, adapter_expert_stride=0, g13=li.g13, g2=li.g2)
     gu.check_rows(out, ref, fmt, f"fmt {fmt} shared oft")
+
+
+def test_binding_rejects_mis_sized_tensors():
+    """The binding checks every tensor against the sizes the layer implies
+    before the library is called (a short or strided tensor would be read or
+    written out of bounds on the GPU)."""
+    cfg = small(3, T=40, H=256, I=256, E=6, k=2, cfg_id=190)
+    d = gu.DevInputs(synth.make_inputs(cfg))
+    c = d.li.cfg
+    args = dict(adapter=None, chunk_experts=2, g13=None, g2=None)
+    with pytest.raises(ValueError):
+        binding.expert_forward(d.layer, d.x[:-1], d.logits, d.w13, d.w2, d.s13, d.s2, **args)   # short x
+    with pytest.raises(ValueError):
+        binding.expert_forward(d.layer, d.x, d.logits, d.w13.reshape(-1)[: d.w13.numel() // 2], d.w2, d.s13, d.s2, **args)
+    with pytest.raises(ValueError):
+        binding.expert_forward(d.layer, d.x, d.logits.t(), d.w13, d.w2, d.s13, d.s2, **args)  # strided
+    with pytest.raises(ValueError):
+        binding.expert_forward(d.layer, d.x.view(torch.int16).to(torch.int32), d.logits, d.w13, d.w2, d.s13, d.s2,
+                               **args)                                                        # 4-byte elements
+    out = binding.expert_forward(d.layer, d.x, d.logits, d.w13, d.w2, d.s13, d.s2, **args)
+    assert out.shape == (c.T, c.H)
