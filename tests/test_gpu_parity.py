@@ -190,6 +190,27 @@ def test_forward_every_tile_height(fmt, tile_rows):
     gu.check_rows(out, oracle.forward_inputs(li), li.cfg.fmt, f"fmt {fmt} tile {tile_rows}")
 
 
+@pytest.mark.parametrize("oft,zipf,chunk", [(False, 0.0, 2), (True, 0.0, 3), (False, 1.2, 1)])
+def test_mxfp4_128_row_tiles(oft, zipf, chunk):
+    """MXFP4 at 128-row tiles, the headline tile height, on a shape whose H
+    and I are multiples of 512 like the DeepSeek-V3 one: ~240 rows per
+    expert, so the tiles run full and ragged; GEMM1 has four 128-wide h
+    blocks and 8 K steps, GEMM2 four 256-wide output blocks and 4 K steps.
+    Also bitwise independent of the chunk size."""
+    cfg = small(3, T=300, H=1024, I=512, E=5, k=4, oft=oft, zipf=zipf, chunk=chunk,
+                cfg_id=200 + 2 * int(oft) + int(zipf > 0))
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    d.layer.tile_rows = 128
+    out = d.forward()
+    torch.cuda.synchronize()
+    gu.check_rows(gu.bf16_to_np(out), oracle.forward_inputs(li), 3, f"mxfp4 128-row tiles oft={oft} zipf={zipf}")
+    for c in (1, 5):
+        o = d.forward(chunk=c)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16)), f"chunk {c} differs"
+
+
 def _scaled_int4_case(cfg_id, s_lo, s_hi, x_scale, x_max=None):
     cfg = small(1, T=64, H=512, I=256, E=6, k=2, chunk=3, cfg_id=cfg_id)
     li = synth.make_inputs(cfg)
