@@ -40,6 +40,27 @@ DTYPE = {1: "int4_w_fp16_mfma", 2: "fp8_e4m3", 3: "mxfp4_w_mxfp8_a", 4: "fp8_e4m
 FLUSH_BYTES = 512 << 20
 
 
+class CacheFlush:
+    """Between timed steps: write FLUSH_BYTES (more than the 256 MB MALL, so
+    no weight byte of the last step is left in any cache), then read another
+    FLUSH_BYTES buffer.  The write alone leaves the caches full of dirty
+    lines, and writing those back to HBM takes ~60 us of the next kernel's
+    bandwidth (a 459 MB stream measured 138 us after the write, 78 us after
+    write + read); the read replaces them with clean lines, so the timed
+    step starts cold and pays only for its own traffic.  Both are untimed."""
+
+    def __init__(self):
+        import torch
+        self.w = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.r = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
+        self.sink = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def __call__(self, i: int):
+        import torch
+        self.w.fill_(i & 0x7F)
+        torch.sum(self.r, dim=0, out=self.sink)
+
+
 def weight_bytes_per_expert(fmt: int, N: int, K: int) -> float:
     """Packed codes + scales of one expert matrix [N][K]."""
     if fmt == 1:
@@ -179,7 +200,7 @@ class Workload:
 
 def time_steps(fn, steps, warmup, flush):
     """Median / mean per-step HIP-event time (ms) of fn() on the current stream,
-    with the 512 MiB flush written before every step (outside the events)."""
+    with the cache flush (CacheFlush) before every step (outside the events)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -187,7 +208,7 @@ def time_steps(fn, steps, warmup, flush):
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
-        flush.fill_(i & 0x7F)
+        flush(i)
         evs[i][0].record(stream)
         fn()
         evs[i][1].record(stream)
@@ -204,7 +225,7 @@ def stage_times(w: Workload, chunk, reps, flush):
     stage_ms = {s: 0.0 for s in binding.STAGES}
     stage_n = {s: 0 for s in binding.STAGES}
     for i in range(reps):
-        flush.fill_(i & 0x7F)
+        flush(i)
         torch.cuda.synchronize()
         st = w.step(chunk, timed=True)
         for s, (ms, n) in st.items():
@@ -374,7 +395,7 @@ def main():
 
     from precision_moe_expert_amd import binding
     mode = "materialized" if args.materialized else ("backward" if args.backward else "fused")
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = CacheFlush()
     head, w = measure_layer(args.config, args, flush, chunk=args.chunk, mode=mode)
     cfg = w.cfg
     result = {
