@@ -333,20 +333,11 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
       const int r = m * 16 + ln;
       return *reinterpret_cast<const f16x8*>(st + r * 256 + (((4 * lg + s) ^ (r & 15)) << 4));
     };
-    // The activation fragments of sub-step s + 1 are read while sub-step s
-    // unpacks its weights and runs its MFMAs (the scheduling barriers keep
-    // the compiler from sinking the reads to their first use).
-    f16x8 af[2][MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) af[0][m] = read_a(m, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) af[(s + 1) & 1][m] = read_a(m, s + 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8 bf[4];
+    // Sub-step s (32 K) runs its MFMAs while the VALU unpacks the weights of
+    // sub-step s + 1 and the activation fragments of sub-step s + 1 are
+    // read: the scheduling groups alternate one MFMA with a few VALU
+    // instructions, so the unpack hides behind the matrix core.
+    auto unpack = [&](int s, f16x8 (&bf)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (FMT == FMT_FP8) {
@@ -362,10 +353,33 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
                                   : e2m1x8_to_f16_se(dword_of(bq[i][0], s), sc);
         }
       }
+    };
+    f16x8 af[2][MT];
+    f16x8 bf[2][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) af[0][m] = read_a(m, 0);
+    unpack(0, bf[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < 4) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) af[(s + 1) & 1][m] = read_a(m, s + 1);
+        unpack(s + 1, bf[(s + 1) & 1]);
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[i], acc[m][i]);
+        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[s & 1][i], acc[m][i]);
+      if (s + 1 < 4) {
+        // one MFMA, then the next sub-step's LDS reads and VALU work between MFMAs
+#pragma unroll
+        for (int j = 0; j < MT * 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j < MT + 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
