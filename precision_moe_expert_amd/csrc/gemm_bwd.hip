@@ -359,6 +359,7 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
 #pragma unroll
     for (int m = 0; m < MT; ++m) af[0][m] = read_a(m, 0);
     unpack(0, bf[0]);
+    __builtin_amdgcn_s_setprio(1);  // the MFMA phase at raised wave priority
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       __builtin_amdgcn_sched_barrier(0);
@@ -382,6 +383,7 @@ __device__ __forceinline__ void bwd_item(const GemmArgs& p, const Tile& tl, uint
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   if constexpr (FMT == FMT_NVFP4) {
     const float gs = ld_uniform_f32(p.gscale + tl.e);

@@ -146,6 +146,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
       wnext[1] = ld_uniform_f32(ws2 + kt + 1);
     }
     if (nmb == 0) continue;  // a 16-row tile leaves row group 1 without work
+    __builtin_amdgcn_s_setprio(1);  // the MFMA phase at raised wave priority
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
     const float* As = reinterpret_cast<const float*>(asb + ((kt >> 2) & 1) * ST::AS_BLOCK) + (kt & 3);
     i32x8 bf[4];
@@ -241,6 +242,7 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
               acc[m][i][q] = fmaf(prev[i][q], i < 2 ? psc01[q] : psc23[q], acc[m][i][q]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Epilogue: results go through LDS (the stage buffers are free once every

@@ -162,6 +162,10 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     i32x8 af[2];
     int sa[2];
     read_a(0, af[0], sa[0]);
+    // the MFMA phase at raised wave priority: when this SIMD's other wave
+    // (the other workgroup) is ready too, the matrix core's feeder issues
+    // first (headline GEMM 1.2% faster)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m + 1 < MT) read_a(m + 1, af[(m + 1) & 1], sa[(m + 1) & 1]);
@@ -171,6 +175,7 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
         acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(af[m & 1], bf[i], sa[m & 1], sb[i], acc[m][i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Epilogue: results go through LDS (the stage buffers are free once every
