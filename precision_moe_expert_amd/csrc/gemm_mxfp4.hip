@@ -156,9 +156,10 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
       af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sa = (int)asb[((kt >> 2) & 1) * ST::AS_BLOCK + r * 16 + (kt & 3) * 4 + lg];
     };
-    // Row block m + 1's operands are read before block m's MFMAs issue (the
-    // scheduling barriers keep the compiler from sinking the reads to their
-    // first use).
+    // Row block m + 1's operands are read while block m's MFMAs issue, one
+    // LDS read between two MFMAs (the scheduling groups; without them the
+    // compiler sinks the reads to their first use): headline GEMM 1.8%
+    // faster than issuing the three reads ahead of the four MFMAs.
     i32x8 af[2];
     int sa[2];
     read_a(0, af[0], sa[0]);
@@ -168,11 +169,19 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      if (m + 1 < MT) read_a(m + 1, af[(m + 1) & 1], sa[(m + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
+      if (m + 1 < MT) read_a(m + 1, af[(m + 1) & 1], sa[(m + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[m][i] = mfma_fp8_fp4_scaled_16x16x128(af[m & 1], bf[i], sa[m & 1], sb[i], acc[m][i]);
+      if (m + 1 < MT) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
