@@ -349,8 +349,8 @@ moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const fl
                        const int32_t* row_of, void* out_bf16, void* stream);
 
 /* Workspace bytes moe_lm_head_logprob needs: 2*T*V fp32 partial logits (two
- * K slices) and T*ceil(V/4096)*3 fp32 per-chunk log-softmax statistics, each
- * 256-byte aligned. */
+ * K slices) and T*4*3 fp32 log-softmax statistics of four vocabulary parts,
+ * each 256-byte aligned. */
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V);
 
 /* Log-prob of target tokens under an LM head (the rollout log-probs whose

@@ -147,91 +147,129 @@ __global__ __launch_bounds__(LM_WAVES * 64, 1) void k_lm_gemm(const uint16_t* __
   }
 }
 
-// Per token and vocabulary chunk of LM_VC entries: logits = inv_rms[t] *
-// (part[0] + part[1]) (slices summed in order), the chunk's maximum m, its
-// sum of exp(logit - m), and the target's logit if it falls in the chunk.
-constexpr int LM_VC = 4096;
-__global__ __launch_bounds__(256) void k_lm_softmax_part(const float* __restrict__ part, int ks_n,
-                                                         const uint16_t* __restrict__ h, int H,
-                                                         const int32_t* __restrict__ tgt, int T, int V,
-                                                         float* __restrict__ stats) {
-  const int t = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
-  const int v0 = ch * LM_VC, v1 = min(V, v0 + LM_VC);
-  __shared__ float red[4];
-  // inv_rms = 1 / sqrt(mean(h[t]^2) + 1e-6): the final parameter-free
-  // RMSNorm, applied to the logits instead of the input; every chunk's
-  // workgroup recomputes it (one 14 KB row from L2) in the same order
+// Per token and quarter of the vocabulary, one workgroup of 1024 threads:
+// inv_rms = 1 / sqrt(mean(h^2) + 1e-6) (the final parameter-free RMSNorm,
+// applied to the logits instead of the input), logits = inv_rms * (part[0] +
+// part[1]) (slices summed in order), and the quarter's maximum logit m, its
+// sum s of exp(logit - m) and the target's logit if it falls in the quarter.
+// The token's h row and all of the quarter's partial logits of both slices
+// are requested before the first reduction; thread i owns entries v0 + i +
+// 1024 j.  Each thread keeps (max, sum) over its entries; the 64 lanes of a
+// wave merge in a fixed butterfly and the 16 waves in order, so the result
+// does not depend on timing.
+constexpr int LMS_T = 1024;   // threads per workgroup
+constexpr int LMS_Q = 4;      // vocabulary parts per token
+constexpr int LMS_J = 8;      // entries per thread per pass
+
+MOE_DEV void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 == -INFINITY) return;  // an empty pair changes nothing
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  s = s * expf(m - M) + s2 * expf(m2 - M);
+  m = M;
+}
+
+__global__ __launch_bounds__(LMS_T) void k_lm_softmax_part(const float* __restrict__ part, const uint16_t* __restrict__ h,
+                                                           int H, const int32_t* __restrict__ tgt, int T, int V,
+                                                           float* __restrict__ stats) {
+  const int t = blockIdx.x, q = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (V + LMS_Q - 1) / LMS_Q, v0 = q * per, v1 = min(V, v0 + per);
+  __shared__ float red_a[LMS_T / 64], red_b[LMS_T / 64];
+  __shared__ float s_ir;
+  const float* p0 = part + (int64_t)t * V;
+  const float* p1 = part + ((int64_t)T + t) * V;
+  // sum of squares of the h row: 8 values per thread per 8 K columns
   float ss = 0.0f;
-  for (int c = threadIdx.x * 8; c < H; c += 2048) {
+  for (int c = tid * 8; c < H; c += LMS_T * 8) {
     const uint4 u = *reinterpret_cast<const uint4*>(h + (int64_t)t * H + c);
     const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = bf16_bits_to_f32(w4[q] & 0xFFFFu), b = bf16_bits_to_f32(w4[q] >> 16);
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf16_bits_to_f32(w4[k] & 0xFFFFu), b = bf16_bits_to_f32(w4[k] >> 16);
       ss = fmaf(a, a, ss);
       ss = fmaf(b, b, ss);
     }
   }
+  float a0[LMS_J], a1[LMS_J];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float ir = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + 1e-6f);
-  __syncthreads();
-  float lv[LM_VC / 256];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < LM_VC / 256; ++i) {
-    const int v = v0 + i * 256 + threadIdx.x;
-    float z = -INFINITY;
-    if (v < v1) {
-      float sum = part[(int64_t)t * V + v];
-      for (int q = 1; q < ks_n; ++q) sum += part[((int64_t)q * T + t) * V + v];
-      z = sum * ir;
-    }
-    lv[i] = z;
-    mx = fmaxf(mx, z);
+  for (int j = 0; j < LMS_J; ++j) {
+    const int v = v0 + tid + j * LMS_T;
+    a0[j] = v < v1 ? p0[v] : 0.0f;
+    a1[j] = v < v1 ? p1[v] : 0.0f;
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor(mx, m));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  for (int x = 1; x < 64; x <<= 1) ss += shfl_xor(ss, x);
+  if (lane == 0) red_a[wave] = ss;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float se = 0.0f;
-#pragma unroll
-  for (int i = 0; i < LM_VC / 256; ++i)
-    if (v0 + i * 256 + (int)threadIdx.x < v1) se += expf(lv[i] - mx);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) se += shfl_xor(se, m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = se;
-  __syncthreads();
-  float* st = stats + ((int64_t)t * nch + ch) * 3;
-  if (threadIdx.x == 0) {
-    st[0] = mx;
-    st[1] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) {
+    float sum = red_a[0];
+    for (int w = 1; w < LMS_T / 64; ++w) sum += red_a[w];
+    s_ir = 1.0f / sqrtf(sum / (float)H + 1e-6f);
   }
+  __syncthreads();
+  const float ir = s_ir;
   const int y = tgt[t];
-  if (y >= v0 && y < v1 && ((y - v0) & 255) == (int)threadIdx.x) {
+  float* st = stats + ((int64_t)t * LMS_Q + q) * 3;
+  float m = -INFINITY, s = 0.0f;
+  for (int base = v0;; base += LMS_T * LMS_J) {
+    float z[LMS_J];
+    float cm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < LM_VC / 256; ++i)
-      if (i == (y - v0) / 256) st[2] = lv[i];
+    for (int j = 0; j < LMS_J; ++j) {
+      const int v = base + tid + j * LMS_T;
+      z[j] = v < v1 ? (a0[j] + a1[j]) * ir : -INFINITY;
+      if (v == y) st[2] = z[j];
+      cm = fmaxf(cm, z[j]);
+    }
+    if (cm != -INFINITY) {
+      float cs = 0.0f;
+#pragma unroll
+      for (int j = 0; j < LMS_J; ++j) cs += expf(z[j] - cm);
+      lse_merge(m, s, cm, cs);
+    }
+    if (base + LMS_T * LMS_J >= v1) break;
+    // the next pass (quarters wider than 8 K entries)
+#pragma unroll
+    for (int j = 0; j < LMS_J; ++j) {
+      const int v = base + LMS_T * LMS_J + tid + j * LMS_T;
+      a0[j] = v < v1 ? p0[v] : 0.0f;
+      a1[j] = v < v1 ? p1[v] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) {
+    const float m2 = shfl_xor(m, x), s2 = shfl_xor(s, x);
+    lse_merge(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    red_a[wave] = m;
+    red_b[wave] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = red_a[0], S = red_b[0];
+    for (int w = 1; w < LMS_T / 64; ++w) lse_merge(M, S, red_a[w], red_b[w]);
+    st[0] = M;
+    st[1] = S;
   }
 }
 
-// logprob[t] = logit[t][y_t] - (M + log sum_c s_c exp(m_c - M)), chunks in order.
-__global__ __launch_bounds__(64) void k_lm_softmax_final(const float* __restrict__ stats, int nch,
+// logprob[t] = logit[t][y_t] - (M + log S), the parts merged in order.
+__global__ __launch_bounds__(64) void k_lm_softmax_final(const float* __restrict__ stats,
                                                          const int32_t* __restrict__ tgt, int T, int V,
                                                          float* __restrict__ lp) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= T) return;
-  const float* st = stats + (int64_t)t * nch * 3;
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c * 3]);
-  float S = 0.0f;
-  for (int c = 0; c < nch; ++c) S += st[c * 3 + 1] * expf(st[c * 3] - M);
+  const float* st = stats + (int64_t)t * LMS_Q * 3;
+  float M = st[0], S = st[1];
+  for (int q = 1; q < LMS_Q; ++q) lse_merge(M, S, st[q * 3], st[q * 3 + 1]);
   const int y = tgt[t];  // out-of-range targets give NaN instead of a stray read
-  lp[t] = (y >= 0 && y < V) ? st[(y / LM_VC) * 3 + 2] - (M + logf(S)) : __builtin_nanf("");
+  const int per = (V + LMS_Q - 1) / LMS_Q;
+  lp[t] = (y >= 0 && y < V) ? st[(y / per) * 3 + 2] - (M + logf(S)) : __builtin_nanf("");
 }
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
@@ -241,16 +279,16 @@ void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, in
 }
 
 int lm_head_slices(int H) { (void)H; return 2; }
-int lm_head_chunks(int V) { return (V + LM_VC - 1) / LM_VC; }
+int lm_head_parts() { return LMS_Q; }
 
 void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,
                     float* part_ws, float* stats_ws, float* logprob, hipStream_t s) {
   if (T == 0) return;
-  const int ks = lm_head_slices(H), nch = lm_head_chunks(V);
+  const int ks = lm_head_slices(H);
   hipLaunchKernelGGL(k_lm_gemm, dim3((V + LM_VB - 1) / LM_VB, ks, (T + 63) / 64), dim3(LM_WAVES * 64), 0, s, h, wlm, T, H, V,
                      H / ks, part_ws);
-  hipLaunchKernelGGL(k_lm_softmax_part, dim3(T, nch), dim3(256), 0, s, part_ws, ks, h, H, targets, T, V, stats_ws);
-  hipLaunchKernelGGL(k_lm_softmax_final, dim3((T + 63) / 64), dim3(64), 0, s, stats_ws, nch, targets, T, V, logprob);
+  hipLaunchKernelGGL(k_lm_softmax_part, dim3(T, LMS_Q), dim3(LMS_T), 0, s, part_ws, h, H, targets, T, V, stats_ws);
+  hipLaunchKernelGGL(k_lm_softmax_final, dim3((T + 63) / 64), dim3(64), 0, s, stats_ws, targets, T, V, logprob);
 }
 
 }  // namespace moe

@@ -993,7 +993,7 @@ moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const fl
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V) {
   if (T < 0 || V <= 0) return 0;
   // room for two K slices of partial logits (the most lm_head_slices returns)
-  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * lm_head_chunks(V) * 3 * 4);
+  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * lm_head_parts() * 3 * 4);
 }
 
 

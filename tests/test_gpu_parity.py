@@ -167,6 +167,28 @@ def test_lm_head_logprob_vs_oracle():
     assert np.max(np.abs(lp - ref)) <= 1e-3
 
 
+@pytest.mark.parametrize("T,H,V", [(130, 256, 700), (1, 128, 100), (64, 384, 256), (65, 256, 513)])
+def test_lm_head_blocks_and_edges(T, H, V):
+    # several 64-token blocks, a last vocabulary block of 1..255 rows, targets on
+    # block edges; a second call on the same workspace gives the same bits
+    r = np.random.default_rng(T * 1000 + V)
+    h = synth._to_bf16_bits((r.standard_normal((T, H)) * 3).astype(np.float32))
+    w = synth._to_bf16_bits((r.standard_normal((V, H)) * (4 / np.sqrt(H))).astype(np.float32))
+    edges = [v for v in (0, V - 1, 255, 256, 511, 512) if v < V]
+    tg = r.integers(0, V, T).astype(np.int32)
+    tg[:len(edges)] = edges[:T]
+    ws = binding.alloc_workspace(binding.lib().moe_lm_head_workspace_bytes(T, V))
+    ws.fill_(0x7F)  # the call must not rely on a cleared workspace
+    hd, wd, td = gu.dev(h, "bf16"), gu.dev(w, "bf16"), gu.dev(tg)
+    lp = binding.lm_head_logprob(hd, wd, td, ws=ws)
+    lp2 = binding.lm_head_logprob(hd, wd, td, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lp, lp2)
+    from tests import refimpl
+    ref = oracle.lm_head_logprob(refimpl.bf16_to_f32(h), w, tg)
+    assert np.max(np.abs(lp.cpu().numpy() - ref)) <= 1e-3
+
+
 def test_t0_is_noop():
     layer = binding.make_layer(0, 256, 256, 8, 2, 1)
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
