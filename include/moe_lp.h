@@ -90,10 +90,10 @@ typedef enum {
    * codes (B = 64 bytes of 4-bit codes in the usual nibble order, 128 bytes
    * of E4M3) contiguous within its tile, tiles K-fastest.  A GEMM step then
    * streams 1-2 KB runs instead of 64- or 128-byte pieces of rows K/2 or K
-   * bytes apart.  Fused forward and frozen-base backward (the backward's
-   * transposed copy is made from either order); the materialized forward
-   * returns MOE_ERR_UNSUPPORTED (workspace size 0).  Written by
-   * moe_pack_weights_kblocked.  Scales keep their layout. */
+   * bytes apart.  Fused forward, materialized forward (its BF16 copy is in
+   * rows either way) and frozen-base backward (the backward's transposed
+   * copy is made from either order).  Written by moe_pack_weights_kblocked.
+   * Scales keep their layout. */
   MOE_WL_KBLOCKED = 1
 } moe_wlayout;
 

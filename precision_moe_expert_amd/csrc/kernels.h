@@ -104,7 +104,7 @@ void launch_oft_bf16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stri
 // {16, 32, 64, 128}.
 void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
                           const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
-                          const float* g13, const float* g2, uint16_t* scratch, hipStream_t s);
+                          const float* g13, const float* g2, bool kblocked, uint16_t* scratch, hipStream_t s);
 void launch_gemm_bf16_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s);
 

@@ -51,14 +51,24 @@ struct Raw8 {
   uint32_t s;    // scale bits (fp32, bf16, E8M0 or E4M3)
 };
 
+// Byte offset of code (n, k0) in one expert's matrix of N x K codes: rows
+// (each row's K codes contiguous) or 16 x 128 tiles (tile (n/16, k0/128)
+// K-fastest, a row's 128 codes contiguous inside it); RB = bytes of 128 codes.
+template <int RB>
+MOE_DEV int64_t code_offset(bool kblocked, int K, int n, int k0) {
+  if (!kblocked) return ((int64_t)n * K + k0) * RB / 128;
+  return ((int64_t)(n >> 4) * (K / 128) + (k0 >> 7)) * (16 * RB) + (n & 15) * RB + (k0 & 127) * RB / 128;
+}
+
 template <int FMT>
-MOE_DEV Raw8 load8(const uint8_t* __restrict__ w, const void* __restrict__ sc, int N, int K, int n, int k0) {
+MOE_DEV Raw8 load8(const uint8_t* __restrict__ w, const void* __restrict__ sc, int N, int K, int n, int k0,
+                   bool kblocked) {
   Raw8 r;
   if (FMT == FMT_FP8) {
-    r.q = *reinterpret_cast<const uint2*>(w + (int64_t)n * K + k0);
+    r.q = *reinterpret_cast<const uint2*>(w + code_offset<128>(kblocked, K, n, k0));
     r.s = static_cast<const uint32_t*>(sc)[(n / 128) * (K / 128) + k0 / 128];
   } else {
-    r.q.x = *reinterpret_cast<const uint32_t*>(w + ((int64_t)n * K + k0) / 2);
+    r.q.x = *reinterpret_cast<const uint32_t*>(w + code_offset<64>(kblocked, K, n, k0));
     r.q.y = 0;
     const int si = (k0 / (FMT == FMT_NVFP4 ? 16 : 32)) * N + n;  // group-major [K/32][N] ([K/16][N])
     r.s = FMT == FMT_INT4 ? (uint32_t) static_cast<const uint16_t*>(sc)[si]
@@ -110,14 +120,16 @@ MOE_DEV uint4 cvt8(const Raw8& r, float g) {
 }
 
 // grid.y = chunk slot (slots past the chunk's last active expert exit).
-// Units u < u13 are W13's, the rest W2's, both in row-major order.
+// Units u < u13 are W13's, the rest W2's, both in row-major order of the
+// copy; the codes are read from rows or from 16 x 128 tiles (kblocked).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict__ w13, const void* __restrict__ s13,
                                                        const uint8_t* __restrict__ w2, const void* __restrict__ s2,
                                                        const int32_t* __restrict__ active,
                                                        const int32_t* __restrict__ num_active, int chunk, int C,
                                                        int H, int I, const float* __restrict__ g13,
-                                                       const float* __restrict__ g2, uint16_t* __restrict__ scratch) {
+                                                       const float* __restrict__ g2, bool kblocked,
+                                                       uint16_t* __restrict__ scratch) {
   const int na = *num_active;
   const int slot = blockIdx.y;
   const int a = chunk * C + slot;
@@ -144,10 +156,10 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
       const int u = u0 + j * stride;
       if (u < u13) {
         const int n = u / KU1;
-        r[j] = load8<FMT>(w13e, s13e, 2 * I, H, n, (u - n * KU1) * 8);
+        r[j] = load8<FMT>(w13e, s13e, 2 * I, H, n, (u - n * KU1) * 8, kblocked);
       } else if (u < total) {
         const int v = u - u13, n = v / KU2;
-        r[j] = load8<FMT>(w2e, s2e, H, I, n, (v - n * KU2) * 8);
+        r[j] = load8<FMT>(w2e, s2e, H, I, n, (v - n * KU2) * 8, kblocked);
       }
     }
 #pragma unroll
@@ -160,22 +172,22 @@ __global__ __launch_bounds__(256) void k_dequant_chunk(const uint8_t* __restrict
 
 void launch_dequant_chunk(int fmt, const uint8_t* w13, const void* s13, const uint8_t* w2, const void* s2,
                           const int32_t* active, const int32_t* num_active, int chunk, int C, int H, int I,
-                          const float* g13, const float* g2, uint16_t* scratch, hipStream_t s) {
+                          const float* g13, const float* g2, bool kblocked, uint16_t* scratch, hipStream_t s) {
   // about 4096 workgroups over the chunk's slots, at least 16 per slot
   const int gx = C >= 256 ? 16 : 4096 / C;
   const dim3 grid(gx, C), block(256);
   if (fmt == FMT_INT4)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_INT4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
-                       H, I, g13, g2, scratch);
+                       H, I, g13, g2, kblocked, scratch);
   else if (fmt == FMT_FP8)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_FP8>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk, C,
-                       H, I, g13, g2, scratch);
+                       H, I, g13, g2, kblocked, scratch);
   else if (fmt == FMT_NVFP4)
     hipLaunchKernelGGL(k_dequant_chunk<FMT_NVFP4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk,
-                       C, H, I, g13, g2, scratch);
+                       C, H, I, g13, g2, kblocked, scratch);
   else
     hipLaunchKernelGGL(k_dequant_chunk<FMT_MXFP4>, grid, block, 0, s, w13, s13, w2, s2, active, num_active, chunk,
-                       C, H, I, g13, g2, scratch);
+                       C, H, I, g13, g2, kblocked, scratch);
 }
 
 // ------------------------------------------------------------- BF16 GEMM

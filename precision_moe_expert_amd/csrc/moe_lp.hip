@@ -529,7 +529,6 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
   Dims d;
   moe_status st = check_layer(layer, &d);
   if (st != MOE_OK) return st;
-  if (d.kblocked) return MOE_ERR_UNSUPPORTED;  // the dequant kernel reads K-contiguous rows
   if (chunk_experts < 1 || qw == nullptr || sc == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((adapter_bf16 != nullptr) != d.oft) return MOE_ERR_INVALID_ARGUMENT;
   if (d.T == 0) return MOE_OK;
@@ -612,7 +611,7 @@ moe_status forward_materialized_impl(const moe_layer* layer, const void* x_bf16,
     { Scope sc_(tm, MOE_STAGE_DEQUANT);
       launch_dequant_chunk(d.fmt, static_cast<const uint8_t*>(qw->w13), sc->s13,
                            static_cast<const uint8_t*>(qw->w2), sc->s2, active, num_active, c, C, d.H, d.I, sc->g13,
-                           sc->g2, copy, s); }
+                           sc->g2, d.kblocked, copy, s); }
     g1.chunk = c;
     g2.chunk = -1;
     { Scope sc_(tm, MOE_STAGE_GEMM1); launch_gemm_bf16_pair(g1, g2, queue + 16 * c, bm, grid1, s); }
@@ -1016,7 +1015,7 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
 
 size_t moe_materialized_workspace_bytes(const moe_layer* layer, int32_t chunk_experts) {
   Dims d;
-  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1 || d.kblocked) return 0;
+  if (check_layer(layer, &d) != MOE_OK || chunk_experts < 1) return 0;
   return mat_layout(d, chunk_experts < d.E ? chunk_experts : d.E).total;
 }
 

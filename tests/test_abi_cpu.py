@@ -188,10 +188,9 @@ def test_materialized_rejects_bad_args():
 
 
 def test_kblocked_layout_host_checks():
-    """The 16 x 128 tiled code layout: fused forward and backward; an unknown layout
-    value is invalid; the materialized forward reports unsupported and a zero
-    size, the backward takes either order; the pack entry rejects bad
-    pointers."""
+    """The 16 x 128 tiled code layout: fused forward, materialized forward and
+    backward take it with the same workspace sizes as rows; an unknown layout
+    value is invalid; the pack entry rejects bad pointers."""
     lib = binding.lib()
     Lk = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4, weight_layout=binding.WL_KBLOCKED)
     Lr = binding.make_layer(64, 256, 512, 8, 2, binding.FMT_INT4)
@@ -203,10 +202,11 @@ def test_kblocked_layout_host_checks():
     for fmt in (binding.FMT_FP8, binding.FMT_FP8_POW2, binding.FMT_MXFP4):
         Lf = binding.make_layer(64, 256, 512, 8, 2, fmt, weight_layout=binding.WL_KBLOCKED)
         assert _fwd(Lf, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
-        assert binding.materialized_workspace_bytes(Lf, 4) == 0
+        Lfr = binding.make_layer(64, 256, 512, 8, 2, fmt)
+        assert binding.materialized_workspace_bytes(Lf, 4) == binding.materialized_workspace_bytes(Lfr, 4) > 0
         assert binding.backward_weights_bytes(Lf) > 0
-    assert binding.materialized_workspace_bytes(Lk, 4) == 0
-    assert _mat(Lk) == binding.MOE_ERR_UNSUPPORTED
+    assert binding.materialized_workspace_bytes(Lk, 4) == binding.materialized_workspace_bytes(Lr, 4) > 0
+    assert _mat(Lk, ws_bytes=0) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
     assert binding.backward_weights_bytes(Lk) == binding.backward_weights_bytes(Lr) > 0
     assert binding.backward_workspace_bytes(Lk, 4) == binding.backward_workspace_bytes(Lr, 4) > 0
     qw = binding.MoeQWeights(FAKE, FAKE)

@@ -61,6 +61,22 @@ def test_materialized_chunk_size_bitwise_invariance(fmt):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False), (5, False)])
+def test_materialized_tiled_codes_bitwise(fmt, oft):
+    """Codes in 16 x 128 tiles give the same BF16 copy, so the same bits as rows."""
+    cfg = small(fmt, H=512, I=384, oft=oft, cfg_id=170 + fmt + (10 if oft else 0))
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    a = d.forward_materialized().clone()
+    w13, w2 = binding.pack_weights_kblocked(d.layer, d.w13, d.w2)
+    lk = binding.make_layer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.fmt, oft=cfg.oft,
+                            weight_layout=binding.WL_KBLOCKED)
+    b = binding.expert_forward_materialized(lk, d.x, d.logits, w13, w2, d.s13, d.s2, adapter=d.oft,
+                                            chunk_experts=cfg.chunk, g13=d.g13, g2=d.g2)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_materialized_timed_matches_untimed():
     li = synth.make_inputs(small(2))
     d = gu.DevInputs(li)
