@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256) void k_unpermute_sum(const float* __restrict__
         }
     }
     *reinterpret_cast<uint2*>(out + (int64_t)t * H + c) =
-        make_uint2(f32_to_bf16_bits(s[0]) | (f32_to_bf16_bits(s[1]) << 16),
-                   f32_to_bf16_bits(s[2]) | (f32_to_bf16_bits(s[3]) << 16));
+        make_uint2(bf16x2_bits(s[0], s[1]),
+                   bf16x2_bits(s[2], s[3]));
   }
 }
 

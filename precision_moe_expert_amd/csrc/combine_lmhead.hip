@@ -39,10 +39,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
         }
     }
     uint4 o;
-    o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-    o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-    o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-    o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+    o.x = bf16x2_bits(acc[0], acc[1]);
+    o.y = bf16x2_bits(acc[2], acc[3]);
+    o.z = bf16x2_bits(acc[4], acc[5]);
+    o.w = bf16x2_bits(acc[6], acc[7]);
     *reinterpret_cast<uint4*>(out + (int64_t)t * H + c * 8) = o;
   }
 }

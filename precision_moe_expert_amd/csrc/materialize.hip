@@ -105,7 +105,7 @@ MOE_DEV uint4 cvt8(const Raw8& r, float g) {
       const uint32_t b = r.q.x >> (i * 8);
       const float lo = (float)((int32_t)(b << 28) >> 28), hi = (float)((int32_t)(b << 24) >> 28);
       // a 4-bit integer times a bf16 scale is exact in fp32
-      o[i] = f32_to_bf16_bits(lo * s) | (f32_to_bf16_bits(hi * s) << 16);
+      o[i] = bf16x2_bits(lo * s, hi * s);
     }
   } else {
     const float s = __uint_as_float(r.s ? r.s << 23 : 0x00400000u);  // 2^(s - 127)
@@ -113,7 +113,7 @@ MOE_DEV uint4 cvt8(const Raw8& r, float g) {
     for (int i = 0; i < 4; ++i) {
       const uint32_t b = r.q.x >> (i * 8);
       // E2M1 times a power of two is exact in bf16
-      o[i] = f32_to_bf16_bits(e2m1_to_f32(b & 15u) * s) | (f32_to_bf16_bits(e2m1_to_f32((b >> 4) & 15u) * s) << 16);
+      o[i] = bf16x2_bits(e2m1_to_f32(b & 15u) * s, e2m1_to_f32((b >> 4) & 15u) * s);
     }
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
