@@ -254,24 +254,37 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
         }
       }
     if constexpr (!QUANT) {
-      uint16_t* o = static_cast<uint16_t*>(out);
+      // The wave's 16 rows x 128 columns go through its own R slice (free
+      // once the MFMAs above hold their operands; a wave's LDS accesses run
+      // in order) and leave as 16-byte row pieces instead of 2-byte stores.
+      // The INT4 activation order permutes within aligned groups of 8, so
+      // it can be applied to the column within the wave's 128.
+      uint8_t* stg = reinterpret_cast<uint8_t*>(rs[wave]);
+      constexpr int SR = 272;  // staged row stride (bytes), 4 banks apart
 #pragma unroll
       for (int j = 0; j < BPW; ++j)
         if (j < nbw)
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int c = (b0 + j) * 32 + half * 16 + ln;
+            const int c = j * 32 + half * 16 + ln;
             const int col = OUT == OFT_F16_I4 ? i4act_pos(c) : c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int m = lg * 4 + i;
-              if (m < nrows) {
-                const _Float16 hv = (_Float16)acc[j][half][i];
-                o[(int64_t)(r0 + m) * H + col] =
-                    OUT == OFT_BF16 ? (uint16_t)f32_to_bf16_bits(acc[j][half][i]) : __builtin_bit_cast(uint16_t, hv);
-              }
+              const _Float16 hv = (_Float16)acc[j][half][i];
+              *reinterpret_cast<uint16_t*>(stg + (lg * 4 + i) * SR + col * 2) =
+                  OUT == OFT_BF16 ? (uint16_t)f32_to_bf16_bits(acc[j][half][i]) : __builtin_bit_cast(uint16_t, hv);
             }
           }
+      oft_wave_lds_sync();
+      uint16_t* o = static_cast<uint16_t*>(out);
+      const int nparts = nbw * 4;  // 16-byte pieces of a row that this wave holds
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int q = lane + h * 64, row = q >> 4, part = q & 15;
+        if (row < nrows && part < nparts)
+          *reinterpret_cast<uint4*>(o + (int64_t)(r0 + row) * H + b0 * 32 + part * 8) =
+              *reinterpret_cast<const uint4*>(stg + row * SR + part * 16);
+      }
     } else {
       // block maxima per row (the row's 16 lanes share lg), codes into the
       // wave's staging slice qs[wave][row][col - 128 * (b0 / 4)]
