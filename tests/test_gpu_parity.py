@@ -167,10 +167,12 @@ def test_lm_head_logprob_vs_oracle():
     assert np.max(np.abs(lp - ref)) <= 1e-3
 
 
-@pytest.mark.parametrize("T,H,V", [(130, 256, 700), (1, 128, 100), (64, 384, 256), (65, 256, 513)])
+@pytest.mark.parametrize("T,H,V", [(130, 256, 700), (1, 128, 100), (64, 384, 256), (65, 256, 513), (3, 128, 40000),
+                                   (2, 256, 70001)])
 def test_lm_head_blocks_and_edges(T, H, V):
     # several 64-token blocks, a last vocabulary block of 1..255 rows, targets on
-    # block edges; a second call on the same workspace gives the same bits
+    # block edges, vocabularies whose log-softmax parts take more than one pass
+    # of 8192 entries; a second call on the same workspace gives the same bits
     r = np.random.default_rng(T * 1000 + V)
     h = synth._to_bf16_bits((r.standard_normal((T, H)) * 3).astype(np.float32))
     w = synth._to_bf16_bits((r.standard_normal((V, H)) * (4 / np.sqrt(H))).astype(np.float32))
