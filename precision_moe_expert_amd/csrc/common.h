@@ -121,6 +121,34 @@ MOE_DEV void lds_barrier() {
 template <typename T>
 MOE_DEV T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Writes a tile of ROWS rows staged in LDS (row stride LS bytes, RB bytes per
+// row in 16-byte pieces) to global memory: row r goes to g + r * gs, rows at
+// or beyond nrows are skipped.  NT threads share the pieces; each thread
+// reads its pieces in groups of up to GMAX (at most four) before storing
+// them, so the LDS latency is paid once per group rather than once per piece
+// (the outer loop stays rolled to keep the calling kernel's registers down).
+template <int ROWS, int RB, int LS, int NT, int GMAX = 4>
+MOE_DEV void copy_out_rows(const uint8_t* lds, char* g, int64_t gs, int nrows) {
+  constexpr int PPR = RB / 16;
+  constexpr int NP = ROWS * PPR;
+  constexpr int NI = (NP + NT - 1) / NT;
+  constexpr int G = (NI % 4 == 0 && GMAX >= 4) ? 4 : ((NI % 2 == 0 && GMAX >= 2) ? 2 : 1);
+#pragma unroll 1
+  for (int j0 = 0; j0 < NI; j0 += G) {
+    u32x4 v[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int c = min((int)threadIdx.x + (j0 + j) * NT, NP - 1);
+      v[j] = *reinterpret_cast<const u32x4*>(lds + (c / PPR) * LS + (c % PPR) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int c = (int)threadIdx.x + (j0 + j) * NT, row = c / PPR;
+      if (c < NP && row < nrows) *reinterpret_cast<u32x4*>(g + row * gs + (c % PPR) * 16) = v[j];
+    }
+  }
+}
+
 // Maximum of non-negative floats (e.g. |x|) over the 16 lanes of a DPP row
 // (lanes 16r .. 16r+15), returned in every lane of the row: quad swaps
 // (xor 1, xor 2), then row rotations by 4 and 8, register to register.  For

@@ -313,13 +313,8 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         }
       }
     lds_barrier();
-    uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
-    for (int c = threadIdx.x; c < BM * 8; c += FP8_THREADS) {
-      const int row = c >> 3, part = c & 7;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
-    }
+    copy_out_rows<BM, 128, HS, FP8_THREADS>(smem, static_cast<char*>(p.out) + tl.nb * 128 + (int64_t)tl.rbase * p.inter,
+                                            (int64_t)p.inter, tl.nrows);
   } else {
     constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
     lds_barrier();
@@ -336,13 +331,8 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
         }
       }
     lds_barrier();
-    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
-    for (int c = threadIdx.x; c < BM * 32; c += FP8_THREADS) {
-      const int row = c >> 5, part = c & 31;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
-    }
+    copy_out_rows<BM, 512, YS, FP8_THREADS>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 512 + (int64_t)tl.rbase * p.N * 2,
+                                            (int64_t)p.N * 2, tl.nrows);
   }
 }
 

@@ -225,13 +225,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
         }
       }
     lds_barrier();
-    char* H = static_cast<char*>(p.out) + (int64_t)tl.nb * 256;
-    for (int c = threadIdx.x; c < BM * 16; c += 256) {
-      const int row = c >> 4, part = c & 15;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(H + (int64_t)(tl.rbase + row) * p.inter * 2 + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
-    }
+    copy_out_rows<BM, 256, HS, 256, 1>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 256 + (int64_t)tl.rbase * p.inter * 2,
+                                    (int64_t)p.inter * 2, tl.nrows);
   } else {
     constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
 #pragma unroll
@@ -245,13 +240,8 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
               (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
       }
     lds_barrier();
-    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
-    for (int c = threadIdx.x; c < BM * 32; c += 256) {
-      const int row = c >> 5, part = c & 31;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
-    }
+    copy_out_rows<BM, 512, YS, 256, (BM <= 128 ? 4 : 1)>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 512 + (int64_t)tl.rbase * p.N * 2,
+                                    (int64_t)p.N * 2, tl.nrows);
   }
 }
 

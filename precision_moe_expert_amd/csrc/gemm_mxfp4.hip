@@ -230,13 +230,8 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
         if (ln == 0) smem[BM * HS + row * 4 + wave] = (uint8_t)(X + 127);
       }
     lds_barrier();
-    uint8_t* Hq = static_cast<uint8_t*>(p.out) + tl.nb * 128;
-    for (int c = threadIdx.x; c < BM * 8; c += 256) {
-      const int row = c >> 3, part = c & 7;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(Hq + (int64_t)(tl.rbase + row) * p.inter + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * HS + part * 16);
-    }
+    copy_out_rows<BM, 128, HS, 256, 1>(smem, static_cast<char*>(p.out) + tl.nb * 128 + (int64_t)tl.rbase * p.inter,
+                                    (int64_t)p.inter, tl.nrows);
     for (int row = threadIdx.x; row < tl.nrows; row += 256)
       *reinterpret_cast<uint32_t*>(He + (int64_t)(tl.rbase + row) * p.out_scale_stride + tl.nb * 4) =
           *reinterpret_cast<const uint32_t*>(smem + BM * HS + row * 4);
@@ -254,13 +249,8 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
               (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
       }
     lds_barrier();
-    char* Y = static_cast<char*>(p.out) + (int64_t)tl.nb * 512;
-    for (int c = threadIdx.x; c < BM * 32; c += 256) {
-      const int row = c >> 5, part = c & 31;
-      if (row < tl.nrows)
-        *reinterpret_cast<u32x4*>(Y + (int64_t)(tl.rbase + row) * p.N * 2 + part * 16) =
-            *reinterpret_cast<const u32x4*>(smem + row * YS + part * 16);
-    }
+    copy_out_rows<BM, 512, YS, 256, (BM <= 128 ? 4 : 1)>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 512 + (int64_t)tl.rbase * p.N * 2,
+                                    (int64_t)p.N * 2, tl.nrows);
   }
 }
 
