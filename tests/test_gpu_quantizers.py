@@ -4,6 +4,7 @@ code for code and scale for scale, through moe_quantize_activations.
 Rows are built to sit on the quantizers' edges: all-zero blocks (with -0),
 block maxima at exact powers of two and just below them, values that land
 exactly on E4M3 rounding midpoints after scaling (ties to the even code),
+also under scales whose reciprocal is inexact, and one bf16 step off them,
 blocks whose scaled maximum reaches the saturation range [448, 512) of the
 MX shared exponent, tiny values next to large ones (E4M3 subnormals and
 underflow to zero), bf16 subnormals and very large magnitudes.  Both sides
@@ -24,6 +25,12 @@ pytestmark = pytest.mark.gpu
 
 def bf16_bits(v: np.ndarray) -> np.ndarray:
     return synth._to_bf16_bits(np.asarray(v, np.float32))
+
+
+def bf16_neighbour(v: np.ndarray, step: int) -> np.ndarray:
+    """The bf16 value `step` codes from each (bf16-exact, nonzero) value."""
+    b = bf16_bits(v).astype(np.int32) + step
+    return (b.astype(np.uint32) << 16).view(np.float32)
 
 
 def adversarial_rows(H: int, seed: int) -> np.ndarray:
@@ -53,6 +60,15 @@ def adversarial_rows(H: int, seed: int) -> np.ndarray:
     v = v.copy()
     v[::32] = -448.0
     rows.append(v)
+    # the same midpoints under FP8 scales 1.5 and 1.25 (block maxima 672 and
+    # 560), whose reciprocals are inexact, and one bf16 step to either side
+    for sc in (1.5, 1.25):
+        m = (np.concatenate([mids, -mids]) * np.float32(sc)).astype(np.float32)
+        near = np.concatenate([m, bf16_neighbour(m, +1), bf16_neighbour(m, -1)]).astype(np.float32)
+        v = np.resize(near, H).astype(np.float32)
+        v[::32] = np.float32(448.0 * sc)
+        assert np.array_equal(bf16_bits(v).astype(np.uint32) << 16, v.view(np.uint32)), "rows must be bf16 values"
+        rows.append(v)
     # saturation range of the MX exponent: amax mantissa >= 1.75 scales to [448, 512)
     v = r.uniform(-1, 1, H).astype(np.float32)
     v[::32] = 1.9375 * 4
