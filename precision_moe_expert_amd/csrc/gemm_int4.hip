@@ -36,14 +36,21 @@ MOE_DEV f16x8 e2m1x8_to_f16(uint32_t w, f16x2 s2) {
   return r;
 }
 
-// One work item: a BM-row tile times one N block (GEMM1: 128 h columns, i.e.
-// 128 gate + 128 up weight rows; GEMM2: 256 output columns).  NV: NVFP4
-// weights (activations and h in natural order, results times the expert's
-// second-level scale); else INT4 (activations and h in the unpack order).
-template <int BM, bool G1, bool NV>
+// One work item: a BM-row tile times one N block.  Each wave owns NS
+// subtiles of 16 columns: GEMM1 items cover NS*32 h columns (NS*32 gate +
+// NS*32 up weight rows), GEMM2 items NS*64 output columns.  NS = 4, except
+// for the 16-row tiles of decode-sized batches, whose items take NS = 2:
+// there an item streams a weight slice that no other item of its tile
+// shares, and halving it halves the idle time at the end of each launch
+// (a workgroup's last item then ends at most half as late as the others).
+// NV: NVFP4 weights (activations and h in natural order, results times the
+// expert's second-level scale); else INT4 (activations and h in the unpack
+// order).
+template <int BM, bool G1, bool NV, int NS>
 __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
+  static_assert(NS == 4 || (NS == 2 && !NV), "subtiles per wave");
   constexpr int MT = BM / 16;
-  using ST = I4Stage<BM>;
+  using ST = I4Stage<BM, NS>;
   constexpr int S = ST::S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
@@ -51,35 +58,42 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   const char* Abase = static_cast<const char*>(p.a);
   const uint32_t smem0 = lds_u32(smem);
   lds_barrier();  // every wave is done with the previous item's stages
-  int col[4];
+  // subtile i's 16 weight rows start at col[i]; GEMM1: the first NS/2 are
+  // gate rows, the rest the matching up rows (I + the same h columns)
+  int col[NS];
   if (G1) {
-    const int g0 = tl.nb * 128 + wave * 32;
-    col[0] = g0; col[1] = g0 + 16; col[2] = p.inter + g0; col[3] = p.inter + g0 + 16;
-  } else {
-    const int c0 = tl.nb * 256 + wave * 64;
+    const int g0 = tl.nb * (NS * 32) + wave * (NS * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) col[i] = c0 + 16 * i;
+    for (int i = 0; i < NS / 2; ++i) {
+      col[i] = g0 + 16 * i;
+      col[NS / 2 + i] = p.inter + g0 + 16 * i;
+    }
+  } else {
+    const int c0 = tl.nb * (NS * 64) + wave * (NS * 16);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) col[i] = c0 + 16 * i;
   }
   // per-lane global sources of this item's DMA pieces (K offset added per step)
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
   const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * (NV ? 1 : 2);
-  const char* bsrc[4];
+  const char* bsrc[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NS; ++i)
     bsrc[i] = p.w_kblocked ? wexp + (int64_t)(col[i] / 16) * (K / 128) * 1024 + ln * 64 + lg * 16
                            : wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
   const int bstep = p.w_kblocked ? 1024 : 64;  // bytes between K steps of one lane's piece
-  // group scales: INT4 lane l < 32 takes 8 consecutive weight rows (bf16)
-  // of 32-group l/8; NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
-  // bytes) of 16-group l/4.  Either way 16 bytes, 512 per wave and step.
+  // group scales: INT4 lane l < 8*NS takes 8 consecutive weight rows (bf16)
+  // of 32-group l/(2*NS); NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
+  // bytes) of 16-group l/4.  Either way 16 bytes, NS*128 per wave and step.
+  constexpr int PCN = 2 * NS;  // INT4: 16-byte scale pieces per group and wave
   const char* bssrc;
   if constexpr (NV) {
     const int g = (lane >> 2) & 7, pc = lane & 3;
     const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
     bssrc = sexp + (int64_t)g * p.N + c;
   } else {
-    const int g = (lane >> 3) & 3, pc = lane & 7;
-    const int c = G1 ? (pc < 4 ? col[0] + pc * 8 : col[2] + (pc - 4) * 8) : col[0] + pc * 8;
+    const int g = (lane / PCN) & 3, pc = lane % PCN;
+    const int c = G1 ? (pc < NS ? col[0] + pc * 8 : col[NS / 2] + (pc - NS) * 8) : col[0] + pc * 8;
     bssrc = sexp + ((int64_t)g * p.N + c) * 2;
   }
   const char* asrc[ST::NA];
@@ -98,14 +112,15 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b128(bsrc[i] + kt * bstep, sb + ST::B_OFF + (wave * 4 + i) * 1024);
-    if (lane < 32) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * 512);  // 8 N per step either way
+    for (int i = 0; i < NS; ++i) dma_b128(bsrc[i] + kt * bstep, sb + ST::B_OFF + (wave * NS + i) * 1024);
+    // 8 N scale bytes per step either way
+    if (lane < (NV ? 32 : 4 * PCN)) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * (NS * 128));
   };
-  f32x4 acc[MT][4];
+  f32x4 acc[MT][NS];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < NS; ++i) acc[m][i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
   for (int s = 0; s + 1 < S; ++s)
@@ -115,20 +130,21 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     lds_barrier();                                    // ... and every other wave's
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const uint8_t* st = smem + (kt % S) * ST::BYTES;
-    u32x4 bq[4];
-    f16x2 s2[4], s2_16[4];  // NVFP4: the scales of 16-groups 2 lg and 2 lg + 1
+    u32x4 bq[NS];
+    f16x2 s2[NS], s2_16[NS];  // NVFP4: the scales of 16-groups 2 lg and 2 lg + 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * 4 + i) * 1024 + lane * 16);
+    for (int i = 0; i < NS; ++i) {
+      bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * NS + i) * 1024 + lane * 16);
       if constexpr (NV) {
-        const uint8_t* sr = st + ST::BS_OFF + wave * 512 + i * 16 + ln;
+        const uint8_t* sr = st + ST::BS_OFF + wave * (NS * 128) + i * 16 + ln;
         const uint32_t codes = (uint32_t)sr[(2 * lg) * 64] | ((uint32_t)sr[(2 * lg + 1) * 64] << 8);
         const f16x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
         s2[i] = (f16x2){sv[0], sv[0]};
         s2_16[i] = (f16x2){sv[1], sv[1]};
       } else {
-        const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * 512 + lg * 128 +
-                                                               (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
+        const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * (NS * 128) +
+                                                               lg * (PCN * 16) + (2 * i + (ln >> 3)) * 16 +
+                                                               (ln & 7) * 2);
         const _Float16 sh = (_Float16)bf16_bits_to_f32(sw);
         s2[i] = (f16x2){sh, sh};
       }
@@ -143,14 +159,14 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     // read: the scheduling groups below alternate one MFMA with a few VALU
     // instructions, so the unpack hides behind the matrix core instead of
     // preceding it (Kimi-K2 shape: 7.52 -> 7.39 ms of GEMM).
-    auto unpack = [&](int s, f16x8 (&bf)[4]) {
+    auto unpack = [&](int s, f16x8 (&bf)[NS]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NS; ++i)
         bf[i] = NV ? e2m1x8_to_f16(dword_of(bq[i], s), s < 2 ? s2[i] : s2_16[i])
                    : int4x8_to_f16(dword_of(bq[i], s), s2[i]);
     };
     f16x8 af[2][MT];
-    f16x8 bf[2][4];
+    f16x8 bf[2][NS];
 #pragma unroll
     for (int m = 0; m < MT; ++m) af[0][m] = read_a(m, 0);
     unpack(0, bf[0]);
@@ -168,11 +184,11 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[s & 1][i], acc[m][i]);
+        for (int i = 0; i < NS; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[s & 1][i], acc[m][i]);
       if (s + 1 < 4) {
         // one MFMA, then the next sub-step's LDS reads and VALU work between MFMAs
 #pragma unroll
-        for (int j = 0; j < MT * 4; ++j) {
+        for (int j = 0; j < MT * NS; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (j < MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
@@ -191,7 +207,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] *= gs;
+      for (int i = 0; i < NS; ++i) acc[m][i] *= gs;
   }
   lds_barrier();
   if (G1 && p.save_ab) {
@@ -204,61 +220,64 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
         const int row = m * 16 + lg * 4 + i;
         if (row < tl.nrows) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) AB[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = acc[m][n][i];
+          for (int n = 0; n < NS; ++n) AB[(int64_t)(tl.rbase + row) * p.N + col[n] + ln] = acc[m][n][i];
         }
       }
   } else if (G1) {
-    constexpr int HS = 272;  // staged row stride (bytes) of the 128 fp16 h values
+    constexpr int HS = NS * 64 + 16;  // staged row stride (bytes) of the NS*32 fp16 h values
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + lg * 4 + i;
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const float hv = silu_f32(acc[m][n][i]) * acc[m][n + 2][i];
+        for (int n = 0; n < NS / 2; ++n) {
+          const float hv = silu_f32(acc[m][n][i]) * acc[m][n + NS / 2][i];
           const _Float16 hh = (_Float16)hv;
           // h is stored in the activation order that GEMM2's unpack expects
-          const int c = wave * 32 + n * 16 + ln;
+          const int c = wave * (NS * 8) + n * 16 + ln;
           *reinterpret_cast<uint16_t*>(smem + row * HS + (NV ? c : i4act_pos(c)) * 2) =
               __builtin_bit_cast(uint16_t, hh);
         }
       }
     lds_barrier();
-    copy_out_rows<BM, 256, HS, 256, 1>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 256 + (int64_t)tl.rbase * p.inter * 2,
-                                    (int64_t)p.inter * 2, tl.nrows);
+    copy_out_rows<BM, NS * 64, HS, 256, 1>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * (NS * 64) +
+                                                       (int64_t)tl.rbase * p.inter * 2,
+                                           (int64_t)p.inter * 2, tl.nrows);
   } else {
-    constexpr int YS = 528;  // staged row stride (bytes) of the 256 bf16 outputs
+    constexpr int YS = NS * 128 + 16;  // staged row stride (bytes) of the NS*64 bf16 outputs
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + lg * 4 + i;
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * 64 + n * 16 + ln) * 2) =
+        for (int n = 0; n < NS; ++n)
+          *reinterpret_cast<uint16_t*>(smem + row * YS + (wave * (NS * 16) + n * 16 + ln) * 2) =
               (uint16_t)f32_to_bf16_bits(acc[m][n][i]);
       }
     lds_barrier();
-    copy_out_rows<BM, 512, YS, 256, (BM <= 128 ? 4 : 1)>(smem, static_cast<char*>(p.out) + (int64_t)tl.nb * 512 + (int64_t)tl.rbase * p.N * 2,
-                                    (int64_t)p.N * 2, tl.nrows);
+    copy_out_rows<BM, NS * 128, YS, 256, (BM <= 128 ? 4 : 1)>(smem, static_cast<char*>(p.out) +
+                                                                      (int64_t)tl.nb * (NS * 128) +
+                                                                      (int64_t)tl.rbase * p.N * 2,
+                                                              (int64_t)p.N * 2, tl.nrows);
   }
 }
 
 // Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
 // items of chunk p2.chunk (either may be empty), dealt through per-XCD
 // atomic work counters exactly as for the FP8 weights.
-template <int BM, bool NV>
+template <int BM, bool NV, int NS>
 __device__ __forceinline__ void w4_pair(const GemmArgs& p1, const GemmArgs& p2, int32_t* queue) {
-  using ST = I4Stage<BM>;
+  using ST = I4Stage<BM, NS>;
   constexpr int S = ST::S;
   static_assert(S >= 2 && S <= 7, "LDS stages");
   __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
-  static_assert(S * ST::BYTES >= BM * 528, "epilogue staging fits in the stage buffers");
+  static_assert(S * ST::BYTES >= BM * (NS * 128 + 16), "epilogue staging fits in the stage buffers");
   __shared__ int s_item;
   ChunkWork c1, c2;
-  const int n1 = chunk_work(p1, p1.inter / 128, c1) ? c1.nwork : 0;
-  const int n2 = chunk_work(p2, p2.N / 256, c2) ? c2.nwork : 0;
+  const int n1 = chunk_work(p1, p1.inter / (NS * 32), c1) ? c1.nwork : 0;
+  const int n2 = chunk_work(p2, p2.N / (NS * 64), c2) ? c2.nwork : 0;
   const int x = blockIdx.x & 7;
   const int per1 = (n1 + 7) >> 3, per2 = (n2 + 7) >> 3;
   const int b1 = x * per1, b2 = x * per2;
@@ -272,22 +291,22 @@ __device__ __forceinline__ void w4_pair(const GemmArgs& p1, const GemmArgs& p2, 
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) i4_item<BM, true, NV>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
-    else i4_item<BM, false, NV>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (cur < len1) i4_item<BM, true, NV, NS>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else i4_item<BM, false, NV, NS>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;
   }
 }
 
-template <int BM>
+template <int BM, int NS>
 __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
-  w4_pair<BM, false>(p1, p2, queue);
+  w4_pair<BM, false, NS>(p1, p2, queue);
 }
 
 template <int BM>
 __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
-  w4_pair<BM, true>(p1, p2, queue);
+  w4_pair<BM, true, 4>(p1, p2, queue);
 }
 
 // One thread per 16-byte piece of the tiled copy: piece (e, n/16, k/128, row,
@@ -337,13 +356,13 @@ void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* que
 void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent2<k_gemm_int4<16>>(g1, g2, queue, grid, s); break;
-    case 32: launch_persistent2<k_gemm_int4<32>>(g1, g2, queue, grid, s); break;
-    case 64: launch_persistent2<k_gemm_int4<64>>(g1, g2, queue, grid, s); break;
-    case 48: launch_persistent2<k_gemm_int4<48>>(g1, g2, queue, grid, s); break;
-    case 96: launch_persistent2<k_gemm_int4<96>>(g1, g2, queue, grid, s); break;
-    case 128: launch_persistent2<k_gemm_int4<128>>(g1, g2, queue, grid, s); break;
-    default: launch_persistent2<k_gemm_int4<192>>(g1, g2, queue, grid, s); break;
+    case 16: launch_persistent2<k_gemm_int4<16, 2>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_int4<32, 4>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_int4<64, 4>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_int4<48, 4>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_int4<96, 4>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_int4<128, 4>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_int4<192, 4>>(g1, g2, queue, grid, s); break;
   }
 }
 

@@ -41,19 +41,20 @@ MOE_DEV f16x8 int4x8_to_f16(uint32_t w, f16x2 s2) {
 MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; }
 
 // LDS bytes of one pipeline stage: activation rows (256 B = 128 fp16 each,
-// 16-byte parts XOR-swizzled by row), each wave's weight fragments (4
-// subtiles x 1 KB of nibbles) and the bf16 group scales of the wave's 64
-// weight rows for the step's 4 groups (512 B).  Scales are stored
+// 16-byte parts XOR-swizzled by row), each wave's weight fragments (NS
+// subtiles x 1 KB of nibbles) and the bf16 group scales of the wave's NS*16
+// weight rows for the step's 4 groups (NS*128 B).  Scales are stored
 // group-major, so those are 4 (GEMM2) or 8 (GEMM1: gate and up) contiguous
-// runs: 32 lanes x 16 B.  (Per-row scale requests, 64 per wave per step,
-// were measured to cost more time than the weight nibbles themselves.)
-template <int BM>
+// runs of 16-byte pieces, one per lane.  (Per-row scale requests, 64 per
+// wave per step, were measured to cost more time than the weight nibbles
+// themselves.)
+template <int BM, int NS = 4>
 struct I4Stage {
   static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
   static constexpr int A_BYTES = BM * 256;
   static constexpr int B_OFF = A_BYTES;
-  static constexpr int BS_OFF = B_OFF + 4 * 4 * 1024;
-  static constexpr int BYTES = BS_OFF + 4 * 512;
+  static constexpr int BS_OFF = B_OFF + 4 * NS * 1024;
+  static constexpr int BYTES = BS_OFF + 4 * NS * 128;
   // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
   // a second resident workgroup covers one's item start-up and waits; one at
   // 32 rows (a deeper ring wins there) and above 64 rows, where the
@@ -61,7 +62,7 @@ struct I4Stage {
   static constexpr int WPC = (BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
   static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
-  static constexpr int NPER = NA + 4 + 1;             // DMA instructions per wave per stage
+  static constexpr int NPER = NA + NS + 1;            // DMA instructions per wave per stage
 };
 
 // The same 8 codes with one scale per element: sc holds the fp16 pairs
