@@ -109,7 +109,7 @@ typedef struct {
   int32_t top_k;       /* k: 1..min(16, E)                                  */
   int32_t wformat;     /* a moe_wformat value                               */
   int32_t oft_block;   /* 0: no adapter; 32: block-diagonal 32x32 rotation (every weight format) */
-  int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128 or 192 */
+  int32_t tile_rows;   /* rows per grouped-GEMM tile: 0 = automatic, else 16, 32, 48, 64, 96, 128, 160 or 192 */
   int64_t adapter_expert_stride; /* elements between experts' R; 0 = one R shared by all */
   int32_t weight_layout;         /* a moe_wlayout value; other values: MOE_ERR_INVALID_ARGUMENT */
 } moe_layer;

@@ -388,6 +388,7 @@ static void launch_fp8(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, i
     case 48: launch_persistent2<k_gemm_fp8<48, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
     case 96: launch_persistent2<k_gemm_fp8<96, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
     case 128: launch_persistent2<k_gemm_fp8<128, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
+    case 160: launch_persistent2<k_gemm_fp8<160, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
     default: launch_persistent2<k_gemm_fp8<192, P2>, FP8_THREADS>(g1, g2, queue, grid, s); break;
   }
 }

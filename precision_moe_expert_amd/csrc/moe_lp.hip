@@ -53,7 +53,7 @@ moe_status check_layer(const moe_layer* L, Dims* d) {
   if ((int64_t)L->num_tokens * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (L->weight_layout != MOE_WL_ROWS && L->weight_layout != MOE_WL_KBLOCKED) return MOE_ERR_INVALID_ARGUMENT;
   if (L->tile_rows != 0 && L->tile_rows != 16 && L->tile_rows != 32 && L->tile_rows != 48 && L->tile_rows != 64 &&
-      L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 192)
+      L->tile_rows != 96 && L->tile_rows != 128 && L->tile_rows != 160 && L->tile_rows != 192)
     return MOE_ERR_UNSUPPORTED;
   // the GEMMs address activation rows with 32-bit byte offsets
   if ((int64_t)L->num_tokens * L->top_k * (int64_t)(L->hidden > L->inter ? L->hidden : L->inter) * 2 >= (1ll << 32))
@@ -132,7 +132,10 @@ WsLayout layout(const Dims& d) {
 
 // Rows per GEMM tile from the mean rows per expert and the weight format
 // (measured on MI355X: the INT4 unpack favours two workgroups per CU at 64
-// rows; FP8 and MXFP4 favour 128-row tiles once experts have that many rows).
+// rows; FP8 and MXFP4 favour 128-row tiles once experts have that many rows,
+// and FP8 160-row tiles above that: experts of ~256 rows then take two tiles
+// instead of two full ones and a nearly empty third).  A kernel without a
+// 160-row instantiation runs such tiles in its 192-row one.
 int choose_bm(const Dims& d) {
   if (d.tile_rows) return d.tile_rows;
   const int64_t mean = d.R / d.E;
@@ -140,6 +143,7 @@ int choose_bm(const Dims& d) {
   if (mean <= 32) return 32;
   if (d.fmt == MOE_W_INT4_G32_BF16 || d.fmt == MOE_W_NVFP4) return 64;
   if (mean <= 96) return 64;
+  if (d.fmt == MOE_W_FP8_E4M3_B128 && mean > 128) return 160;
   return 128;
 }
 

@@ -139,7 +139,7 @@ def test_backward_max_experts_and_top_k(fmt, oft):
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3, 5])
-@pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
+@pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 160, 192])
 def test_backward_every_tile_height(fmt, tile_rows):
     li = synth.make_inputs(small(T=300, H=512, I=512, E=5, k=4, chunk=2, oft=fmt == 1, cfg_id=250 + fmt, fmt=fmt))
     dout = d_out_of(li.cfg, 6)

@@ -46,7 +46,7 @@ def test_pack_bitexact(fmt):
 
 
 @pytest.mark.parametrize("fmt,oft", [(1, False), (1, True), (2, False), (3, False), (4, False), (5, False)])
-@pytest.mark.parametrize("tile_rows", [16, 32, 64, 128, 192])
+@pytest.mark.parametrize("tile_rows", [16, 32, 64, 128, 160, 192])
 def test_forward_kblocked_equals_rows(fmt, oft, tile_rows):
     cfg = synth.LayerConfig("kblk_fwd", 300 + fmt + (5 if oft else 0), T=150, H=512, E=7, k=3, I=384, fmt=fmt,
                             chunk=3, oft=oft, zipf_alpha=0.8)

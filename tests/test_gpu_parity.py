@@ -202,7 +202,7 @@ def test_t0_is_noop():
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 192])
+@pytest.mark.parametrize("tile_rows", [16, 32, 48, 64, 96, 128, 160, 192])
 def test_forward_every_tile_height(fmt, tile_rows):
     """Each grouped-GEMM tile height against the oracle: ~250 rows per expert,
     so tall tiles run full and ragged; I = 768 gives three 256-wide N blocks."""
