@@ -11,6 +11,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Native 16-byte vector (HIP's uint4 is a union struct whose copies become
 // memcpys through the stack; this one stays in registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define MOE_DEV __device__ __forceinline__

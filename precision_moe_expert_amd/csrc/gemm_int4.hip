@@ -46,15 +46,20 @@ MOE_DEV f16x8 e2m1x8_to_f16(uint32_t w, f16x2 s2) {
 // NV: NVFP4 weights (activations and h in natural order, results times the
 // expert's second-level scale); else INT4 (activations and h in the unpack
 // order).
-template <int BM, bool G1, bool NV, int NS>
+// KS: K per pipeline stage, 128 or (INT4) 64; a stage runs KS/32 MFMA
+// sub-steps of 32 K.
+template <int BM, bool G1, bool NV, int NS, int KS>
 __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
   static_assert(NS == 4 || (NS == 2 && !NV), "subtiles per wave");
+  static_assert(KS == 128 || !NV, "64-K steps take INT4 weights");
   constexpr int MT = BM / 16;
-  using ST = I4Stage<BM, NS>;
+  using ST = I4Stage<BM, NS, KS>;
+  constexpr bool K64 = ST::K64;
+  constexpr int NSUB = KS / 32;
   constexpr int S = ST::S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ln = lane & 15, lg = lane >> 4;
-  const int K = p.K, KT = K / 128;
+  const int K = p.K, KT = K / KS;
   const char* Abase = static_cast<const char*>(p.a);
   const uint32_t smem0 = lds_u32(smem);
   lds_barrier();  // every wave is done with the previous item's stages
@@ -76,12 +81,28 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   // per-lane global sources of this item's DMA pieces (K offset added per step)
   const char* wexp = reinterpret_cast<const char*>(p.w) + tl.e * p.w_expert_bytes;
   const char* sexp = static_cast<const char*>(p.w_scale) + tl.e * p.ws_expert_elems * (NV ? 1 : 2);
-  const char* bsrc[NS];
+  // 128-K steps: DMA i moves subtile i, lane (ln, lg) the 16 bytes (32 K)
+  // that it feeds to the MFMA.  64-K steps: DMA j moves subtiles 2j and
+  // 2j+1, lane L the 16 bytes of row (L/2)%16 holding K [32 q, 32 q + 32),
+  // q = L%2, of subtile 2j + L/32: the fragments of lanes (row, 2q) and
+  // (row, 2q + 1), 8 bytes each.
+  constexpr int NB = K64 ? NS / 2 : NS;
+  const char* bsrc[NB];
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
-    bsrc[i] = p.w_kblocked ? wexp + (int64_t)(col[i] / 16) * (K / 128) * 1024 + ln * 64 + lg * 16
-                           : wexp + (int64_t)(col[i] + ln) * (K / 2) + lg * 16;
-  const int bstep = p.w_kblocked ? 1024 : 64;  // bytes between K steps of one lane's piece
+  for (int i = 0; i < NB; ++i) {
+    const int sub = K64 ? 2 * i + (lane >> 5) : i;
+    const int r = K64 ? (lane >> 1) & 15 : ln;
+    const int part = K64 ? (lane & 1) : lg;
+    const int c = K64 ? ((lane >> 5) ? col[K64 ? 2 * i + 1 : i] : col[K64 ? 2 * i : i]) : col[i];
+    (void)sub;
+    bsrc[i] = p.w_kblocked ? wexp + (int64_t)(c / 16) * (K / 128) * 1024 + r * 64 + part * 16
+                           : wexp + (int64_t)(c + r) * (K / 2) + part * 16;
+  }
+  // bytes from step 0 to step kt of one lane's piece
+  auto boff = [&](int kt) -> int64_t {
+    if (K64) return p.w_kblocked ? (int64_t)(kt >> 1) * 1024 + (kt & 1) * 32 : (int64_t)kt * 32;
+    return (int64_t)kt * (p.w_kblocked ? 1024 : 64);
+  };
   // group scales: INT4 lane l < 8*NS takes 8 consecutive weight rows (bf16)
   // of 32-group l/(2*NS); NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
   // bytes) of 16-group l/4.  Either way 16 bytes, NS*128 per wave and step.
@@ -92,16 +113,18 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
     bssrc = sexp + (int64_t)g * p.N + c;
   } else {
-    const int g = (lane / PCN) & 3, pc = lane % PCN;
+    const int g = (lane / PCN) & (K64 ? 1 : 3), pc = lane % PCN;
     const int c = G1 ? (pc < NS ? col[0] + pc * 8 : col[NS / 2] + (pc - NS) * 8) : col[0] + pc * 8;
     bssrc = sexp + ((int64_t)g * p.N + c) * 2;
   }
   const char* asrc[ST::NA];
 #pragma unroll
   for (int j = 0; j < ST::NA; ++j) {
-    const int c = (wave * ST::NA + j) * 64 + lane;   // activation piece: row c/16, slot c%16
-    const int row = c >> 4, slot = c & 15;
-    const int part = slot ^ (row & 15);              // XOR swizzle of 16-byte parts
+    // activation piece: row c/PPR, slot c%PPR (PPR 16-byte parts per row and step)
+    constexpr int PPR = KS / 8;
+    const int c = (wave * ST::NA + j) * 64 + lane;
+    const int row = c / PPR, slot = c % PPR;
+    const int part = slot ^ (row % PPR);             // XOR swizzle of 16-byte parts
     const int rr = tl.rbase + min(row, tl.nrows - 1);
     const int sr = p.sorted_rows[rr];
     const int src = p.a_per_token ? sr / p.top_k : rr;
@@ -110,11 +133,12 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   auto issue = [&](int kt, int slot) {
     const uint32_t sb = smem0 + slot * ST::BYTES;
 #pragma unroll
-    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * 256, sb + (wave * ST::NA + j) * 1024);
+    for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * (KS * 2), sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) dma_b128(bsrc[i] + kt * bstep, sb + ST::B_OFF + (wave * NS + i) * 1024);
-    // 8 N scale bytes per step either way
-    if (lane < (NV ? 32 : 4 * PCN)) dma_b128(bssrc + (int64_t)kt * 8 * p.N, sb + ST::BS_OFF + wave * (NS * 128));
+    for (int i = 0; i < NB; ++i) dma_b128(bsrc[i] + boff(kt), sb + ST::B_OFF + (wave * NB + i) * 1024);
+    // KS/16 * N scale bytes per step: 8 N for 128 K either way, 4 N for 64 K
+    if (lane < (NV ? 32 : (KS / 32) * PCN))
+      dma_b128(bssrc + (int64_t)kt * (KS / 16) * p.N, sb + ST::BS_OFF + wave * (NS * KS));
   };
   f32x4 acc[MT][NS];
 #pragma unroll
@@ -134,7 +158,13 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     f16x2 s2[NS], s2_16[NS];  // NVFP4: the scales of 16-groups 2 lg and 2 lg + 1
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * NS + i) * 1024 + lane * 16);
+      if constexpr (K64) {
+        const u32x2 b2 = *reinterpret_cast<const u32x2*>(st + ST::B_OFF + (wave * NB + (i >> 1)) * 1024 +
+                                                         ((i & 1) * 32 + ln * 2 + (lg >> 1)) * 16 + (lg & 1) * 8);
+        bq[i] = (u32x4){b2.x, b2.y, 0u, 0u};
+      } else {
+        bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * NS + i) * 1024 + lane * 16);
+      }
       if constexpr (NV) {
         const uint8_t* sr = st + ST::BS_OFF + wave * (NS * 128) + i * 16 + ln;
         const uint32_t codes = (uint32_t)sr[(2 * lg) * 64] | ((uint32_t)sr[(2 * lg + 1) * 64] << 8);
@@ -142,17 +172,21 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
         s2[i] = (f16x2){sv[0], sv[0]};
         s2_16[i] = (f16x2){sv[1], sv[1]};
       } else {
-        const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * (NS * 128) +
-                                                               lg * (PCN * 16) + (2 * i + (ln >> 3)) * 16 +
-                                                               (ln & 7) * 2);
+        // the lane's 32-group: lg of four (128-K steps), lg/2 of two (64-K steps)
+        const uint16_t sw = *reinterpret_cast<const uint16_t*>(st + ST::BS_OFF + wave * (NS * KS) +
+                                                               (K64 ? lg >> 1 : lg) * (PCN * 16) +
+                                                               (2 * i + (ln >> 3)) * 16 + (ln & 7) * 2);
         const _Float16 sh = (_Float16)bf16_bits_to_f32(sw);
         s2[i] = (f16x2){sh, sh};
       }
     }
-    // activation fragment of row block m, 32-K sub-step s: logical part 4*lg + s
+    // activation fragment of row block m, 32-K sub-step s: logical part
+    // NSUB*lg + s (the lane's weight fragment covers K [32 lg, 32 lg + 32) of
+    // a 128-K step, [16 lg, 16 lg + 16) of a 64-K step)
     auto read_a = [&](int m, int s) {
+      constexpr int PPR = KS / 8;
       const int r = m * 16 + ln;
-      return *reinterpret_cast<const f16x8*>(st + r * 256 + (((4 * lg + s) ^ (r & 15)) << 4));
+      return *reinterpret_cast<const f16x8*>(st + r * (KS * 2) + (((NSUB * lg + s) ^ (r % PPR)) << 4));
     };
     // Sub-step s (32 K) runs its MFMAs while the VALU unpacks the weights of
     // sub-step s + 1 and the activation fragments of sub-step s + 1 are
@@ -174,9 +208,9 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     // SIMD's other wave, of the other workgroup, issues behind it)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NSUB; ++s) {
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < 4) {
+      if (s + 1 < NSUB) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) af[(s + 1) & 1][m] = read_a(m, s + 1);
         unpack(s + 1, bf[(s + 1) & 1]);
@@ -185,7 +219,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < NS; ++i) acc[m][i] = mfma_f16_16x16x32(af[s & 1][m], bf[s & 1][i], acc[m][i]);
-      if (s + 1 < 4) {
+      if (s + 1 < NSUB) {
         // one MFMA, then the next sub-step's LDS reads and VALU work between MFMAs
 #pragma unroll
         for (int j = 0; j < MT * NS; ++j) {
@@ -267,9 +301,9 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 // Persistent pair launch: the GEMM1 items of chunk p1.chunk and the GEMM2
 // items of chunk p2.chunk (either may be empty), dealt through per-XCD
 // atomic work counters exactly as for the FP8 weights.
-template <int BM, bool NV, int NS>
+template <int BM, bool NV, int NS, int KS>
 __device__ __forceinline__ void w4_pair(const GemmArgs& p1, const GemmArgs& p2, int32_t* queue) {
-  using ST = I4Stage<BM, NS>;
+  using ST = I4Stage<BM, NS, KS>;
   constexpr int S = ST::S;
   static_assert(S >= 2 && S <= 7, "LDS stages");
   __shared__ __align__(16) uint8_t smem[S * ST::BYTES];
@@ -291,22 +325,23 @@ __device__ __forceinline__ void w4_pair(const GemmArgs& p1, const GemmArgs& p2, 
   while (cur < len1 + len2) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(q, 1) + wpx;  // claimed now, read after the item
-    if (cur < len1) i4_item<BM, true, NV, NS>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
-    else i4_item<BM, false, NV, NS>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
+    if (cur < len1) i4_item<BM, true, NV, NS, KS>(p1, tile_of(p1, c1, b1 + cur, BM), smem);
+    else i4_item<BM, false, NV, NS, KS>(p2, tile_of(p2, c2, b2 + cur - len1, BM), smem);
     if (threadIdx.x == 0) s_item = nxt;
     lds_barrier();
     cur = s_item;
   }
 }
 
-template <int BM, int NS>
-__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_int4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
-  w4_pair<BM, false, NS>(p1, p2, queue);
+template <int BM, int NS, int KS>
+__global__ __launch_bounds__(256, (I4Stage<BM, NS, KS>::WPC)) void k_gemm_int4(GemmArgs p1, GemmArgs p2,
+                                                                            int32_t* queue) {
+  w4_pair<BM, false, NS, KS>(p1, p2, queue);
 }
 
 template <int BM>
 __global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
-  w4_pair<BM, true, 4>(p1, p2, queue);
+  w4_pair<BM, true, 4, 128>(p1, p2, queue);
 }
 
 // One thread per 16-byte piece of the tiled copy: piece (e, n/16, k/128, row,
@@ -356,13 +391,13 @@ void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* que
 void launch_gemm_int4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                            hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent2<k_gemm_int4<16, 2>>(g1, g2, queue, grid, s); break;
-    case 32: launch_persistent2<k_gemm_int4<32, 4>>(g1, g2, queue, grid, s); break;
-    case 64: launch_persistent2<k_gemm_int4<64, 4>>(g1, g2, queue, grid, s); break;
-    case 48: launch_persistent2<k_gemm_int4<48, 4>>(g1, g2, queue, grid, s); break;
-    case 96: launch_persistent2<k_gemm_int4<96, 4>>(g1, g2, queue, grid, s); break;
-    case 128: launch_persistent2<k_gemm_int4<128, 4>>(g1, g2, queue, grid, s); break;
-    default: launch_persistent2<k_gemm_int4<192, 4>>(g1, g2, queue, grid, s); break;
+    case 16: launch_persistent2<k_gemm_int4<16, 2, 128>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_int4<32, 4, 128>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_int4<64, 4, 128>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_int4<48, 4, 128>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_int4<96, 4, 64>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_int4<128, 4, 128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_int4<192, 4, 128>>(g1, g2, queue, grid, s); break;
   }
 }
 

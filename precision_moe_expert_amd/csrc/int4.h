@@ -48,21 +48,30 @@ MOE_DEV uint32_t dword_of(const u32x4& v, int s) { return s == 0 ? v.x : s == 1 
 // runs of 16-byte pieces, one per lane.  (Per-row scale requests, 64 per
 // wave per step, were measured to cost more time than the weight nibbles
 // themselves.)
-template <int BM, int NS = 4>
+//
+// KS = 64 (INT4 only): a stage holds 64 K, i.e. activation rows of 128 B,
+// NS subtiles x 512 B of nibbles and the scales of the step's two groups
+// (NS*64 B) per wave: about half the LDS of a 128-K stage, so that taller
+// tiles keep two workgroups per CU.
+template <int BM, int NS = 4, int KS = 128>
 struct I4Stage {
-  static constexpr int NA = BM / 16;                 // activation DMA groups per wave (4 rows each)
-  static constexpr int A_BYTES = BM * 256;
+  static_assert(KS == 128 || KS == 64, "K step");
+  static constexpr bool K64 = KS == 64;
+  // activation DMA groups per wave (4 rows of 256 B, or 8 rows of 128 B, each)
+  static constexpr int NA = K64 ? (BM + 31) / 32 : BM / 16;
+  static constexpr int A_BYTES = NA * 4 * 1024;
   static constexpr int B_OFF = A_BYTES;
-  static constexpr int BS_OFF = B_OFF + 4 * NS * 1024;
-  static constexpr int BYTES = BS_OFF + 4 * NS * 128;
+  static constexpr int BS_OFF = B_OFF + 4 * NS * (KS * 8);
+  static constexpr int BYTES = BS_OFF + 4 * NS * KS;
   // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
   // a second resident workgroup covers one's item start-up and waits; one at
   // 32 rows (a deeper ring wins there) and above 64 rows, where the
   // activation tile fills the LDS.
-  static constexpr int WPC = (BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
+  static constexpr int WPC = (K64 || BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
   static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
-  static constexpr int NPER = NA + NS + 1;            // DMA instructions per wave per stage
+  // DMA instructions per wave per stage (64-K steps: one per two subtiles)
+  static constexpr int NPER = NA + (K64 ? NS / 2 : NS) + 1;
 };
 
 // The same 8 codes with one scale per element: sc holds the fp16 pairs
