@@ -245,6 +245,8 @@ def kernel_name(cfg, bm, mode):
         return f"k_gemm_fp8<{bm}, {'true' if cfg.fmt == 4 else 'false'}>", None
     if cfg.fmt == 1:  # 16-row tiles take two 16-column subtiles per wave, taller ones four; 96-row tiles 64-K steps
         return f"k_gemm_int4<{bm}, {2 if bm == 16 else 4}, {64 if bm == 96 else 128}>", None
+    if cfg.fmt == 5:  # 96-row tiles take 64-K steps
+        return f"k_gemm_nvfp4<{bm}, {64 if bm == 96 else 128}>", None
     return f"k_gemm_{fmt_name}<{bm}>", None
 
 

@@ -51,7 +51,6 @@ MOE_DEV f16x8 e2m1x8_to_f16(uint32_t w, f16x2 s2) {
 template <int BM, bool G1, bool NV, int NS, int KS>
 __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8_t* smem) {
   static_assert(NS == 4 || (NS == 2 && !NV), "subtiles per wave");
-  static_assert(KS == 128 || !NV, "64-K steps take INT4 weights");
   constexpr int MT = BM / 16;
   using ST = I4Stage<BM, NS, KS>;
   constexpr bool K64 = ST::K64;
@@ -109,7 +108,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   constexpr int PCN = 2 * NS;  // INT4: 16-byte scale pieces per group and wave
   const char* bssrc;
   if constexpr (NV) {
-    const int g = (lane >> 2) & 7, pc = lane & 3;
+    const int g = (lane >> 2) & (K64 ? 3 : 7), pc = lane & 3;
     const int c = G1 ? (pc < 2 ? col[0] + pc * 16 : col[2] + (pc - 2) * 16) : col[0] + pc * 16;
     bssrc = sexp + (int64_t)g * p.N + c;
   } else {
@@ -137,7 +136,7 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma_b128(bsrc[i] + boff(kt), sb + ST::B_OFF + (wave * NB + i) * 1024);
     // KS/16 * N scale bytes per step: 8 N for 128 K either way, 4 N for 64 K
-    if (lane < (NV ? 32 : (KS / 32) * PCN))
+    if (lane < (NV ? KS / 4 : (KS / 32) * PCN))
       dma_b128(bssrc + (int64_t)kt * (KS / 16) * p.N, sb + ST::BS_OFF + wave * (NS * KS));
   };
   f32x4 acc[MT][NS];
@@ -166,8 +165,11 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
         bq[i] = *reinterpret_cast<const u32x4*>(st + ST::B_OFF + (wave * NS + i) * 1024 + lane * 16);
       }
       if constexpr (NV) {
-        const uint8_t* sr = st + ST::BS_OFF + wave * (NS * 128) + i * 16 + ln;
-        const uint32_t codes = (uint32_t)sr[(2 * lg) * 64] | ((uint32_t)sr[(2 * lg + 1) * 64] << 8);
+        // E4M3 scales of the lane's 16-groups: 2 lg and 2 lg + 1 of a 128-K
+        // step (sub-steps 0-1 and 2-3), lg of a 64-K step (both sub-steps)
+        const uint8_t* sr = st + ST::BS_OFF + wave * (NS * KS) + i * 16 + ln;
+        const uint32_t codes = K64 ? (uint32_t)sr[lg * 64]
+                                   : (uint32_t)sr[(2 * lg) * 64] | ((uint32_t)sr[(2 * lg + 1) * 64] << 8);
         const f16x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
         s2[i] = (f16x2){sv[0], sv[0]};
         s2_16[i] = (f16x2){sv[1], sv[1]};
@@ -339,9 +341,10 @@ __global__ __launch_bounds__(256, (I4Stage<BM, NS, KS>::WPC)) void k_gemm_int4(G
   w4_pair<BM, false, NS, KS>(p1, p2, queue);
 }
 
-template <int BM>
-__global__ __launch_bounds__(256, I4Stage<BM>::WPC) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2, int32_t* queue) {
-  w4_pair<BM, true, 4, 128>(p1, p2, queue);
+template <int BM, int KS>
+__global__ __launch_bounds__(256, (I4Stage<BM, 4, KS>::WPC)) void k_gemm_nvfp4(GemmArgs p1, GemmArgs p2,
+                                                                               int32_t* queue) {
+  w4_pair<BM, true, 4, KS>(p1, p2, queue);
 }
 
 // One thread per 16-byte piece of the tiled copy: piece (e, n/16, k/128, row,
@@ -378,13 +381,13 @@ void launch_pack_kblocked(const uint8_t* w, int E, int N, int K, bool bytes, uin
 void launch_gemm_nvfp4_pair(const GemmArgs& g1, const GemmArgs& g2, int32_t* queue, int bm, int grid,
                             hipStream_t s) {
   switch (bm) {
-    case 16: launch_persistent2<k_gemm_nvfp4<16>>(g1, g2, queue, grid, s); break;
-    case 32: launch_persistent2<k_gemm_nvfp4<32>>(g1, g2, queue, grid, s); break;
-    case 64: launch_persistent2<k_gemm_nvfp4<64>>(g1, g2, queue, grid, s); break;
-    case 48: launch_persistent2<k_gemm_nvfp4<48>>(g1, g2, queue, grid, s); break;
-    case 96: launch_persistent2<k_gemm_nvfp4<96>>(g1, g2, queue, grid, s); break;
-    case 128: launch_persistent2<k_gemm_nvfp4<128>>(g1, g2, queue, grid, s); break;
-    default: launch_persistent2<k_gemm_nvfp4<192>>(g1, g2, queue, grid, s); break;
+    case 16: launch_persistent2<k_gemm_nvfp4<16, 128>>(g1, g2, queue, grid, s); break;
+    case 32: launch_persistent2<k_gemm_nvfp4<32, 128>>(g1, g2, queue, grid, s); break;
+    case 64: launch_persistent2<k_gemm_nvfp4<64, 128>>(g1, g2, queue, grid, s); break;
+    case 48: launch_persistent2<k_gemm_nvfp4<48, 128>>(g1, g2, queue, grid, s); break;
+    case 96: launch_persistent2<k_gemm_nvfp4<96, 64>>(g1, g2, queue, grid, s); break;
+    case 128: launch_persistent2<k_gemm_nvfp4<128, 128>>(g1, g2, queue, grid, s); break;
+    default: launch_persistent2<k_gemm_nvfp4<192, 128>>(g1, g2, queue, grid, s); break;
   }
 }
 

@@ -134,7 +134,8 @@ WsLayout layout(const Dims& d) {
 // (measured on MI355X: the INT4 unpack favours two workgroups per CU at 64
 // rows, and at 96 rows with 64-K stages, which cost about 8% less per row,
 // where those pad an expert's rows less than 64-row tiles do; NVFP4 takes
-// 64; FP8 and MXFP4 favour 128-row tiles once experts have that many rows,
+// the 96-row, 64-K tiles above 64 rows (the DeepSeek-V3 Zipf shape: 4%
+// faster than 64); FP8 and MXFP4 favour 128-row tiles once experts have that many rows,
 // and FP8 160-row tiles above that: experts of ~256 rows then take two tiles
 // instead of two full ones and a nearly empty third).  A kernel without a
 // 160-row instantiation runs such tiles in its 192-row one.
@@ -147,7 +148,7 @@ int choose_bm(const Dims& d) {
     const int64_t p64 = (mean + 63) / 64 * 64, p96 = (mean + 95) / 96 * 96;  // padded rows
     return p96 * 12 < p64 * 13 ? 96 : 64;
   }
-  if (d.fmt == MOE_W_NVFP4) return 64;
+  if (d.fmt == MOE_W_NVFP4) return mean > 64 ? 96 : 64;
   if (mean <= 96) return 64;
   if (d.fmt == MOE_W_FP8_E4M3_B128 && mean > 128) return 160;
   return 128;
