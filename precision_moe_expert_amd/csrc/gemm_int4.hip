@@ -89,11 +89,16 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
   const char* bsrc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int sub = K64 ? 2 * i + (lane >> 5) : i;
-    const int r = K64 ? (lane >> 1) & 15 : ln;
-    const int part = K64 ? (lane & 1) : lg;
-    const int c = K64 ? ((lane >> 5) ? col[K64 ? 2 * i + 1 : i] : col[K64 ? 2 * i : i]) : col[i];
-    (void)sub;
+    int c, r, part;  // first weight row of the subtile, row in it, 16-byte part of its 64-byte K block
+    if constexpr (K64) {
+      c = (lane >> 5) ? col[2 * i + 1] : col[2 * i];
+      r = (lane >> 1) & 15;
+      part = lane & 1;
+    } else {
+      c = col[i];
+      r = ln;
+      part = lg;
+    }
     bsrc[i] = p.w_kblocked ? wexp + (int64_t)(c / 16) * (K / 128) * 1024 + r * 64 + part * 16
                            : wexp + (int64_t)(c + r) * (K / 2) + part * 16;
   }
@@ -102,9 +107,10 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
     if (K64) return p.w_kblocked ? (int64_t)(kt >> 1) * 1024 + (kt & 1) * 32 : (int64_t)kt * 32;
     return (int64_t)kt * (p.w_kblocked ? 1024 : 64);
   };
-  // group scales: INT4 lane l < 8*NS takes 8 consecutive weight rows (bf16)
-  // of 32-group l/(2*NS); NVFP4 lane l < 32 takes 16 consecutive rows (E4M3
-  // bytes) of 16-group l/4.  Either way 16 bytes, NS*128 per wave and step.
+  // group scales: INT4 lane l < (KS/32)*2*NS takes 8 consecutive weight rows
+  // (bf16) of 32-group l/(2*NS); NVFP4 lane l < KS/4 takes 16 consecutive
+  // rows (E4M3 bytes) of 16-group l/4.  Either way 16 bytes, NS*KS per wave
+  // and step.
   constexpr int PCN = 2 * NS;  // INT4: 16-byte scale pieces per group and wave
   const char* bssrc;
   if constexpr (NV) {
