@@ -167,6 +167,23 @@ MOE_DEV float row16_max_nonneg(float v) {
   x = max(x, dpp_i32<0x128>(x));  // row_ror:8
   return __int_as_float(x);
 }
+// The same for four values, the four reductions interleaved so that no DPP
+// read directly follows the write of its operand (no wait states between).
+MOE_DEV void row16_max_nonneg4(float (&v)[4]) {
+  int x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __float_as_int(v[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = max(x[i], dpp_i32<0xB1>(x[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = max(x[i], dpp_i32<0x4E>(x[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = max(x[i], dpp_i32<0x124>(x[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = max(x[i], dpp_i32<0x128>(x[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __int_as_float(x[i]);
+}
 
 // Position of element n inside the INT4-path activation layout: every aligned
 // group of 8 fp16 values is stored in the order [0,4,1,5,2,6,3,7], matching

@@ -17,10 +17,14 @@
 
 namespace moe {
 
-MOE_DEV float floor_log2_pos_mx(float a) {
-  const uint32_t b = __float_as_uint(a);
-  const int ef = (int)(b >> 23);
-  return ef > 0 ? (float)(ef - 127) : (float)((31 - __builtin_clz(b & 0x7FFFFFu)) - 149);
+// MXFP8 shared exponent of a block with maximum magnitude am:
+// X = floor(log2(am)) - 8 clamped to [-127, 127], 0 when am = 0 (or NaN).
+// For a normal am, floor(log2(am)) is its biased exponent minus 127; a
+// subnormal am (exponent field 0) gives X <= -135 and clamps to -127, which
+// the exponent field gives too; the largest exponent field (255: inf) gives
+// X = 120, so the upper clamp never applies.
+MOE_DEV int mx_shared_exp(float am) {
+  return am > 0.0f ? max((int)(__float_as_uint(am) >> 23) - 135, -127) : 0;
 }
 
 // LDS bytes of one pipeline stage: activation rows (128 B of E4M3 codes each,
@@ -209,26 +213,28 @@ __device__ __forceinline__ void mx_item(const GemmArgs& p, const Tile& tl, uint8
     uint8_t* He = static_cast<uint8_t*>(p.out_scale);
     lds_barrier();
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+      float h0[4], h1[4], am[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float h0 = silu_f32(acc[m][0][i]) * acc[m][2][i];
-        const float h1 = silu_f32(acc[m][1][i]) * acc[m][3][i];
-        // this wave's 32 h columns of the row are one MXFP8 block
-        const float am = row16_max_nonneg(fmaxf(fabsf(h0), fabsf(h1)));
-        int X = 0;
-        if (am > 0.0f) {
-          X = (int)floor_log2_pos_mx(am) - 8;
-          X = X < -127 ? -127 : (X > 127 ? 127 : X);
-        }
-        const float mul = (-X >= -126) ? __uint_as_float((uint32_t)(-X + 127) << 23) : __uint_as_float(0x00400000u);
+        h0[i] = silu_f32(acc[m][0][i]) * acc[m][2][i];
+        h1[i] = silu_f32(acc[m][1][i]) * acc[m][3][i];
+        am[i] = fmaxf(fabsf(h0[i]), fabsf(h1[i]));
+      }
+      // this wave's 32 h columns of a row are one MXFP8 block
+      row16_max_nonneg4(am);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int X = mx_shared_exp(am[i]);
+        const float mul = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, X in [-127, 120]
         const int row = m * 16 + lg * 4 + i;
-        const uint32_t c2 = cvt_e4m3x2(h0 * mul, h1 * mul);
+        const uint32_t c2 = cvt_e4m3x2(h0[i] * mul, h1[i] * mul);
         smem[row * HS + wave * 32 + ln] = (uint8_t)(c2 & 0xFF);
         smem[row * HS + wave * 32 + 16 + ln] = (uint8_t)(c2 >> 8);
         // the row's four block scales (one per wave) are staged as one dword
         if (ln == 0) smem[BM * HS + row * 4 + wave] = (uint8_t)(X + 127);
       }
+    }
     lds_barrier();
     copy_out_rows<BM, 128, HS, 256, 1>(smem, static_cast<char*>(p.out) + tl.nb * 128 + (int64_t)tl.rbase * p.inter,
                                     (int64_t)p.inter, tl.nrows);
