@@ -203,6 +203,11 @@ MOE_DEV uint32_t lds_u32(const void* p) {
 MOE_DEV void dma_b128(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
 }
+// The same for data read once (non-temporal: streamed past the caches'
+// normal allocation), e.g. weight slices that no other work item reads.
+MOE_DEV void dma_b128_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
 MOE_DEV void dma_b32(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
 }

@@ -140,7 +140,11 @@ __device__ __forceinline__ void i4_item(const GemmArgs& p, const Tile& tl, uint8
 #pragma unroll
     for (int j = 0; j < ST::NA; ++j) dma_b128(asrc[j] + kt * (KS * 2), sb + (wave * ST::NA + j) * 1024);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma_b128(bsrc[i] + boff(kt), sb + ST::B_OFF + (wave * NB + i) * 1024);
+    for (int i = 0; i < NB; ++i) {
+      // a 16-row tile's weight slice is read by no other item: non-temporal
+      if constexpr (BM == 16) dma_b128_nt(bsrc[i] + boff(kt), sb + ST::B_OFF + (wave * NB + i) * 1024);
+      else dma_b128(bsrc[i] + boff(kt), sb + ST::B_OFF + (wave * NB + i) * 1024);
+    }
     // KS/16 * N scale bytes per step: 8 N for 128 K either way, 4 N for 64 K
     if (lane < (NV ? KS / 4 : (KS / 32) * PCN))
       dma_b128(bssrc + (int64_t)kt * (KS / 16) * p.N, sb + ST::BS_OFF + wave * (NS * KS));
