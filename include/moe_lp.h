@@ -348,9 +348,10 @@ moe_status moe_quantize_activations(const moe_layer* layer, const void* x_bf16, 
 moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const float* topk_w,
                        const int32_t* row_of, void* out_bf16, void* stream);
 
-/* Workspace bytes moe_lm_head_logprob needs: 2*T*V fp32 partial logits (two
- * K slices) and T*4*3 fp32 log-softmax statistics of four vocabulary parts,
- * each 256-byte aligned. */
+/* Workspace bytes moe_lm_head_logprob needs: T*ceil(V/128)*2 fp32
+ * log-softmax statistics (maximum and sum of exponentials per token and
+ * block of 128 vocabulary rows) and T fp32 target logits, each 256-byte
+ * aligned. */
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V);
 
 /* Log-prob of target tokens under an LM head (the rollout log-probs whose

@@ -182,12 +182,11 @@ inline void launch_persistent2(const GemmArgs& a, const GemmArgs& b, int32_t* q,
 
 void launch_combine(const uint16_t* y, const float* w, const int32_t* row_of, int T, int k, int H, uint16_t* out,
                     hipStream_t s);
-// LM head: K slices of the GEMM (2) and vocabulary parts of the
-// log-softmax; workspace = slices x T x V fp32 partial logits and
-// T x parts x 3 fp32 part statistics.
-int lm_head_slices(int H);
-int lm_head_parts();
+// LM head: per (token, block of 128 vocabulary rows) log-softmax statistics
+// (maximum, sum of exponentials: T x blocks x 2 fp32) and the target logits
+// (T fp32), then the per-token merge.
+int lm_head_blocks(int V);
 void launch_lm_head(const uint16_t* h, const uint16_t* wlm, const int32_t* targets, int T, int H, int V,
-                    float* part_ws, float* stats_ws, float* logprob, hipStream_t s);
+                    float* stats_ws, float* tz_ws, float* logprob, hipStream_t s);
 
 }  // namespace moe

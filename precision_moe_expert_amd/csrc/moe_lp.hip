@@ -1002,8 +1002,8 @@ moe_status moe_combine(const moe_layer* layer, const void* y_perm_bf16, const fl
 
 size_t moe_lm_head_workspace_bytes(int32_t T, int32_t V) {
   if (T < 0 || V <= 0) return 0;
-  // room for two K slices of partial logits (the most lm_head_slices returns)
-  return align_up((size_t)2 * T * (size_t)V * 4) + align_up((size_t)T * lm_head_parts() * 3 * 4);
+  // per (token, vocabulary block) maximum and sum of exponentials, then the target logits
+  return align_up((size_t)T * lm_head_blocks(V) * 2 * 4) + align_up((size_t)T * 4);
 }
 
 
@@ -1017,10 +1017,10 @@ moe_status moe_lm_head_logprob(int32_t T, int32_t H, int32_t V, const void* h_bf
     if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   if (ws_bytes < moe_lm_head_workspace_bytes(T, V)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   char* base = static_cast<char*>(ws);
-  float* part = reinterpret_cast<float*>(base);
-  float* stats = reinterpret_cast<float*>(base + align_up((size_t)2 * T * (size_t)V * 4));
+  float* stats = reinterpret_cast<float*>(base);
+  float* tz = reinterpret_cast<float*>(base + align_up((size_t)T * lm_head_blocks(V) * 2 * 4));
   launch_lm_head(static_cast<const uint16_t*>(h_bf16), static_cast<const uint16_t*>(w_lm_bf16), targets, T, H, V,
-                 part, stats, logprob, static_cast<hipStream_t>(stream));
+                 stats, tz, logprob, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

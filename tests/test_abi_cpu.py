@@ -55,7 +55,8 @@ def test_workspace_sizes():
     assert n >= R * 2048 * 2 + R * 768 + 4096 * 2048  # y + h + x codes
     assert binding.workspace_bytes(L, 1) == n          # independent of the chunk size
     assert binding.workspace_bytes(binding.make_layer(4096, 2048, 768, 128, 8, 9), 16) == 0
-    assert binding.lib().moe_lm_head_workspace_bytes(64, 32000) >= 64 * 32000 * 4
+    # LM head: (max, sum of exponentials) per token and 128-row vocabulary block, then the target logits
+    assert binding.lib().moe_lm_head_workspace_bytes(64, 32000) == 64 * 250 * 2 * 4 + 256
 
 
 FAKE = 1 << 20  # aligned non-null address; never dereferenced because validation fails first
