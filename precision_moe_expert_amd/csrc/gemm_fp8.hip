@@ -163,19 +163,37 @@ __device__ __forceinline__ void fp8_item(const GemmArgs& p, const Tile& tl, uint
       // activation scale) and 2^ew (the weight block's) exactly, so the
       // partials accumulate directly
       const int ew0 = e8m0_of_pow2(wc0), ew2 = e8m0_of_pow2(wc2);
+      auto read_a2 = [&](int m, i32x8& af, int& ea) {
+        const int r = (mb0 + m) * 16 + ln;
+        const uint8_t* arow = st + r * 128;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
+        af = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        ea = e8m0_of_pow2(As[r * 4]);
+      };
+      // row block m + 1's operands are read while block m's MFMAs issue, one
+      // LDS read between two MFMAs (as in the MXFP4 kernel)
+      i32x8 af[2];
+      int ea[2];
+      read_a2(0, af[0], ea[0]);
 #pragma unroll
       for (int m = 0; m < MTW; ++m)
         if (m < nmb) {
-          const int r = (mb0 + m) * 16 + ln;
-          const uint8_t* arow = st + r * 128;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + ((lg ^ (r & 7)) << 4));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + (((lg + 4) ^ (r & 7)) << 4));
-          const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          const int ea = e8m0_of_pow2(As[r * 4]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m + 1 < nmb) read_a2(m + 1, af[(m + 1) & 1], ea[(m + 1) & 1]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[m][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[i], acc[m][i], 0, 0, 0, ea, 0,
-                                                                          i < 2 ? ew0 : ew2);
+            acc[m][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m & 1], bf[i], acc[m][i], 0, 0, 0,
+                                                                          ea[m & 1], 0, i < 2 ? ew0 : ew2);
+          if (m + 1 < nmb) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
     } else {
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
