@@ -63,11 +63,14 @@ struct I4Stage {
   static constexpr int B_OFF = A_BYTES;
   static constexpr int BS_OFF = B_OFF + 4 * NS * (KS * 8);
   static constexpr int BYTES = BS_OFF + 4 * NS * KS;
-  // Workgroups per CU (measured on MI355X): two at 16, 48 and 64 rows, where
-  // a second resident workgroup covers one's item start-up and waits; one at
-  // 32 rows (a deeper ring wins there) and above 64 rows, where the
-  // activation tile fills the LDS.
-  static constexpr int WPC = (K64 || BM == 16 || BM == 48 || BM == 64) ? 2 : 1;
+  // Workgroups per CU (measured on MI355X): two at 16 (four subtiles), 48
+  // and 64 rows and with 64-K stages, where a second resident workgroup
+  // covers one's item start-up and waits; three at 16 rows with two
+  // subtiles (INT4 decode: more items start and end at different times, 2%
+  // faster than two with deeper rings); one at 32 rows (a deeper ring wins
+  // there) and above 64 rows with 128-K stages, where the activation tile
+  // fills the LDS.
+  static constexpr int WPC = (BM == 16 && NS == 2) ? 3 : ((K64 || BM == 16 || BM == 48 || BM == 64) ? 2 : 1);
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
   static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
   // DMA instructions per wave per stage (64-K steps: one per two subtiles)
