@@ -72,7 +72,11 @@ struct I4Stage {
   // fills the LDS.
   static constexpr int WPC = (BM == 16 && NS == 2) ? 3 : ((K64 || BM == 16 || BM == 48 || BM == 64) ? 2 : 1);
   static constexpr int SMAX = BM <= 32 ? 7 : 5;
-  static constexpr int S = (152 * 1024 / WPC) / BYTES > SMAX ? SMAX : (152 * 1024 / WPC) / BYTES;  // stages
+  // LDS for the rings: 152 KB of the CU's 160, or all but 256 B per
+  // workgroup with three of them (four 13-KB decode stages each: 2% faster
+  // than three)
+  static constexpr int LDS = WPC == 3 ? 160 * 1024 - 3 * 256 : 152 * 1024;
+  static constexpr int S = (LDS / WPC) / BYTES > SMAX ? SMAX : (LDS / WPC) / BYTES;  // stages
   // DMA instructions per wave per stage (64-K steps: one per two subtiles)
   static constexpr int NPER = NA + (K64 ? NS / 2 : NS) + 1;
 };
