@@ -256,8 +256,70 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
   }
 }
 
+// The same selection with one token per wave (few tokens: decode): lane l
+// keeps experts l, l + 64, ... (SLOTS of them, E <= 64 SLOTS), and each
+// round's maximum is the 16-lane row maximum followed by two cross-row
+// exchanges.  The keys and their order are those above, so both kernels
+// select the same experts in the same order.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void k_route_topk_wave(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves only
+  const float* row = logits + (int64_t)t * E;
+  uint64_t key[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? (((uint64_t)float_key(row[e]) << 32) | (uint64_t)(0xFFFFu - e)) : 0ull;
+  }
+  float sel_val[MAX_TOPK];
+  int sel_id[MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MAX_TOPK; ++j) {
+    if (j < k) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) best = key[i] > best ? key[i] : best;
+      best = row16_max_u64(best);
+#pragma unroll
+      for (int x = 16; x < 64; x <<= 1) {
+        const uint32_t lo = (uint32_t)shfl_xor((int)(uint32_t)best, x);
+        const uint32_t hi = (uint32_t)shfl_xor((int)(uint32_t)(best >> 32), x);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+      }
+      sel_id[j] = 0xFFFF - (int)(best & 0xFFFFu);
+      sel_val[j] = key_float((uint32_t)(best >> 32));
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i)
+        if (key[i] == best) key[i] = 0;
+    }
+  }
+  float z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < MAX_TOPK; ++j)
+    if (j < k) z += expf(sel_val[j] - sel_val[0]);
+#pragma unroll
+  for (int j = 0; j < MAX_TOPK; ++j)
+    if (j < k && lane == j) {
+      ids[(int64_t)t * k + j] = sel_id[j];
+      w[(int64_t)t * k + j] = expf(sel_val[j] - sel_val[0]) / z;
+    }
+}
+
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return;
+  if (T <= 1024 && E > 64) {  // few tokens: one per wave, fewer slots per lane
+    const dim3 g((T + 3) / 4), b(256);
+    if (E <= 128) hipLaunchKernelGGL(k_route_topk_wave<2>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 256) hipLaunchKernelGGL(k_route_topk_wave<4>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 384) hipLaunchKernelGGL(k_route_topk_wave<6>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 512) hipLaunchKernelGGL(k_route_topk_wave<8>, g, b, 0, s, logits, T, E, k, ids, w);
+    else hipLaunchKernelGGL(k_route_topk_wave<16>, g, b, 0, s, logits, T, E, k, ids, w);
+    return;
+  }
   const dim3 g((T + 15) / 16), b(256);
   if (E <= 64) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, T, E, k, ids, w);
   else if (E <= 128) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, T, E, k, ids, w);
