@@ -228,16 +228,27 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ row_of) {
   __shared__ int32_t cnt[MAX_EXPERTS];
   const int lane = lane_id();
+  const int p0 = blockIdx.x * PAIRS_PER_BLOCK;
+  // every id of the block is requested, together with the block's scatter
+  // bases, before the first ranking step (one memory round trip per block
+  // instead of one per 64 pairs)
+  constexpr int NC = PAIRS_PER_BLOCK / 64;
+  int eid[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int p = p0 + c * 64 + lane;
+    eid[c] = p < R ? ids[p] : 0;
+  }
   for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int p0 = blockIdx.x * PAIRS_PER_BLOCK;
-  for (int c = 0; c < PAIRS_PER_BLOCK; c += 64) {
-    const int p = p0 + c + lane;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int p = p0 + c * 64 + lane;
     const bool valid = p < R;
-    const int e = valid ? ids[p] : 0;
+    const int e = eid[c];
     uint64_t m = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       uint64_t bb = __ballot(valid && ((e >> b) & 1));
