@@ -97,6 +97,13 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, i
   for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
+// Orders one wave's LDS accesses before and after it (no other wave waits).
+MOE_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Exclusive scan, over the 1024 threads of the block, of four independent
 // ints per thread: a shuffle scan inside each wave, then each thread adds the
 // totals of the waves before it (two barriers instead of twenty per scan).
@@ -130,19 +137,35 @@ MOE_DEV i32x4 block_excl_scan4_1024(i32x4 v, i32x4* sh, i32x4* total) {
 // contiguous ranges: thread (g, e) sums range g of expert e's column (all
 // loads of a range in flight together), the experts' totals are scanned with
 // thread = expert, and each thread then writes the bases of its range.
+//
+// ONE: all pairs form a single block (few tokens: decode).  The same
+// workgroup then also counts them (LDS histogram, in place of k_hist) and
+// scatters them (wave 0, the ranking of k_scatter with the expert offsets
+// as its counters), so the permutation takes one launch instead of three.
+template <bool ONE>
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int bm_a,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                int32_t* __restrict__ num_active, int32_t* __restrict__ tile_a,
                                                int32_t* __restrict__ tile_16, int32_t* __restrict__ tile_desc,
-                                               int32_t* __restrict__ queue, int nqueue) {
+                                               int32_t* __restrict__ queue, int nqueue,
+                                               const int32_t* __restrict__ ids, int R,
+                                               int32_t* __restrict__ sorted_rows, int32_t* __restrict__ row_of) {
   __shared__ i32x4 sh4[16];
   __shared__ int s_tstart[MAX_EXPERTS + 1], s_exp[MAX_EXPERTS], s_off[MAX_EXPERTS], s_cnt[MAX_EXPERTS];
   __shared__ int s_part[1024], s_base[MAX_EXPERTS];
+  __shared__ int s_hist[ONE ? MAX_EXPERTS : 1];
   const int G = 1024 / E;
   const int tid = threadIdx.x;
   const int g = tid / E, ce = tid - g * E;  // this thread's range and column (g < G)
   const int b0 = (int)((int64_t)nblk * g / G), b1 = (int)((int64_t)nblk * (g + 1) / G);
-  if (g < G) {
+  if constexpr (ONE) {
+    for (int e = tid; e < E; e += 1024) s_hist[e] = 0;
+    __syncthreads();
+    for (int q = tid; q < R; q += 1024) atomicAdd(&s_hist[ids[q]], 1);  // counting only: order-independent
+    __syncthreads();
+    // the one block sits in exactly one range
+    if (g < G) s_part[tid] = b0 < b1 ? s_hist[ce] : 0;
+  } else if (g < G) {
     int sum = 0;
     for (int b = b0; b < b1; b += 16) {
       int h[16];
@@ -187,9 +210,41 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   }
   for (int i = threadIdx.x; i < nqueue; i += blockDim.x) queue[i] = 0;  // GEMM work-queue counters
   __syncthreads();
-  // scatter bases of this thread's range: the expert's offset, the ranges
-  // before it, then the blocks before it within the range
-  if (g < G) {
+  if constexpr (ONE) {
+    // stable scatter of the block's pairs by wave 0 (k_scatter's ranking);
+    // the other waves go on to the tile descriptors
+    if (tid < 64) {
+      const int lane = tid;
+      constexpr int NC = PAIRS_PER_BLOCK / 64;
+      int eid[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) eid[c] = c * 64 + lane < R ? ids[c * 64 + lane] : 0;
+      int nbits = 0;
+      while ((1 << nbits) < E) ++nbits;
+      const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int q = c * 64 + lane;
+        const bool valid = q < R;
+        const int e = eid[c];
+        uint64_t m = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+          const uint64_t bb = __ballot(valid && ((e >> b) & 1));
+          m &= ((e >> b) & 1) ? bb : ~bb;
+        }
+        const int pos = valid ? s_base[e] + __popcll(m & lt_mask) : 0;
+        wave_lds_sync();  // every lane has read its counter before any is advanced
+        if (valid) {
+          sorted_rows[pos] = q;
+          row_of[q] = pos;
+          if ((m >> lane) == 1ull) s_base[e] = pos + 1;  // highest lane of the group advances the counter
+        }
+        wave_lds_sync();
+      }
+    }
+  } else if (g < G) {
+    // scatter bases of this thread's range: the expert's offset, the ranges
+    // before it, then the blocks before it within the range
     int base = s_base[ce];
     for (int q = 0; q < g; ++q) base += s_part[q * E + ce];
     for (int b = b0; b < b1; b += 16) {
@@ -344,9 +399,14 @@ void launch_permute(const int32_t* ids, int R, int E, int bm_a, int32_t* hist, i
                     int32_t* sorted_rows, int32_t* row_of, int32_t* active, int32_t* num_active, int32_t* tile_a,
                     int32_t* tile_16, int32_t* tile_desc, int32_t* queue, int nqueue, hipStream_t s) {
   const int nblk = (R + PAIRS_PER_BLOCK - 1) / PAIRS_PER_BLOCK;
+  if (nblk == 1) {  // one launch: histogram, scan and scatter in one workgroup
+    hipLaunchKernelGGL(k_scan<true>, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active,
+                       tile_a, tile_16, tile_desc, queue, nqueue, ids, R, sorted_rows, row_of);
+    return;
+  }
   if (nblk > 0) hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(256), 0, s, ids, R, E, hist);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active, tile_a,
-                     tile_16, tile_desc, queue, nqueue);
+  hipLaunchKernelGGL(k_scan<false>, dim3(1), dim3(1024), 0, s, hist, nblk, E, bm_a, offsets, active, num_active,
+                     tile_a, tile_16, tile_desc, queue, nqueue, ids, R, sorted_rows, row_of);
   if (nblk > 0) hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(64), 0, s, ids, R, E, hist, sorted_rows, row_of);
 }
 
