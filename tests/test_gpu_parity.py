@@ -47,7 +47,9 @@ def test_route_bitexact_configs(name):
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (5, 4, 4), (300, 130, 16), (2049, 1024, 8), (4099, 64, 1),
                                    (20000, 8, 2), (9000, 384, 8),
                                    # up to 1024 tokens and more than 64 experts take one token per wave
-                                   (700, 1024, 16), (64, 512, 8), (1024, 257, 8), (1025, 257, 8), (3, 65, 16)])
+                                   (700, 1024, 16), (64, 512, 8), (1024, 257, 8), (1025, 257, 8), (3, 65, 16),
+                                   # up to 512 pairs the permutation runs in one workgroup (one launch)
+                                   (64, 384, 8), (65, 384, 8), (32, 384, 16), (1, 1024, 16)])
 def test_route_bitexact_edge(T, E, k):
     r = np.random.default_rng(T * 7 + E)
     lg = r.standard_normal((T, E)).astype(np.float32)
