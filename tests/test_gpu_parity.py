@@ -83,6 +83,18 @@ def test_forward_int4_oft_small(oft):
     gu.check_rows(out, ref, li.cfg.fmt, f"oft {oft}")
 
 
+@pytest.mark.parametrize("T,fmt", [(64, 1), (65, 1), (64, 4), (65, 4)])
+def test_forward_across_one_block_permutation(T, fmt):
+    """64 tokens x top-8 = 512 pairs take the one-workgroup permutation, 65
+    tokens (520 pairs) the histogram / scan / scatter launches; the whole
+    layer (OFT on the INT4 base) must match the oracle on both sides."""
+    cfg = small(fmt, T=T, H=256, I=256, E=40, k=8, oft=fmt == 1, chunk=8, cfg_id=90 + T + fmt)
+    li = synth.make_inputs(cfg)
+    d = gu.DevInputs(li)
+    out = gu.bf16_to_np(d.forward())
+    gu.check_rows(out, oracle.forward_inputs(li), li.cfg.fmt, f"T {T} fmt {fmt}")
+
+
 def test_forward_int4_oft_partial_block_chunk():
     """H = 1280: 40 diagonal blocks, so the rotation's second 32-block item
     has blocks for one wave only (8), and 16-row groups are ragged."""
