@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
                                              const int32_t* __restrict__ sorted_rows,
                                              const int32_t* __restrict__ active,
                                              const int32_t* __restrict__ num_active,
-                                             const int32_t* __restrict__ tile16, void* __restrict__ out,
+                                             const int32_t* __restrict__ tile16,
+                                             const int32_t* __restrict__ desc16, void* __restrict__ out,
                                              void* __restrict__ out_scale, int scale_stride) {
   constexpr int BPW = 4;  // diagonal blocks per wave and item
   constexpr bool QUANT = OUT == OFT_FP8 || OUT == OFT_FP8_POW2 || OUT == OFT_MXFP8;
@@ -202,17 +203,27 @@ __global__ __launch_bounds__(256) void k_oft(const uint16_t* __restrict__ x, con
   const int64_t nitems = (int64_t)ngroups * nbc;
   for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {
     const int gi = (int)(it / nbc), bc = (int)(it - (int64_t)gi * nbc);
-    int lo = 0, hi = na - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_t16[mid] <= gi) lo = mid; else hi = mid - 1;
-    }
     const int b0 = (bc * 4 + wave) * BPW;
     const int nbw = min(BPW, nb - b0);  // <= 0: no blocks for this wave
     if (nbw <= 0) continue;
-    const int e = active[lo];
-    const int r0 = offsets[e] + (gi - s_t16[lo]) * 16;
-    const int nrows = min(16, offsets[e + 1] - r0);
+    int e, r0, nrows;
+    if (desc16 != nullptr) {
+      // the group's descriptor {expert, first row, rows, active index}: one
+      // load instead of the search and the expert / offset loads after it
+      const i32x4 dd = *reinterpret_cast<const i32x4*>(desc16 + 4 * (int64_t)gi);
+      e = dd[0];
+      r0 = dd[1];
+      nrows = dd[2];
+    } else {
+      int lo = 0, hi = na - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_t16[mid] <= gi) lo = mid; else hi = mid - 1;
+      }
+      e = active[lo];
+      r0 = offsets[e] + (gi - s_t16[lo]) * 16;
+      nrows = min(16, offsets[e + 1] - r0);
+    }
     const int tok = sorted_rows[r0 + min(ln, nrows - 1)] / k;
     const uint16_t* xrow = x + (int64_t)tok * H;
     const uint4* src = reinterpret_cast<const uint4*>(R + (int64_t)e * r_stride + (int64_t)b0 * 1024);
@@ -373,12 +384,13 @@ void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, 
 }
 void launch_oft(int out_fmt, const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                 const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
-                const int32_t* tile16, void* out, void* out_scale, int scale_stride, hipStream_t s) {
+                const int32_t* tile16, const int32_t* desc16, void* out, void* out_scale, int scale_stride,
+                hipStream_t s) {
   switch (out_fmt) {
 #define MOE_OFT_CASE(F)                                                                                              \
     case F:                                                                                                          \
       hipLaunchKernelGGL(k_oft<F>, dim3(1024), dim3(256), 0, s, x, R, r_expert_stride, H, k, offsets, sorted_rows, \
-                         active, num_active, tile16, out, out_scale, scale_stride);                                  \
+                         active, num_active, tile16, desc16, out, out_scale, scale_stride);                          \
       break;
     MOE_OFT_CASE(OFT_F16_I4)
     MOE_OFT_CASE(OFT_BF16)
@@ -395,14 +407,14 @@ void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_strid
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                     const int32_t* num_active, const int32_t* tile16, int E, uint16_t* out, hipStream_t s) {
   (void)E;
-  launch_oft(OFT_F16_I4, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, out, nullptr,
+  launch_oft(OFT_F16_I4, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, nullptr, out, nullptr,
              0, s);
 }
 
 void launch_oft_bf16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                      const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,
                      const int32_t* num_active, const int32_t* tile16, uint16_t* out, hipStream_t s) {
-  launch_oft(OFT_BF16, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, out, nullptr, 0,
+  launch_oft(OFT_BF16, x, R, r_expert_stride, H, k, offsets, sorted_rows, active, num_active, tile16, nullptr, out, nullptr, 0,
              s);
 }
 

@@ -86,7 +86,8 @@ void launch_act_mxfp8(const uint16_t* x, int T, int H, uint8_t* q, uint8_t* e8, 
 // out_scale rows of scale_stride bytes (quantized formats).
 void launch_oft(int out_fmt, const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                 const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active, const int32_t* num_active,
-                const int32_t* tile16, void* out, void* out_scale, int scale_stride, hipStream_t s);
+                const int32_t* tile16, const int32_t* desc16, void* out, void* out_scale, int scale_stride,
+                hipStream_t s);
 // OFT rotation of every permuted row into the INT4-path activation layout.
 void launch_oft_f16(const uint16_t* x, const uint16_t* R, int64_t r_expert_stride, int H, int k,
                     const int32_t* offsets, const int32_t* sorted_rows, const int32_t* active,

@@ -384,8 +384,10 @@ moe_status forward_impl(const moe_layer* layer, const void* x_bf16, const float*
   {
   Scope sc_(tm, MOE_STAGE_ACT);
   if (d.oft) {
+    // with 16-row GEMM tiles the tile descriptors are the rotation's row groups
     launch_oft(oft_out_format(d), x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H,
-               d.k, offsets, sorted_rows, active, num_active, tile_16, act, act_scale, scale_row_bytes(d.H), s);
+               d.k, offsets, sorted_rows, active, num_active, tile_16, bm == 16 ? tiles : nullptr, act, act_scale,
+               scale_row_bytes(d.H), s);
   } else if (d.fmt == MOE_W_INT4_G32_BF16) {
     launch_act_f16(x, d.T, d.H, static_cast<uint16_t*>(act), s);
   } else if (d.fmt == MOE_W_NVFP4) {
@@ -837,7 +839,8 @@ moe_status backward_impl(const moe_layer* layer, const void* x_bf16, const float
   // the forward's GEMM1 input
   if (d.oft)
     launch_oft(oft_out_format(d), x, static_cast<const uint16_t*>(adapter_bf16), layer->adapter_expert_stride, d.H,
-               d.k, offsets, sorted_rows, active, num_active, tile_16, act, act_scale, scale_row_bytes(d.H), s);
+               d.k, offsets, sorted_rows, active, num_active, tile_16, nullptr, act, act_scale, scale_row_bytes(d.H),
+               s);
   else if (d.fmt == MOE_W_FP8_E4M3_B128)
     launch_act_fp8(x, d.T, d.H, static_cast<uint8_t*>(act), static_cast<float*>(act_scale), scale_row_bytes(d.H),
                    d.pow2, s);
